@@ -1,0 +1,21 @@
+"""Row-major FP32 GEMM for AMD Instinct MI355X (gfx950).
+
+``C = alpha * A @ B + beta * C`` on row-major operands with leading
+dimensions, computed by hand-written HIP kernels in ``libsgemm_rm.so`` behind
+a C ABI (``include/sgemm_rm.h``).  The Python side only marshals arguments.
+"""
+from .binding import (  # noqa: F401
+    SGEMM_RM_VARIANT_AUTO,
+    SGEMM_RM_VARIANT_LDS_TILED,
+    SGEMM_RM_VARIANT_MFMA,
+    SGEMM_RM_VARIANT_NAIVE,
+    SGEMM_RM_VARIANT_REGBLOCK,
+    VARIANTS,
+    SgemmError,
+    library_path,
+    load_library,
+    sgemm,
+    sgemm_rm,
+    sgemm_rm_ex,
+    sgemm_rm_strerror,
+)

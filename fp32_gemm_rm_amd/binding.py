@@ -1,0 +1,123 @@
+"""ctypes binding of ``libsgemm_rm.so`` (declared in ``include/sgemm_rm.h``).
+
+Argument marshalling only: every step of the GEMM runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current HIP stream.  The
+library is loaded on first use and its absence is an error: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+SGEMM_RM_VARIANT_AUTO = 0
+SGEMM_RM_VARIANT_NAIVE = 1
+SGEMM_RM_VARIANT_LDS_TILED = 2
+SGEMM_RM_VARIANT_REGBLOCK = 3
+SGEMM_RM_VARIANT_MFMA = 4
+VARIANTS = {
+    "auto": SGEMM_RM_VARIANT_AUTO,
+    "naive": SGEMM_RM_VARIANT_NAIVE,
+    "lds_tiled": SGEMM_RM_VARIANT_LDS_TILED,
+    "regblock": SGEMM_RM_VARIANT_REGBLOCK,
+    "mfma": SGEMM_RM_VARIANT_MFMA,
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libsgemm_rm.so"
+_lib = None
+
+#: Names the header declares; the CPU tests check that the library exports each.
+EXPORTED_SYMBOLS = ("sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strerror", "sgemm_rm_version")
+
+
+class SgemmError(RuntimeError):
+    """A nonzero return code of the library."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"sgemm_rm error {code}: {message}")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def load_library():
+    """Load the built library (torch first, so that its HIP runtime is the one in use)."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (loads torch's HIP runtime before the library binds to one)
+
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        args = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+                ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        lib.sgemm_rm.argtypes = args
+        lib.sgemm_rm.restype = ctypes.c_int
+        lib.sgemm_rm_ex.argtypes = args + [ctypes.c_int]
+        lib.sgemm_rm_ex.restype = ctypes.c_int
+        lib.sgemm_rm_strerror.argtypes = [ctypes.c_int]
+        lib.sgemm_rm_strerror.restype = ctypes.c_char_p
+        lib.sgemm_rm_version.argtypes = []
+        lib.sgemm_rm_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def sgemm_rm_strerror(code: int) -> str:
+    return load_library().sgemm_rm_strerror(int(code)).decode()
+
+
+def _check(code: int) -> int:
+    if code != 0:
+        raise SgemmError(code, sgemm_rm_strerror(code))
+    return code
+
+
+def sgemm_rm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0):
+    """C := alpha*A*B + beta*C on raw device pointers (ints); raises SgemmError on failure."""
+    lib = load_library()
+    return _check(lib.sgemm_rm(int(M), int(N), int(K), float(alpha), A or None, int(lda), B or None,
+                               int(ldb), float(beta), C or None, int(ldc), stream or None))
+
+
+def sgemm_rm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0, variant=SGEMM_RM_VARIANT_AUTO):
+    """As ``sgemm_rm`` with the kernel family forced; raises SgemmError on failure."""
+    lib = load_library()
+    return _check(lib.sgemm_rm_ex(int(M), int(N), int(K), float(alpha), A or None, int(lda), B or None,
+                                  int(ldb), float(beta), C or None, int(ldc), stream or None, int(variant)))
+
+
+def _matrix_view(t, name):
+    import torch
+
+    if t.dtype != torch.float32 or t.dim() != 2 or not t.is_cuda:
+        raise TypeError(f"{name} must be a 2-D float32 device tensor")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    if rows > 1 and ld < max(cols, 1):
+        raise ValueError(f"{name} rows overlap (stride(0) = {ld} < {cols} columns)")
+    return t.data_ptr(), ld
+
+
+def sgemm(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, stream=None):
+    """C := alpha*A@B + beta*C in place on 2-D float32 device tensors (row-major views,
+    leading dimension = stride(0)), on torch's current stream unless ``stream`` is given."""
+    import torch
+
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    a, lda = _matrix_view(A, "A")
+    b, ldb = _matrix_view(B, "B")
+    c, ldc = _matrix_view(C, "C")
+    s = (stream if stream is not None else torch.cuda.current_stream(C.device)).cuda_stream
+    return sgemm_rm_ex(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, s, variant)

@@ -1,0 +1,97 @@
+/*
+ * sgemm_rm.h: row-major single-precision GEMM on AMD Instinct MI355X (gfx950).
+ *
+ *     C := alpha * A * B + beta * C
+ *
+ * A is M x K, B is K x N and C is M x N, all float32 and row-major with
+ * leading dimensions: element (i, j) of X lives at X[i*ldX + j].  This is the
+ * operation defined at the top of "Deep dive into the sgemmNN algorithm"
+ * (lazypool-blog; C = alpha*A*B + beta*C, A is m x k, B is k x n, C is
+ * m x n), with the row-major indexing of the one-thread-per-element kernels
+ * in m.lqnn.cn/news/94381 section 1.1 and "GPU-accelerated matrix computation
+ * optimisation and CUDA programming practice" section 3.1, and the lda / ldb /
+ * ldc arguments of the sgemmNN kernel's signature.
+ *
+ * Ownership: the caller owns every buffer.  A, B and C are device pointers
+ * (hipMalloc'd or equivalent, e.g. a PyTorch tensor's data pointer on the
+ * current device).  The library never allocates, frees or retains them and
+ * writes only the M x N window of C: columns N..ldc-1 of C are never touched,
+ * and A and B are only read within their logical M x K and K x N windows.
+ * C must not overlap A or B.
+ *
+ * Streams: every call only enqueues work on `stream` (0 = the null stream)
+ * and returns; the caller synchronises.  Calls are reentrant; the library
+ * keeps no state beyond cached device properties.
+ *
+ * Special cases (BLAS convention; the pages say nothing about them):
+ *   - M == 0 or N == 0: nothing is launched.
+ *   - alpha == 0 or K == 0: C := beta * C and A, B are not read (they may be
+ *     NULL); with beta == 1 nothing is launched.
+ *   - beta == 0: C is written without being read, so NaN or Inf in the
+ *     initial C does not reach the result.
+ *
+ * Results match the definition within
+ *     |C_gpu(i,j) - C(i,j)| <= 1e-5 * sum_k |A(i,k)| |B(k,j)| + 1e-6;
+ * the summation order is fixed per variant and shape, so repeated calls with
+ * the same inputs are bitwise identical.
+ *
+ * Return value: 0 on success.  A negative value -p names the first invalid
+ * argument by its 1-based position p (checked before any HIP call):
+ *   -1 M < 0          -2 N < 0            -3 K < 0
+ *   -5 A == NULL while A is read          -6 lda < max(1, K)
+ *   -7 B == NULL while B is read          -8 ldb < max(1, N)
+ *   -10 C == NULL while M*N > 0           -11 ldc < max(1, N)
+ *   -13 (sgemm_rm_ex only) unknown variant
+ * A positive value is the hipError_t reported by the HIP runtime for the
+ * launch (the analogue of checking cudaGetLastError after a launch that the
+ * mlqm.cn/news/1180856 troubleshooting table, section 7, recommends).
+ */
+#ifndef SGEMM_RM_H
+#define SGEMM_RM_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Kernel families, in the order the pages build them up. */
+enum sgemm_rm_variant {
+  SGEMM_RM_VARIANT_AUTO = 0,      /* library's choice for the shape (MFMA + edge path) */
+  SGEMM_RM_VARIANT_NAIVE = 1,     /* one thread per C element, m.lqnn.cn/news/94381 section 1.1 */
+  SGEMM_RM_VARIANT_LDS_TILED = 2, /* LDS tiles, 128-bit loads, zero-filled edges, padded rows:
+                                     m.lqnn.cn/news/94381 sections 2-5 */
+  SGEMM_RM_VARIANT_REGBLOCK = 3,  /* register-blocked, double-buffered LDS pipeline:
+                                     "GEMM advanced: ILP and bank conflicts" (mhpn.cn) section 2-3,
+                                     and the sgemmNN page's register blocking */
+  SGEMM_RM_VARIANT_MFMA = 4       /* FP32 matrix-core tiles for full tiles, scalar edge-tile path
+                                     for ragged M/N; ragged K handled inside every tile */
+};
+
+/*
+ * C := alpha*A*B + beta*C (row-major, leading dimensions), asynchronously on
+ * `stream`, with the library's choice of kernels for the shape.
+ */
+int sgemm_rm(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb,
+             float beta, float* C, int ldc, hipStream_t stream);
+
+/*
+ * As sgemm_rm, with the kernel family forced (enum sgemm_rm_variant).  Every
+ * variant accepts every valid shape, leading dimension and 4-byte-aligned
+ * pointer; 128-bit global loads are used only where the base pointers and the
+ * leading dimensions keep them 16-byte aligned.
+ */
+int sgemm_rm_ex(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb,
+                float beta, float* C, int ldc, hipStream_t stream, int variant);
+
+/* Static, NUL-terminated description of a return code of the calls above. */
+const char* sgemm_rm_strerror(int code);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int sgemm_rm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_RM_H */
