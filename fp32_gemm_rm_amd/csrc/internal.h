@@ -1,0 +1,56 @@
+// Internal declarations shared by the kernels and the dispatcher of libsgemm_rm.
+// Device code here targets gfx950 only (64-lane wavefronts, 160 KiB LDS per CU,
+// FP32 MFMA).  Nothing in this directory is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm_impl {
+
+// One GEMM problem as the kernels see it.  Leading dimensions are 64-bit so that
+// every offset i*ld + j is computed without 32-bit overflow.
+struct Problem {
+  int M, N, K;
+  float alpha, beta;
+  const float* A;
+  long long lda;
+  const float* B;
+  long long ldb;
+  float* C;
+  long long ldc;
+};
+
+// Sub-problem covering rows [m0, m0+rows) and columns [n0, n0+cols) of C.
+inline Problem sub_problem(const Problem& p, int m0, int n0, int rows, int cols) {
+  Problem q = p;
+  q.M = rows;
+  q.N = cols;
+  q.A = p.A + (long long)m0 * p.lda;
+  q.B = p.B + n0;
+  q.C = p.C + (long long)m0 * p.ldc + n0;
+  return q;
+}
+
+// True when 128-bit loads along rows of X (base pointer x, leading dimension ld)
+// stay 16-byte aligned: the base is 16-byte aligned and ld is a multiple of 4.
+inline bool vec4_ok(const void* x, long long ld) {
+  return ((uintptr_t)x % 16 == 0) && (ld % 4 == 0);
+}
+
+// Launchers.  Each enqueues its kernel(s) on `stream` and returns the launch status.
+// Every launcher accepts any M, N >= 1 and K >= 1 and any leading dimensions.
+hipError_t launch_naive(const Problem& p, hipStream_t stream);
+hipError_t launch_lds_tiled(const Problem& p, hipStream_t stream);
+hipError_t launch_regblock(const Problem& p, hipStream_t stream);
+// Small-tile register-blocked kernel with bounds checks: the edge-tile path of the
+// MFMA variant, also usable on its own for thin problems.
+hipError_t launch_edge(const Problem& p, hipStream_t stream);
+hipError_t launch_mfma(const Problem& p, hipStream_t stream);
+// C := beta*C on the M x N window (zeros when beta == 0; C is then not read).
+hipError_t launch_scale(const Problem& p, hipStream_t stream);
+
+// Largest grid the launchers use (one-dimensional grids).
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+}  // namespace sgemm_impl

@@ -1,0 +1,64 @@
+// Naive SGEMM: one thread per element of C, reading A and B straight from
+// global memory (m.lqnn.cn/news/94381 section 1.1; "GPU-accelerated matrix
+// computation ..." section 3.1; mlqm.cn/news/1180856 section 4.1).
+//
+// gfx950 mapping: a workgroup is 64 x 4 threads, so one 64-lane wavefront
+// covers 64 consecutive columns of one row.  Its B loads B[k*ldb + j] are one
+// contiguous 256-byte segment per k and its A load A[i*lda + k] is the same
+// address for the whole wavefront (a broadcast).  The kernel's limit is reuse,
+// not coalescing: every k-step moves 2 floats per 2 FLOP.
+#include "internal.h"
+
+namespace sgemm_impl {
+namespace {
+
+constexpr int kNaiveCols = 64;  // one wavefront across columns
+constexpr int kNaiveRows = 4;
+
+__global__ __launch_bounds__(kNaiveCols* kNaiveRows) void naive_kernel(Problem p, int col_blocks) {
+  const int bm = blockIdx.x / col_blocks;
+  const int bn = blockIdx.x - bm * col_blocks;
+  const int i = bm * kNaiveRows + threadIdx.y;
+  const int j = bn * kNaiveCols + threadIdx.x;
+  if (i >= p.M || j >= p.N) return;
+  const float* a = p.A + (long long)i * p.lda;
+  const float* b = p.B + j;
+  float acc = 0.0f;
+  for (int k = 0; k < p.K; ++k) acc = fmaf(a[k], b[(long long)k * p.ldb], acc);
+  float* c = p.C + (long long)i * p.ldc + j;
+  *c = (p.beta == 0.0f) ? p.alpha * acc : fmaf(p.alpha, acc, p.beta * *c);
+}
+
+// C := beta*C (zeros when beta == 0, without reading C).  One thread per element.
+__global__ __launch_bounds__(256) void scale_kernel(float* C, long long ldc, int M, int N, float beta,
+                                                    int col_blocks) {
+  const int bm = blockIdx.x / col_blocks;
+  const int bn = blockIdx.x - bm * col_blocks;
+  const int i = bm * 4 + threadIdx.y;
+  const int j = bn * 64 + threadIdx.x;
+  if (i >= M || j >= N) return;
+  float* c = C + (long long)i * ldc + j;
+  *c = (beta == 0.0f) ? 0.0f : beta * *c;
+}
+
+}  // namespace
+
+hipError_t launch_naive(const Problem& p, hipStream_t stream) {
+  const long long cb = (p.N + kNaiveCols - 1) / kNaiveCols;
+  const long long rb = (p.M + kNaiveRows - 1) / kNaiveRows;
+  if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(naive_kernel, dim3((unsigned)(cb * rb)), dim3(kNaiveCols, kNaiveRows), 0, stream, p,
+                     (int)cb);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale(const Problem& p, hipStream_t stream) {
+  const long long cb = (p.N + 63) / 64;
+  const long long rb = (p.M + 3) / 4;
+  if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)(cb * rb)), dim3(64, 4), 0, stream, p.C, p.ldc, p.M, p.N,
+                     p.beta, (int)cb);
+  return hipGetLastError();
+}
+
+}  // namespace sgemm_impl

@@ -1,0 +1,255 @@
+"""GPU parity: every kernel family against the CPU oracle, through the C ABI.
+
+Small and mid-size workloads (256^3, 1024^3, the ragged 1000 x 1030 x 999 with
+padded leading dimensions) are compared element by element; 4096^3 and
+8192^3 are compared on sampled entries (whole rows and columns at tile
+boundaries plus random entries) in the launch configuration the benchmark
+times.  Closed forms that float32 must reproduce exactly are compared bit for
+bit.
+"""
+import numpy as np
+import pytest
+
+from fp32_gemm_rm_amd.workloads import (
+    C_PAD_SENTINEL,
+    WORKLOAD_BY_NAME,
+    integer_matrix,
+    make_inputs,
+    pad_rows,
+    workload_inputs,
+)
+
+from .parity import assert_within_bound, c_window, check_padding, device, run_gemm
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = {"naive": 1, "lds_tiled": 2, "regblock": 3, "mfma": 4, "auto": 0}
+SMALL = ["sgemm_256", "sgemm_1024", "sgemm_ragged_1000x1030x999"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp32_gemm_rm_amd import load_library
+
+    load_library()
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_full(oracle, name, variant):
+    w = WORKLOAD_BY_NAME[name]
+    print(f"[parity] {name} variant={variant}", flush=True)
+    A, B, C = workload_inputs(w)
+    out = run_gemm(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, VARIANTS[variant])
+    ref, S = oracle.full(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc)
+    r = assert_within_bound(c_window(out, w.M, w.N, w.ldc), ref, S, f"{name}/{variant}")
+    check_padding(out, C, w.M, w.N, w.ldc)
+    print(f"[parity] {name} variant={variant} max err/bound {r:.3g}", flush=True)
+
+
+def _sample_entries(M, N, seed, n_random=4096):
+    rng = np.random.default_rng(seed)
+    rows = [rng.integers(0, M, n_random)]
+    cols = [rng.integers(0, N, n_random)]
+    for r in sorted({0, 63, 64, 127, 128, M // 2, M - 129, M - 1}):
+        rows.append(np.full(N, r))
+        cols.append(np.arange(N))
+    for c in sorted({0, 31, 32, 127, 128, N // 2, N - 1}):
+        rows.append(np.arange(M))
+        cols.append(np.full(M, c))
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+@pytest.mark.parametrize("name", ["sgemm_4096", "sgemm_8192"])
+def test_workload_sampled(oracle, name):
+    """Full-size workloads on the default (benchmarked) path, checked at sampled entries."""
+    w = WORKLOAD_BY_NAME[name]
+    print(f"[parity] {name} sampled", flush=True)
+    A, B, C = workload_inputs(w)
+    out = run_gemm(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, 0)
+    rows, cols = _sample_entries(w.M, w.N, seed=w.seed)
+    ref, S = oracle.entries(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, rows, cols)
+    got = c_window(out, w.M, w.N, w.ldc)[rows, cols]
+    r = assert_within_bound(got, ref, S, name)
+    assert np.all(np.isfinite(c_window(out, w.M, w.N, w.ldc)))
+    print(f"[parity] {name} sampled max err/bound {r:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_integer_exact_full_size(oracle, variant):
+    """Integer inputs at 4096^3 make every summation order exact: sampled entries bit-exact."""
+    M = N = K = 4096 if variant in ("mfma", "auto", "regblock") else 1024
+    a = integer_matrix(M, K, -4, 4, seed=41)
+    b = integer_matrix(K, N, -4, 4, seed=42)
+    A, B = a.reshape(-1), b.reshape(-1)
+    C = np.full(M * N, np.nan, np.float32)
+    out = run_gemm(M, N, K, 1.0, A, K, B, N, 0.0, C, N, VARIANTS[variant])
+    rows, cols = _sample_entries(M, N, seed=43, n_random=2048)
+    ref, _ = oracle.entries(M, N, K, 1.0, A, K, B, N, 0.0, C, N, rows, cols)
+    got = out.reshape(M, N)[rows, cols].astype(np.float64)
+    np.testing.assert_array_equal(got, ref)
+
+
+EDGE_DIMS = [1, 2, 3, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def _edge_shapes():
+    rng = np.random.default_rng(2024)
+    shapes = {(d, d, d) for d in (1, 17, 64, 129, 257)}
+    while len(shapes) < 40:
+        shapes.add(tuple(int(x) for x in rng.choice(EDGE_DIMS, 3)))
+    return sorted(shapes)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_edge_shapes_integer_exact(oracle, variant):
+    """Ragged shapes around tile sizes, integer inputs: bit-exact against the oracle,
+    with NaN in A/B padding and a sentinel in C padding."""
+    for t, (M, N, K) in enumerate(_edge_shapes()):
+        lda, ldb, ldc = K + (t % 5), N + (t % 3), N + 1 + (t % 4)
+        a = integer_matrix(M, K, -4, 4, seed=500 + t)
+        b = integer_matrix(K, N, -4, 4, seed=600 + t)
+        c = integer_matrix(M, N, -4, 4, seed=700 + t)
+        A, B, C = pad_rows(a, lda, np.nan), pad_rows(b, ldb, np.nan), pad_rows(c, ldc, C_PAD_SENTINEL)
+        out = run_gemm(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, VARIANTS[variant])
+        ref, _ = oracle.full(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc)
+        got = c_window(out, M, N, ldc).astype(np.float64)
+        assert np.array_equal(got, ref), f"shape {(M, N, K)} lds {(lda, ldb, ldc)} variant {variant}"
+        check_padding(out, C, M, N, ldc)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_edge_shapes_random_bound(oracle, variant):
+    """Ragged random shapes with alpha = 1.5, beta = -0.5 within the bound."""
+    for t, (M, N, K) in enumerate(_edge_shapes()[::3]):
+        lda, ldb, ldc = K + 3, N + 2, N + 1
+        A, B, C = make_inputs(M, N, K, lda, ldb, ldc, "normal", seed=800 + t, c_init="random")
+        out = run_gemm(M, N, K, 1.5, A, lda, B, ldb, -0.5, C, ldc, VARIANTS[variant])
+        ref, S = oracle.full(M, N, K, 1.5, A, lda, B, ldb, -0.5, C, ldc)
+        assert_within_bound(c_window(out, M, N, ldc), ref, S, f"{(M, N, K)}/{variant}")
+        check_padding(out, C, M, N, ldc)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_closed_forms(variant):
+    v = VARIANTS[variant]
+    # identity: A = I gives C = B bit for bit
+    M = K = 192
+    N = 200
+    eye = pad_rows(np.eye(M, K, dtype=np.float32), K + 4, np.nan)
+    _, B, C = make_inputs(M, N, K, K + 4, N + 4, N + 4, "normal", seed=9, c_init="nan")
+    out = run_gemm(M, N, K, 1.0, eye, K + 4, B, N + 4, 0.0, C, N + 4, v)
+    np.testing.assert_array_equal(c_window(out, M, N, N + 4), B.reshape(K, N + 4)[:, :N])
+    # all ones: C = K exactly, and 1.5K - 0.5 with beta = -0.5, C = 1
+    M, N, K = 130, 250, 777
+    ones_a = np.ones(M * K, np.float32)
+    ones_b = np.ones(K * N, np.float32)
+    out = run_gemm(M, N, K, 1.0, ones_a, K, ones_b, N, 0.0, np.full(M * N, np.nan, np.float32), N, v)
+    np.testing.assert_array_equal(out.reshape(M, N), np.full((M, N), K, np.float32))
+    out = run_gemm(M, N, K, 1.5, ones_a, K, ones_b, N, -0.5, np.ones(M * N, np.float32), N, v)
+    np.testing.assert_array_equal(out.reshape(M, N), np.full((M, N), 1.5 * K - 0.5, np.float32))
+    # rank one: K = 1 gives fl(a_i * b_j) bit for bit
+    M, N, K = 300, 257, 1
+    A, B, C = make_inputs(M, N, K, 1, N, N, "normal", seed=10, c_init="nan")
+    out = run_gemm(M, N, K, 1.0, A, 1, B, N, 0.0, C, N, v)
+    np.testing.assert_array_equal(out.reshape(M, N), np.outer(A[:M], B[:N]).astype(np.float32))
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_alpha_zero_and_k_zero(variant):
+    """alpha = 0 (or K = 0) gives beta*C bit for bit and never reads A or B (NaN)."""
+    M, N, K = 100, 70, 33
+    A = np.full(M * K, np.nan, np.float32)
+    B = np.full(K * N, np.nan, np.float32)
+    _, _, C = make_inputs(M, N, K, K, N, N + 5, "uniform", seed=14, c_init="random")
+    out = run_gemm(M, N, K, 0.0, A, K, B, N, -0.5, C, N + 5, VARIANTS[variant])
+    want = (np.float32(-0.5) * c_window(C, M, N, N + 5)).astype(np.float32)
+    np.testing.assert_array_equal(c_window(out, M, N, N + 5), want)
+    check_padding(out, C, M, N, N + 5)
+    out = run_gemm(M, N, 0, 1.0, A, 1, B, N, 0.0, C, N + 5, VARIANTS[variant])
+    np.testing.assert_array_equal(c_window(out, M, N, N + 5), np.zeros((M, N), np.float32))
+    out = run_gemm(M, N, 0, 1.0, A, 1, B, N, 1.0, C, N + 5, VARIANTS[variant])
+    np.testing.assert_array_equal(out, C)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_beta_zero_ignores_nan_c(oracle, variant):
+    M, N, K = 257, 129, 65
+    A, B, C = make_inputs(M, N, K, K, N, N, "uniform", seed=15, c_init="nan")
+    out = run_gemm(M, N, K, 1.0, A, K, B, N, 0.0, C, N, VARIANTS[variant])
+    ref, S = oracle.full(M, N, K, 1.0, A, K, B, N, 0.0, C, N)
+    assert_within_bound(out.reshape(M, N), ref, S, f"beta0/{variant}")
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_misaligned_pointers(oracle, variant):
+    """Base pointers off 16-byte alignment and odd leading dimensions take the scalar-load path."""
+    import torch
+
+    M, N, K = 300, 270, 145
+    lda, ldb, ldc = K + 1, N + 3, N + 1
+    A, B, C = make_inputs(M, N, K, lda, ldb, ldc, "uniform", seed=16, c_init="random")
+    dA = device(np.concatenate([np.zeros(1, np.float32), A]))
+    dB = device(np.concatenate([np.zeros(3, np.float32), B]))
+    dC = device(np.concatenate([np.zeros(2, np.float32), C]))
+    from fp32_gemm_rm_amd import sgemm_rm_ex
+
+    s = torch.cuda.current_stream()
+    sgemm_rm_ex(M, N, K, 1.5, dA.data_ptr() + 4, lda, dB.data_ptr() + 12, ldb, -0.5, dC.data_ptr() + 8, ldc,
+                s.cuda_stream, VARIANTS[variant])
+    s.synchronize()
+    out = dC.cpu().numpy()[2:]
+    ref, S = oracle.full(M, N, K, 1.5, A, lda, B, ldb, -0.5, C, ldc)
+    assert_within_bound(c_window(out, M, N, ldc), ref, S, f"misaligned/{variant}")
+    check_padding(out, C, M, N, ldc)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_deterministic(variant):
+    w = WORKLOAD_BY_NAME["sgemm_ragged_1000x1030x999"]
+    A, B, C = workload_inputs(w)
+    o1 = run_gemm(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, VARIANTS[variant])
+    o2 = run_gemm(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, VARIANTS[variant])
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+def test_side_stream_ordering(oracle):
+    """Work enqueued on a non-default stream sees the producer's writes and is ordered after them."""
+    import torch
+
+    w = WORKLOAD_BY_NAME["sgemm_1024"]
+    A, B, C = workload_inputs(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dA, dB, dC = device(A), device(B), device(C)
+        dC.fill_(np.nan)  # beta == 0: must be ignored
+        from fp32_gemm_rm_amd import sgemm
+
+        sgemm(dA.view(w.M, w.K), dB.view(w.K, w.N), dC.view(w.M, w.N), 1.0, 0.0)
+    s.synchronize()
+    ref, S = oracle.full(w.M, w.N, w.K, 1.0, A, w.K, B, w.N, 0.0, C, w.N)
+    assert_within_bound(dC.cpu().numpy().reshape(w.M, w.N), ref, S, "side stream")
+
+
+def test_invalid_arguments_on_device():
+    from fp32_gemm_rm_amd import SgemmError, sgemm_rm_ex
+
+    with pytest.raises(SgemmError) as e:
+        sgemm_rm_ex(4, 4, 4, 1.0, 0, 4, 0, 4, 0.0, 0, 4, 0, 4)
+    assert e.value.code == -5
+
+
+def test_single_hip_runtime():
+    """torch and the library share one HIP runtime in the process."""
+    import torch  # noqa: F401
+
+    from fp32_gemm_rm_amd import load_library
+
+    load_library()
+    maps = open("/proc/self/maps").read().splitlines()
+    libs = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(libs) == 1, libs
