@@ -43,9 +43,8 @@ inline bool vec4_ok(const void* x, long long ld) {
 hipError_t launch_naive(const Problem& p, hipStream_t stream);
 hipError_t launch_lds_tiled(const Problem& p, hipStream_t stream);
 hipError_t launch_regblock(const Problem& p, hipStream_t stream);
-// Small-tile register-blocked kernel with bounds checks: the edge-tile path of the
-// MFMA variant, also usable on its own for thin problems.
-hipError_t launch_edge(const Problem& p, hipStream_t stream);
+// MFMA tiles for the full BM x BN tiles plus bounds-checked register-blocked
+// tiles (the scalar edge-tile path) for the strips past them, in one launch.
 hipError_t launch_mfma(const Problem& p, hipStream_t stream);
 // C := beta*C on the M x N window (zeros when beta == 0; C is then not read).
 hipError_t launch_scale(const Problem& p, hipStream_t stream);

@@ -4,84 +4,139 @@
 // double-buffered shared memory (sgemmNN page; mhpn.cn "GEMM advanced" page
 // sections 2-3) and, for half precision only, warp-level matrix fragments
 // ("GPU-accelerated matrix computation ..." section 2.2).  On gfx950 the dense
-// FP32 contraction belongs on the matrix cores, which accept float32 operands
-// directly, so this kernel keeps the page's tiling and double buffering and
+// FP32 contraction belongs on the matrix cores, which take float32 operands
+// directly, so this kernel keeps the pages' tiling and double buffering and
 // replaces the per-thread FMA block with 32 x 32 x 2 MFMA tiles.
 //
 // MFMA operand layout (32x32x2, checked on the device with one-hot operands):
 // lane l supplies A(l%32, kk = l/32) and B(kk = l/32, l%32); accumulator
-// register i of lane l holds D(8*(i/4) + 4*(l/32) + i%4, l%32).  Because the
-// sum over k may visit k in any order, lane half h = l/32 of one MFMA step e
-// takes k = 16g + 8h + e of K-group g (e = 0..7): a lane then reads its eight A
-// values for a group as two contiguous 128-bit LDS loads.
+// register i of lane l holds D(8*(i/4) + 4*(l/32) + i%4, l%32).  The sum over
+// k may visit k in any order, so lane half h = l/32 of MFMA step e takes
+// k = 8h + e of the 16-wide K-tile (e = 0..7): a lane then reads its eight A
+// values as two contiguous 128-bit LDS loads.
 //
-// Workgroup: WM x WN wavefronts of 64 lanes, macro-tile BM x BN, K-tile BK = 16.
-// Each wavefront owns a (BM/WM) x (BN/WN) block of C as (BM/WM/32) x (BN/WN/32)
-// accumulators of 16 registers.
+// Workgroup: WM x WN wavefronts; each owns a 64 x 64 block of C held as 2 x 2
+// accumulators of 16 registers.  K advances in tiles of 16.
 //
-// LDS (two stages):
-//   As[m][k] with row stride 20 words: A tile as loaded (k contiguous), written
-//     with 128-bit stores.  A fragment read by lanes 0-15 touches words
-//     20r .. 20r+3 for r = 0..15, 64 distinct banks.
-//   Bs[k][n] with row stride BN + 4 words: B tile as loaded.  A fragment read
-//     is one word per lane: lanes 0-31 read 32 consecutive words of row e and
-//     lanes 32-63 the same columns of row 8+e, (8*(BN+4)) mod 64 = 32 banks
-//     apart, so the 64 lanes hit 64 distinct banks.
-// Global loads are 128-bit (rows 16-byte aligned) or scalar; the last K-tile
-// loads zeros past K.  Only full BM x BN tiles run here: the partial tiles along
-// M and N go to the scalar edge-tile path.
-#include "internal.h"
+// LDS, two stages (one barrier per K-tile; the global loads of tile t+1 are in
+// flight while tile t is multiplied):
+//   A tile, BM rows of BK floats (BK/4 16-byte chunks), no padding.  For
+//     BK = 16, chunk c of row r is stored at chunk position c ^ ((r/4) % 4).  On
+//     gfx950 a 128-bit LDS access serves 16 lanes per cycle from 64 banks of 4
+//     bytes (16 chunk slots): the 16 lanes of a fragment read cover rows
+//     r..r+15 at one logical chunk, and the 16 lanes of a tile store cover rows
+//     r..r+3 (r a multiple of 4) at chunks 0..3; the XOR spreads both over 16
+//     distinct chunk slots.  (With +4-word padding instead, the reads are
+//     conflict-free but the stores are not.)
+//   B tile, 16 rows of BN floats with stride BN + 4 words, stored as loaded.
+//     A fragment read is one word per lane: each half-wavefront reads 32
+//     consecutive words of one row.
+// Tile order: the hardware hands workgroups to the 8 XCDs round robin; block
+// ids are remapped so that each XCD works on a contiguous run of tiles, and
+// the run walks GROUP_M tile-rows at a time, so the A and B panels of the
+// tiles in flight on one XCD share its L2.
+//
+// Edge tiles: the MFMA tiles cover [0, Mf) x [0, Nf) with Mf, Nf the largest
+// multiples of BM, BN.  The strips past them (columns [Nf, N) of rows [0, Mf),
+// then rows [Mf, M) in full) are cut into EBM x EBN tiles computed by the
+// bounds-checked register-blocked VALU tile (regblock_tile.h): the scalar
+// edge-tile path.  Those tiles are extra workgroups of the same launch, with
+// the highest block ids, so they run beside the MFMA tiles instead of after
+// them.  Ragged K is handled inside every MFMA tile: its last K-tile loads
+// zeros past K.
+#include "regblock_tile.h"
 
 namespace sgemm_impl {
 namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 16;
-constexpr int SA = BK + 4;
+template <int BM, int BN, int BK, int WM, int WN>
+struct MfmaCfg {
+  static constexpr int KC = BK / 4;  // 16-byte chunks per A row
+  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;  // 32x32 blocks per wavefront
+  static constexpr int SB = BN + 4;
+  static constexpr int A_LOADS = BM * BK / 4 / kThreads;  // float4 of A per thread per K-tile
+  static constexpr int B_LOADS = BN * BK / 4 / kThreads;
+  static_assert(FM >= 1 && FN >= 1, "wavefront tile at least 32 x 32");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "every thread loads A and B");
+  static_assert(A_LOADS * kThreads * 4 == BM * BK && B_LOADS * kThreads * 4 == BN * BK, "even load split");
+};
 
-template <bool VEC, bool GUARD>
-__device__ __forceinline__ float4 gload4(const float* p, int c0, int cols) {
-  if (!GUARD) {
+// Word offset of A(row, 4*chunk) inside one LDS stage whose rows hold BK floats.
+// 64 banks hold 16 chunks, i.e. 64/BK rows; chunk indices are XORed with the row's
+// index in units of that period, so 16 consecutive rows at one chunk, and 16/KC
+// rows at all KC chunks, both land on 16 distinct chunk slots.
+template <int BK>
+__device__ __forceinline__ int a_slot(int row, int chunk) {
+  return row * BK + 4 * (chunk ^ ((row / (64 / BK)) & (BK / 4 - 1)));
+}
+
+template <bool VEC>
+__device__ __forceinline__ float4 load_a4(const float* p, int k_left) {
+  if (k_left >= 4) {
     if (VEC) return *reinterpret_cast<const float4*>(p);
     return make_float4(p[0], p[1], p[2], p[3]);
   }
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (VEC && c0 + 3 < cols) return *reinterpret_cast<const float4*>(p);
-  if (c0 + 0 < cols) v.x = p[0];
-  if (c0 + 1 < cols) v.y = p[1];
-  if (c0 + 2 < cols) v.z = p[2];
-  if (c0 + 3 < cols) v.w = p[3];
+  if (k_left > 0) v.x = p[0];
+  if (k_left > 1) v.y = p[1];
+  if (k_left > 2) v.z = p[2];
   return v;
 }
 
-template <int BM, int BN, int WM, int WN>
-struct MfmaCfg {
-  static constexpr int kThreads = WM * WN * 64;
-  static constexpr int WTM = BM / WM, WTN = BN / WN;  // wavefront tile
-  static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wavefront
-  static constexpr int SB = BN + 4;
-  static constexpr int A_LOADS = BM * BK / 4 / kThreads;  // float4 per thread per K-tile
-  static constexpr int B_LOADS = BN * BK / 4 / kThreads;
-  static_assert(FM >= 1 && FN >= 1, "wavefront tile at least 32 x 32");
-  static_assert(A_LOADS * kThreads * 4 == BM * BK && B_LOADS * kThreads * 4 == BN * BK, "even load split");
+template <bool VEC>
+__device__ __forceinline__ float4 load_b4(const float* p) {
+  if (VEC) return *reinterpret_cast<const float4*>(p);
+  return make_float4(p[0], p[1], p[2], p[3]);
+}
+
+// Where the tiles of one launch are: MFMA tiles first, then the edge tiles of the
+// right strip, then those of the bottom strip.
+struct TileMap {
+  int tiles_m, tiles_n;  // MFMA tiles
+  int Mf, Nf;            // extent they cover
+  int right_m, right_n;  // edge tiles in columns [Nf, N) of rows [0, Mf)
+  int bottom_m, bottom_n;  // edge tiles in rows [Mf, M)
 };
 
-template <int BM, int BN, int WM, int WN, bool VEC>
-__global__ __launch_bounds__(WM* WN * 64) void mfma_kernel(Problem p, int tiles_n) {
-  using Cfg = MfmaCfg<BM, BN, WM, WN>;
-  constexpr int NT = Cfg::kThreads, FM = Cfg::FM, FN = Cfg::FN, SB = Cfg::SB;
-  __shared__ __attribute__((aligned(16))) float As[2][BM][SA];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BK][SB];
+template <int BM, int BN, int BK, int WM, int WN, int GROUP_M, bool VEC>
+__device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m, int tiles_n, float* smem) {
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN>;
+  constexpr int NT = Cfg::kThreads, FM = Cfg::FM, FN = Cfg::FN, SB = Cfg::SB, KC = Cfg::KC;
+  float (*As)[BM * BK] = reinterpret_cast<float (*)[BM * BK]>(smem);
+  float (*Bs)[BK * SB] = reinterpret_cast<float (*)[BK * SB]>(smem + 2 * BM * BK);
 
   const int t = threadIdx.x;
   const int w = t / 64, l = t % 64;
   const int lr = l % 32, lh = l / 32;
-  const int wm0 = (w / WN) * Cfg::WTM, wn0 = (w % WN) * Cfg::WTN;
+  const int wm0 = (w / WN) * (BM / WM), wn0 = (w % WN) * (BN / WN);
 
-  const int bm = blockIdx.x / tiles_n;
-  const int bn = blockIdx.x - bm * tiles_n;
+  // XCD-contiguous, GROUP_M-row-major tile order
+  const int nblk = tiles_m * tiles_n;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int group = GROUP_M * tiles_n;
+  const int first_m = (bid / group) * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int bm = first_m + (bid % group) % gsz;
+  const int bn = (bid % group) / gsz;
   const int m0 = bm * BM, n0 = bn * BN;
+
+  // this thread's global-load coordinates (fixed across K-tiles)
+  int a_row[Cfg::A_LOADS], a_chunk[Cfg::A_LOADS], b_row[Cfg::B_LOADS], b_col[Cfg::B_LOADS];
+#pragma unroll
+  for (int i = 0; i < Cfg::A_LOADS; ++i) {
+    const int q = t + i * NT;
+    a_row[i] = q / KC;
+    a_chunk[i] = q % KC;
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::B_LOADS; ++i) {
+    const int q = t + i * NT;
+    b_row[i] = q / (BN / 4);
+    b_col[i] = (q % (BN / 4)) * 4;
+  }
   const float* Ablk = p.A + (long long)m0 * p.lda;
   const float* Bblk = p.B + n0;
 
@@ -93,78 +148,83 @@ __global__ __launch_bounds__(WM* WN * 64) void mfma_kernel(Problem p, int tiles_
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  const int nfull = p.K / BK;                // K-tiles with no element past K
   const int ntiles = (p.K + BK - 1) / BK;
-  const bool k_ragged = (p.K % BK) != 0;
-
   float4 ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * BK;
-    const bool guard = k_ragged && kt == ntiles - 1;
-#pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) {
-      const int q = t + i * NT;
-      const int row = q / (BK / 4), k4 = (q % (BK / 4)) * 4;
-      const float* src = Ablk + (long long)row * p.lda + k0 + k4;
-      ra[i] = guard ? gload4<VEC, true>(src, k4, p.K - k0) : gload4<VEC, false>(src, k4, p.K - k0);
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) {
-      const int q = t + i * NT;
-      const int kr = q / (BN / 4), n4 = (q % (BN / 4)) * 4;
-      if (guard && k0 + kr >= p.K) {
-        rb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      } else {
-        rb[i] = gload4<VEC, false>(Bblk + (long long)(k0 + kr) * p.ldb + n4, n4, BN);
-      }
-    }
-  };
-  auto store_tile = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) {
-      const int q = t + i * NT;
-      const int row = q / (BK / 4), k4 = (q % (BK / 4)) * 4;
-      *reinterpret_cast<float4*>(&As[s][row][k4]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) {
-      const int q = t + i * NT;
-      const int kr = q / (BN / 4), n4 = (q % (BN / 4)) * 4;
-      *reinterpret_cast<float4*>(&Bs[s][kr][n4]) = rb[i];
-    }
-  };
 
-  load_tile(0);
-  store_tile(0);
+  // Global -> registers for K-tile kt.  The guarded form (last, partial K-tile only)
+  // loads zeros past K; it is kept out of the steady-state loop.
+#define SGEMM_LOAD_FULL(kt)                                                                      \
+  do {                                                                                           \
+    const int k0_ = (kt) * BK;                                                                   \
+    _Pragma("unroll") for (int i = 0; i < Cfg::A_LOADS; ++i)                                     \
+        ra[i] = load_a4<VEC>(Ablk + (long long)a_row[i] * p.lda + k0_ + 4 * a_chunk[i], 4);      \
+    _Pragma("unroll") for (int i = 0; i < Cfg::B_LOADS; ++i)                                     \
+        rb[i] = load_b4<VEC>(Bblk + (long long)(k0_ + b_row[i]) * p.ldb + b_col[i]);             \
+  } while (0)
+#define SGEMM_LOAD_TAIL(kt)                                                                      \
+  do {                                                                                           \
+    const int k0_ = (kt) * BK;                                                                   \
+    const int kl_ = p.K - k0_;                                                                   \
+    _Pragma("unroll") for (int i = 0; i < Cfg::A_LOADS; ++i)                                     \
+        ra[i] = load_a4<VEC>(Ablk + (long long)a_row[i] * p.lda + k0_ + 4 * a_chunk[i],          \
+                             kl_ - 4 * a_chunk[i]);                                              \
+    _Pragma("unroll") for (int i = 0; i < Cfg::B_LOADS; ++i)                                     \
+        rb[i] = (b_row[i] < kl_) ? load_b4<VEC>(Bblk + (long long)(k0_ + b_row[i]) * p.ldb + b_col[i]) \
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);                              \
+  } while (0)
+#define SGEMM_STORE_TILE(s)                                                                      \
+  do {                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < Cfg::A_LOADS; ++i)                                     \
+        *reinterpret_cast<float4*>(&As[s][a_slot<BK>(a_row[i], a_chunk[i])]) = ra[i];            \
+    _Pragma("unroll") for (int i = 0; i < Cfg::B_LOADS; ++i)                                     \
+        *reinterpret_cast<float4*>(&Bs[s][b_row[i] * SB + b_col[i]]) = rb[i];                    \
+  } while (0)
+
+  if (nfull > 0)
+    SGEMM_LOAD_FULL(0);
+  else
+    SGEMM_LOAD_TAIL(0);
+  SGEMM_STORE_TILE(0);
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int s = kt & 1;
-    const bool more = kt + 1 < ntiles;
-    if (more) load_tile(kt + 1);
+    if (kt + 1 < nfull)
+      SGEMM_LOAD_FULL(kt + 1);
+    else if (kt + 1 < ntiles)
+      SGEMM_LOAD_TAIL(kt + 1);
 
-    float af[FM][8], bf[FN][8];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const float4 x0 = *reinterpret_cast<const float4*>(&As[s][wm0 + i * 32 + lr][lh * 8]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&As[s][wm0 + i * 32 + lr][lh * 8 + 4]);
-      af[i][0] = x0.x; af[i][1] = x0.y; af[i][2] = x0.z; af[i][3] = x0.w;
-      af[i][4] = x1.x; af[i][5] = x1.y; af[i][6] = x1.z; af[i][7] = x1.w;
+    for (int g = 0; g < BK / 16; ++g) {
+      float af[FM][8], bf[FN][8];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm0 + i * 32 + lr;
+        const float4 x0 = *reinterpret_cast<const float4*>(&As[s][a_slot<BK>(row, 4 * g + 2 * lh)]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&As[s][a_slot<BK>(row, 4 * g + 2 * lh + 1)]);
+        af[i][0] = x0.x; af[i][1] = x0.y; af[i][2] = x0.z; af[i][3] = x0.w;
+        af[i][4] = x1.x; af[i][5] = x1.y; af[i][6] = x1.z; af[i][7] = x1.w;
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bf[j][e] = Bs[s][(16 * g + lh * 8 + e) * SB + wn0 + j * 32 + lr];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][e], bf[j][e], acc[i][j], 0, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bf[j][e] = Bs[s][lh * 8 + e][wn0 + j * 32 + lr];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][e], bf[j][e], acc[i][j], 0, 0, 0);
 
-    if (more) store_tile(s ^ 1);
+    if (kt + 1 < ntiles) SGEMM_STORE_TILE(s ^ 1);
     __syncthreads();
   }
+#undef SGEMM_LOAD_FULL
+#undef SGEMM_LOAD_TAIL
+#undef SGEMM_STORE_TILE
 
   // epilogue: register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its block
   const bool beta0 = p.beta == 0.0f;
@@ -182,41 +242,73 @@ __global__ __launch_bounds__(WM* WN * 64) void mfma_kernel(Problem p, int tiles_
       }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, int GROUP_M, class Edge, bool VEC>
+__global__ __launch_bounds__(WM* WN * 64) void mfma_kernel(Problem p, TileMap map) {
+  constexpr int kMfmaFloats = 2 * BM * BK + 2 * BK * MfmaCfg<BM, BN, BK, WM, WN>::SB;
+  constexpr int kFloats = kMfmaFloats > Edge::kLdsFloats ? kMfmaFloats : Edge::kLdsFloats;
+  __shared__ __attribute__((aligned(16))) float smem[kFloats];
+  const int nmfma = map.tiles_m * map.tiles_n;
+  int e = (int)blockIdx.x - nmfma;
+  if (e < 0) {
+    mfma_tile<BM, BN, BK, WM, WN, GROUP_M, VEC>(p, blockIdx.x, map.tiles_m, map.tiles_n, smem);
+    return;
+  }
+  constexpr int EBM = Edge::kThrM * (Edge::GM * Edge::VM), EBN = Edge::kThrN * (Edge::GN * Edge::VN);
+  int m0, n0;
+  if (e < map.right_m * map.right_n) {
+    m0 = (e / map.right_n) * EBM;
+    n0 = map.Nf + (e % map.right_n) * EBN;
+  } else {
+    e -= map.right_m * map.right_n;
+    m0 = map.Mf + (e / map.bottom_n) * EBM;
+    n0 = (e % map.bottom_n) * EBN;
+  }
+  Edge::template tile<VEC, true>(p, m0, n0, smem, threadIdx.x);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int GROUP_M, class Edge>
 hipError_t launch_cfg(const Problem& p, hipStream_t stream) {
-  const int Mf = (p.M / BM) * BM, Nf = (p.N / BN) * BN;
-  if (Mf > 0 && Nf > 0) {
-    const long long tn = Nf / BN, tm = Mf / BM;
-    if (tn * tm > kMaxGrid) return hipErrorInvalidConfiguration;
-    Problem q = sub_problem(p, 0, 0, Mf, Nf);
-    const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
-    if (vec)
-      hipLaunchKernelGGL((mfma_kernel<BM, BN, WM, WN, true>), dim3((unsigned)(tn * tm)), dim3(WM * WN * 64), 0,
-                         stream, q, (int)tn);
-    else
-      hipLaunchKernelGGL((mfma_kernel<BM, BN, WM, WN, false>), dim3((unsigned)(tn * tm)), dim3(WM * WN * 64),
-                         0, stream, q, (int)tn);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  constexpr int EBM = Edge::kThrM * (Edge::GM * Edge::VM), EBN = Edge::kThrN * (Edge::GN * Edge::VN);
+  static_assert(BM % EBM == 0, "edge tiles of the right strip end at Mf");
+  TileMap map;
+  map.Mf = (p.M / BM) * BM;
+  map.Nf = (p.N / BN) * BN;
+  map.tiles_m = map.Mf / BM;
+  map.tiles_n = map.Nf / BN;
+  if (map.tiles_m == 0 || map.tiles_n == 0) {  // no full tile: everything is edge
+    map.tiles_m = map.tiles_n = 0;
+    map.Mf = map.Nf = 0;
   }
-  // scalar edge-tile path: columns [Nf, N) of rows [0, Mf), then rows [Mf, M) in full
-  if (Mf > 0 && Nf < p.N) {
-    hipError_t e = launch_edge(sub_problem(p, 0, Nf, Mf, p.N - Nf), stream);
-    if (e != hipSuccess) return e;
-  }
-  if (Mf < p.M) {
-    hipError_t e = launch_edge(sub_problem(p, Mf, 0, p.M - Mf, p.N), stream);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  map.right_m = (map.Nf < p.N) ? map.Mf / EBM : 0;
+  map.right_n = (map.Nf < p.N) ? (p.N - map.Nf + EBN - 1) / EBN : 0;
+  map.bottom_m = (p.M - map.Mf + EBM - 1) / EBM;
+  map.bottom_n = map.bottom_m > 0 ? (p.N + EBN - 1) / EBN : 0;
+  const long long blocks = (long long)map.tiles_m * map.tiles_n + (long long)map.right_m * map.right_n +
+                           (long long)map.bottom_m * map.bottom_n;
+  if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks), block(WM * WN * 64);
+  if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, GROUP_M, Edge, true>), grid, block, 0, stream, p, map);
+  else
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, GROUP_M, Edge, false>), grid, block, 0, stream, p, map);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mfma(const Problem& p, hipStream_t stream) {
-  const long long tiles128 = (long long)(p.M / 128) * (p.N / 128);
-  if (tiles128 >= 512) return launch_cfg<128, 128, 2, 2>(p, stream);
-  return launch_cfg<64, 64, 2, 2>(p, stream);
+  // 256 x 256 tiles (one 16-wavefront workgroup per CU) once they fill the 256 CUs;
+  // smaller tiles keep mid-size problems spread over the chip.
+  const long long t256 = (long long)(p.M / 256) * (p.N / 256);
+  const long long t128 = (long long)(p.M / 128) * (p.N / 128);
+  // Edge tiles are small (2 x 2 outputs per thread) so that thin strips are cut
+  // into many workgroups that run beside the MFMA tiles, with few registers so
+  // that the edge path never needs more than the MFMA path.
+  using Edge256 = RegBlock<32, 32, 32, 2, 2, 256, 2, 8>;    // 32 x 32 tiles, 256 threads
+  using Edge1024 = RegBlock<64, 64, 64, 2, 2, 1024, 2, 8>;  // 64 x 64 tiles, 1024 threads
+  if (t256 >= 256) return launch_cfg<256, 256, 16, 4, 4, 8, Edge1024>(p, stream);
+  if (t128 >= 256) return launch_cfg<128, 128, 16, 2, 2, 8, Edge256>(p, stream);
+  return launch_cfg<64, 64, 16, 2, 2, 8, Edge256>(p, stream);
 }
 
 }  // namespace sgemm_impl

@@ -1,0 +1,174 @@
+// Register-blocked, double-buffered SGEMM tile on the vector ALU (device code).
+//
+// Prior art on the pages: each thread keeps an S x S block of C in registers
+// ("GPU-accelerated matrix computation ..." section 3.3, register-cache GEMM);
+// the sgemmNN page keeps 16 accumulators per thread, streams operands through
+// registers and pads its transposing shared-memory store (bs[16][17]); the
+// mhpn.cn page ("GEMM advanced: ILP and bank conflicts") sections 2-3
+// double-buffers A (stored K-major) and B tiles in shared memory with one
+// barrier per K-step and rearranges which lanes read which fragment.
+//
+// gfx950 design: NT threads form a (BM/TM) x (BN/TN) grid; each owns TM x TN
+// outputs.  Every 64-lane wavefront covers an 8 x 8 block of that grid, so each
+// fragment read is 8 distinct contiguous vectors, each broadcast to 8 lanes.
+//   - The A tile BM x BK is loaded with one 128-bit load per thread (4
+//     consecutive k of one row) and stored transposed into As[k][m] (K-major),
+//     so that the inner loop reads a thread's TM rows as float4 / float2.
+//   - The B tile BK x BN is loaded with one 128-bit load per thread and stored
+//     as is into Bs[k][n].
+//   - As rows are padded by PAD_A words.  A wavefront's transposing store
+//     writes 64/KQ consecutive rows at each of KQ = BK/4 K-offsets 4q; 32-bit
+//     LDS accesses are served per half-wavefront from 32 banks, so the padding
+//     is chosen to spread {row + 4q*(BM + PAD_A)} over distinct banks.
+//   - Two LDS stages; the global loads of tile t+1 are issued before the FMAs
+//     of tile t and stored after them, with a single barrier per tile.
+//   - UNROLL bounds how many k-steps of fragment reads the compiler may hoist,
+//     which bounds the registers the tile needs.
+//   - Loads outside M, N or K read zeros and stores outside M x N are skipped
+//     when GUARD is set (tiles that reach past the matrix, and the last K-tile
+//     of every tile when K is not a multiple of BK).
+#pragma once
+
+#include "internal.h"
+
+namespace sgemm_impl {
+
+template <int BM, int BN, int BK, int TM, int TN, int NT, int PAD_A, int UNROLL = BK>
+struct RegBlock {
+  static constexpr int kThrM = BM / TM, kThrN = BN / TN;
+  static_assert(kThrM * kThrN == NT, "thread grid covers the tile");
+  static_assert(kThrM % 8 == 0 && kThrN % 8 == 0, "8 x 8 threads per wavefront");
+  static_assert(BM * BK / 4 == NT && BN * BK / 4 == NT, "one float4 of A and of B per thread");
+  static constexpr int VM = TM >= 4 ? 4 : TM, VN = TN >= 4 ? 4 : TN;  // fragment vector widths
+  static constexpr int GM = TM / VM, GN = TN / VN;                    // fragment groups
+  static constexpr int KQ = BK / 4;
+  static constexpr int SA = BM + PAD_A;
+  static_assert((SA * 4) % (VM * 4) == 0, "fragment reads stay aligned");
+  static constexpr int kLdsFloats = 2 * BK * SA + 2 * BK * BN;  // two stages of As and Bs
+
+  template <int V>
+  static __device__ __forceinline__ void read_vec(float* dst, const float* src) {
+    if constexpr (V == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src);
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    } else if constexpr (V == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(src);
+      dst[0] = v.x; dst[1] = v.y;
+    } else {
+      dst[0] = src[0];
+    }
+  }
+
+  // One float4 of row r, columns c0..c0+3 of a rows x cols matrix; zero outside when checked.
+  template <bool VEC, bool CHECK>
+  static __device__ __forceinline__ float4 gload4(const float* base, long long ld, int r, int c0, int rows,
+                                                  int cols) {
+    if (!CHECK) {
+      const float* q = base + (long long)r * ld + c0;
+      if (VEC) return *reinterpret_cast<const float4*>(q);
+      return make_float4(q[0], q[1], q[2], q[3]);
+    }
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r >= rows) return v;
+    const float* q = base + (long long)r * ld + c0;
+    if (VEC && c0 + 3 < cols) return *reinterpret_cast<const float4*>(q);
+    if (c0 + 0 < cols) v.x = q[0];
+    if (c0 + 1 < cols) v.y = q[1];
+    if (c0 + 2 < cols) v.z = q[2];
+    if (c0 + 3 < cols) v.w = q[3];
+    return v;
+  }
+
+  // C[m0.., n0..] = alpha * A[m0.., :] B[:, n0..] + beta * C for one BM x BN tile.
+  // lds points to kLdsFloats floats of 16-byte aligned LDS.  tid in [0, NT).
+  template <bool VEC, bool GUARD>
+  static __device__ __forceinline__ void tile(const Problem& p, int m0, int n0, float* lds, int tid) {
+    float* As = lds;                 // [2][BK][SA]
+    float* Bs = lds + 2 * BK * SA;   // [2][BK][BN]
+    const int w = tid / 64, l = tid % 64;
+    constexpr int WAVES_N = kThrN / 8;
+    const int tm = (w / WAVES_N) * 8 + l / 8;
+    const int tn = (w % WAVES_N) * 8 + l % 8;
+
+    const int a_row = tid / KQ, a_k4 = (tid % KQ) * 4;
+    const int b_k = tid / (BN / 4), b_n4 = (tid % (BN / 4)) * 4;
+    const float* Ablk = p.A + (long long)m0 * p.lda;
+    const float* Bblk = p.B + n0;
+    const int rows_left = p.M - m0, cols_left = p.N - n0;
+
+    float acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
+
+    const int ntiles = (p.K + BK - 1) / BK;
+    const int nfull = p.K / BK;
+    float4 av, bv;
+    auto load_tile = [&](int kt) {
+      const int k0 = kt * BK;
+      if (GUARD || kt >= nfull) {
+        av = gload4<VEC, true>(Ablk + k0, p.lda, a_row, a_k4, rows_left, p.K - k0);
+        bv = gload4<VEC, true>(Bblk + (long long)k0 * p.ldb, p.ldb, b_k, b_n4, p.K - k0, cols_left);
+      } else {
+        av = gload4<VEC, false>(Ablk + k0, p.lda, a_row, a_k4, rows_left, p.K - k0);
+        bv = gload4<VEC, false>(Bblk + (long long)k0 * p.ldb, p.ldb, b_k, b_n4, p.K - k0, cols_left);
+      }
+    };
+    auto store_tile = [&](int s) {
+      float* as = As + s * BK * SA;
+      as[(a_k4 + 0) * SA + a_row] = av.x;
+      as[(a_k4 + 1) * SA + a_row] = av.y;
+      as[(a_k4 + 2) * SA + a_row] = av.z;
+      as[(a_k4 + 3) * SA + a_row] = av.w;
+      *reinterpret_cast<float4*>(Bs + s * BK * BN + b_k * BN + b_n4) = bv;
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int s = kt & 1;
+      const bool more = kt + 1 < ntiles;
+      if (more) load_tile(kt + 1);
+      const float* as = As + s * BK * SA;
+      const float* bs = Bs + s * BK * BN;
+#pragma unroll UNROLL
+      for (int k = 0; k < BK; ++k) {
+        float a[TM], b[TN];
+#pragma unroll
+        for (int g = 0; g < GM; ++g) read_vec<VM>(&a[g * VM], as + k * SA + g * (BM / GM) + tm * VM);
+#pragma unroll
+        for (int g = 0; g < GN; ++g) read_vec<VN>(&b[g * VN], bs + k * BN + g * (BN / GN) + tn * VN);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      }
+      if (more) store_tile(s ^ 1);
+      __syncthreads();
+    }
+
+    // epilogue: C = alpha*acc + beta*C; rows past M and columns past N untouched
+    const bool beta0 = p.beta == 0.0f;
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi)
+#pragma unroll
+      for (int vi = 0; vi < VM; ++vi) {
+        const int r = gi * (BM / GM) + tm * VM + vi;
+        if (GUARD && r >= rows_left) continue;
+        float* crow = p.C + (long long)(m0 + r) * p.ldc + n0;
+#pragma unroll
+        for (int gj = 0; gj < GN; ++gj)
+#pragma unroll
+          for (int vj = 0; vj < VN; ++vj) {
+            const int c = gj * (BN / GN) + tn * VN + vj;
+            if (GUARD && c >= cols_left) continue;
+            const float x = acc[gi * VM + vi][gj * VN + vj];
+            crow[c] = beta0 ? p.alpha * x : fmaf(p.alpha, x, p.beta * crow[c]);
+          }
+      }
+  }
+};
+
+}  // namespace sgemm_impl

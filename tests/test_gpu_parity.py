@@ -253,3 +253,28 @@ def test_single_hip_runtime():
     maps = open("/proc/self/maps").read().splitlines()
     libs = {line.split()[-1] for line in maps if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+@pytest.mark.parametrize(
+    "M,N,K",
+    [
+        (2048, 2048, 300),   # 128 x 128 MFMA tiles
+        (2176, 2112, 129),   # 128 x 128 tiles plus edge strips
+        (4196, 4132, 77),    # 256 x 256 tiles plus edge strips, ragged K
+        (4096, 4096, 17),    # 256 x 256 tiles, K just past one K-tile
+    ],
+)
+def test_tile_configs_integer_exact(oracle, M, N, K):
+    """Every MFMA tile configuration the dispatcher can pick, with edges: bit-exact on
+    integer inputs, padded leading dimensions, NaN padding in A/B, sentinel in C."""
+    lda, ldb, ldc = K + 4, N + 8, N + 3
+    a = integer_matrix(M, K, -4, 4, seed=M + K)
+    b = integer_matrix(K, N, -4, 4, seed=N + K)
+    c = integer_matrix(M, N, -4, 4, seed=M + N)
+    A, B, C = pad_rows(a, lda, np.nan), pad_rows(b, ldb, np.nan), pad_rows(c, ldc, C_PAD_SENTINEL)
+    out = run_gemm(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, VARIANTS["mfma"])
+    ref, _ = oracle.full(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc)
+    got = c_window(out, M, N, ldc).astype(np.float64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+    check_padding(out, C, M, N, ldc)
