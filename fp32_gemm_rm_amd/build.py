@@ -36,6 +36,26 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_DIR = os.path.join(ROOT, "tests", "probes")
+PROBES = ["mfma_layout_probe.hip", "lds_bank_probe.hip"]
+
+
+def build_probes() -> list:
+    """Compile the hardware probes the tests run (tests/probes/*.hip -> tests/probes/bin/)."""
+    out_dir = os.path.join(PROBE_DIR, "bin")
+    os.makedirs(out_dir, exist_ok=True)
+    built = []
+    for src in PROBES:
+        exe = os.path.join(out_dir, os.path.splitext(src)[0])
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", os.path.join(PROBE_DIR, src), "-o", exe]
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        if proc.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{proc.stdout}\n{proc.stderr}")
+        built.append(exe)
+    return built
+
+
 def build(verbose: bool = False) -> str:
     """Compile every kernel source and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
