@@ -15,8 +15,14 @@
 // k = 8h + e of the 16-wide K-tile (e = 0..7): a lane then reads its eight A
 // values as two contiguous 128-bit LDS loads.
 //
-// Workgroup: WM x WN wavefronts; each owns a 64 x 64 block of C held as 2 x 2
-// accumulators of 16 registers.  K advances in tiles of 16.
+// Workgroup: WM x WN x KS wavefronts.  WM x WN of them tile the BM x BN block
+// of C (each owning (BM/WM) x (BN/WN) as 32 x 32 accumulators of 16 registers);
+// KS of them share each such block and split every K-tile of BK = 16*KS*KG
+// between them (KG 16-deep k-groups each).  Their partial sums are added through
+// LDS in the fixed order ks = 0, 1, ..., KS-1 before the epilogue, so results are
+// deterministic.  KS > 1 lets small problems, whose output alone would give each
+// SIMD a single wavefront, run 4 wavefronts per SIMD and hide LDS, barrier and
+// MFMA latencies.
 //
 // LDS, two stages (one barrier per K-tile; the global loads of tile t+1 are in
 // flight while tile t is multiplied):
@@ -38,12 +44,14 @@
 //
 // Edge tiles: the MFMA tiles cover [0, Mf) x [0, Nf) with Mf, Nf the largest
 // multiples of BM, BN.  The strips past them (columns [Nf, N) of rows [0, Mf),
-// then rows [Mf, M) in full) are cut into EBM x EBN tiles computed by the
-// bounds-checked register-blocked VALU tile (regblock_tile.h): the scalar
-// edge-tile path.  Those tiles are extra workgroups of the same launch, with
-// the highest block ids, so they run beside the MFMA tiles instead of after
-// them.  Ragged K is handled inside every MFMA tile: its last K-tile loads
-// zeros past K.
+// then rows [Mf, M) in full) are cut into 32 x 32 tiles computed by the
+// bounds-checked register-blocked VALU tile (regblock_tile.h, 256 threads, 2 x 2
+// outputs each): the scalar edge-tile path.  One edge tile per workgroup; its
+// NT/256 groups of 256 threads split the tile's K range (all groups run the same
+// number of K-steps, so their barriers match) and add their partial sums through
+// LDS in the fixed group order.  Edge workgroups take the highest block ids of
+// the same launch, so they run beside the MFMA tiles instead of after them.  Ragged K is handled inside every
+// MFMA tile: its last K-tile loads zeros past K.
 #include "regblock_tile.h"
 
 namespace sgemm_impl {
@@ -51,15 +59,20 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, int KS>
 struct MfmaCfg {
-  static constexpr int KC = BK / 4;  // 16-byte chunks per A row
-  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int KC = BK / 4;   // 16-byte chunks per A row
+  static constexpr int KG = BK / (16 * KS);  // 16-deep k-groups per wavefront per K-tile
+  static constexpr int kThreads = WM * WN * KS * 64;
   static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;  // 32x32 blocks per wavefront
   static constexpr int SB = BN + 4;
   static constexpr int A_LOADS = BM * BK / 4 / kThreads;  // float4 of A per thread per K-tile
   static constexpr int B_LOADS = BN * BK / 4 / kThreads;
+  static constexpr int kStageFloats = BM * BK + BK * SB;
+  static constexpr int kReduceFloats = (KS - 1) * BM * BN;
+  static constexpr int kLdsFloats = 2 * kStageFloats > kReduceFloats ? 2 * kStageFloats : kReduceFloats;
   static_assert(FM >= 1 && FN >= 1, "wavefront tile at least 32 x 32");
+  static_assert(KG >= 1 && KG * 16 * KS == BK && BK <= 64, "K-tile split into 16-deep k-groups");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "every thread loads A and B");
   static_assert(A_LOADS * kThreads * 4 == BM * BK && B_LOADS * kThreads * 4 == BN * BK, "even load split");
 };
@@ -95,23 +108,24 @@ __device__ __forceinline__ float4 load_b4(const float* p) {
 // Where the tiles of one launch are: MFMA tiles first, then the edge tiles of the
 // right strip, then those of the bottom strip.
 struct TileMap {
-  int tiles_m, tiles_n;  // MFMA tiles
-  int Mf, Nf;            // extent they cover
-  int right_m, right_n;  // edge tiles in columns [Nf, N) of rows [0, Mf)
-  int bottom_m, bottom_n;  // edge tiles in rows [Mf, M)
+  int tiles_m, tiles_n;    // MFMA tiles
+  int Mf, Nf;              // extent they cover
+  int right_m, right_n;    // 32 x 32 edge tiles in columns [Nf, N) of rows [0, Mf)
+  int bottom_m, bottom_n;  // 32 x 32 edge tiles in rows [Mf, M)
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int GROUP_M, bool VEC>
+template <int BM, int BN, int BK, int WM, int WN, int KS, int GROUP_M, bool VEC>
 __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m, int tiles_n, float* smem) {
-  using Cfg = MfmaCfg<BM, BN, BK, WM, WN>;
-  constexpr int NT = Cfg::kThreads, FM = Cfg::FM, FN = Cfg::FN, SB = Cfg::SB, KC = Cfg::KC;
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS>;
+  constexpr int NT = Cfg::kThreads, FM = Cfg::FM, FN = Cfg::FN, SB = Cfg::SB, KC = Cfg::KC, KG = Cfg::KG;
   float (*As)[BM * BK] = reinterpret_cast<float (*)[BM * BK]>(smem);
   float (*Bs)[BK * SB] = reinterpret_cast<float (*)[BK * SB]>(smem + 2 * BM * BK);
 
   const int t = threadIdx.x;
   const int w = t / 64, l = t % 64;
   const int lr = l % 32, lh = l / 32;
-  const int wm0 = (w / WN) * (BM / WM), wn0 = (w % WN) * (BN / WN);
+  const int ks = w / (WM * WN), sp = w % (WM * WN);  // K-group and spatial position of this wavefront
+  const int wm0 = (sp / WN) * (BM / WM), wn0 = (sp % WN) * (BN / WN);
 
   // XCD-contiguous, GROUP_M-row-major tile order
   const int nblk = tiles_m * tiles_n;
@@ -196,7 +210,8 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
       SGEMM_LOAD_TAIL(kt + 1);
 
 #pragma unroll
-    for (int g = 0; g < BK / 16; ++g) {
+    for (int r = 0; r < KG; ++r) {
+      const int g = ks * KG + r;  // 16-deep k-group of this K-tile
       float af[FM][8], bf[FN][8];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -226,6 +241,33 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
 #undef SGEMM_LOAD_TAIL
 #undef SGEMM_STORE_TILE
 
+  if constexpr (KS > 1) {
+    // partial sums of K-groups 1..KS-1 through LDS (free after the last barrier),
+    // added to K-group 0's in the fixed order 1, 2, ..., KS-1
+    constexpr int kPart = FM * FN * 16 * 64;  // floats per wavefront
+    if (ks > 0) {
+      float* dst = smem + ((ks - 1) * (WM * WN) + sp) * kPart + l;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll 1
+    for (int q = 1; q < KS; ++q) {
+      const float* src = smem + ((q - 1) * (WM * WN) + sp) * kPart + l;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
+    }
+  }
+
   // epilogue: register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its block
   const bool beta0 = p.beta == 0.0f;
 #pragma unroll
@@ -242,34 +284,70 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
       }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int GROUP_M, class Edge, bool VEC>
-__global__ __launch_bounds__(WM* WN * 64) void mfma_kernel(Problem p, TileMap map) {
-  constexpr int kMfmaFloats = 2 * BM * BK + 2 * BK * MfmaCfg<BM, BN, BK, WM, WN>::SB;
-  constexpr int kFloats = kMfmaFloats > Edge::kLdsFloats ? kMfmaFloats : Edge::kLdsFloats;
+// Scalar edge-tile path: one 32 x 32 register-blocked VALU tile per workgroup; the
+// workgroup's NT/256 groups of 256 threads split its K range and add their partial
+// sums through LDS in the fixed group order.
+using EdgeTile = RegBlock<32, 32, 32, 2, 2, 256, 2, 8>;
+constexpr int kEdge = 32;
+
+template <int GROUPS, bool VEC>
+__device__ __forceinline__ void edge_tile(const Problem& p, int m0, int n0, float* smem) {
+  constexpr int BK = 32;
+  const int g = threadIdx.x / 256, tid = threadIdx.x % 256;
+  // every group runs the same number of K-steps (the block's barriers must match);
+  // group g covers k in [g*span, g*span + span), clipped to K
+  const int steps = (p.K + BK * GROUPS - 1) / (BK * GROUPS);
+  const int span = steps * BK;
+  const int kbeg = min(g * span, p.K);
+  const int klen = min(span, p.K - kbeg);
+  float acc[2][2];
+  EdgeTile::template compute<VEC, true>(p, m0, n0, kbeg, klen, steps, smem + g * EdgeTile::kLdsFloats, tid, acc);
+  if constexpr (GROUPS > 1) {
+    float* red = smem;  // [GROUPS-1][4][256]; the stages are free after compute()'s last barrier
+    if (g > 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[((g - 1) * 4 + i) * 256 + tid] = acc[i / 2][i % 2];
+    __syncthreads();
+    if (g > 0) return;
+#pragma unroll 1
+    for (int q = 1; q < GROUPS; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i / 2][i % 2] += red[((q - 1) * 4 + i) * 256 + tid];
+  }
+  EdgeTile::template store<true>(p, m0, n0, tid, acc);
+}
+
+// MIN_BLOCKS workgroups must fit on one CU at once (a register budget for the compiler).
+template <int BM, int BN, int BK, int WM, int WN, int KS, int GROUP_M, int MIN_BLOCKS, bool VEC>
+__global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
+void mfma_kernel(Problem p, TileMap map) {
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS>;
+  constexpr int kGroups = Cfg::kThreads / 256;
+  constexpr int kEdgeFloats = kGroups * EdgeTile::kLdsFloats;  // >= the (kGroups-1)*4*256 reduction floats
+  constexpr int kFloats = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
   const int nmfma = map.tiles_m * map.tiles_n;
   int e = (int)blockIdx.x - nmfma;
   if (e < 0) {
-    mfma_tile<BM, BN, BK, WM, WN, GROUP_M, VEC>(p, blockIdx.x, map.tiles_m, map.tiles_n, smem);
+    mfma_tile<BM, BN, BK, WM, WN, KS, GROUP_M, VEC>(p, blockIdx.x, map.tiles_m, map.tiles_n, smem);
     return;
   }
-  constexpr int EBM = Edge::kThrM * (Edge::GM * Edge::VM), EBN = Edge::kThrN * (Edge::GN * Edge::VN);
   int m0, n0;
-  if (e < map.right_m * map.right_n) {
-    m0 = (e / map.right_n) * EBM;
-    n0 = map.Nf + (e % map.right_n) * EBN;
+  const int n_right = map.right_m * map.right_n;
+  if (e < n_right) {
+    m0 = (e / map.right_n) * kEdge;
+    n0 = map.Nf + (e % map.right_n) * kEdge;
   } else {
-    e -= map.right_m * map.right_n;
-    m0 = map.Mf + (e / map.bottom_n) * EBM;
-    n0 = (e % map.bottom_n) * EBN;
+    e -= n_right;
+    m0 = map.Mf + (e / map.bottom_n) * kEdge;
+    n0 = (e % map.bottom_n) * kEdge;
   }
-  Edge::template tile<VEC, true>(p, m0, n0, smem, threadIdx.x);
+  edge_tile<kGroups, VEC>(p, m0, n0, smem);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int GROUP_M, class Edge>
+template <int BM, int BN, int BK, int WM, int WN, int KS, int GROUP_M, int MIN_BLOCKS>
 hipError_t launch_cfg(const Problem& p, hipStream_t stream) {
-  constexpr int EBM = Edge::kThrM * (Edge::GM * Edge::VM), EBN = Edge::kThrN * (Edge::GN * Edge::VN);
-  static_assert(BM % EBM == 0, "edge tiles of the right strip end at Mf");
+  static_assert(BM % kEdge == 0 && BN % kEdge == 0, "edge tiles of the right strip end at Mf");
   TileMap map;
   map.Mf = (p.M / BM) * BM;
   map.Nf = (p.N / BN) * BN;
@@ -279,36 +357,34 @@ hipError_t launch_cfg(const Problem& p, hipStream_t stream) {
     map.tiles_m = map.tiles_n = 0;
     map.Mf = map.Nf = 0;
   }
-  map.right_m = (map.Nf < p.N) ? map.Mf / EBM : 0;
-  map.right_n = (map.Nf < p.N) ? (p.N - map.Nf + EBN - 1) / EBN : 0;
-  map.bottom_m = (p.M - map.Mf + EBM - 1) / EBM;
-  map.bottom_n = map.bottom_m > 0 ? (p.N + EBN - 1) / EBN : 0;
-  const long long blocks = (long long)map.tiles_m * map.tiles_n + (long long)map.right_m * map.right_n +
-                           (long long)map.bottom_m * map.bottom_n;
+  map.right_m = (map.Nf < p.N) ? map.Mf / kEdge : 0;
+  map.right_n = (map.Nf < p.N) ? (p.N - map.Nf + kEdge - 1) / kEdge : 0;
+  map.bottom_m = (p.M - map.Mf + kEdge - 1) / kEdge;
+  map.bottom_n = map.bottom_m > 0 ? (p.N + kEdge - 1) / kEdge : 0;
+  const long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
+  const long long blocks = (long long)map.tiles_m * map.tiles_n + edge_tiles;
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks), block(WM * WN * 64);
+  const dim3 grid((unsigned)blocks), block(WM * WN * KS * 64);
   if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, GROUP_M, Edge, true>), grid, block, 0, stream, p, map);
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, GROUP_M, MIN_BLOCKS, true>), grid, block, 0, stream,
+                       p, map);
   else
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, GROUP_M, Edge, false>), grid, block, 0, stream, p, map);
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, GROUP_M, MIN_BLOCKS, false>), grid, block, 0, stream,
+                       p, map);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mfma(const Problem& p, hipStream_t stream) {
-  // 256 x 256 tiles (one 16-wavefront workgroup per CU) once they fill the 256 CUs;
-  // smaller tiles keep mid-size problems spread over the chip.
+  // 256 x 256 tiles (one 16-wavefront workgroup per CU) once they fill the 256 CUs.
+  // Smaller problems use 128 x 128 or 64 x 64 tiles with the K-tile split over 4
+  // wavefronts per output block, so every SIMD still has 4 wavefronts.
   const long long t256 = (long long)(p.M / 256) * (p.N / 256);
   const long long t128 = (long long)(p.M / 128) * (p.N / 128);
-  // Edge tiles are small (2 x 2 outputs per thread) so that thin strips are cut
-  // into many workgroups that run beside the MFMA tiles, with few registers so
-  // that the edge path never needs more than the MFMA path.
-  using Edge256 = RegBlock<32, 32, 32, 2, 2, 256, 2, 8>;    // 32 x 32 tiles, 256 threads
-  using Edge1024 = RegBlock<64, 64, 64, 2, 2, 1024, 2, 8>;  // 64 x 64 tiles, 1024 threads
-  if (t256 >= 256) return launch_cfg<256, 256, 16, 4, 4, 8, Edge1024>(p, stream);
-  if (t128 >= 256) return launch_cfg<128, 128, 16, 2, 2, 8, Edge256>(p, stream);
-  return launch_cfg<64, 64, 16, 2, 2, 8, Edge256>(p, stream);
+  if (t256 >= 256) return launch_cfg<256, 256, 16, 4, 4, 1, 8, 1>(p, stream);
+  if (t128 >= 256) return launch_cfg<128, 128, 32, 2, 2, 2, 8, 1>(p, stream);
+  return launch_cfg<64, 64, 64, 2, 2, 4, 8, 2>(p, stream);
 }
 
 }  // namespace sgemm_impl

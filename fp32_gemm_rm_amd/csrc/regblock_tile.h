@@ -27,6 +27,9 @@
 //   - Loads outside M, N or K read zeros and stores outside M x N are skipped
 //     when GUARD is set (tiles that reach past the matrix, and the last K-tile
 //     of every tile when K is not a multiple of BK).
+//   - compute() may cover a sub-range of K, so that several thread groups can
+//     share one tile's K range and add their partial sums (the edge tiles of
+//     the MFMA kernel do).
 #pragma once
 
 #include "internal.h"
@@ -79,10 +82,13 @@ struct RegBlock {
     return v;
   }
 
-  // C[m0.., n0..] = alpha * A[m0.., :] B[:, n0..] + beta * C for one BM x BN tile.
-  // lds points to kLdsFloats floats of 16-byte aligned LDS.  tid in [0, NT).
+  // acc = A[m0.., kbeg : kbeg+klen] B[kbeg : kbeg+klen, n0..] for one BM x BN tile, in
+  // `ntiles` K-steps of BK (ntiles * BK >= klen; every thread of the workgroup must pass
+  // the same ntiles, since each K-step ends with a workgroup barrier).  lds points to
+  // kLdsFloats floats of 16-byte aligned LDS; tid in [0, NT).
   template <bool VEC, bool GUARD>
-  static __device__ __forceinline__ void tile(const Problem& p, int m0, int n0, float* lds, int tid) {
+  static __device__ __forceinline__ void compute(const Problem& p, int m0, int n0, int kbeg, int klen, int ntiles,
+                                                 float* lds, int tid, float (&acc)[TM][TN]) {
     float* As = lds;                 // [2][BK][SA]
     float* Bs = lds + 2 * BK * SA;   // [2][BK][BN]
     const int w = tid / 64, l = tid % 64;
@@ -92,27 +98,25 @@ struct RegBlock {
 
     const int a_row = tid / KQ, a_k4 = (tid % KQ) * 4;
     const int b_k = tid / (BN / 4), b_n4 = (tid % (BN / 4)) * 4;
-    const float* Ablk = p.A + (long long)m0 * p.lda;
-    const float* Bblk = p.B + n0;
+    const float* Ablk = p.A + (long long)m0 * p.lda + kbeg;
+    const float* Bblk = p.B + (long long)kbeg * p.ldb + n0;
     const int rows_left = p.M - m0, cols_left = p.N - n0;
 
-    float acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
 
-    const int ntiles = (p.K + BK - 1) / BK;
-    const int nfull = p.K / BK;
+    const int nfull = klen / BK;
     float4 av, bv;
     auto load_tile = [&](int kt) {
       const int k0 = kt * BK;
       if (GUARD || kt >= nfull) {
-        av = gload4<VEC, true>(Ablk + k0, p.lda, a_row, a_k4, rows_left, p.K - k0);
-        bv = gload4<VEC, true>(Bblk + (long long)k0 * p.ldb, p.ldb, b_k, b_n4, p.K - k0, cols_left);
+        av = gload4<VEC, true>(Ablk + k0, p.lda, a_row, a_k4, rows_left, klen - k0);
+        bv = gload4<VEC, true>(Bblk + (long long)k0 * p.ldb, p.ldb, b_k, b_n4, klen - k0, cols_left);
       } else {
-        av = gload4<VEC, false>(Ablk + k0, p.lda, a_row, a_k4, rows_left, p.K - k0);
-        bv = gload4<VEC, false>(Bblk + (long long)k0 * p.ldb, p.ldb, b_k, b_n4, p.K - k0, cols_left);
+        av = gload4<VEC, false>(Ablk + k0, p.lda, a_row, a_k4, rows_left, klen - k0);
+        bv = gload4<VEC, false>(Bblk + (long long)k0 * p.ldb, p.ldb, b_k, b_n4, klen - k0, cols_left);
       }
     };
     auto store_tile = [&](int s) {
@@ -148,8 +152,17 @@ struct RegBlock {
       if (more) store_tile(s ^ 1);
       __syncthreads();
     }
+  }
 
-    // epilogue: C = alpha*acc + beta*C; rows past M and columns past N untouched
+  // C = alpha*acc + beta*C for the tile; rows past M and columns past N untouched.
+  template <bool GUARD>
+  static __device__ __forceinline__ void store(const Problem& p, int m0, int n0, int tid,
+                                               const float (&acc)[TM][TN]) {
+    const int w = tid / 64, l = tid % 64;
+    constexpr int WAVES_N = kThrN / 8;
+    const int tm = (w / WAVES_N) * 8 + l / 8;
+    const int tn = (w % WAVES_N) * 8 + l % 8;
+    const int rows_left = p.M - m0, cols_left = p.N - n0;
     const bool beta0 = p.beta == 0.0f;
 #pragma unroll
     for (int gi = 0; gi < GM; ++gi)
@@ -168,6 +181,14 @@ struct RegBlock {
             crow[c] = beta0 ? p.alpha * x : fmaf(p.alpha, x, p.beta * crow[c]);
           }
       }
+  }
+
+  // The whole tile: C[m0.., n0..] = alpha * A[m0.., :] B[:, n0..] + beta * C.
+  template <bool VEC, bool GUARD>
+  static __device__ __forceinline__ void tile(const Problem& p, int m0, int n0, float* lds, int tid) {
+    float acc[TM][TN];
+    compute<VEC, GUARD>(p, m0, n0, 0, p.K, (p.K + BK - 1) / BK, lds, tid, acc);
+    store<GUARD>(p, m0, n0, tid, acc);
   }
 };
 
