@@ -278,3 +278,30 @@ def test_tile_configs_integer_exact(oracle, M, N, K):
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
     check_padding(out, C, M, N, ldc)
+
+
+@pytest.mark.parametrize("variant,N", [("mfma", 64), ("auto", 64), ("regblock", 64), ("lds_tiled", 64), ("naive", 4)])
+def test_offsets_past_2_pow_31(oracle, variant, N):
+    """A with more than 2^31 elements (65539 x 32772): row offsets i*lda need 64 bits.
+    A lives only on the device (integer pattern drawn there); the oracle gets the sampled
+    rows of A, so every check is bit-exact on integer inputs."""
+    import torch
+
+    M, K = 65539, 32768
+    lda, ldb, ldc = K + 4, N, N
+    assert M * lda > 2**31
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    dA = torch.randint(-2, 3, (M * lda,), generator=gen, device="cuda", dtype=torch.int8).to(torch.float32)
+    b = integer_matrix(K, N, -2, 2, seed=78)
+    dB = device(b.reshape(-1))
+    dC = torch.full((M * ldc,), float("nan"), device="cuda")
+    out = run_gemm(M, N, K, 1.0, None, lda, None, ldb, 0.0, None, ldc, VARIANTS[variant], tensors=(dA, dB, dC))
+    rows = np.array([0, 1, 32767, 32768, 65535, 65536, 65537, 65538])
+    a_rows = dA.view(M, lda)[torch.from_numpy(rows).cuda()].cpu().numpy().reshape(-1)
+    r = np.repeat(np.arange(len(rows)), N)
+    c = np.tile(np.arange(N), len(rows))
+    ref, _ = oracle.entries(len(rows), N, K, 1.0, a_rows, lda, b.reshape(-1), ldb, 0.0, None, ldc, r, c)
+    got = out.reshape(M, ldc)[rows][:, :N].reshape(-1).astype(np.float64)
+    np.testing.assert_array_equal(got, ref)
+    del dA
+    torch.cuda.empty_cache()
