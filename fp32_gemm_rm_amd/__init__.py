@@ -15,7 +15,10 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     sgemm,
+    sgemm_batched,
     sgemm_rm,
     sgemm_rm_ex,
     sgemm_rm_strerror,
+    sgemm_rm_strided_batched,
+    sgemm_rm_strided_batched_ex,
 )

@@ -28,7 +28,8 @@ LIB_NAME = "libsgemm_rm.so"
 _lib = None
 
 #: Names the header declares; the CPU tests check that the library exports each.
-EXPORTED_SYMBOLS = ("sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strerror", "sgemm_rm_version")
+EXPORTED_SYMBOLS = ("sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex",
+                    "sgemm_rm_strerror", "sgemm_rm_version")
 
 
 class SgemmError(RuntimeError):
@@ -59,6 +60,13 @@ def load_library():
         lib.sgemm_rm.restype = ctypes.c_int
         lib.sgemm_rm_ex.argtypes = args + [ctypes.c_int]
         lib.sgemm_rm_ex.restype = ctypes.c_int
+        bargs = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+                 ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float,
+                 ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+        lib.sgemm_rm_strided_batched.argtypes = bargs
+        lib.sgemm_rm_strided_batched.restype = ctypes.c_int
+        lib.sgemm_rm_strided_batched_ex.argtypes = bargs + [ctypes.c_int]
+        lib.sgemm_rm_strided_batched_ex.restype = ctypes.c_int
         lib.sgemm_rm_strerror.argtypes = [ctypes.c_int]
         lib.sgemm_rm_strerror.restype = ctypes.c_char_p
         lib.sgemm_rm_version.argtypes = []
@@ -91,6 +99,24 @@ def sgemm_rm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0, variant=
                                   int(ldb), float(beta), C or None, int(ldc), stream or None, int(variant)))
 
 
+def sgemm_rm_strided_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+                             stream=0):
+    """Strided batch of C_b := alpha*A_b*B_b + beta*C_b on raw device pointers; raises SgemmError."""
+    lib = load_library()
+    return _check(lib.sgemm_rm_strided_batched(
+        int(M), int(N), int(K), float(alpha), A or None, int(lda), int(strideA), B or None, int(ldb),
+        int(strideB), float(beta), C or None, int(ldc), int(strideC), int(batch), stream or None))
+
+
+def sgemm_rm_strided_batched_ex(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+                                stream=0, variant=SGEMM_RM_VARIANT_AUTO):
+    """As ``sgemm_rm_strided_batched`` with the kernel family forced."""
+    lib = load_library()
+    return _check(lib.sgemm_rm_strided_batched_ex(
+        int(M), int(N), int(K), float(alpha), A or None, int(lda), int(strideA), B or None, int(ldb),
+        int(strideB), float(beta), C or None, int(ldc), int(strideC), int(batch), stream or None, int(variant)))
+
+
 def _matrix_view(t, name):
     import torch
 
@@ -103,6 +129,28 @@ def _matrix_view(t, name):
     if rows > 1 and ld < max(cols, 1):
         raise ValueError(f"{name} rows overlap (stride(0) = {ld} < {cols} columns)")
     return t.data_ptr(), ld
+
+
+def sgemm_batched(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, stream=None):
+    """C[b] := alpha*A[b]@B[b] + beta*C[b] in place on 3-D float32 device tensors (row-major
+    matrices; stride(0) is the batch stride, stride(1) the leading dimension)."""
+    import torch
+
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    for t, name in ((A, "A"), (B, "B"), (C, "C")):
+        if t.dtype != torch.float32 or t.dim() != 3 or not t.is_cuda:
+            raise TypeError(f"{name} must be a 3-D float32 device tensor")
+    nb, M, K = A.shape
+    nb2, K2, N = B.shape
+    if K2 != K or nb2 != nb or tuple(C.shape) != (nb, M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    a, lda = _matrix_view(A[0], "A") if nb else (A.data_ptr(), max(K, 1))
+    b, ldb = _matrix_view(B[0], "B") if nb else (B.data_ptr(), max(N, 1))
+    c, ldc = _matrix_view(C[0], "C") if nb else (C.data_ptr(), max(N, 1))
+    s = (stream if stream is not None else torch.cuda.current_stream(C.device)).cuda_stream
+    return sgemm_rm_strided_batched_ex(M, N, K, alpha, a, lda, A.stride(0), b, ldb, B.stride(0), beta, c, ldc,
+                                       C.stride(0), nb, s, variant)
 
 
 def sgemm(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, stream=None):

@@ -19,7 +19,19 @@ struct Problem {
   long long ldb;
   float* C;
   long long ldc;
+  // strided batch: matrix b of the batch starts at A + b*sA, B + b*sB, C + b*sC;
+  // the batch index is blockIdx.y (0 for a single GEMM)
+  long long sA, sB, sC;
 };
+
+// The problem of batch entry blockIdx.y (device side, at the top of every kernel).
+__device__ __forceinline__ Problem batch_entry(Problem p) {
+  const long long b = blockIdx.y;
+  p.A += b * p.sA;
+  p.B += b * p.sB;
+  p.C += b * p.sC;
+  return p;
+}
 
 // Sub-problem covering rows [m0, m0+rows) and columns [n0, n0+cols) of C.
 inline Problem sub_problem(const Problem& p, int m0, int n0, int rows, int cols) {
@@ -39,17 +51,19 @@ inline bool vec4_ok(const void* x, long long ld) {
 }
 
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the launch status.
-// Every launcher accepts any M, N >= 1 and K >= 1 and any leading dimensions.
-hipError_t launch_naive(const Problem& p, hipStream_t stream);
-hipError_t launch_lds_tiled(const Problem& p, hipStream_t stream);
-hipError_t launch_regblock(const Problem& p, hipStream_t stream);
+// Every launcher accepts any M, N >= 1 and K >= 1 and any leading dimensions, and runs
+// `batch` (1 .. kMaxBatch) problems spaced by p.sA, p.sB, p.sC as grid dimension y.
+hipError_t launch_naive(const Problem& p, int batch, hipStream_t stream);
+hipError_t launch_lds_tiled(const Problem& p, int batch, hipStream_t stream);
+hipError_t launch_regblock(const Problem& p, int batch, hipStream_t stream);
 // MFMA tiles for the full BM x BN tiles plus bounds-checked register-blocked
 // tiles (the scalar edge-tile path) for the strips past them, in one launch.
-hipError_t launch_mfma(const Problem& p, hipStream_t stream);
+hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream);
 // C := beta*C on the M x N window (zeros when beta == 0; C is then not read).
-hipError_t launch_scale(const Problem& p, hipStream_t stream);
+hipError_t launch_scale(const Problem& p, int batch, hipStream_t stream);
 
-// Largest grid the launchers use (one-dimensional grids).
+// Largest grid the launchers use: x counts tiles, y counts batch entries.
 constexpr long long kMaxGrid = 0x7fffffffLL;
+constexpr int kMaxBatch = 65535;
 
 }  // namespace sgemm_impl

@@ -41,6 +41,7 @@ __device__ __forceinline__ float4 load4_guarded(const float* base, long long ld,
 
 template <bool VEC>
 __global__ __launch_bounds__(256) void lds_tiled_kernel(Problem p, int col_blocks) {
+  p = batch_entry(p);
   __shared__ __attribute__((aligned(16))) float As[T][T + 1];
   __shared__ __attribute__((aligned(16))) float Bs[T][T];
   const int t = threadIdx.x;
@@ -87,15 +88,15 @@ __global__ __launch_bounds__(256) void lds_tiled_kernel(Problem p, int col_block
 
 }  // namespace
 
-hipError_t launch_lds_tiled(const Problem& p, hipStream_t stream) {
+hipError_t launch_lds_tiled(const Problem& p, int batch, hipStream_t stream) {
   const long long cb = (p.N + T - 1) / T;
   const long long rb = (p.M + T - 1) / T;
   if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
   const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
   if (vec)
-    hipLaunchKernelGGL(lds_tiled_kernel<true>, dim3((unsigned)(cb * rb)), dim3(256), 0, stream, p, (int)cb);
+    hipLaunchKernelGGL(lds_tiled_kernel<true>, dim3((unsigned)(cb * rb), batch), dim3(256), 0, stream, p, (int)cb);
   else
-    hipLaunchKernelGGL(lds_tiled_kernel<false>, dim3((unsigned)(cb * rb)), dim3(256), 0, stream, p, (int)cb);
+    hipLaunchKernelGGL(lds_tiled_kernel<false>, dim3((unsigned)(cb * rb), batch), dim3(256), 0, stream, p, (int)cb);
   return hipGetLastError();
 }
 

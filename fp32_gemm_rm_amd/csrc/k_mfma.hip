@@ -325,6 +325,7 @@ template <int BM, int BN, int BK, int WM, int WN, int KS, int GROUP_M, int MIN_B
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS>;
+  p = batch_entry(p);
   constexpr int kGroups = Cfg::kThreads / 256;
   constexpr int kEdgeFloats = kGroups * EdgeTile::kLdsFloats;  // >= the (kGroups-1)*4*256 reduction floats
   constexpr int kFloats = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
@@ -349,7 +350,7 @@ void mfma_kernel(Problem p, TileMap map) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int KS, int GROUP_M, int MIN_BLOCKS>
-hipError_t launch_cfg(const Problem& p, hipStream_t stream) {
+hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   static_assert(BM % kEdge == 0 && BN % kEdge == 0, "edge tiles of the right strip end at Mf");
   TileMap map;
   map.Mf = (p.M / BM) * BM;
@@ -367,7 +368,7 @@ hipError_t launch_cfg(const Problem& p, hipStream_t stream) {
   const long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
   const long long blocks = (long long)map.tiles_m * map.tiles_n + edge_tiles;
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks), block(WM * WN * KS * 64);
+  const dim3 grid((unsigned)blocks, batch), block(WM * WN * KS * 64);
   if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
     hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, GROUP_M, MIN_BLOCKS, true>), grid, block, 0, stream,
                        p, map);
@@ -379,15 +380,16 @@ hipError_t launch_cfg(const Problem& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_mfma(const Problem& p, hipStream_t stream) {
+hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream) {
   // 256 x 256 tiles (one 16-wavefront workgroup per CU) once they fill the 256 CUs.
   // Smaller problems use 128 x 128 or 64 x 64 tiles with the K-tile split over 4
-  // wavefronts per output block, so every SIMD still has 4 wavefronts.
-  const long long t256 = (long long)(p.M / 256) * (p.N / 256);
-  const long long t128 = (long long)(p.M / 128) * (p.N / 128);
-  if (t256 >= 256) return launch_cfg<256, 256, 16, 4, 4, 1, 8, 1>(p, stream);
-  if (t128 >= 256) return launch_cfg<128, 128, 32, 2, 2, 2, 8, 1>(p, stream);
-  return launch_cfg<64, 64, 64, 2, 2, 4, 8, 2>(p, stream);
+  // wavefronts per output block, so every SIMD still has 4 wavefronts.  Tiles are
+  // counted over the whole batch.
+  const long long t256 = (long long)(p.M / 256) * (p.N / 256) * batch;
+  const long long t128 = (long long)(p.M / 128) * (p.N / 128) * batch;
+  if (t256 >= 256) return launch_cfg<256, 256, 16, 4, 4, 1, 8, 1>(p, batch, stream);
+  if (t128 >= 256) return launch_cfg<128, 128, 32, 2, 2, 2, 8, 1>(p, batch, stream);
+  return launch_cfg<64, 64, 64, 2, 2, 4, 8, 2>(p, batch, stream);
 }
 
 }  // namespace sgemm_impl

@@ -16,6 +16,7 @@ constexpr int kNaiveCols = 64;  // one wavefront across columns
 constexpr int kNaiveRows = 4;
 
 __global__ __launch_bounds__(kNaiveCols* kNaiveRows) void naive_kernel(Problem p, int col_blocks) {
+  p = batch_entry(p);
   const int bm = blockIdx.x / col_blocks;
   const int bn = blockIdx.x - bm * col_blocks;
   const int i = bm * kNaiveRows + threadIdx.y;
@@ -30,8 +31,9 @@ __global__ __launch_bounds__(kNaiveCols* kNaiveRows) void naive_kernel(Problem p
 }
 
 // C := beta*C (zeros when beta == 0, without reading C).  One thread per element.
-__global__ __launch_bounds__(256) void scale_kernel(float* C, long long ldc, int M, int N, float beta,
-                                                    int col_blocks) {
+__global__ __launch_bounds__(256) void scale_kernel(float* C, long long ldc, long long sC, int M, int N,
+                                                    float beta, int col_blocks) {
+  C += blockIdx.y * sC;
   const int bm = blockIdx.x / col_blocks;
   const int bn = blockIdx.x - bm * col_blocks;
   const int i = bm * 4 + threadIdx.y;
@@ -43,21 +45,21 @@ __global__ __launch_bounds__(256) void scale_kernel(float* C, long long ldc, int
 
 }  // namespace
 
-hipError_t launch_naive(const Problem& p, hipStream_t stream) {
+hipError_t launch_naive(const Problem& p, int batch, hipStream_t stream) {
   const long long cb = (p.N + kNaiveCols - 1) / kNaiveCols;
   const long long rb = (p.M + kNaiveRows - 1) / kNaiveRows;
   if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(naive_kernel, dim3((unsigned)(cb * rb)), dim3(kNaiveCols, kNaiveRows), 0, stream, p,
+  hipLaunchKernelGGL(naive_kernel, dim3((unsigned)(cb * rb), batch), dim3(kNaiveCols, kNaiveRows), 0, stream, p,
                      (int)cb);
   return hipGetLastError();
 }
 
-hipError_t launch_scale(const Problem& p, hipStream_t stream) {
+hipError_t launch_scale(const Problem& p, int batch, hipStream_t stream) {
   const long long cb = (p.N + 63) / 64;
   const long long rb = (p.M + 3) / 4;
   if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)(cb * rb)), dim3(64, 4), 0, stream, p.C, p.ldc, p.M, p.N,
-                     p.beta, (int)cb);
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)(cb * rb), batch), dim3(64, 4), 0, stream, p.C, p.ldc, p.sC, p.M,
+                     p.N, p.beta, (int)cb);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ namespace {
 
 template <int BM, int BN, int BK, int TM, int TN, int PAD_A, bool VEC>
 __global__ __launch_bounds__(256) void regblock_kernel(Problem p, int col_blocks) {
+  p = batch_entry(p);
   using RB = RegBlock<BM, BN, BK, TM, TN, 256, PAD_A>;
   __shared__ __attribute__((aligned(16))) float lds[RB::kLdsFloats];
   const int bm = blockIdx.x / col_blocks;
@@ -22,11 +23,11 @@ __global__ __launch_bounds__(256) void regblock_kernel(Problem p, int col_blocks
 }
 
 template <int BM, int BN, int BK, int TM, int TN, int PAD_A>
-hipError_t launch_cfg(const Problem& p, hipStream_t stream) {
+hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   const long long cb = (p.N + BN - 1) / BN;
   const long long rb = (p.M + BM - 1) / BM;
   if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)(cb * rb)), block(256);
+  const dim3 grid((unsigned)(cb * rb), batch), block(256);
   if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
     hipLaunchKernelGGL((regblock_kernel<BM, BN, BK, TM, TN, PAD_A, true>), grid, block, 0, stream, p, (int)cb);
   else
@@ -36,10 +37,10 @@ hipError_t launch_cfg(const Problem& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_regblock(const Problem& p, hipStream_t stream) {
-  const long long tiles128 = (long long)((p.M + 127) / 128) * ((p.N + 127) / 128);
-  if (tiles128 >= 512) return launch_cfg<128, 128, 8, 8, 8, 4>(p, stream);
-  return launch_cfg<64, 64, 16, 4, 4, 4>(p, stream);
+hipError_t launch_regblock(const Problem& p, int batch, hipStream_t stream) {
+  const long long tiles128 = (long long)((p.M + 127) / 128) * ((p.N + 127) / 128) * batch;
+  if (tiles128 >= 512) return launch_cfg<128, 128, 8, 8, 8, 4>(p, batch, stream);
+  return launch_cfg<64, 64, 16, 4, 4, 4>(p, batch, stream);
 }
 
 }  // namespace sgemm_impl

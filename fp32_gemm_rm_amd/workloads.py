@@ -104,6 +104,74 @@ def workload_inputs(w: GemmWorkload):
     return make_inputs(w.M, w.N, w.K, w.lda, w.ldb, w.ldc, w.dist, w.seed, w.c_init)
 
 
+@dataclass(frozen=True)
+class BatchedWorkload:
+    """A strided batch of equal-shape SGEMMs (contiguous matrices, stride = matrix size)."""
+
+    name: str
+    batch: int
+    M: int
+    N: int
+    K: int
+    dist: str
+    seed: int
+    alpha: float
+    beta: float
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.M * self.N * self.K
+
+
+#: Batched workload of "GPU-accelerated matrix computation ..." section 4.2: 1024 products
+#: of 64 x 64 matrices in one call (batchCount = 1024; strides M*K, K*N, M*N).
+BATCHED_WORKLOADS = (
+    BatchedWorkload("sgemm_batched_1024x64", 1024, 64, 64, 64, "uniform", 5, 1.0, 0.0),
+)
+BATCHED_BY_NAME = {w.name: w for w in BATCHED_WORKLOADS}
+
+
+def make_batched_inputs(batch, M, N, K, lda, ldb, ldc, sA, sB, sC, dist="uniform", seed=0, c_init="zeros"):
+    """Flat buffers (A, B, C) of a strided batch.  Entry b is drawn as make_inputs would draw it
+    (A, B, then C) from one generator, in batch order; everything outside the entries' logical
+    windows (row padding and the gaps between entries) is NaN for A and B and the C sentinel for C.
+    A stride of 0 shares one matrix between all entries (drawn once)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    nA = max((batch - 1) * sA + (M - 1) * lda + K, M * lda) if batch else 0
+    nB = max((batch - 1) * sB + (K - 1) * ldb + N, K * ldb) if batch else 0
+    nC = max((batch - 1) * sC + (M - 1) * ldc + N, M * ldc) if batch else 0
+    A = np.full(nA, np.nan, np.float32)
+    B = np.full(nB, np.nan, np.float32)
+    C = np.full(nC, C_PAD_SENTINEL, np.float32)
+    for b in range(batch):
+        a = _draw(gen, M, K, dist)
+        bb = _draw(gen, K, N, dist)
+        if c_init == "random":
+            c = _draw(gen, M, N, dist)
+        elif c_init == "zeros":
+            c = np.zeros((M, N), np.float32)
+        else:
+            c = np.full((M, N), np.nan, np.float32)
+        if b == 0 or sA:
+            _put(A, b * sA, a, lda)
+        if b == 0 or sB:
+            _put(B, b * sB, bb, ldb)
+        _put(C, b * sC, c, ldc)
+    return A, B, C
+
+
+def _put(buf: np.ndarray, offset: int, mat: np.ndarray, ld: int) -> None:
+    """Write mat's rows into the flat buffer at offset, row i at offset + i*ld."""
+    rows, cols = mat.shape
+    if rows == 0 or cols == 0:
+        return
+    if offset + rows * ld <= buf.size:
+        buf[offset: offset + rows * ld].reshape(rows, ld)[:, :cols] = mat
+    else:  # the last entry's last row may end at its logical width
+        for i in range(rows):
+            buf[offset + i * ld: offset + i * ld + cols] = mat[i]
+
+
 def integer_matrix(rows: int, cols: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """Integer-valued float32 matrix with entries drawn uniformly from [lo, hi]."""
     gen = torch.Generator(device="cpu").manual_seed(int(seed))

@@ -36,15 +36,17 @@
  * the same inputs are bitwise identical.
  *
  * Return value: 0 on success.  A negative value -p names the first invalid
- * argument by its 1-based position p (checked before any HIP call):
+ * argument by its 1-based position p in the call's parameter list, checked in
+ * that order before any HIP call.  For sgemm_rm / sgemm_rm_ex:
  *   -1 M < 0          -2 N < 0            -3 K < 0
  *   -5 A == NULL while A is read          -6 lda < max(1, K)
  *   -7 B == NULL while B is read          -8 ldb < max(1, N)
  *   -10 C == NULL while M*N > 0           -11 ldc < max(1, N)
  *   -13 (sgemm_rm_ex only) unknown variant
- * A positive value is the hipError_t reported by the HIP runtime for the
- * launch (the analogue of checking cudaGetLastError after a launch that the
- * mlqm.cn/news/1180856 troubleshooting table, section 7, recommends).
+ * For the strided-batched calls see their declarations.  A positive value is
+ * the hipError_t reported by the HIP runtime for a launch (the analogue of
+ * checking cudaGetLastError after a launch, which the mlqm.cn/news/1180856
+ * troubleshooting table, section 7, recommends).
  */
 #ifndef SGEMM_RM_H
 #define SGEMM_RM_H
@@ -84,7 +86,34 @@ int sgemm_rm(int M, int N, int K, float alpha, const float* A, int lda, const fl
 int sgemm_rm_ex(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb,
                 float beta, float* C, int ldc, hipStream_t stream, int variant);
 
-/* Static, NUL-terminated description of a return code of the calls above. */
+/*
+ * Strided batch of independent GEMMs, all with the same M, N, K, alpha, beta and
+ * leading dimensions (the strided-batched form of "GPU-accelerated matrix
+ * computation ..." section 4.2, which batches many small products in one call):
+ *
+ *     for b in [0, batch):  C_b := alpha * A_b * B_b + beta * C_b
+ *     A_b = A + b*strideA,  B_b = B + b*strideB,  C_b = C + b*strideC   (in floats)
+ *
+ * Strides may be 0 for A or B (the same operand for every entry).  The C
+ * matrices of different entries must not overlap: strideC >= (M-1)*ldc + N
+ * when batch > 1.  One launch covers up to 65535 entries; larger batches are
+ * split into several launches on the same stream.  Return codes, by position:
+ *   -1 M, -2 N, -3 K < 0; -5 A NULL while read; -6 lda < max(1,K);
+ *   -7 strideA < 0; -8 B NULL while read; -9 ldb < max(1,N); -10 strideB < 0;
+ *   -12 C NULL while written; -13 ldc < max(1,N); -14 strideC < 0 or outputs
+ *   overlap; -15 batch < 0; -17 (the _ex form) unknown variant.
+ */
+int sgemm_rm_strided_batched(int M, int N, int K, float alpha, const float* A, int lda, long long strideA,
+                             const float* B, int ldb, long long strideB, float beta, float* C, int ldc,
+                             long long strideC, int batch, hipStream_t stream);
+
+/* As sgemm_rm_strided_batched, with the kernel family forced (enum sgemm_rm_variant). */
+int sgemm_rm_strided_batched_ex(int M, int N, int K, float alpha, const float* A, int lda, long long strideA,
+                                const float* B, int ldb, long long strideB, float beta, float* C, int ldc,
+                                long long strideC, int batch, hipStream_t stream, int variant);
+
+/* Static, NUL-terminated description of a return code of the calls above
+ * ("invalid argument p" for -p, the HIP runtime's text for a hipError_t). */
 const char* sgemm_rm_strerror(int code);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */

@@ -26,7 +26,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strerror", "sgemm_rm_version"]
+    assert _declared_functions() == ["sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strerror", "sgemm_rm_strided_batched",
+                                     "sgemm_rm_strided_batched_ex", "sgemm_rm_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(raw, name), name
     assert set(EXPORTED_SYMBOLS) == set(_declared_functions())
-    assert lib.sgemm_rm_version() == 100
+    assert lib.sgemm_rm_version() == 200
 
 
 F = 0x1000  # a non-null dummy pointer: never dereferenced, the calls return before any launch
@@ -86,8 +87,8 @@ def test_strerror(lib):
     from fp32_gemm_rm_amd import sgemm_rm_strerror
 
     assert sgemm_rm_strerror(0) == "success"
-    for code in (-1, -2, -3, -5, -6, -7, -8, -10, -11, -13):
-        assert sgemm_rm_strerror(code).startswith(f"invalid argument {-code}")
+    for code in range(-17, 0):
+        assert sgemm_rm_strerror(code) == f"invalid argument {-code}"
     assert sgemm_rm_strerror(-99) == "unknown error code"
 
 
@@ -97,3 +98,39 @@ def test_binding_raises_on_invalid_arguments(lib):
     with pytest.raises(SgemmError) as e:
         sgemm_rm(4, 4, 4, 1.0, F, 2, F, 4, 0.0, F, 4)
     assert e.value.code == -6
+
+
+G = 1 << 20  # a batch stride large enough for the 4 x 4 problems below
+
+
+@pytest.mark.parametrize(
+    "args,code",
+    [
+        ((-1, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2), -1),
+        ((4, -1, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2), -2),
+        ((4, 4, -1, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2), -3),
+        ((4, 4, 4, 1.0, None, 4, G, F, 4, G, 0.0, F, 4, G, 2), -5),
+        ((4, 4, 4, 1.0, F, 3, G, F, 4, G, 0.0, F, 4, G, 2), -6),
+        ((4, 4, 4, 1.0, F, 4, -1, F, 4, G, 0.0, F, 4, G, 2), -7),
+        ((4, 4, 4, 1.0, F, 4, G, None, 4, G, 0.0, F, 4, G, 2), -8),
+        ((4, 4, 4, 1.0, F, 4, G, F, 3, G, 0.0, F, 4, G, 2), -9),
+        ((4, 4, 4, 1.0, F, 4, G, F, 4, -4, 0.0, F, 4, G, 2), -10),
+        ((4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, None, 4, G, 2), -12),
+        ((4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 3, G, 2), -13),
+        ((4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, 15, 2), -14),  # outputs overlap: 3*4+4 = 16 > 15
+        ((4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, -16, 2), -14),
+        ((4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, -1), -15),
+    ],
+)
+def test_batched_invalid_arguments(lib, args, code):
+    assert lib.sgemm_rm_strided_batched(*args, None) == code
+    assert lib.sgemm_rm_strided_batched_ex(*args, None, 0) == code
+
+
+def test_batched_quick_returns_and_variant(lib):
+    # batch == 0, M == 0 or N == 0: nothing launched, NULL buffers allowed
+    assert lib.sgemm_rm_strided_batched(4, 4, 4, 1.0, None, 4, 0, None, 4, 0, 0.0, None, 4, 0, 0, None) == 0
+    assert lib.sgemm_rm_strided_batched(0, 4, 4, 1.0, None, 4, 0, None, 4, 0, 0.0, None, 4, 0, 3, None) == 0
+    # a single entry may use any strideC (nothing can overlap)
+    assert lib.sgemm_rm_strided_batched(4, 4, 4, 0.0, None, 4, 0, None, 4, 0, 1.0, F, 4, 0, 1, None) == 0
+    assert lib.sgemm_rm_strided_batched_ex(4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2, None, 7) == -17
