@@ -1,10 +1,14 @@
 """Row-major FP32 GEMM for AMD Instinct MI355X (gfx950).
 
 ``C = alpha * A @ B + beta * C`` on row-major operands with leading
-dimensions, computed by hand-written HIP kernels in ``libsgemm_rm.so`` behind
-a C ABI (``include/sgemm_rm.h``).  The Python side only marshals arguments.
+dimensions, with transposed operands, column-major storage and strided
+batches as further forms, computed by hand-written HIP kernels in
+``libsgemm_rm.so`` behind a C ABI (``include/sgemm_rm.h``).  The Python side
+only marshals arguments.
 """
 from .binding import (  # noqa: F401
+    SGEMM_RM_OP_N,
+    SGEMM_RM_OP_T,
     SGEMM_RM_VARIANT_AUTO,
     SGEMM_RM_VARIANT_LDS_TILED,
     SGEMM_RM_VARIANT_MFMA,
@@ -16,8 +20,12 @@ from .binding import (  # noqa: F401
     load_library,
     sgemm,
     sgemm_batched,
+    sgemm_cm,
+    sgemm_cm_strided_batched_ex,
     sgemm_rm,
     sgemm_rm_ex,
+    sgemm_rm_op,
+    sgemm_rm_op_strided_batched_ex,
     sgemm_rm_strerror,
     sgemm_rm_strided_batched,
     sgemm_rm_strided_batched_ex,

@@ -23,12 +23,16 @@ VARIANTS = {
     "mfma": SGEMM_RM_VARIANT_MFMA,
 }
 
+SGEMM_RM_OP_N = 0
+SGEMM_RM_OP_T = 1
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libsgemm_rm.so"
 _lib = None
 
 #: Names the header declares; the CPU tests check that the library exports each.
 EXPORTED_SYMBOLS = ("sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex",
+                    "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex", "sgemm_cm", "sgemm_cm_strided_batched_ex",
                     "sgemm_rm_strerror", "sgemm_rm_version")
 
 
@@ -67,6 +71,14 @@ def load_library():
         lib.sgemm_rm_strided_batched.restype = ctypes.c_int
         lib.sgemm_rm_strided_batched_ex.argtypes = bargs + [ctypes.c_int]
         lib.sgemm_rm_strided_batched_ex.restype = ctypes.c_int
+        oargs = [ctypes.c_int, ctypes.c_int] + args
+        for name in ("sgemm_rm_op", "sgemm_cm"):
+            getattr(lib, name).argtypes = oargs
+            getattr(lib, name).restype = ctypes.c_int
+        obargs = [ctypes.c_int, ctypes.c_int] + bargs + [ctypes.c_int]
+        for name in ("sgemm_rm_op_strided_batched_ex", "sgemm_cm_strided_batched_ex"):
+            getattr(lib, name).argtypes = obargs
+            getattr(lib, name).restype = ctypes.c_int
         lib.sgemm_rm_strerror.argtypes = [ctypes.c_int]
         lib.sgemm_rm_strerror.restype = ctypes.c_char_p
         lib.sgemm_rm_version.argtypes = []
@@ -117,17 +129,78 @@ def sgemm_rm_strided_batched_ex(M, N, K, alpha, A, lda, strideA, B, ldb, strideB
         int(strideB), float(beta), C or None, int(ldc), int(strideC), int(batch), stream or None, int(variant)))
 
 
-def _matrix_view(t, name):
+def sgemm_rm_op(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0):
+    """C := alpha*op(A)*op(B) + beta*C, row-major, on raw device pointers; raises SgemmError."""
+    lib = load_library()
+    return _check(lib.sgemm_rm_op(int(transA), int(transB), int(M), int(N), int(K), float(alpha), A or None,
+                                  int(lda), B or None, int(ldb), float(beta), C or None, int(ldc), stream or None))
+
+
+def sgemm_rm_op_strided_batched_ex(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                                   strideC, batch, stream=0, variant=SGEMM_RM_VARIANT_AUTO):
+    """The general row-major call (operation arguments, strided batch, kernel family)."""
+    lib = load_library()
+    return _check(lib.sgemm_rm_op_strided_batched_ex(
+        int(transA), int(transB), int(M), int(N), int(K), float(alpha), A or None, int(lda), int(strideA),
+        B or None, int(ldb), int(strideB), float(beta), C or None, int(ldc), int(strideC), int(batch),
+        stream or None, int(variant)))
+
+
+def sgemm_cm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0):
+    """C := alpha*op(A)*op(B) + beta*C, column-major (BLAS), on raw device pointers."""
+    lib = load_library()
+    return _check(lib.sgemm_cm(int(transA), int(transB), int(M), int(N), int(K), float(alpha), A or None,
+                               int(lda), B or None, int(ldb), float(beta), C or None, int(ldc), stream or None))
+
+
+def sgemm_cm_strided_batched_ex(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                                strideC, batch, stream=0, variant=SGEMM_RM_VARIANT_AUTO):
+    """Strided batch of column-major problems with the kernel family forced."""
+    lib = load_library()
+    return _check(lib.sgemm_cm_strided_batched_ex(
+        int(transA), int(transB), int(M), int(N), int(K), float(alpha), A or None, int(lda), int(strideA),
+        B or None, int(ldb), int(strideB), float(beta), C or None, int(ldc), int(strideC), int(batch),
+        stream or None, int(variant)))
+
+
+def operand_layout(rows, cols, stride0, stride1, name="X"):
+    """(ld, op) of a rows x cols view with element strides (stride0, stride1), read as
+    op(X): a view with unit column stride is a row-major matrix (op N, ld = stride0);
+    one with unit row stride (``X.t()`` of a row-major X) is the transpose of the
+    row-major matrix underneath (op T, ld = stride1)."""
+    if cols <= 1 or stride1 == 1:
+        ld = stride0 if rows > 1 else max(cols, 1)
+        if ld < max(cols, 1):
+            raise ValueError(f"{name} rows overlap (stride(0) = {ld} < {cols} columns)")
+        return ld, SGEMM_RM_OP_N
+    if rows <= 1 or stride0 == 1:
+        ld = stride1 if cols > 1 else max(rows, 1)
+        if ld < max(rows, 1):
+            raise ValueError(f"{name} columns overlap (stride(1) = {ld} < {rows} rows)")
+        return ld, SGEMM_RM_OP_T
+    raise ValueError(f"{name} needs a unit stride along one dimension")
+
+
+def _device_matrix(t, name):
     import torch
 
     if t.dtype != torch.float32 or t.dim() != 2 or not t.is_cuda:
         raise TypeError(f"{name} must be a 2-D float32 device tensor")
-    rows, cols = t.shape
-    if cols > 1 and t.stride(1) != 1:
+
+
+def _operand_view(t, name):
+    """(pointer, ld, op) of a 2-D float32 device tensor read as op(X)."""
+    _device_matrix(t, name)
+    ld, op = operand_layout(t.shape[0], t.shape[1], t.stride(0), t.stride(1), name)
+    return t.data_ptr(), ld, op
+
+
+def _matrix_view(t, name):
+    """(pointer, ld) of a row-major 2-D float32 device tensor view."""
+    _device_matrix(t, name)
+    ld, op = operand_layout(t.shape[0], t.shape[1], t.stride(0), t.stride(1), name)
+    if op != SGEMM_RM_OP_N:
         raise ValueError(f"{name} must have unit column stride (row-major)")
-    ld = t.stride(0) if rows > 1 else max(cols, 1)
-    if rows > 1 and ld < max(cols, 1):
-        raise ValueError(f"{name} rows overlap (stride(0) = {ld} < {cols} columns)")
     return t.data_ptr(), ld
 
 
@@ -154,8 +227,10 @@ def sgemm_batched(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, s
 
 
 def sgemm(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, stream=None):
-    """C := alpha*A@B + beta*C in place on 2-D float32 device tensors (row-major views,
-    leading dimension = stride(0)), on torch's current stream unless ``stream`` is given."""
+    """C := alpha*A@B + beta*C in place on 2-D float32 device tensors, on torch's current
+    stream unless ``stream`` is given.  C is a row-major view (leading dimension =
+    stride(0)); A and B may be row-major views or transposed ones (``X.t()`` of a
+    row-major X), which run as the transposed-operand forms without a copy."""
     import torch
 
     if isinstance(variant, str):
@@ -164,8 +239,9 @@ def sgemm(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, stream=No
     K2, N = B.shape
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
-    a, lda = _matrix_view(A, "A")
-    b, ldb = _matrix_view(B, "B")
+    a, lda, ta = _operand_view(A, "A")
+    b, ldb, tb = _operand_view(B, "B")
     c, ldc = _matrix_view(C, "C")
     s = (stream if stream is not None else torch.cuda.current_stream(C.device)).cuda_stream
-    return sgemm_rm_ex(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, s, variant)
+    return sgemm_rm_op_strided_batched_ex(ta, tb, M, N, K, alpha, a, lda, 0, b, ldb, 0, beta, c, ldc, 0, 1, s,
+                                          variant)

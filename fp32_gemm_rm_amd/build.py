@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libsgemm_rm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["sgemm_rm.hip", "k_naive.hip", "k_lds_tiled.hip", "k_regblock.hip", "k_mfma.hip"]
+SOURCES = ["sgemm_rm.hip", "k_naive.hip", "k_lds_tiled.hip", "k_regblock.hip", "k_mfma_nn.hip", "k_mfma_nt.hip",
+           "k_mfma_tn.hip", "k_mfma_tt.hip"]
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

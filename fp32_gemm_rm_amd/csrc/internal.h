@@ -22,6 +22,9 @@ struct Problem {
   // strided batch: matrix b of the batch starts at A + b*sA, B + b*sB, C + b*sC;
   // the batch index is blockIdx.y (0 for a single GEMM)
   long long sA, sB, sC;
+  // op(A) = A^T (A stored K x M, element (m, k) at A[k*lda + m]) / op(B) = B^T (B stored
+  // N x K, element (k, n) at B[n*ldb + k]); C is always the M x N row-major result
+  int ta, tb;
 };
 
 // The problem of batch entry blockIdx.y (device side, at the top of every kernel).
@@ -57,8 +60,16 @@ hipError_t launch_naive(const Problem& p, int batch, hipStream_t stream);
 hipError_t launch_lds_tiled(const Problem& p, int batch, hipStream_t stream);
 hipError_t launch_regblock(const Problem& p, int batch, hipStream_t stream);
 // MFMA tiles for the full BM x BN tiles plus bounds-checked register-blocked
-// tiles (the scalar edge-tile path) for the strips past them, in one launch.
-hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream);
+// tiles (the scalar edge-tile path) for the strips past them, in one launch; one
+// instantiation per operand orientation (p.ta, p.tb), dispatched by launch_mfma.
+hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream);
+hipError_t launch_mfma_nt(const Problem& p, int batch, hipStream_t stream);
+hipError_t launch_mfma_tn(const Problem& p, int batch, hipStream_t stream);
+hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream);
+inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream) {
+  if (p.ta) return p.tb ? launch_mfma_tt(p, batch, stream) : launch_mfma_tn(p, batch, stream);
+  return p.tb ? launch_mfma_nt(p, batch, stream) : launch_mfma_nn(p, batch, stream);
+}
 // C := beta*C on the M x N window (zeros when beta == 0; C is then not read).
 hipError_t launch_scale(const Problem& p, int batch, hipStream_t stream);
 

@@ -39,7 +39,11 @@ __device__ __forceinline__ float4 load4_guarded(const float* base, long long ld,
   return v;
 }
 
-template <bool VEC>
+// TA / TB: A stored K x M (element (i, k) at A[k*lda + i]) / B stored N x K.  A
+// transposed operand is read with the same coalesced float4 loads along its
+// contiguous dimension, and the four values are written down a column of the
+// As[m][k] / Bs[k][n] tile instead of along a row.
+template <bool VEC, bool TA, bool TB>
 __global__ __launch_bounds__(256) void lds_tiled_kernel(Problem p, int col_blocks) {
   p = batch_entry(p);
   __shared__ __attribute__((aligned(16))) float As[T][T + 1];
@@ -49,19 +53,35 @@ __global__ __launch_bounds__(256) void lds_tiled_kernel(Problem p, int col_block
   const int bm = blockIdx.x / col_blocks;
   const int bn = blockIdx.x - bm * col_blocks;
   const int m0 = bm * T, n0 = bn * T;
-  const float* A = p.A + (long long)m0 * p.lda;
-  const float* B = p.B + n0;
+  const float* A = TA ? p.A + m0 : p.A + (long long)m0 * p.lda;
+  const float* B = TB ? p.B + (long long)n0 * p.ldb : p.B + n0;
   const int rows_left = p.M - m0, cols_left = p.N - n0;
 
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
   for (int k0 = 0; k0 < p.K; k0 += T) {
-    const float4 a = load4_guarded<VEC>(A + k0, p.lda, ty, 4 * tx, rows_left, p.K - k0);
-    const float4 b = load4_guarded<VEC>(B + (long long)k0 * p.ldb, p.ldb, ty, 4 * tx, p.K - k0, cols_left);
-    As[ty][4 * tx + 0] = a.x;
-    As[ty][4 * tx + 1] = a.y;
-    As[ty][4 * tx + 2] = a.z;
-    As[ty][4 * tx + 3] = a.w;
-    *reinterpret_cast<float4*>(&Bs[ty][4 * tx]) = b;
+    if (TA) {  // a = A(m0 + 4tx .. 4tx+3, k0 + ty)
+      const float4 a = load4_guarded<VEC>(A + (long long)k0 * p.lda, p.lda, ty, 4 * tx, p.K - k0, rows_left);
+      As[4 * tx + 0][ty] = a.x;
+      As[4 * tx + 1][ty] = a.y;
+      As[4 * tx + 2][ty] = a.z;
+      As[4 * tx + 3][ty] = a.w;
+    } else {  // a = A(m0 + ty, k0 + 4tx .. 4tx+3)
+      const float4 a = load4_guarded<VEC>(A + k0, p.lda, ty, 4 * tx, rows_left, p.K - k0);
+      As[ty][4 * tx + 0] = a.x;
+      As[ty][4 * tx + 1] = a.y;
+      As[ty][4 * tx + 2] = a.z;
+      As[ty][4 * tx + 3] = a.w;
+    }
+    if (TB) {  // b = B(k0 + 4tx .. 4tx+3, n0 + ty)
+      const float4 b = load4_guarded<VEC>(B + k0, p.ldb, ty, 4 * tx, cols_left, p.K - k0);
+      Bs[4 * tx + 0][ty] = b.x;
+      Bs[4 * tx + 1][ty] = b.y;
+      Bs[4 * tx + 2][ty] = b.z;
+      Bs[4 * tx + 3][ty] = b.w;
+    } else {  // b = B(k0 + ty, n0 + 4tx .. 4tx+3)
+      *reinterpret_cast<float4*>(&Bs[ty][4 * tx]) =
+          load4_guarded<VEC>(B + (long long)k0 * p.ldb, p.ldb, ty, 4 * tx, p.K - k0, cols_left);
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < T; ++k) {
@@ -93,10 +113,21 @@ hipError_t launch_lds_tiled(const Problem& p, int batch, hipStream_t stream) {
   const long long rb = (p.M + T - 1) / T;
   if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
   const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
-  if (vec)
-    hipLaunchKernelGGL(lds_tiled_kernel<true>, dim3((unsigned)(cb * rb), batch), dim3(256), 0, stream, p, (int)cb);
-  else
-    hipLaunchKernelGGL(lds_tiled_kernel<false>, dim3((unsigned)(cb * rb), batch), dim3(256), 0, stream, p, (int)cb);
+  const dim3 grid((unsigned)(cb * rb), batch), block(256);
+#define SGEMM_LAUNCH_TILED(V, TA_, TB_) \
+  hipLaunchKernelGGL((lds_tiled_kernel<V, TA_, TB_>), grid, block, 0, stream, p, (int)cb)
+  if (vec) {
+    if (p.ta && p.tb) SGEMM_LAUNCH_TILED(true, true, true);
+    else if (p.ta) SGEMM_LAUNCH_TILED(true, true, false);
+    else if (p.tb) SGEMM_LAUNCH_TILED(true, false, true);
+    else SGEMM_LAUNCH_TILED(true, false, false);
+  } else {
+    if (p.ta && p.tb) SGEMM_LAUNCH_TILED(false, true, true);
+    else if (p.ta) SGEMM_LAUNCH_TILED(false, true, false);
+    else if (p.tb) SGEMM_LAUNCH_TILED(false, false, true);
+    else SGEMM_LAUNCH_TILED(false, false, false);
+  }
+#undef SGEMM_LAUNCH_TILED
   return hipGetLastError();
 }
 

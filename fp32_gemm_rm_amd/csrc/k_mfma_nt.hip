@@ -1,0 +1,10 @@
+// MFMA SGEMM instantiated for op(A) = A, op(B) = B^T (see mfma_gemm.h).
+#include "mfma_gemm.h"
+
+namespace sgemm_impl {
+
+hipError_t launch_mfma_nt(const Problem& p, int batch, hipStream_t stream) {
+  return mfma_detail::launch_op<false, true>(p, batch, stream);
+}
+
+}  // namespace sgemm_impl

@@ -1,0 +1,10 @@
+// MFMA SGEMM instantiated for op(A) = A^T, op(B) = B^T (see mfma_gemm.h).
+#include "mfma_gemm.h"
+
+namespace sgemm_impl {
+
+hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream) {
+  return mfma_detail::launch_op<true, true>(p, batch, stream);
+}
+
+}  // namespace sgemm_impl

@@ -6,7 +6,9 @@
 // covers 64 consecutive columns of one row.  Its B loads B[k*ldb + j] are one
 // contiguous 256-byte segment per k and its A load A[i*lda + k] is the same
 // address for the whole wavefront (a broadcast).  The kernel's limit is reuse,
-// not coalescing: every k-step moves 2 floats per 2 FLOP.
+// not coalescing: every k-step moves 2 floats per 2 FLOP.  With B stored
+// transposed (N x K) the wavefront's B loads stride by ldb instead; the
+// baseline keeps its one-thread-per-element form in every orientation.
 #include "internal.h"
 
 namespace sgemm_impl {
@@ -15,6 +17,8 @@ namespace {
 constexpr int kNaiveCols = 64;  // one wavefront across columns
 constexpr int kNaiveRows = 4;
 
+// TA / TB: A stored K x M (element (i, k) at A[k*lda + i]) / B stored N x K.
+template <bool TA, bool TB>
 __global__ __launch_bounds__(kNaiveCols* kNaiveRows) void naive_kernel(Problem p, int col_blocks) {
   p = batch_entry(p);
   const int bm = blockIdx.x / col_blocks;
@@ -22,10 +26,11 @@ __global__ __launch_bounds__(kNaiveCols* kNaiveRows) void naive_kernel(Problem p
   const int i = bm * kNaiveRows + threadIdx.y;
   const int j = bn * kNaiveCols + threadIdx.x;
   if (i >= p.M || j >= p.N) return;
-  const float* a = p.A + (long long)i * p.lda;
-  const float* b = p.B + j;
+  const float* a = TA ? p.A + i : p.A + (long long)i * p.lda;
+  const float* b = TB ? p.B + (long long)j * p.ldb : p.B + j;
+  const long long sa = TA ? p.lda : 1, sb = TB ? 1 : p.ldb;  // steps along k
   float acc = 0.0f;
-  for (int k = 0; k < p.K; ++k) acc = fmaf(a[k], b[(long long)k * p.ldb], acc);
+  for (int k = 0; k < p.K; ++k) acc = fmaf(a[k * sa], b[k * sb], acc);
   float* c = p.C + (long long)i * p.ldc + j;
   *c = (p.beta == 0.0f) ? p.alpha * acc : fmaf(p.alpha, acc, p.beta * *c);
 }
@@ -49,8 +54,15 @@ hipError_t launch_naive(const Problem& p, int batch, hipStream_t stream) {
   const long long cb = (p.N + kNaiveCols - 1) / kNaiveCols;
   const long long rb = (p.M + kNaiveRows - 1) / kNaiveRows;
   if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(naive_kernel, dim3((unsigned)(cb * rb), batch), dim3(kNaiveCols, kNaiveRows), 0, stream, p,
-                     (int)cb);
+  const dim3 grid((unsigned)(cb * rb), batch), block(kNaiveCols, kNaiveRows);
+  if (p.ta && p.tb)
+    hipLaunchKernelGGL((naive_kernel<true, true>), grid, block, 0, stream, p, (int)cb);
+  else if (p.ta)
+    hipLaunchKernelGGL((naive_kernel<true, false>), grid, block, 0, stream, p, (int)cb);
+  else if (p.tb)
+    hipLaunchKernelGGL((naive_kernel<false, true>), grid, block, 0, stream, p, (int)cb);
+  else
+    hipLaunchKernelGGL((naive_kernel<false, false>), grid, block, 0, stream, p, (int)cb);
   return hipGetLastError();
 }
 

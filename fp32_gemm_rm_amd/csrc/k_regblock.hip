@@ -8,7 +8,7 @@
 namespace sgemm_impl {
 namespace {
 
-template <int BM, int BN, int BK, int TM, int TN, int PAD_A, bool VEC>
+template <int BM, int BN, int BK, int TM, int TN, int PAD_A, bool VEC, bool TA, bool TB>
 __global__ __launch_bounds__(256) void regblock_kernel(Problem p, int col_blocks) {
   p = batch_entry(p);
   using RB = RegBlock<BM, BN, BK, TM, TN, 256, PAD_A>;
@@ -17,9 +17,9 @@ __global__ __launch_bounds__(256) void regblock_kernel(Problem p, int col_blocks
   const int bn = blockIdx.x - bm * col_blocks;
   const int m0 = bm * BM, n0 = bn * BN;
   if (m0 + BM <= p.M && n0 + BN <= p.N)
-    RB::template tile<VEC, false>(p, m0, n0, lds, threadIdx.x);
+    RB::template tile<VEC, false, TA, TB>(p, m0, n0, lds, threadIdx.x);
   else
-    RB::template tile<VEC, true>(p, m0, n0, lds, threadIdx.x);
+    RB::template tile<VEC, true, TA, TB>(p, m0, n0, lds, threadIdx.x);
 }
 
 template <int BM, int BN, int BK, int TM, int TN, int PAD_A>
@@ -28,10 +28,21 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   const long long rb = (p.M + BM - 1) / BM;
   if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(cb * rb), batch), block(256);
-  if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
-    hipLaunchKernelGGL((regblock_kernel<BM, BN, BK, TM, TN, PAD_A, true>), grid, block, 0, stream, p, (int)cb);
-  else
-    hipLaunchKernelGGL((regblock_kernel<BM, BN, BK, TM, TN, PAD_A, false>), grid, block, 0, stream, p, (int)cb);
+  const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
+#define SGEMM_LAUNCH_RB(V, TA_, TB_) \
+  hipLaunchKernelGGL((regblock_kernel<BM, BN, BK, TM, TN, PAD_A, V, TA_, TB_>), grid, block, 0, stream, p, (int)cb)
+  if (vec) {
+    if (p.ta && p.tb) SGEMM_LAUNCH_RB(true, true, true);
+    else if (p.ta) SGEMM_LAUNCH_RB(true, true, false);
+    else if (p.tb) SGEMM_LAUNCH_RB(true, false, true);
+    else SGEMM_LAUNCH_RB(true, false, false);
+  } else {
+    if (p.ta && p.tb) SGEMM_LAUNCH_RB(false, true, true);
+    else if (p.ta) SGEMM_LAUNCH_RB(false, true, false);
+    else if (p.tb) SGEMM_LAUNCH_RB(false, false, true);
+    else SGEMM_LAUNCH_RB(false, false, false);
+  }
+#undef SGEMM_LAUNCH_RB
   return hipGetLastError();
 }
 

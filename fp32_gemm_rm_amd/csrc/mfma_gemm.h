@@ -1,4 +1,5 @@
-// SGEMM on the FP32 matrix cores of gfx950 (v_mfma_f32_32x32x2_f32).
+// SGEMM on the FP32 matrix cores of gfx950 (v_mfma_f32_32x32x2_f32): device code and
+// launch templates, instantiated per operand orientation by k_mfma_{nn,nt,tn,tt}.hip.
 //
 // The pages' fastest designs are register-blocked tiles fed from padded,
 // double-buffered shared memory (sgemmNN page; mhpn.cn "GEMM advanced" page
@@ -34,9 +35,13 @@
 //     r..r+3 (r a multiple of 4) at chunks 0..3; the XOR spreads both over 16
 //     distinct chunk slots.  (With +4-word padding instead, the reads are
 //     conflict-free but the stores are not.)
-//   B tile, 16 rows of BN floats with stride BN + 4 words, stored as loaded.
+//   B tile, BK rows of BN floats with stride BN + 4 words, stored as loaded.
 //     A fragment read is one word per lane: each half-wavefront reads 32
 //     consecutive words of one row.
+//   Transposed operands swap layouts: an operand whose rows run along k in
+//   global memory (A, or B^T stored N x K) takes the swizzled k-contiguous form
+//   and 128-bit fragment reads; one whose rows run along m or n (A^T stored
+//   K x M, or B) takes the k-major padded form and 32-bit fragment reads.
 // Tile order: the hardware hands workgroups to the 8 XCDs round robin; block
 // ids are remapped so that each XCD works on a contiguous run of tiles, and
 // the run walks GROUP_M tile-rows at a time, so the A and B panels of the
@@ -52,58 +57,115 @@
 // LDS in the fixed group order.  Edge workgroups take the highest block ids of
 // the same launch, so they run beside the MFMA tiles instead of after them.  Ragged K is handled inside every
 // MFMA tile: its last K-tile loads zeros past K.
+#pragma once
+
 #include "regblock_tile.h"
 
 namespace sgemm_impl {
-namespace {
+namespace mfma_detail {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <int BM, int BN, int BK, int WM, int WN, int KS>
-struct MfmaCfg {
-  static constexpr int KC = BK / 4;   // 16-byte chunks per A row
-  static constexpr int KG = BK / (16 * KS);  // 16-deep k-groups per wavefront per K-tile
-  static constexpr int kThreads = WM * WN * KS * 64;
-  static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;  // 32x32 blocks per wavefront
-  static constexpr int SB = BN + 4;
-  static constexpr int A_LOADS = BM * BK / 4 / kThreads;  // float4 of A per thread per K-tile
-  static constexpr int B_LOADS = BN * BK / 4 / kThreads;
-  static constexpr int kStageFloats = BM * BK + BK * SB;
-  static constexpr int kReduceFloats = (KS - 1) * BM * BN;
-  static constexpr int kLdsFloats = 2 * kStageFloats > kReduceFloats ? 2 * kStageFloats : kReduceFloats;
-  static_assert(FM >= 1 && FN >= 1, "wavefront tile at least 32 x 32");
-  static_assert(KG >= 1 && KG * 16 * KS == BK && BK <= 64, "K-tile split into 16-deep k-groups");
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "every thread loads A and B");
-  static_assert(A_LOADS * kThreads * 4 == BM * BK && B_LOADS * kThreads * 4 == BN * BK, "even load split");
-};
-
-// Word offset of A(row, 4*chunk) inside one LDS stage whose rows hold BK floats.
+// Word offset of X(row, 4*chunk) inside one LDS stage whose rows hold BK floats.
 // 64 banks hold 16 chunks, i.e. 64/BK rows; chunk indices are XORed with the row's
 // index in units of that period, so 16 consecutive rows at one chunk, and 16/KC
 // rows at all KC chunks, both land on 16 distinct chunk slots.
 template <int BK>
-__device__ __forceinline__ int a_slot(int row, int chunk) {
+__device__ __forceinline__ int swz_slot(int row, int chunk) {
   return row * BK + 4 * (chunk ^ ((row / (64 / BK)) & (BK / 4 - 1)));
 }
 
 template <bool VEC>
-__device__ __forceinline__ float4 load_a4(const float* p, int k_left) {
-  if (k_left >= 4) {
+__device__ __forceinline__ float4 load4(const float* p, int left) {
+  if (left >= 4) {
     if (VEC) return *reinterpret_cast<const float4*>(p);
     return make_float4(p[0], p[1], p[2], p[3]);
   }
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (k_left > 0) v.x = p[0];
-  if (k_left > 1) v.y = p[1];
-  if (k_left > 2) v.z = p[2];
+  if (left > 0) v.x = p[0];
+  if (left > 1) v.y = p[1];
+  if (left > 2) v.z = p[2];
   return v;
 }
 
-template <bool VEC>
-__device__ __forceinline__ float4 load_b4(const float* p) {
-  if (VEC) return *reinterpret_cast<const float4*>(p);
-  return make_float4(p[0], p[1], p[2], p[3]);
-}
+// One MFMA operand of a K-tile: its R x BK slice (R = BM for A, BN for B) as the
+// thread loads it from global memory, stores it in an LDS stage and reads it as
+// MFMA fragments.  KROWS: the operand's rows in memory run along k (A, or B^T):
+// the stage holds R rows of BK floats with swizzled 16-byte chunks and a fragment
+// is two 128-bit reads.  Otherwise (A^T, or B) the stage holds BK rows of R floats
+// with stride R + 4 and a fragment is eight 32-bit reads.
+template <int R, int BK, int NT, bool KROWS>
+struct Operand {
+  static constexpr int KC = BK / 4;
+  static constexpr int LOADS = R * BK / 4 / NT;  // float4 per thread per K-tile
+  static constexpr int STRIDE = KROWS ? BK : R + 4;
+  static constexpr int kStageFloats = KROWS ? R * BK : BK * (R + 4);
+  static_assert(LOADS >= 1 && LOADS * NT * 4 == R * BK, "even load split");
+
+  const float* base;  // element (r0, k = 0) of this tile's slice
+  long long ld;
+  int row[LOADS], col[LOADS];  // KROWS: (r, chunk); else (k, 4 * r-quad)
+  float4 reg[LOADS];
+
+  __device__ __forceinline__ void init(const float* X, long long ldx, int r0, int t) {
+    ld = ldx;
+    base = KROWS ? X + (long long)r0 * ldx : X + r0;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int q = t + i * NT;
+      row[i] = KROWS ? q / KC : q / (R / 4);
+      col[i] = KROWS ? q % KC : (q % (R / 4)) * 4;
+    }
+  }
+  // full K-tile starting at k0
+  template <bool VEC>
+  __device__ __forceinline__ void load_full(int k0) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      reg[i] = KROWS ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], 4)
+                     : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
+  }
+  // last K-tile: kl = K - k0 < BK valid k; zeros past K
+  template <bool VEC>
+  __device__ __forceinline__ void load_tail(int k0, int kl) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      reg[i] = KROWS ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], kl - 4 * col[i])
+                     : (row[i] < kl ? load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f));
+  }
+  __device__ __forceinline__ void store(float* stage) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : row[i] * STRIDE + col[i])) = reg[i];
+  }
+  // out[e] = X(rr, 16g + 8lh + e), e = 0..7: this lane's values for the 8 MFMA steps of k-group g
+  __device__ __forceinline__ static void read(const float* stage, int rr, int g, int lh, float (&out)[8]) {
+    if constexpr (KROWS) {
+      const float4 x0 = *reinterpret_cast<const float4*>(stage + swz_slot<BK>(rr, 4 * g + 2 * lh));
+      const float4 x1 = *reinterpret_cast<const float4*>(stage + swz_slot<BK>(rr, 4 * g + 2 * lh + 1));
+      out[0] = x0.x; out[1] = x0.y; out[2] = x0.z; out[3] = x0.w;
+      out[4] = x1.x; out[5] = x1.y; out[6] = x1.z; out[7] = x1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = stage[(16 * g + 8 * lh + e) * STRIDE + rr];
+    }
+  }
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB>
+struct MfmaCfg {
+  static constexpr int KG = BK / (16 * KS);  // 16-deep k-groups per wavefront per K-tile
+  static constexpr int kThreads = WM * WN * KS * 64;
+  static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;  // 32x32 blocks per wavefront
+  using OpA = Operand<BM, BK, kThreads, !TA>;
+  using OpB = Operand<BN, BK, kThreads, TB>;
+  static constexpr int kStageFloats = OpA::kStageFloats + OpB::kStageFloats;
+  static constexpr int kReduceFloats = (KS - 1) * BM * BN;
+  static constexpr int kLdsFloats = 2 * kStageFloats > kReduceFloats ? 2 * kStageFloats : kReduceFloats;
+  static_assert(FM >= 1 && FN >= 1, "wavefront tile at least 32 x 32");
+  static_assert(KG >= 1 && KG * 16 * KS == BK && BK <= 64, "K-tile split into 16-deep k-groups");
+};
 
 // Where the tiles of one launch are: MFMA tiles first, then the edge tiles of the
 // right strip, then those of the bottom strip.
@@ -114,12 +176,15 @@ struct TileMap {
   int bottom_m, bottom_n;  // 32 x 32 edge tiles in rows [Mf, M)
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int KS, int GROUP_M, bool VEC>
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, bool VEC>
 __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m, int tiles_n, float* smem) {
-  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS>;
-  constexpr int NT = Cfg::kThreads, FM = Cfg::FM, FN = Cfg::FN, SB = Cfg::SB, KC = Cfg::KC, KG = Cfg::KG;
-  float (*As)[BM * BK] = reinterpret_cast<float (*)[BM * BK]>(smem);
-  float (*Bs)[BK * SB] = reinterpret_cast<float (*)[BK * SB]>(smem + 2 * BM * BK);
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
+  using OpA = typename Cfg::OpA;
+  using OpB = typename Cfg::OpB;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, KG = Cfg::KG;
+  // stage s: A at smem + s * kStageFloats, B right after it
+  auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
+  auto b_stage = [&](int s) { return smem + s * Cfg::kStageFloats + OpA::kStageFloats; };
 
   const int t = threadIdx.x;
   const int w = t / 64, l = t % 64;
@@ -137,22 +202,10 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
   const int bn = (bid % group) / gsz;
   const int m0 = bm * BM, n0 = bn * BN;
 
-  // this thread's global-load coordinates (fixed across K-tiles)
-  int a_row[Cfg::A_LOADS], a_chunk[Cfg::A_LOADS], b_row[Cfg::B_LOADS], b_col[Cfg::B_LOADS];
-#pragma unroll
-  for (int i = 0; i < Cfg::A_LOADS; ++i) {
-    const int q = t + i * NT;
-    a_row[i] = q / KC;
-    a_chunk[i] = q % KC;
-  }
-#pragma unroll
-  for (int i = 0; i < Cfg::B_LOADS; ++i) {
-    const int q = t + i * NT;
-    b_row[i] = q / (BN / 4);
-    b_col[i] = (q % (BN / 4)) * 4;
-  }
-  const float* Ablk = p.A + (long long)m0 * p.lda;
-  const float* Bblk = p.B + n0;
+  OpA opa;
+  OpB opb;
+  opa.init(p.A, p.lda, m0, t);
+  opb.init(p.B, p.ldb, n0, t);
 
   v16f acc[FM][FN];
 #pragma unroll
@@ -162,69 +215,36 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nfull = p.K / BK;                // K-tiles with no element past K
+  const int nfull = p.K / BK;  // K-tiles with no element past K
   const int ntiles = (p.K + BK - 1) / BK;
-  float4 ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
+  // global -> registers for K-tile kt; the guarded form (the last, partial K-tile
+  // only) loads zeros past K and is kept out of the steady-state loop
+  auto load = [&](int kt) {
+    if (kt < nfull) {
+      opa.template load_full<VEC>(kt * BK);
+      opb.template load_full<VEC>(kt * BK);
+    } else {
+      opa.template load_tail<VEC>(kt * BK, p.K - kt * BK);
+      opb.template load_tail<VEC>(kt * BK, p.K - kt * BK);
+    }
+  };
 
-  // Global -> registers for K-tile kt.  The guarded form (last, partial K-tile only)
-  // loads zeros past K; it is kept out of the steady-state loop.
-#define SGEMM_LOAD_FULL(kt)                                                                      \
-  do {                                                                                           \
-    const int k0_ = (kt) * BK;                                                                   \
-    _Pragma("unroll") for (int i = 0; i < Cfg::A_LOADS; ++i)                                     \
-        ra[i] = load_a4<VEC>(Ablk + (long long)a_row[i] * p.lda + k0_ + 4 * a_chunk[i], 4);      \
-    _Pragma("unroll") for (int i = 0; i < Cfg::B_LOADS; ++i)                                     \
-        rb[i] = load_b4<VEC>(Bblk + (long long)(k0_ + b_row[i]) * p.ldb + b_col[i]);             \
-  } while (0)
-#define SGEMM_LOAD_TAIL(kt)                                                                      \
-  do {                                                                                           \
-    const int k0_ = (kt) * BK;                                                                   \
-    const int kl_ = p.K - k0_;                                                                   \
-    _Pragma("unroll") for (int i = 0; i < Cfg::A_LOADS; ++i)                                     \
-        ra[i] = load_a4<VEC>(Ablk + (long long)a_row[i] * p.lda + k0_ + 4 * a_chunk[i],          \
-                             kl_ - 4 * a_chunk[i]);                                              \
-    _Pragma("unroll") for (int i = 0; i < Cfg::B_LOADS; ++i)                                     \
-        rb[i] = (b_row[i] < kl_) ? load_b4<VEC>(Bblk + (long long)(k0_ + b_row[i]) * p.ldb + b_col[i]) \
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);                              \
-  } while (0)
-#define SGEMM_STORE_TILE(s)                                                                      \
-  do {                                                                                           \
-    _Pragma("unroll") for (int i = 0; i < Cfg::A_LOADS; ++i)                                     \
-        *reinterpret_cast<float4*>(&As[s][a_slot<BK>(a_row[i], a_chunk[i])]) = ra[i];            \
-    _Pragma("unroll") for (int i = 0; i < Cfg::B_LOADS; ++i)                                     \
-        *reinterpret_cast<float4*>(&Bs[s][b_row[i] * SB + b_col[i]]) = rb[i];                    \
-  } while (0)
-
-  if (nfull > 0)
-    SGEMM_LOAD_FULL(0);
-  else
-    SGEMM_LOAD_TAIL(0);
-  SGEMM_STORE_TILE(0);
+  load(0);
+  opa.store(a_stage(0));
+  opb.store(b_stage(0));
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int s = kt & 1;
-    if (kt + 1 < nfull)
-      SGEMM_LOAD_FULL(kt + 1);
-    else if (kt + 1 < ntiles)
-      SGEMM_LOAD_TAIL(kt + 1);
-
+    if (kt + 1 < ntiles) load(kt + 1);
 #pragma unroll
     for (int r = 0; r < KG; ++r) {
       const int g = ks * KG + r;  // 16-deep k-group of this K-tile
       float af[FM][8], bf[FN][8];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm0 + i * 32 + lr;
-        const float4 x0 = *reinterpret_cast<const float4*>(&As[s][a_slot<BK>(row, 4 * g + 2 * lh)]);
-        const float4 x1 = *reinterpret_cast<const float4*>(&As[s][a_slot<BK>(row, 4 * g + 2 * lh + 1)]);
-        af[i][0] = x0.x; af[i][1] = x0.y; af[i][2] = x0.z; af[i][3] = x0.w;
-        af[i][4] = x1.x; af[i][5] = x1.y; af[i][6] = x1.z; af[i][7] = x1.w;
-      }
+      for (int i = 0; i < FM; ++i) OpA::read(a_stage(s), wm0 + i * 32 + lr, g, lh, af[i]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bf[j][e] = Bs[s][(16 * g + lh * 8 + e) * SB + wn0 + j * 32 + lr];
+      for (int j = 0; j < FN; ++j) OpB::read(b_stage(s), wn0 + j * 32 + lr, g, lh, bf[j]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
 #pragma unroll
@@ -235,14 +255,14 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
         // store the next tile into the other stage half-way through the last k-group's MFMAs
         // (that stage was last read before the previous barrier), so that the LDS writes
         // overlap MFMAs instead of bunching up before the barrier: +1.5% at 4096^3
-        if (e == 3 && r == KG - 1 && kt + 1 < ntiles) SGEMM_STORE_TILE(s ^ 1);
+        if (e == 3 && r == KG - 1 && kt + 1 < ntiles) {
+          opa.store(a_stage(s ^ 1));
+          opb.store(b_stage(s ^ 1));
+        }
       }
     }
     __syncthreads();
   }
-#undef SGEMM_LOAD_FULL
-#undef SGEMM_LOAD_TAIL
-#undef SGEMM_STORE_TILE
 
   if constexpr (KS > 1) {
     // partial sums of K-groups 1..KS-1 through LDS (free after the last barrier),
@@ -293,7 +313,7 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
 using EdgeTile = RegBlock<32, 32, 32, 2, 2, 256, 2, 8>;
 constexpr int kEdge = 32;
 
-template <int GROUPS, bool VEC>
+template <int GROUPS, bool TA, bool TB, bool VEC>
 __device__ __forceinline__ void edge_tile(const Problem& p, int m0, int n0, float* smem) {
   constexpr int BK = 32;
   const int g = threadIdx.x / 256, tid = threadIdx.x % 256;
@@ -304,7 +324,8 @@ __device__ __forceinline__ void edge_tile(const Problem& p, int m0, int n0, floa
   const int kbeg = min(g * span, p.K);
   const int klen = min(span, p.K - kbeg);
   float acc[2][2];
-  EdgeTile::template compute<VEC, true>(p, m0, n0, kbeg, klen, steps, smem + g * EdgeTile::kLdsFloats, tid, acc);
+  EdgeTile::template compute<VEC, true, TA, TB>(p, m0, n0, kbeg, klen, steps, smem + g * EdgeTile::kLdsFloats, tid,
+                                                acc);
   if constexpr (GROUPS > 1) {
     float* red = smem;  // [GROUPS-1][4][256]; the stages are free after compute()'s last barrier
     if (g > 0)
@@ -321,10 +342,10 @@ __device__ __forceinline__ void edge_tile(const Problem& p, int m0, int n0, floa
 }
 
 // MIN_BLOCKS workgroups must fit on one CU at once (a register budget for the compiler).
-template <int BM, int BN, int BK, int WM, int WN, int KS, int GROUP_M, int MIN_BLOCKS, bool VEC>
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS, bool VEC>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
-  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS>;
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   p = batch_entry(p);
   constexpr int kGroups = Cfg::kThreads / 256;
   constexpr int kEdgeFloats = kGroups * EdgeTile::kLdsFloats;  // >= the (kGroups-1)*4*256 reduction floats
@@ -333,7 +354,7 @@ void mfma_kernel(Problem p, TileMap map) {
   const int nmfma = map.tiles_m * map.tiles_n;
   int e = (int)blockIdx.x - nmfma;
   if (e < 0) {
-    mfma_tile<BM, BN, BK, WM, WN, KS, GROUP_M, VEC>(p, blockIdx.x, map.tiles_m, map.tiles_n, smem);
+    mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, VEC>(p, blockIdx.x, map.tiles_m, map.tiles_n, smem);
     return;
   }
   int m0, n0;
@@ -346,10 +367,10 @@ void mfma_kernel(Problem p, TileMap map) {
     m0 = map.Mf + (e / map.bottom_n) * kEdge;
     n0 = (e % map.bottom_n) * kEdge;
   }
-  edge_tile<kGroups, VEC>(p, m0, n0, smem);
+  edge_tile<kGroups, TA, TB, VEC>(p, m0, n0, smem);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int KS, int GROUP_M, int MIN_BLOCKS>
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   static_assert(BM % kEdge == 0 && BN % kEdge == 0, "edge tiles of the right strip end at Mf");
   TileMap map;
@@ -370,26 +391,26 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks, batch), block(WM * WN * KS * 64);
   if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, GROUP_M, MIN_BLOCKS, true>), grid, block, 0, stream,
-                       p, map);
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, true>), grid, block, 0,
+                       stream, p, map);
   else
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, GROUP_M, MIN_BLOCKS, false>), grid, block, 0, stream,
-                       p, map);
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false>), grid, block, 0,
+                       stream, p, map);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream) {
-  // 256 x 256 tiles (one 16-wavefront workgroup per CU) once they fill the 256 CUs.
-  // Smaller problems use 128 x 128 or 64 x 64 tiles with the K-tile split over 4
-  // wavefronts per output block, so every SIMD still has 4 wavefronts.  Tiles are
-  // counted over the whole batch.
+// 256 x 256 tiles (one 16-wavefront workgroup per CU) once they fill the 256 CUs.
+// Smaller problems use 128 x 128 or 64 x 64 tiles with the K-tile split over 2 or 4
+// wavefronts per output block, so that every SIMD still has several wavefronts.
+// Tiles are counted over the whole batch.
+template <bool TA, bool TB>
+hipError_t launch_op(const Problem& p, int batch, hipStream_t stream) {
   const long long t256 = (long long)(p.M / 256) * (p.N / 256) * batch;
   const long long t128 = (long long)(p.M / 128) * (p.N / 128) * batch;
-  if (t256 >= 256) return launch_cfg<256, 256, 16, 4, 4, 1, 8, 1>(p, batch, stream);
-  if (t128 >= 256) return launch_cfg<128, 128, 32, 2, 2, 2, 8, 1>(p, batch, stream);
-  return launch_cfg<64, 64, 64, 2, 2, 4, 8, 2>(p, batch, stream);
+  if (t256 >= 256) return launch_cfg<256, 256, 16, 4, 4, 1, TA, TB, 8, 1>(p, batch, stream);
+  if (t128 >= 256) return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
+  return launch_cfg<64, 64, 64, 2, 2, 4, TA, TB, 8, 2>(p, batch, stream);
 }
 
+}  // namespace mfma_detail
 }  // namespace sgemm_impl

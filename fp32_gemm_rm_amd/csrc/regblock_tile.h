@@ -16,6 +16,9 @@
 //     so that the inner loop reads a thread's TM rows as float4 / float2.
 //   - The B tile BK x BN is loaded with one 128-bit load per thread and stored
 //     as is into Bs[k][n].
+//   - Transposed operands (A stored K x M, B stored N x K) load along their own
+//     contiguous dimension and land in the same As[k][m] / Bs[k][n] layout: A^T
+//     rows store straight, B^T rows store transposed.
 //   - As rows are padded by PAD_A words.  A wavefront's transposing store
 //     writes 64/KQ consecutive rows at each of KQ = BK/4 K-offsets 4q; 32-bit
 //     LDS accesses are served per half-wavefront from 32 banks, so the padding
@@ -45,6 +48,7 @@ struct RegBlock {
   static constexpr int VM = TM >= 4 ? 4 : TM, VN = TN >= 4 ? 4 : TN;  // fragment vector widths
   static constexpr int GM = TM / VM, GN = TN / VN;                    // fragment groups
   static constexpr int KQ = BK / 4;
+  static_assert(KQ <= NT && BM / 4 <= NT && BN / 4 <= NT, "load coordinates");
   static constexpr int SA = BM + PAD_A;
   static_assert((SA * 4) % (VM * 4) == 0, "fragment reads stay aligned");
   static constexpr int kLdsFloats = 2 * BK * SA + 2 * BK * BN;  // two stages of As and Bs
@@ -82,11 +86,12 @@ struct RegBlock {
     return v;
   }
 
-  // acc = A[m0.., kbeg : kbeg+klen] B[kbeg : kbeg+klen, n0..] for one BM x BN tile, in
-  // `ntiles` K-steps of BK (ntiles * BK >= klen; every thread of the workgroup must pass
-  // the same ntiles, since each K-step ends with a workgroup barrier).  lds points to
+  // acc = op(A)[m0.., kbeg : kbeg+klen] op(B)[kbeg : kbeg+klen, n0..] for one BM x BN tile,
+  // in `ntiles` K-steps of BK (ntiles * BK >= klen; every thread of the workgroup must pass
+  // the same ntiles, since each K-step ends with a workgroup barrier).  TA / TB: A is
+  // stored K x M (element (m, k) at A[k*lda + m]) / B is stored N x K.  lds points to
   // kLdsFloats floats of 16-byte aligned LDS; tid in [0, NT).
-  template <bool VEC, bool GUARD>
+  template <bool VEC, bool GUARD, bool TA = false, bool TB = false>
   static __device__ __forceinline__ void compute(const Problem& p, int m0, int n0, int kbeg, int klen, int ntiles,
                                                  float* lds, int tid, float (&acc)[TM][TN]) {
     float* As = lds;                 // [2][BK][SA]
@@ -96,10 +101,14 @@ struct RegBlock {
     const int tm = (w / WAVES_N) * 8 + l / 8;
     const int tn = (w % WAVES_N) * 8 + l % 8;
 
-    const int a_row = tid / KQ, a_k4 = (tid % KQ) * 4;
-    const int b_k = tid / (BN / 4), b_n4 = (tid % (BN / 4)) * 4;
-    const float* Ablk = p.A + (long long)m0 * p.lda + kbeg;
-    const float* Bblk = p.B + (long long)kbeg * p.ldb + n0;
+    // one float4 of A and one of B per thread and K-step, along the operand's contiguous
+    // dimension: A rows of k (A untransposed) or rows of m (transposed), likewise for B
+    const int a_r = TA ? tid / (BM / 4) : tid / KQ;
+    const int a_c = TA ? (tid % (BM / 4)) * 4 : (tid % KQ) * 4;
+    const int b_r = TB ? tid / KQ : tid / (BN / 4);
+    const int b_c = TB ? (tid % KQ) * 4 : (tid % (BN / 4)) * 4;
+    const float* Ablk = TA ? p.A + (long long)kbeg * p.lda + m0 : p.A + (long long)m0 * p.lda + kbeg;
+    const float* Bblk = TB ? p.B + (long long)n0 * p.ldb + kbeg : p.B + (long long)kbeg * p.ldb + n0;
     const int rows_left = p.M - m0, cols_left = p.N - n0;
 
 #pragma unroll
@@ -111,21 +120,41 @@ struct RegBlock {
     float4 av, bv;
     auto load_tile = [&](int kt) {
       const int k0 = kt * BK;
+      const float* ap = TA ? Ablk + (long long)k0 * p.lda : Ablk + k0;
+      const float* bp = TB ? Bblk + k0 : Bblk + (long long)k0 * p.ldb;
+      const int a_rows = TA ? klen - k0 : rows_left, a_cols = TA ? rows_left : klen - k0;
+      const int b_rows = TB ? cols_left : klen - k0, b_cols = TB ? klen - k0 : cols_left;
       if (GUARD || kt >= nfull) {
-        av = gload4<VEC, true>(Ablk + k0, p.lda, a_row, a_k4, rows_left, klen - k0);
-        bv = gload4<VEC, true>(Bblk + (long long)k0 * p.ldb, p.ldb, b_k, b_n4, klen - k0, cols_left);
+        av = gload4<VEC, true>(ap, p.lda, a_r, a_c, a_rows, a_cols);
+        bv = gload4<VEC, true>(bp, p.ldb, b_r, b_c, b_rows, b_cols);
       } else {
-        av = gload4<VEC, false>(Ablk + k0, p.lda, a_row, a_k4, rows_left, klen - k0);
-        bv = gload4<VEC, false>(Bblk + (long long)k0 * p.ldb, p.ldb, b_k, b_n4, klen - k0, cols_left);
+        av = gload4<VEC, false>(ap, p.lda, a_r, a_c, a_rows, a_cols);
+        bv = gload4<VEC, false>(bp, p.ldb, b_r, b_c, b_rows, b_cols);
       }
     };
+    // LDS holds A as As[k][m] and B as Bs[k][n] in every case
     auto store_tile = [&](int s) {
       float* as = As + s * BK * SA;
-      as[(a_k4 + 0) * SA + a_row] = av.x;
-      as[(a_k4 + 1) * SA + a_row] = av.y;
-      as[(a_k4 + 2) * SA + a_row] = av.z;
-      as[(a_k4 + 3) * SA + a_row] = av.w;
-      *reinterpret_cast<float4*>(Bs + s * BK * BN + b_k * BN + b_n4) = bv;
+      float* bs = Bs + s * BK * BN;
+      if (TA) {
+        as[a_r * SA + a_c + 0] = av.x;
+        as[a_r * SA + a_c + 1] = av.y;
+        as[a_r * SA + a_c + 2] = av.z;
+        as[a_r * SA + a_c + 3] = av.w;
+      } else {
+        as[(a_c + 0) * SA + a_r] = av.x;
+        as[(a_c + 1) * SA + a_r] = av.y;
+        as[(a_c + 2) * SA + a_r] = av.z;
+        as[(a_c + 3) * SA + a_r] = av.w;
+      }
+      if (TB) {
+        bs[(b_c + 0) * BN + b_r] = bv.x;
+        bs[(b_c + 1) * BN + b_r] = bv.y;
+        bs[(b_c + 2) * BN + b_r] = bv.z;
+        bs[(b_c + 3) * BN + b_r] = bv.w;
+      } else {
+        *reinterpret_cast<float4*>(bs + b_r * BN + b_c) = bv;
+      }
     };
 
     load_tile(0);
@@ -183,11 +212,11 @@ struct RegBlock {
       }
   }
 
-  // The whole tile: C[m0.., n0..] = alpha * A[m0.., :] B[:, n0..] + beta * C.
-  template <bool VEC, bool GUARD>
+  // The whole tile: C[m0.., n0..] = alpha * op(A)[m0.., :] op(B)[:, n0..] + beta * C.
+  template <bool VEC, bool GUARD, bool TA = false, bool TB = false>
   static __device__ __forceinline__ void tile(const Problem& p, int m0, int n0, float* lds, int tid) {
     float acc[TM][TN];
-    compute<VEC, GUARD>(p, m0, n0, 0, p.K, (p.K + BK - 1) / BK, lds, tid, acc);
+    compute<VEC, GUARD, TA, TB>(p, m0, n0, 0, p.K, (p.K + BK - 1) / BK, lds, tid, acc);
     store<GUARD>(p, m0, n0, tid, acc);
   }
 };

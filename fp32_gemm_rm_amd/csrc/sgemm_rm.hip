@@ -9,20 +9,64 @@ namespace {
 
 using sgemm_impl::Problem;
 
-// Checks shared by the single and the batched calls; positions are those of
-// sgemm_rm (M N K alpha A lda B ldb beta C ldc).  Returns 0 or -(position).
-int check_gemm(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb,
-               const float* C, int ldc) {
-  if (M < 0) return -1;
-  if (N < 0) return -2;
-  if (K < 0) return -3;
-  const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
-  if (reads_ab && A == nullptr) return -5;
-  if (lda < (K > 1 ? K : 1)) return -6;
-  if (reads_ab && B == nullptr) return -7;
-  if (ldb < (N > 1 ? N : 1)) return -8;
-  if (M > 0 && N > 0 && C == nullptr) return -10;
-  if (ldc < (N > 1 ? N : 1)) return -11;
+// 1-based positions of the arguments of one entry point; 0 = the entry point has no
+// such argument.  Every entry point lists its arguments in this relative order:
+// transA transB M N K alpha A lda strideA B ldb strideB beta C ldc strideC batch stream variant.
+struct Positions {
+  int ta, tb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, variant;
+};
+constexpr Positions kPosRm = {0, 0, 1, 2, 3, 5, 6, 0, 7, 8, 0, 10, 11, 0, 0, 13};
+constexpr Positions kPosRmBatched = {0, 0, 1, 2, 3, 5, 6, 7, 8, 9, 10, 12, 13, 14, 15, 17};
+constexpr Positions kPosOp = {1, 2, 3, 4, 5, 7, 8, 0, 9, 10, 0, 12, 13, 0, 0, 0};
+constexpr Positions kPosOpBatched = {1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12, 14, 15, 16, 17, 19};
+
+// One call in the caller's terms.  cm: column-major storage (element (i, j) of X at
+// X[j*ldX + i]); ta / tb: A is stored K x M / B is stored N x K (op = transpose).
+struct Call {
+  bool cm;
+  int ta, tb, M, N, K;
+  float alpha;
+  const float* A;
+  int lda;
+  long long sA;
+  const float* B;
+  int ldb;
+  long long sB;
+  float beta;
+  float* C;
+  int ldc;
+  long long sC;
+  int batch, variant;
+};
+
+int at_least(int n) { return n > 1 ? n : 1; }
+
+// Argument checks in parameter order; returns 0 or -(position of the first bad one).
+int check(const Call& c, const Positions& pos) {
+  if (c.ta != 0 && c.ta != 1) return -pos.ta;
+  if (c.tb != 0 && c.tb != 1) return -pos.tb;
+  if (c.M < 0) return -pos.M;
+  if (c.N < 0) return -pos.N;
+  if (c.K < 0) return -pos.K;
+  const bool any = c.M > 0 && c.N > 0 && c.batch > 0;
+  const bool reads_ab = any && c.K > 0 && c.alpha != 0.0f;
+  // stored shapes: the leading dimension spans the other index of the storage order
+  const int a_rows = c.ta ? c.K : c.M, a_cols = c.ta ? c.M : c.K;
+  const int b_rows = c.tb ? c.N : c.K, b_cols = c.tb ? c.K : c.N;
+  if (reads_ab && c.A == nullptr) return -pos.A;
+  if (c.lda < at_least(c.cm ? a_rows : a_cols)) return -pos.lda;
+  if (pos.sA && c.sA < 0) return -pos.sA;
+  if (reads_ab && c.B == nullptr) return -pos.B;
+  if (c.ldb < at_least(c.cm ? b_rows : b_cols)) return -pos.ldb;
+  if (pos.sB && c.sB < 0) return -pos.sB;
+  if (any && c.C == nullptr) return -pos.C;
+  if (c.ldc < at_least(c.cm ? c.M : c.N)) return -pos.ldc;
+  if (pos.sC) {  // the outputs of different batch entries must not overlap
+    const long long extent = c.cm ? (long long)(c.N - 1) * c.ldc + c.M : (long long)(c.M - 1) * c.ldc + c.N;
+    if (c.sC < 0 || (c.batch > 1 && c.M > 0 && c.N > 0 && c.sC < extent)) return -pos.sC;
+  }
+  if (pos.batch && c.batch < 0) return -pos.batch;
+  if (pos.variant && (c.variant < SGEMM_RM_VARIANT_AUTO || c.variant > SGEMM_RM_VARIANT_MFMA)) return -pos.variant;
   return 0;
 }
 
@@ -61,41 +105,21 @@ int launch(Problem p, int batch, hipStream_t stream, int variant) {
   return 0;
 }
 
-int run(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
-        float* C, int ldc, hipStream_t stream, int variant) {
-  const int bad = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+// Validate, then run as a row-major problem.  A column-major product C = op(A) op(B)
+// is the row-major product C^T = op(B)^T op(A)^T over the same memory: a column-major
+// X is the row-major X^T with the same leading dimension, so the operands and M, N
+// swap and each operand keeps its transpose flag.
+int run(const Call& c, const Positions& pos, hipStream_t stream) {
+  const int bad = check(c, pos);
   if (bad != 0) return bad;
-  if (variant < SGEMM_RM_VARIANT_AUTO || variant > SGEMM_RM_VARIANT_MFMA) return -13;
-  if (M == 0 || N == 0) return 0;
-  const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, 0, 0, 0};
-  return launch(p, 1, stream, variant);
-}
-
-// Batched call: checks in parameter order of sgemm_rm_strided_batched
-// (M N K alpha A lda strideA B ldb strideB beta C ldc strideC batch stream [variant]).
-int run_batched(int M, int N, int K, float alpha, const float* A, int lda, long long sA, const float* B, int ldb,
-                long long sB, float beta, float* C, int ldc, long long sC, int batch, hipStream_t stream,
-                int variant) {
-  if (M < 0) return -1;
-  if (N < 0) return -2;
-  if (K < 0) return -3;
-  const bool any = M > 0 && N > 0 && batch > 0;
-  const bool reads_ab = any && K > 0 && alpha != 0.0f;
-  if (reads_ab && A == nullptr) return -5;
-  if (lda < (K > 1 ? K : 1)) return -6;
-  if (sA < 0) return -7;
-  if (reads_ab && B == nullptr) return -8;
-  if (ldb < (N > 1 ? N : 1)) return -9;
-  if (sB < 0) return -10;
-  if (any && C == nullptr) return -12;
-  if (ldc < (N > 1 ? N : 1)) return -13;
-  // the outputs of different batch entries must not overlap
-  if (sC < 0 || (batch > 1 && M > 0 && N > 0 && sC < (long long)(M - 1) * ldc + N)) return -14;
-  if (batch < 0) return -15;
-  if (variant < SGEMM_RM_VARIANT_AUTO || variant > SGEMM_RM_VARIANT_MFMA) return -17;
-  if (!any) return 0;
-  const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, sA, sB, sC};
-  return launch(p, batch, stream, variant);
+  if (c.M == 0 || c.N == 0 || c.batch == 0) return 0;
+  Problem p;
+  if (!c.cm) {
+    p = Problem{c.M, c.N, c.K, c.alpha, c.beta, c.A, c.lda, c.B, c.ldb, c.C, c.ldc, c.sA, c.sB, c.sC, c.ta, c.tb};
+  } else {
+    p = Problem{c.N, c.M, c.K, c.alpha, c.beta, c.B, c.ldb, c.A, c.lda, c.C, c.ldc, c.sB, c.sA, c.sC, c.tb, c.ta};
+  }
+  return launch(p, c.batch, stream, c.variant);
 }
 
 }  // namespace
@@ -104,26 +128,59 @@ extern "C" {
 
 int sgemm_rm(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
              float* C, int ldc, hipStream_t stream) {
-  return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, SGEMM_RM_VARIANT_AUTO);
+  return run({false, 0, 0, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, SGEMM_RM_VARIANT_AUTO}, kPosRm,
+             stream);
 }
 
 int sgemm_rm_ex(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
                 float* C, int ldc, hipStream_t stream, int variant) {
-  return run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+  return run({false, 0, 0, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, variant}, kPosRm, stream);
 }
 
 int sgemm_rm_strided_batched(int M, int N, int K, float alpha, const float* A, int lda, long long strideA,
                              const float* B, int ldb, long long strideB, float beta, float* C, int ldc,
                              long long strideC, int batch, hipStream_t stream) {
-  return run_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch, stream,
-                     SGEMM_RM_VARIANT_AUTO);
+  return run({false, 0, 0, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+              SGEMM_RM_VARIANT_AUTO},
+             kPosRmBatched, stream);
 }
 
 int sgemm_rm_strided_batched_ex(int M, int N, int K, float alpha, const float* A, int lda, long long strideA,
                                 const float* B, int ldb, long long strideB, float beta, float* C, int ldc,
                                 long long strideC, int batch, hipStream_t stream, int variant) {
-  return run_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch, stream,
-                     variant);
+  return run({false, 0, 0, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch, variant},
+             kPosRmBatched, stream);
+}
+
+int sgemm_rm_op(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda, const float* B,
+                int ldb, float beta, float* C, int ldc, hipStream_t stream) {
+  return run({false, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
+              SGEMM_RM_VARIANT_AUTO},
+             kPosOp, stream);
+}
+
+int sgemm_rm_op_strided_batched_ex(int transA, int transB, int M, int N, int K, float alpha, const float* A,
+                                   int lda, long long strideA, const float* B, int ldb, long long strideB,
+                                   float beta, float* C, int ldc, long long strideC, int batch, hipStream_t stream,
+                                   int variant) {
+  return run({false, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+              variant},
+             kPosOpBatched, stream);
+}
+
+int sgemm_cm(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda, const float* B,
+             int ldb, float beta, float* C, int ldc, hipStream_t stream) {
+  return run({true, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
+              SGEMM_RM_VARIANT_AUTO},
+             kPosOp, stream);
+}
+
+int sgemm_cm_strided_batched_ex(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda,
+                                long long strideA, const float* B, int ldb, long long strideB, float beta, float* C,
+                                int ldc, long long strideC, int batch, hipStream_t stream, int variant) {
+  return run({true, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+              variant},
+             kPosOpBatched, stream);
 }
 
 const char* sgemm_rm_strerror(int code) {
@@ -132,13 +189,13 @@ const char* sgemm_rm_strerror(int code) {
       "invalid argument 5",  "invalid argument 6",  "invalid argument 7",  "invalid argument 8",
       "invalid argument 9",  "invalid argument 10", "invalid argument 11", "invalid argument 12",
       "invalid argument 13", "invalid argument 14", "invalid argument 15", "invalid argument 16",
-      "invalid argument 17"};
+      "invalid argument 17", "invalid argument 18", "invalid argument 19"};
   if (code == 0) return "success";
-  if (code < 0 && code >= -17) return kInvalid[-code - 1];
+  if (code < 0 && code >= -19) return kInvalid[-code - 1];
   if (code > 0) return hipGetErrorString((hipError_t)code);
   return "unknown error code";
 }
 
-int sgemm_rm_version(void) { return 200; }
+int sgemm_rm_version(void) { return 300; }
 
 }  // extern "C"

@@ -35,6 +35,14 @@
  * the summation order is fixed per variant and shape, so repeated calls with
  * the same inputs are bitwise identical.
  *
+ * Transposed operands and column-major storage (sgemm_rm_op, sgemm_cm and their
+ * batched forms) follow the BLAS operation arguments of the cuBLAS calls on
+ * "GPU-accelerated matrix computation ..." section 4.1 (CUBLAS_OP_N / _T) and
+ * the sgemmNN page, which is the NN member of that column-major family:
+ *     C := alpha * op(A) * op(B) + beta * C,   op(X) = X or X^T,
+ * op(A) M x K, op(B) K x N, C M x N.  A column-major product is computed as the
+ * row-major product C^T = op(B)^T op(A)^T over the same memory.
+ *
  * Return value: 0 on success.  A negative value -p names the first invalid
  * argument by its 1-based position p in the call's parameter list, checked in
  * that order before any HIP call.  For sgemm_rm / sgemm_rm_ex:
@@ -111,6 +119,64 @@ int sgemm_rm_strided_batched(int M, int N, int K, float alpha, const float* A, i
 int sgemm_rm_strided_batched_ex(int M, int N, int K, float alpha, const float* A, int lda, long long strideA,
                                 const float* B, int ldb, long long strideB, float beta, float* C, int ldc,
                                 long long strideC, int batch, hipStream_t stream, int variant);
+
+/* Operation arguments of the transposing calls. */
+enum sgemm_rm_op {
+  SGEMM_RM_OP_N = 0, /* op(X) = X */
+  SGEMM_RM_OP_T = 1  /* op(X) = X^T */
+};
+
+/*
+ * C := alpha * op(A) * op(B) + beta * C, all row-major (element (i, j) of X at
+ * X[i*ldX + j]).  transA == SGEMM_RM_OP_N: A is stored M x K, lda >= max(1, K);
+ * SGEMM_RM_OP_T: A is stored K x M (op(A)(i, k) = A[k*lda + i]), lda >= max(1, M).
+ * transB == SGEMM_RM_OP_N: B stored K x N, ldb >= max(1, N); SGEMM_RM_OP_T: B
+ * stored N x K, ldb >= max(1, K).  C is M x N, ldc >= max(1, N).  Every kernel
+ * family reads transposed operands along their contiguous dimension; the
+ * MFMA kernel keeps each operand's LDS layout matched to its storage order.
+ * Return codes, by position: -1 transA, -2 transB not 0 or 1; -3 M, -4 N,
+ * -5 K < 0; -7 A NULL while read; -8 lda too small; -9 B NULL while read;
+ * -10 ldb too small; -12 C NULL while written; -13 ldc < max(1, N).
+ * With both flags SGEMM_RM_OP_N this is sgemm_rm.
+ */
+int sgemm_rm_op(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda, const float* B,
+                int ldb, float beta, float* C, int ldc, hipStream_t stream);
+
+/*
+ * The general row-major call: a strided batch (as sgemm_rm_strided_batched) of
+ * C_b := alpha * op(A_b) * op(B_b) + beta * C_b with the operation arguments and
+ * leading-dimension rules of sgemm_rm_op and the kernel family forced (enum
+ * sgemm_rm_variant).  Return codes, by position: -1 transA, -2 transB; -3 M,
+ * -4 N, -5 K < 0; -7 A NULL while read; -8 lda too small; -9 strideA < 0;
+ * -10 B NULL while read; -11 ldb too small; -12 strideB < 0; -14 C NULL while
+ * written; -15 ldc < max(1, N); -16 strideC < 0 or outputs overlap
+ * (strideC < (M-1)*ldc + N with batch > 1); -17 batch < 0; -19 unknown variant.
+ */
+int sgemm_rm_op_strided_batched_ex(int transA, int transB, int M, int N, int K, float alpha, const float* A,
+                                   int lda, long long strideA, const float* B, int ldb, long long strideB,
+                                   float beta, float* C, int ldc, long long strideC, int batch, hipStream_t stream,
+                                   int variant);
+
+/*
+ * Column-major (BLAS) form: C := alpha * op(A) * op(B) + beta * C with element
+ * (i, j) of X at X[j*ldX + i].  transA == SGEMM_RM_OP_N: A is M x K, lda >=
+ * max(1, M); SGEMM_RM_OP_T: A is stored K x M, lda >= max(1, K).  transB ==
+ * SGEMM_RM_OP_N: B is K x N, ldb >= max(1, K); SGEMM_RM_OP_T: B is stored N x K,
+ * ldb >= max(1, N).  C is M x N, ldc >= max(1, M).  Same argument order and
+ * return codes as sgemm_rm_op (-13: ldc < max(1, M)).  The sgemmNN page's
+ * kernel computes the (N, N) case of this call.
+ */
+int sgemm_cm(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda, const float* B,
+             int ldb, float beta, float* C, int ldc, hipStream_t stream);
+
+/*
+ * Strided batch of sgemm_cm problems with the kernel family forced; argument
+ * order and return codes as sgemm_rm_op_strided_batched_ex, except that the
+ * outputs overlap (-16) when batch > 1 and strideC < (N-1)*ldc + M.
+ */
+int sgemm_cm_strided_batched_ex(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda,
+                                long long strideA, const float* B, int ldb, long long strideB, float beta, float* C,
+                                int ldc, long long strideC, int batch, hipStream_t stream, int variant);
 
 /* Static, NUL-terminated description of a return code of the calls above
  * ("invalid argument p" for -p, the HIP runtime's text for a hipError_t). */

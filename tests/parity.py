@@ -55,3 +55,30 @@ def assert_within_bound(got, ref, S, what=""):
         f"{what}: max err/bound {ratio.max():.3g} at {worst}: got {got[worst]!r} ref {ref[worst]!r}"
     )
     return float(ratio.max()) if ratio.size else 0.0
+
+
+def sample_entries(M, N, seed, n_random=4096):
+    """Entries to check on a large output: random ones plus whole rows and columns at
+    tile boundaries (multiples of 32, 64 and 128 and the last ones)."""
+    rng = np.random.default_rng(seed)
+    rows = [rng.integers(0, M, n_random)]
+    cols = [rng.integers(0, N, n_random)]
+    for r in sorted({0, 63, 64, 127, 128, M // 2, M - 129, M - 1}):
+        rows.append(np.full(N, r))
+        cols.append(np.arange(N))
+    for c in sorted({0, 31, 32, 127, 128, N // 2, N - 1}):
+        rows.append(np.arange(M))
+        cols.append(np.full(M, c))
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+EDGE_DIMS = [1, 2, 3, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def edge_shapes():
+    """40 shapes (the 5 cubes plus random picks) with sides around the tile sizes."""
+    rng = np.random.default_rng(2024)
+    shapes = {(d, d, d) for d in (1, 17, 64, 129, 257)}
+    while len(shapes) < 40:
+        shapes.add(tuple(int(x) for x in rng.choice(EDGE_DIMS, 3)))
+    return sorted(shapes)

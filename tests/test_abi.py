@@ -26,8 +26,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strerror", "sgemm_rm_strided_batched",
-                                     "sgemm_rm_strided_batched_ex", "sgemm_rm_version"]
+    assert _declared_functions() == ["sgemm_cm", "sgemm_cm_strided_batched_ex", "sgemm_rm", "sgemm_rm_ex",
+                                     "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex", "sgemm_rm_strerror",
+                                     "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex", "sgemm_rm_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(raw, name), name
     assert set(EXPORTED_SYMBOLS) == set(_declared_functions())
-    assert lib.sgemm_rm_version() == 200
+    assert lib.sgemm_rm_version() == 300
 
 
 F = 0x1000  # a non-null dummy pointer: never dereferenced, the calls return before any launch
@@ -87,7 +88,7 @@ def test_strerror(lib):
     from fp32_gemm_rm_amd import sgemm_rm_strerror
 
     assert sgemm_rm_strerror(0) == "success"
-    for code in range(-17, 0):
+    for code in range(-19, 0):
         assert sgemm_rm_strerror(code) == f"invalid argument {-code}"
     assert sgemm_rm_strerror(-99) == "unknown error code"
 
@@ -134,3 +135,81 @@ def test_batched_quick_returns_and_variant(lib):
     # a single entry may use any strideC (nothing can overlap)
     assert lib.sgemm_rm_strided_batched(4, 4, 4, 0.0, None, 4, 0, None, 4, 0, 1.0, F, 4, 0, 1, None) == 0
     assert lib.sgemm_rm_strided_batched_ex(4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2, None, 7) == -17
+
+
+# Transposed and column-major forms.  M = 6, N = 5, K = 3 keep every leading-dimension
+# bound distinct.  alpha = 0 with beta = 1 makes a valid call return 0 without a launch.
+M6, N5, K3 = 6, 5, 3
+
+
+def _min_lds(cm, ta, tb):
+    """Smallest valid (lda, ldb, ldc) for the stored shapes of op(A) 6 x 3, op(B) 3 x 5, C 6 x 5."""
+    a_rows, a_cols = (K3, M6) if ta else (M6, K3)
+    b_rows, b_cols = (N5, K3) if tb else (K3, N5)
+    if cm:
+        return a_rows, b_rows, M6
+    return a_cols, b_cols, N5
+
+
+ORIENTATIONS = [(0, 0), (0, 1), (1, 0), (1, 1)]
+
+
+@pytest.mark.parametrize("cm", [False, True], ids=["rm", "cm"])
+@pytest.mark.parametrize("ta,tb", ORIENTATIONS)
+def test_op_leading_dimension_bounds(lib, cm, ta, tb):
+    fn = lib.sgemm_cm if cm else lib.sgemm_rm_op
+    lda, ldb, ldc = _min_lds(cm, ta, tb)
+    assert fn(ta, tb, M6, N5, K3, 0.0, F, lda, F, ldb, 1.0, F, ldc, None) == 0
+    assert fn(ta, tb, M6, N5, K3, 0.0, F, lda - 1, F, ldb, 1.0, F, ldc, None) == -8
+    assert fn(ta, tb, M6, N5, K3, 0.0, F, lda, F, ldb - 1, 1.0, F, ldc, None) == -10
+    assert fn(ta, tb, M6, N5, K3, 0.0, F, lda, F, ldb, 1.0, F, ldc - 1, None) == -13
+    bfn = lib.sgemm_cm_strided_batched_ex if cm else lib.sgemm_rm_op_strided_batched_ex
+    extent = (N5 - 1) * ldc + M6 if cm else (M6 - 1) * ldc + N5
+    ok = (ta, tb, M6, N5, K3, 0.0, F, lda, G, F, ldb, G, 1.0, F, ldc, extent, 3, None, 0)
+    assert bfn(*ok) == 0
+    assert bfn(*ok[:7], lda - 1, *ok[8:]) == -8
+    assert bfn(*ok[:10], ldb - 1, *ok[11:]) == -11
+    assert bfn(*ok[:14], ldc - 1, *ok[15:]) == -15
+    assert bfn(*ok[:15], extent - 1, *ok[16:]) == -16
+
+
+@pytest.mark.parametrize("cm", [False, True], ids=["rm", "cm"])
+def test_op_invalid_arguments(lib, cm):
+    fn = lib.sgemm_cm if cm else lib.sgemm_rm_op
+    lda, ldb, ldc = _min_lds(cm, 0, 0)
+    ok = [0, 0, M6, N5, K3, 1.0, F, lda, F, ldb, 0.0, F, ldc, None]
+    for pos, bad in [(1, 2), (1, -1), (2, 2), (3, -1), (4, -1), (5, -1), (7, None), (9, None), (12, None)]:
+        args = list(ok)
+        args[pos - 1] = bad
+        assert fn(*args) == -pos, (pos, bad)
+    bfn = lib.sgemm_cm_strided_batched_ex if cm else lib.sgemm_rm_op_strided_batched_ex
+    bok = [0, 0, M6, N5, K3, 1.0, F, lda, G, F, ldb, G, 0.0, F, ldc, G, 2, None, 0]
+    for pos, bad in [(1, 3), (2, -1), (3, -1), (4, -1), (5, -1), (7, None), (9, -1), (10, None), (12, -1),
+                     (14, None), (16, -1), (17, -1), (19, 5), (19, -1)]:
+        args = list(bok)
+        args[pos - 1] = bad
+        assert bfn(*args) == -pos, (pos, bad)
+
+
+def test_op_first_invalid_argument_wins(lib):
+    assert lib.sgemm_rm_op(7, 7, -1, -1, -1, 1.0, None, 0, None, 0, 0.0, None, 0, None) == -1
+    assert lib.sgemm_cm(0, 7, -1, -1, -1, 1.0, None, 0, None, 0, 0.0, None, 0, None) == -2
+
+
+def test_python_operand_layout():
+    """The tensor-level call reads a row-major view as op N and a transposed view as op T
+    of the row-major matrix underneath, with that matrix's leading dimension."""
+    import torch
+
+    from fp32_gemm_rm_amd.binding import SGEMM_RM_OP_N, SGEMM_RM_OP_T, operand_layout
+
+    base = torch.zeros(7, 9)
+    for view, expect in [(base, (9, SGEMM_RM_OP_N)), (base[:, :5], (9, SGEMM_RM_OP_N)),
+                         (base.t(), (9, SGEMM_RM_OP_T)), (base[:, :5].t(), (9, SGEMM_RM_OP_T)),
+                         (base[:1, :], (9, SGEMM_RM_OP_N)), (base[:, :1], (9, SGEMM_RM_OP_N)),
+                         (base[:1, :].t(), (1, SGEMM_RM_OP_N))]:
+        assert operand_layout(*view.shape, *view.stride()) == expect, (view.shape, view.stride())
+    with pytest.raises(ValueError):
+        operand_layout(*base[::2, ::2].shape, *base[::2, ::2].stride())
+    with pytest.raises(ValueError):  # overlapping rows
+        operand_layout(4, 8, 4, 1)

@@ -19,7 +19,7 @@ from fp32_gemm_rm_amd.workloads import (
     workload_inputs,
 )
 
-from .parity import assert_within_bound, c_window, check_padding, device, run_gemm
+from .parity import assert_within_bound, c_window, check_padding, device, edge_shapes, run_gemm, sample_entries
 
 pytestmark = pytest.mark.gpu
 
@@ -51,19 +51,6 @@ def test_workload_full(oracle, name, variant):
     print(f"[parity] {name} variant={variant} max err/bound {r:.3g}", flush=True)
 
 
-def _sample_entries(M, N, seed, n_random=4096):
-    rng = np.random.default_rng(seed)
-    rows = [rng.integers(0, M, n_random)]
-    cols = [rng.integers(0, N, n_random)]
-    for r in sorted({0, 63, 64, 127, 128, M // 2, M - 129, M - 1}):
-        rows.append(np.full(N, r))
-        cols.append(np.arange(N))
-    for c in sorted({0, 31, 32, 127, 128, N // 2, N - 1}):
-        rows.append(np.arange(M))
-        cols.append(np.full(M, c))
-    return np.concatenate(rows), np.concatenate(cols)
-
-
 @pytest.mark.parametrize("name", ["sgemm_4096", "sgemm_8192"])
 def test_workload_sampled(oracle, name):
     """Full-size workloads on the default (benchmarked) path, checked at sampled entries."""
@@ -71,7 +58,7 @@ def test_workload_sampled(oracle, name):
     print(f"[parity] {name} sampled", flush=True)
     A, B, C = workload_inputs(w)
     out = run_gemm(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, 0)
-    rows, cols = _sample_entries(w.M, w.N, seed=w.seed)
+    rows, cols = sample_entries(w.M, w.N, seed=w.seed)
     ref, S = oracle.entries(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, rows, cols)
     got = c_window(out, w.M, w.N, w.ldc)[rows, cols]
     r = assert_within_bound(got, ref, S, name)
@@ -88,28 +75,17 @@ def test_integer_exact_full_size(oracle, variant):
     A, B = a.reshape(-1), b.reshape(-1)
     C = np.full(M * N, np.nan, np.float32)
     out = run_gemm(M, N, K, 1.0, A, K, B, N, 0.0, C, N, VARIANTS[variant])
-    rows, cols = _sample_entries(M, N, seed=43, n_random=2048)
+    rows, cols = sample_entries(M, N, seed=43, n_random=2048)
     ref, _ = oracle.entries(M, N, K, 1.0, A, K, B, N, 0.0, C, N, rows, cols)
     got = out.reshape(M, N)[rows, cols].astype(np.float64)
     np.testing.assert_array_equal(got, ref)
-
-
-EDGE_DIMS = [1, 2, 3, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
-
-
-def _edge_shapes():
-    rng = np.random.default_rng(2024)
-    shapes = {(d, d, d) for d in (1, 17, 64, 129, 257)}
-    while len(shapes) < 40:
-        shapes.add(tuple(int(x) for x in rng.choice(EDGE_DIMS, 3)))
-    return sorted(shapes)
 
 
 @pytest.mark.parametrize("variant", list(VARIANTS))
 def test_edge_shapes_integer_exact(oracle, variant):
     """Ragged shapes around tile sizes, integer inputs: bit-exact against the oracle,
     with NaN in A/B padding and a sentinel in C padding."""
-    for t, (M, N, K) in enumerate(_edge_shapes()):
+    for t, (M, N, K) in enumerate(edge_shapes()):
         lda, ldb, ldc = K + (t % 5), N + (t % 3), N + 1 + (t % 4)
         a = integer_matrix(M, K, -4, 4, seed=500 + t)
         b = integer_matrix(K, N, -4, 4, seed=600 + t)
@@ -125,7 +101,7 @@ def test_edge_shapes_integer_exact(oracle, variant):
 @pytest.mark.parametrize("variant", list(VARIANTS))
 def test_edge_shapes_random_bound(oracle, variant):
     """Ragged random shapes with alpha = 1.5, beta = -0.5 within the bound."""
-    for t, (M, N, K) in enumerate(_edge_shapes()[::3]):
+    for t, (M, N, K) in enumerate(edge_shapes()[::3]):
         lda, ldb, ldc = K + 3, N + 2, N + 1
         A, B, C = make_inputs(M, N, K, lda, ldb, ldc, "normal", seed=800 + t, c_init="random")
         out = run_gemm(M, N, K, 1.5, A, lda, B, ldb, -0.5, C, ldc, VARIANTS[variant])
