@@ -12,8 +12,13 @@ from .binding import (  # noqa: F401
     SGEMM_RM_VARIANT_AUTO,
     SGEMM_RM_VARIANT_LDS_TILED,
     SGEMM_RM_VARIANT_MFMA,
+    SGEMM_RM_VARIANT_MFMA_T32,
+    SGEMM_RM_VARIANT_MFMA_T64,
+    SGEMM_RM_VARIANT_MFMA_T128,
+    SGEMM_RM_VARIANT_MFMA_T256,
     SGEMM_RM_VARIANT_NAIVE,
     SGEMM_RM_VARIANT_REGBLOCK,
+    TILE_VARIANTS,
     VARIANTS,
     SgemmError,
     library_path,
@@ -26,6 +31,7 @@ from .binding import (  # noqa: F401
     sgemm_rm_ex,
     sgemm_rm_op,
     sgemm_rm_op_strided_batched_ex,
+    sgemm_rm_plan_tiles,
     sgemm_rm_strerror,
     sgemm_rm_strided_batched,
     sgemm_rm_strided_batched_ex,

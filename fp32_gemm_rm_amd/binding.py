@@ -15,13 +15,24 @@ SGEMM_RM_VARIANT_NAIVE = 1
 SGEMM_RM_VARIANT_LDS_TILED = 2
 SGEMM_RM_VARIANT_REGBLOCK = 3
 SGEMM_RM_VARIANT_MFMA = 4
+SGEMM_RM_VARIANT_MFMA_T256 = 5
+SGEMM_RM_VARIANT_MFMA_T128 = 6
+SGEMM_RM_VARIANT_MFMA_T64 = 7
+SGEMM_RM_VARIANT_MFMA_T32 = 8
 VARIANTS = {
     "auto": SGEMM_RM_VARIANT_AUTO,
     "naive": SGEMM_RM_VARIANT_NAIVE,
     "lds_tiled": SGEMM_RM_VARIANT_LDS_TILED,
     "regblock": SGEMM_RM_VARIANT_REGBLOCK,
     "mfma": SGEMM_RM_VARIANT_MFMA,
+    "mfma_t256": SGEMM_RM_VARIANT_MFMA_T256,
+    "mfma_t128": SGEMM_RM_VARIANT_MFMA_T128,
+    "mfma_t64": SGEMM_RM_VARIANT_MFMA_T64,
+    "mfma_t32": SGEMM_RM_VARIANT_MFMA_T32,
 }
+#: Forced MFMA tile configurations by tile side.
+TILE_VARIANTS = {256: SGEMM_RM_VARIANT_MFMA_T256, 128: SGEMM_RM_VARIANT_MFMA_T128, 64: SGEMM_RM_VARIANT_MFMA_T64,
+                 32: SGEMM_RM_VARIANT_MFMA_T32}
 
 SGEMM_RM_OP_N = 0
 SGEMM_RM_OP_T = 1
@@ -33,7 +44,7 @@ _lib = None
 #: Names the header declares; the CPU tests check that the library exports each.
 EXPORTED_SYMBOLS = ("sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex",
                     "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex", "sgemm_cm", "sgemm_cm_strided_batched_ex",
-                    "sgemm_rm_strerror", "sgemm_rm_version")
+                    "sgemm_rm_plan_tiles", "sgemm_rm_strerror", "sgemm_rm_version")
 
 
 class SgemmError(RuntimeError):
@@ -79,12 +90,22 @@ def load_library():
         for name in ("sgemm_rm_op_strided_batched_ex", "sgemm_cm_strided_batched_ex"):
             getattr(lib, name).argtypes = obargs
             getattr(lib, name).restype = ctypes.c_int
+        lib.sgemm_rm_plan_tiles.argtypes = [ctypes.c_int] * 4
+        lib.sgemm_rm_plan_tiles.restype = ctypes.c_int
         lib.sgemm_rm_strerror.argtypes = [ctypes.c_int]
         lib.sgemm_rm_strerror.restype = ctypes.c_char_p
         lib.sgemm_rm_version.argtypes = []
         lib.sgemm_rm_version.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def sgemm_rm_plan_tiles(M, N, K, batch=1) -> int:
+    """Tile side of the MFMA configuration the library picks for the shape (host only)."""
+    code = load_library().sgemm_rm_plan_tiles(int(M), int(N), int(K), int(batch))
+    if code < 0:
+        raise SgemmError(code, sgemm_rm_strerror(code))
+    return code
 
 
 def sgemm_rm_strerror(code: int) -> str:

@@ -62,13 +62,14 @@ hipError_t launch_regblock(const Problem& p, int batch, hipStream_t stream);
 // MFMA tiles for the full BM x BN tiles plus bounds-checked register-blocked
 // tiles (the scalar edge-tile path) for the strips past them, in one launch; one
 // instantiation per operand orientation (p.ta, p.tb), dispatched by launch_mfma.
-hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream);
-hipError_t launch_mfma_nt(const Problem& p, int batch, hipStream_t stream);
-hipError_t launch_mfma_tn(const Problem& p, int batch, hipStream_t stream);
-hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream);
-inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream) {
-  if (p.ta) return p.tb ? launch_mfma_tt(p, batch, stream) : launch_mfma_tn(p, batch, stream);
-  return p.tb ? launch_mfma_nt(p, batch, stream) : launch_mfma_nn(p, batch, stream);
+// tiles: the tile configuration by its side (256, 128, 64 or 32; see tile_plan.h).
+hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream, int tiles);
+hipError_t launch_mfma_nt(const Problem& p, int batch, hipStream_t stream, int tiles);
+hipError_t launch_mfma_tn(const Problem& p, int batch, hipStream_t stream, int tiles);
+hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream, int tiles);
+inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream, int tiles) {
+  if (p.ta) return p.tb ? launch_mfma_tt(p, batch, stream, tiles) : launch_mfma_tn(p, batch, stream, tiles);
+  return p.tb ? launch_mfma_nt(p, batch, stream, tiles) : launch_mfma_nn(p, batch, stream, tiles);
 }
 // C := beta*C on the M x N window (zeros when beta == 0; C is then not read).
 hipError_t launch_scale(const Problem& p, int batch, hipStream_t stream);

@@ -20,8 +20,8 @@
 // of C (each owning (BM/WM) x (BN/WN) as 32 x 32 accumulators of 16 registers);
 // KS of them share each such block and split every K-tile of BK = 16*KS*KG
 // between them (KG 16-deep k-groups each).  Their partial sums are added through
-// LDS in the fixed order ks = 0, 1, ..., KS-1 before the epilogue, so results are
-// deterministic.  KS > 1 lets small problems, whose output alone would give each
+// LDS in the fixed order ks = 0, 1, ..., KS-1, so results are deterministic; each
+// of the KS wavefronts then finishes 1/KS of the block (sum, alpha/beta, store).  KS > 1 lets small problems, whose output alone would give each
 // SIMD a single wavefront, run 4 wavefronts per SIMD and hide LDS, barrier and
 // MFMA latencies.
 //
@@ -67,12 +67,15 @@ namespace mfma_detail {
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Word offset of X(row, 4*chunk) inside one LDS stage whose rows hold BK floats.
-// 64 banks hold 16 chunks, i.e. 64/BK rows; chunk indices are XORed with the row's
-// index in units of that period, so 16 consecutive rows at one chunk, and 16/KC
-// rows at all KC chunks, both land on 16 distinct chunk slots.
+// 64 banks hold 16 chunks, i.e. max(1, 64/BK) rows; chunk indices are XORed with the
+// row's index in units of that period (at most 16 distinct values), so 16 consecutive
+// rows at one chunk, and 16/KC rows at all KC chunks, both land on 16 distinct chunk
+// slots.
 template <int BK>
 __device__ __forceinline__ int swz_slot(int row, int chunk) {
-  return row * BK + 4 * (chunk ^ ((row / (64 / BK)) & (BK / 4 - 1)));
+  constexpr int kPeriod = BK >= 64 ? 1 : 64 / BK;
+  constexpr int kMask = (BK / 4 > 16 ? 16 : BK / 4) - 1;
+  return row * BK + 4 * (chunk ^ ((row / kPeriod) & kMask));
 }
 
 template <bool VEC>
@@ -104,11 +107,13 @@ struct Operand {
 
   const float* base;  // element (r0, k = 0) of this tile's slice
   long long ld;
+  int lim;                     // rows of the slice inside the matrix (R for a full tile)
   int row[LOADS], col[LOADS];  // KROWS: (r, chunk); else (k, 4 * r-quad)
   float4 reg[LOADS];
 
-  __device__ __forceinline__ void init(const float* X, long long ldx, int r0, int t) {
+  __device__ __forceinline__ void init(const float* X, long long ldx, int r0, int rows_left, int t) {
     ld = ldx;
+    lim = rows_left < R ? rows_left : R;
     base = KROWS ? X + (long long)r0 * ldx : X + r0;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -117,22 +122,34 @@ struct Operand {
       col[i] = KROWS ? q % KC : (q % (R / 4)) * 4;
     }
   }
-  // full K-tile starting at k0
-  template <bool VEC>
+  // full K-tile starting at k0.  GUARD: the slice may reach past the matrix (lim < R):
+  // zeros there (a float4 along r that is only partly inside is read element by element)
+  template <bool VEC, bool GUARD>
   __device__ __forceinline__ void load_full(int k0) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      reg[i] = KROWS ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], 4)
-                     : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
+    for (int i = 0; i < LOADS; ++i) {
+      if (KROWS)
+        reg[i] = (!GUARD || row[i] < lim) ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], 4)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      else
+        reg[i] = GUARD ? load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], lim - col[i])
+                       : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
+    }
   }
-  // last K-tile: kl = K - k0 < BK valid k; zeros past K
-  template <bool VEC>
+  // last K-tile: kl = K - k0 < BK valid k; zeros past K (and past the matrix, GUARD)
+  template <bool VEC, bool GUARD>
   __device__ __forceinline__ void load_tail(int k0, int kl) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      reg[i] = KROWS ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], kl - 4 * col[i])
-                     : (row[i] < kl ? load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f));
+    for (int i = 0; i < LOADS; ++i) {
+      if (KROWS)
+        reg[i] = (!GUARD || row[i] < lim) ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], kl - 4 * col[i])
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      else if (row[i] >= kl)
+        reg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      else
+        reg[i] = GUARD ? load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], lim - col[i])
+                       : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
+    }
   }
   __device__ __forceinline__ void store(float* stage) const {
 #pragma unroll
@@ -161,10 +178,10 @@ struct MfmaCfg {
   using OpA = Operand<BM, BK, kThreads, !TA>;
   using OpB = Operand<BN, BK, kThreads, TB>;
   static constexpr int kStageFloats = OpA::kStageFloats + OpB::kStageFloats;
-  static constexpr int kReduceFloats = (KS - 1) * BM * BN;
+  static constexpr int kReduceFloats = KS > 1 ? KS * BM * BN : 0;
   static constexpr int kLdsFloats = 2 * kStageFloats > kReduceFloats ? 2 * kStageFloats : kReduceFloats;
   static_assert(FM >= 1 && FN >= 1, "wavefront tile at least 32 x 32");
-  static_assert(KG >= 1 && KG * 16 * KS == BK && BK <= 64, "K-tile split into 16-deep k-groups");
+  static_assert(KG >= 1 && KG * 16 * KS == BK, "K-tile split into 16-deep k-groups");
 };
 
 // Where the tiles of one launch are: MFMA tiles first, then the edge tiles of the
@@ -176,8 +193,10 @@ struct TileMap {
   int bottom_m, bottom_n;  // 32 x 32 edge tiles in rows [Mf, M)
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, bool VEC>
-__device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m, int tiles_n, float* smem) {
+// One BM x BN tile of C at (m0, n0).  GUARD: the tile reaches past M or N; loads read
+// zeros there and stores skip it.
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool VEC, bool GUARD>
+__device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, float* smem) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
@@ -192,20 +211,10 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
   const int ks = w / (WM * WN), sp = w % (WM * WN);  // K-group and spatial position of this wavefront
   const int wm0 = (sp / WN) * (BM / WM), wn0 = (sp % WN) * (BN / WN);
 
-  // XCD-contiguous, GROUP_M-row-major tile order
-  const int nblk = tiles_m * tiles_n;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int group = GROUP_M * tiles_n;
-  const int first_m = (bid / group) * GROUP_M;
-  const int gsz = min(tiles_m - first_m, GROUP_M);
-  const int bm = first_m + (bid % group) % gsz;
-  const int bn = (bid % group) / gsz;
-  const int m0 = bm * BM, n0 = bn * BN;
-
   OpA opa;
   OpB opb;
-  opa.init(p.A, p.lda, m0, t);
-  opb.init(p.B, p.ldb, n0, t);
+  opa.init(p.A, p.lda, m0, p.M - m0, t);
+  opb.init(p.B, p.ldb, n0, p.N - n0, t);
 
   v16f acc[FM][FN];
 #pragma unroll
@@ -221,11 +230,11 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
   // only) loads zeros past K and is kept out of the steady-state loop
   auto load = [&](int kt) {
     if (kt < nfull) {
-      opa.template load_full<VEC>(kt * BK);
-      opb.template load_full<VEC>(kt * BK);
+      opa.template load_full<VEC, GUARD>(kt * BK);
+      opb.template load_full<VEC, GUARD>(kt * BK);
     } else {
-      opa.template load_tail<VEC>(kt * BK, p.K - kt * BK);
-      opb.template load_tail<VEC>(kt * BK, p.K - kt * BK);
+      opa.template load_tail<VEC, GUARD>(kt * BK, p.K - kt * BK);
+      opb.template load_tail<VEC, GUARD>(kt * BK, p.K - kt * BK);
     }
   };
 
@@ -264,47 +273,51 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int bid, int tiles_m
     __syncthreads();
   }
 
+  const bool beta0 = p.beta == 0.0f;
+  auto store_c = [&](int row, int col, float x) {
+    if (GUARD && (row >= p.M || col >= p.N)) return;
+    float* c = p.C + (long long)row * p.ldc + col;
+    *c = beta0 ? p.alpha * x : fmaf(p.alpha, x, p.beta * *c);
+  };
+
   if constexpr (KS > 1) {
-    // partial sums of K-groups 1..KS-1 through LDS (free after the last barrier),
-    // added to K-group 0's in the fixed order 1, 2, ..., KS-1
-    constexpr int kPart = FM * FN * 16 * 64;  // floats per wavefront
-    if (ks > 0) {
-      float* dst = smem + ((ks - 1) * (WM * WN) + sp) * kPart + l;
+    // The KS wavefronts of one output block pass their partial sums through LDS (free
+    // after the last barrier); then each of them finishes 1/KS of the block's
+    // accumulator registers, adding the partials in the fixed order 0, 1, ..., KS-1,
+    // so that the epilogue's C traffic is spread over all wavefronts.
+    constexpr int kSlots = FM * FN * 16;   // accumulator registers per lane
+    constexpr int kPart = kSlots * 64;     // floats per wavefront
+    constexpr int kStride = WM * WN * kPart;  // between the partials of consecutive K-groups
+    static_assert(kSlots % KS == 0, "registers split evenly over the K-groups");
+    float* mine = smem + (ks * (WM * WN) + sp) * kPart + l;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dst[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
-    }
+        for (int r = 0; r < 16; ++r) mine[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
     __syncthreads();
-    if (ks > 0) return;
-#pragma unroll 1
-    for (int q = 1; q < KS; ++q) {
-      const float* src = smem + ((q - 1) * (WM * WN) + sp) * kPart + l;
+    const float* part = smem + sp * kPart + l;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int u = 0; u < kSlots / KS; ++u) {
+      const int s = ks * (kSlots / KS) + u;  // register (i, j, r) = (s / (16 FN), (s / 16) % FN, s % 16)
+      float x = part[s * 64];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
+      for (int q = 1; q < KS; ++q) x += part[q * kStride + s * 64];
+      const int i = s / (FN * 16), j = (s / 16) % FN, r = s % 16;
+      store_c(m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4), n0 + wn0 + j * 32 + lr, x);
     }
+    return;
   }
 
   // epilogue: register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its block
-  const bool beta0 = p.beta == 0.0f;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-        const int col = n0 + wn0 + j * 32 + lr;
-        float* c = p.C + (long long)row * p.ldc + col;
-        const float x = acc[i][j][r];
-        *c = beta0 ? p.alpha * x : fmaf(p.alpha, x, p.beta * *c);
-      }
+      for (int r = 0; r < 16; ++r)
+        store_c(m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4), n0 + wn0 + j * 32 + lr, acc[i][j][r]);
 }
 
 // Scalar edge-tile path: one 32 x 32 register-blocked VALU tile per workgroup; the
@@ -341,75 +354,120 @@ __device__ __forceinline__ void edge_tile(const Problem& p, int m0, int n0, floa
   EdgeTile::template store<true>(p, m0, n0, tid, acc);
 }
 
+// Tile (bm, bn) of MFMA workgroup `bid`: XCD-contiguous, GROUP_M-row-major order.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& bm, int& bn) {
+  const int nblk = tiles_m * tiles_n;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int group = GROUP_M * tiles_n;
+  const int first_m = (bid / group) * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  bm = first_m + (bid % group) % gsz;
+  bn = (bid % group) / gsz;
+}
+
 // MIN_BLOCKS workgroups must fit on one CU at once (a register budget for the compiler).
-template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS, bool VEC>
+// MFMA_EDGES: the tiles reaching past M or N are guarded MFMA tiles of the same grid
+// (tiles_m x tiles_n covers the whole matrix) instead of scalar edge tiles.
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
+          bool MFMA_EDGES, bool VEC>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   p = batch_entry(p);
   constexpr int kGroups = Cfg::kThreads / 256;
-  constexpr int kEdgeFloats = kGroups * EdgeTile::kLdsFloats;  // >= the (kGroups-1)*4*256 reduction floats
+  constexpr int kEdgeFloats = MFMA_EDGES ? 0 : kGroups * EdgeTile::kLdsFloats;  // >= its reduction floats
   constexpr int kFloats = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
+  static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
   const int nmfma = map.tiles_m * map.tiles_n;
   int e = (int)blockIdx.x - nmfma;
   if (e < 0) {
-    mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, VEC>(p, blockIdx.x, map.tiles_m, map.tiles_n, smem);
+    int bm, bn;
+    tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
+    const int m0 = bm * BM, n0 = bn * BN;
+    if (!MFMA_EDGES || (m0 + BM <= p.M && n0 + BN <= p.N))
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false>(p, m0, n0, smem);
+    else
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, true>(p, m0, n0, smem);
     return;
   }
-  int m0, n0;
-  const int n_right = map.right_m * map.right_n;
-  if (e < n_right) {
-    m0 = (e / map.right_n) * kEdge;
-    n0 = map.Nf + (e % map.right_n) * kEdge;
-  } else {
-    e -= n_right;
-    m0 = map.Mf + (e / map.bottom_n) * kEdge;
-    n0 = (e % map.bottom_n) * kEdge;
+  if constexpr (!MFMA_EDGES) {
+    int m0, n0;
+    const int n_right = map.right_m * map.right_n;
+    if (e < n_right) {
+      m0 = (e / map.right_n) * kEdge;
+      n0 = map.Nf + (e % map.right_n) * kEdge;
+    } else {
+      e -= n_right;
+      m0 = map.Mf + (e / map.bottom_n) * kEdge;
+      n0 = (e % map.bottom_n) * kEdge;
+    }
+    edge_tile<kGroups, TA, TB, VEC>(p, m0, n0, smem);
   }
-  edge_tile<kGroups, TA, TB, VEC>(p, m0, n0, smem);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS>
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
+          bool MFMA_EDGES = false>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   static_assert(BM % kEdge == 0 && BN % kEdge == 0, "edge tiles of the right strip end at Mf");
   TileMap map;
-  map.Mf = (p.M / BM) * BM;
-  map.Nf = (p.N / BN) * BN;
-  map.tiles_m = map.Mf / BM;
-  map.tiles_n = map.Nf / BN;
-  if (map.tiles_m == 0 || map.tiles_n == 0) {  // no full tile: everything is edge
-    map.tiles_m = map.tiles_n = 0;
-    map.Mf = map.Nf = 0;
+  if (MFMA_EDGES) {
+    map.tiles_m = (p.M + BM - 1) / BM;
+    map.tiles_n = (p.N + BN - 1) / BN;
+    map.Mf = p.M;
+    map.Nf = p.N;
+    map.right_m = map.right_n = map.bottom_m = map.bottom_n = 0;
+  } else {
+    map.Mf = (p.M / BM) * BM;
+    map.Nf = (p.N / BN) * BN;
+    map.tiles_m = map.Mf / BM;
+    map.tiles_n = map.Nf / BN;
+    if (map.tiles_m == 0 || map.tiles_n == 0) {  // no full tile: everything is edge
+      map.tiles_m = map.tiles_n = 0;
+      map.Mf = map.Nf = 0;
+    }
+    map.right_m = (map.Nf < p.N) ? map.Mf / kEdge : 0;
+    map.right_n = (map.Nf < p.N) ? (p.N - map.Nf + kEdge - 1) / kEdge : 0;
+    map.bottom_m = (p.M - map.Mf + kEdge - 1) / kEdge;
+    map.bottom_n = map.bottom_m > 0 ? (p.N + kEdge - 1) / kEdge : 0;
   }
-  map.right_m = (map.Nf < p.N) ? map.Mf / kEdge : 0;
-  map.right_n = (map.Nf < p.N) ? (p.N - map.Nf + kEdge - 1) / kEdge : 0;
-  map.bottom_m = (p.M - map.Mf + kEdge - 1) / kEdge;
-  map.bottom_n = map.bottom_m > 0 ? (p.N + kEdge - 1) / kEdge : 0;
   const long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
   const long long blocks = (long long)map.tiles_m * map.tiles_n + edge_tiles;
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks, batch), block(WM * WN * KS * 64);
   if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, true>), grid, block, 0,
-                       stream, p, map);
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, true>), grid,
+                       block, 0, stream, p, map);
   else
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false>), grid, block, 0,
-                       stream, p, map);
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false>), grid,
+                       block, 0, stream, p, map);
   return hipGetLastError();
 }
 
-// 256 x 256 tiles (one 16-wavefront workgroup per CU) once they fill the 256 CUs.
-// Smaller problems use 128 x 128 or 64 x 64 tiles with the K-tile split over 2 or 4
-// wavefronts per output block, so that every SIMD still has several wavefronts.
-// Tiles are counted over the whole batch.
+// The tile configurations (tile_plan.h), by tile side.
+//   256: 256 x 256 tiles, 4 x 4 wavefronts of 64 x 64, BK 16: one workgroup per CU.
+//   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64 and a 2-way K split, BK 32.
+//   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 4-way K split, BK 64; two
+//        workgroups per CU.
+//   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
+//        256 threads; four workgroups per CU.  Partial tiles are guarded MFMA tiles
+//        (the other configurations send them to the scalar edge-tile path).
 template <bool TA, bool TB>
-hipError_t launch_op(const Problem& p, int batch, hipStream_t stream) {
-  const long long t256 = (long long)(p.M / 256) * (p.N / 256) * batch;
-  const long long t128 = (long long)(p.M / 128) * (p.N / 128) * batch;
-  if (t256 >= 256) return launch_cfg<256, 256, 16, 4, 4, 1, TA, TB, 8, 1>(p, batch, stream);
-  if (t128 >= 256) return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
-  return launch_cfg<64, 64, 64, 2, 2, 4, TA, TB, 8, 2>(p, batch, stream);
+hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles) {
+  switch (tiles) {
+    case 256:
+      return launch_cfg<256, 256, 16, 4, 4, 1, TA, TB, 8, 1>(p, batch, stream);
+    case 128:
+      return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
+    case 64:
+      return launch_cfg<64, 64, 64, 2, 2, 4, TA, TB, 8, 2>(p, batch, stream);
+    case 32:
+      if (p.M % 32 == 0 && p.N % 32 == 0) return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4>(p, batch, stream);
+      return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, true>(p, batch, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace mfma_detail

@@ -4,6 +4,7 @@
 #include "sgemm_rm.h"
 
 #include "internal.h"
+#include "tile_plan.h"
 
 namespace {
 
@@ -66,7 +67,7 @@ int check(const Call& c, const Positions& pos) {
     if (c.sC < 0 || (c.batch > 1 && c.M > 0 && c.N > 0 && c.sC < extent)) return -pos.sC;
   }
   if (pos.batch && c.batch < 0) return -pos.batch;
-  if (pos.variant && (c.variant < SGEMM_RM_VARIANT_AUTO || c.variant > SGEMM_RM_VARIANT_MFMA)) return -pos.variant;
+  if (pos.variant && (c.variant < SGEMM_RM_VARIANT_AUTO || c.variant > SGEMM_RM_VARIANT_MFMA_T32)) return -pos.variant;
   return 0;
 }
 
@@ -89,10 +90,22 @@ int launch(Problem p, int batch, hipStream_t stream, int variant) {
         case SGEMM_RM_VARIANT_REGBLOCK:
           err = sgemm_impl::launch_regblock(p, chunk, stream);
           break;
+        case SGEMM_RM_VARIANT_MFMA_T256:
+          err = sgemm_impl::launch_mfma(p, chunk, stream, 256);
+          break;
+        case SGEMM_RM_VARIANT_MFMA_T128:
+          err = sgemm_impl::launch_mfma(p, chunk, stream, 128);
+          break;
+        case SGEMM_RM_VARIANT_MFMA_T64:
+          err = sgemm_impl::launch_mfma(p, chunk, stream, 64);
+          break;
+        case SGEMM_RM_VARIANT_MFMA_T32:
+          err = sgemm_impl::launch_mfma(p, chunk, stream, 32);
+          break;
         case SGEMM_RM_VARIANT_MFMA:
         case SGEMM_RM_VARIANT_AUTO:
         default:
-          err = sgemm_impl::launch_mfma(p, chunk, stream);
+          err = sgemm_impl::launch_mfma(p, chunk, stream, sgemm_impl::plan_tiles(p.M, p.N, p.K, chunk));
           break;
       }
     }
@@ -181,6 +194,15 @@ int sgemm_cm_strided_batched_ex(int transA, int transB, int M, int N, int K, flo
   return run({true, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
               variant},
              kPosOpBatched, stream);
+}
+
+int sgemm_rm_plan_tiles(int M, int N, int K, int batch) {
+  if (M < 0) return -1;
+  if (N < 0) return -2;
+  if (K < 0) return -3;
+  if (batch < 0) return -4;
+  if (M == 0 || N == 0 || K == 0 || batch == 0) return 0;
+  return sgemm_impl::plan_tiles(M, N, K, batch < sgemm_impl::kMaxBatch ? batch : sgemm_impl::kMaxBatch);
 }
 
 const char* sgemm_rm_strerror(int code) {

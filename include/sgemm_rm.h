@@ -74,8 +74,15 @@ enum sgemm_rm_variant {
   SGEMM_RM_VARIANT_REGBLOCK = 3,  /* register-blocked, double-buffered LDS pipeline:
                                      "GEMM advanced: ILP and bank conflicts" (mhpn.cn) section 2-3,
                                      and the sgemmNN page's register blocking */
-  SGEMM_RM_VARIANT_MFMA = 4       /* FP32 matrix-core tiles for full tiles, scalar edge-tile path
-                                     for ragged M/N; ragged K handled inside every tile */
+  SGEMM_RM_VARIANT_MFMA = 4,      /* FP32 matrix-core tiles for full tiles, scalar edge-tile path
+                                     for ragged M/N; ragged K handled inside every tile; tile
+                                     configuration chosen per shape (sgemm_rm_plan_tiles) */
+  /* The MFMA kernel with its tile configuration forced, for tile sweeps (the pages name
+     tuning the tile parameters as the next step: the sgemmNN page's closing section): */
+  SGEMM_RM_VARIANT_MFMA_T256 = 5, /* 256 x 256 tiles, 16 wavefronts of 64 x 64, one workgroup per CU */
+  SGEMM_RM_VARIANT_MFMA_T128 = 6, /* 128 x 128 tiles, 4 x 64 x 64 wavefronts, 2-way in-tile K split */
+  SGEMM_RM_VARIANT_MFMA_T64 = 7,  /* 64 x 64 tiles, 4 x 32 x 32 wavefronts, 4-way in-tile K split */
+  SGEMM_RM_VARIANT_MFMA_T32 = 8   /* 32 x 32 tiles, 4-way in-tile K split, partial tiles on MFMA */
 };
 
 /*
@@ -177,6 +184,15 @@ int sgemm_cm(int transA, int transB, int M, int N, int K, float alpha, const flo
 int sgemm_cm_strided_batched_ex(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda,
                                 long long strideA, const float* B, int ldb, long long strideB, float beta, float* C,
                                 int ldc, long long strideC, int batch, hipStream_t stream, int variant);
+
+/*
+ * Tile side (256, 128, 64 or 32) of the MFMA configuration that SGEMM_RM_VARIANT_AUTO
+ * and SGEMM_RM_VARIANT_MFMA use for an M x N x K problem repeated `batch` times (any
+ * orientation or storage order; batches above 65535 are planned per launch of 65535).
+ * 0 when nothing would be launched for the product (M, N, K or batch 0).  -1 M < 0,
+ * -2 N < 0, -3 K < 0, -4 batch < 0.  Host only: no HIP call.
+ */
+int sgemm_rm_plan_tiles(int M, int N, int K, int batch);
 
 /* Static, NUL-terminated description of a return code of the calls above
  * ("invalid argument p" for -p, the HIP runtime's text for a hipError_t). */

@@ -27,7 +27,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["sgemm_cm", "sgemm_cm_strided_batched_ex", "sgemm_rm", "sgemm_rm_ex",
-                                     "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex", "sgemm_rm_strerror",
+                                     "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex", "sgemm_rm_plan_tiles",
+                                     "sgemm_rm_strerror",
                                      "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex", "sgemm_rm_version"]
 
 
@@ -134,7 +135,7 @@ def test_batched_quick_returns_and_variant(lib):
     assert lib.sgemm_rm_strided_batched(0, 4, 4, 1.0, None, 4, 0, None, 4, 0, 0.0, None, 4, 0, 3, None) == 0
     # a single entry may use any strideC (nothing can overlap)
     assert lib.sgemm_rm_strided_batched(4, 4, 4, 0.0, None, 4, 0, None, 4, 0, 1.0, F, 4, 0, 1, None) == 0
-    assert lib.sgemm_rm_strided_batched_ex(4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2, None, 7) == -17
+    assert lib.sgemm_rm_strided_batched_ex(4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2, None, 9) == -17
 
 
 # Transposed and column-major forms.  M = 6, N = 5, K = 3 keep every leading-dimension
@@ -185,7 +186,7 @@ def test_op_invalid_arguments(lib, cm):
     bfn = lib.sgemm_cm_strided_batched_ex if cm else lib.sgemm_rm_op_strided_batched_ex
     bok = [0, 0, M6, N5, K3, 1.0, F, lda, G, F, ldb, G, 0.0, F, ldc, G, 2, None, 0]
     for pos, bad in [(1, 3), (2, -1), (3, -1), (4, -1), (5, -1), (7, None), (9, -1), (10, None), (12, -1),
-                     (14, None), (16, -1), (17, -1), (19, 5), (19, -1)]:
+                     (14, None), (16, -1), (17, -1), (19, 9), (19, -1)]:
         args = list(bok)
         args[pos - 1] = bad
         assert bfn(*args) == -pos, (pos, bad)
@@ -213,3 +214,24 @@ def test_python_operand_layout():
         operand_layout(*base[::2, ::2].shape, *base[::2, ::2].stride())
     with pytest.raises(ValueError):  # overlapping rows
         operand_layout(4, 8, 4, 1)
+
+
+def test_plan_tiles(lib):
+    """The tile plan is a host-side choice: quick returns, argument codes, and the
+    configurations the model picks for the benchmark workloads."""
+    from fp32_gemm_rm_amd import sgemm_rm_plan_tiles
+
+    assert lib.sgemm_rm_plan_tiles(-1, 4, 4, 1) == -1
+    assert lib.sgemm_rm_plan_tiles(4, -1, 4, 1) == -2
+    assert lib.sgemm_rm_plan_tiles(4, 4, -1, 1) == -3
+    assert lib.sgemm_rm_plan_tiles(4, 4, 4, -1) == -4
+    assert lib.sgemm_rm_plan_tiles(0, 4, 4, 1) == 0 and lib.sgemm_rm_plan_tiles(4, 4, 4, 0) == 0
+    assert sgemm_rm_plan_tiles(4096, 4096, 4096) == 256
+    assert sgemm_rm_plan_tiles(8192, 8192, 8192) == 256
+    assert sgemm_rm_plan_tiles(2048, 2048, 2048) == 128
+    assert sgemm_rm_plan_tiles(1024, 1024, 1024) == 64
+    assert sgemm_rm_plan_tiles(256, 256, 256) == 32
+    assert sgemm_rm_plan_tiles(1000, 1030, 999) == 32
+    assert sgemm_rm_plan_tiles(64, 64, 64, 1024) == 64
+    for M, N, K, b in [(1, 1, 1, 1), (5000, 3, 7, 1), (3, 5000, 70000, 1), (65535, 65535, 1, 1000000)]:
+        assert sgemm_rm_plan_tiles(M, N, K, b) in (256, 128, 64, 32)

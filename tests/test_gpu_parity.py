@@ -231,29 +231,49 @@ def test_single_hip_runtime():
     assert len(libs) == 1, libs
 
 
-@pytest.mark.parametrize(
-    "M,N,K",
-    [
-        (2048, 2048, 300),   # 128 x 128 MFMA tiles
-        (2176, 2112, 129),   # 128 x 128 tiles plus edge strips
-        (4196, 4132, 77),    # 256 x 256 tiles plus edge strips, ragged K
-        (4096, 4096, 17),    # 256 x 256 tiles, K just past one K-tile
-    ],
-)
-def test_tile_configs_integer_exact(oracle, M, N, K):
-    """Every MFMA tile configuration the dispatcher can pick, with edges: bit-exact on
-    integer inputs, padded leading dimensions, NaN padding in A/B, sentinel in C."""
+# Shapes per MFMA tile configuration (forced through its variant): full tiles only,
+# and full tiles plus partial ones (scalar edge tiles, or guarded MFMA tiles for 32).
+TILE_SHAPES = {
+    256: [(4096, 4096, 17), (4000, 3900, 77)],
+    128: [(2048, 2048, 300), (2000, 1950, 129)],
+    64: [(1024, 1024, 129), (1000, 990, 129)],
+    32: [(512, 512, 300), (1000, 1030, 99)],
+}
+
+
+@pytest.mark.parametrize("tiles,M,N,K", [(t, *s) for t, shapes in TILE_SHAPES.items() for s in shapes])
+def test_tile_configs_integer_exact(oracle, tiles, M, N, K):
+    """Every MFMA tile configuration, with and without partial tiles: bit-exact on integer
+    inputs, padded leading dimensions, NaN padding in A/B, sentinel in C.  The default
+    path runs on the same inputs too."""
+    from fp32_gemm_rm_amd import TILE_VARIANTS
+
     lda, ldb, ldc = K + 4, N + 8, N + 3
     a = integer_matrix(M, K, -4, 4, seed=M + K)
     b = integer_matrix(K, N, -4, 4, seed=N + K)
     c = integer_matrix(M, N, -4, 4, seed=M + N)
     A, B, C = pad_rows(a, lda, np.nan), pad_rows(b, ldb, np.nan), pad_rows(c, ldc, C_PAD_SENTINEL)
-    out = run_gemm(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, VARIANTS["mfma"])
     ref, _ = oracle.full(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc)
-    got = c_window(out, M, N, ldc).astype(np.float64)
-    bad = np.argwhere(got != ref)
-    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
-    check_padding(out, C, M, N, ldc)
+    for variant in (TILE_VARIANTS[tiles], VARIANTS["auto"]):
+        out = run_gemm(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, variant)
+        got = c_window(out, M, N, ldc).astype(np.float64)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"variant {variant}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+        check_padding(out, C, M, N, ldc)
+
+
+@pytest.mark.parametrize("tiles", [256, 128, 64, 32])
+def test_tile_configs_random_bound(oracle, tiles):
+    """Each forced tile configuration on the ragged 1000 x 1030 x 999 workload (alpha 1.5,
+    beta -0.5, padded leading dimensions), within the bound."""
+    from fp32_gemm_rm_amd import TILE_VARIANTS
+
+    w = WORKLOAD_BY_NAME["sgemm_ragged_1000x1030x999"]
+    A, B, C = workload_inputs(w)
+    out = run_gemm(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, TILE_VARIANTS[tiles])
+    ref, S = oracle.full(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc)
+    assert_within_bound(c_window(out, w.M, w.N, w.ldc), ref, S, f"tiles {tiles}")
+    check_padding(out, C, w.M, w.N, w.ldc)
 
 
 @pytest.mark.parametrize("variant,N", [("mfma", 64), ("auto", 64), ("regblock", 64), ("lds_tiled", 64), ("naive", 4)])

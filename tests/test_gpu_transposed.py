@@ -125,26 +125,51 @@ def test_ragged_random_bound(oracle, variant, orient):
     print(f"[transposed] ragged {orient} {variant} max err/bound {r:.3g}", flush=True)
 
 
+# Small shapes per forced MFMA tile configuration: several full tiles plus partial ones,
+# and (for 32) full tiles only.
+TILE_SHAPES = [(256, 600, 520, 77), (128, 300, 290, 77), (64, 200, 150, 77), (32, 100, 70, 77), (32, 96, 64, 77)]
+
+
 @pytest.mark.parametrize("orient", ["nt", "tn", "tt"])
-@pytest.mark.parametrize(
-    "M,N,K",
-    [
-        (2048, 2048, 300),   # 128 x 128 MFMA tiles
-        (2176, 2112, 129),   # 128 x 128 tiles plus edge strips
-        (4196, 4132, 77),    # 256 x 256 tiles plus edge strips, ragged K
-        (4096, 4096, 17),    # 256 x 256 tiles, K just past one K-tile
-        (640, 704, 70),      # 64 x 64 tiles with the K-split, ragged K
-    ],
-)
-def test_tile_configs_integer_exact(oracle, M, N, K, orient):
+@pytest.mark.parametrize("tiles,M,N,K", TILE_SHAPES)
+def test_tile_configs_integer_exact(oracle, tiles, M, N, K, orient):
     """Every MFMA tile configuration with transposed operands: bit-exact on integer inputs."""
+    from fp32_gemm_rm_amd import TILE_VARIANTS
+
     ta, tb = ORIENTATIONS[orient]
     a = integer_matrix(M, K, -4, 4, seed=M + K)
     b = integer_matrix(K, N, -4, 4, seed=N + K)
     c = integer_matrix(M, N, -4, 4, seed=M + N)
     lda, ldb, ldc = min_ld(M, K, ta, False) + 4, min_ld(K, N, tb, False) + 8, N + 3
     A, B, C = store(a, ta, False, lda, np.nan), store(b, tb, False, ldb, np.nan), pad_rows(c, ldc, C_PAD_SENTINEL)
-    out = run_op(ta, tb, M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, VARIANTS["mfma"])
+    out = run_op(ta, tb, M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, TILE_VARIANTS[tiles])
+    ref, _ = oracle_logical(oracle, M, N, K, 2.0, a, b, -1.0, c)
+    got = read_c(out, M, N, ldc, False).astype(np.float64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+    assert c_padding_unchanged(out, C, M, N, ldc, False)
+
+
+@pytest.mark.parametrize("orient", ["nt", "tn", "tt"])
+@pytest.mark.parametrize(
+    "M,N,K",
+    [
+        (2048, 2048, 300),   # 128 x 128 tiles
+        (4196, 4132, 77),    # 64 x 64 tiles plus edge strips, ragged K
+        (4096, 4096, 17),    # 256 x 256 tiles, K just past one K-tile
+        (1000, 1030, 99),    # 32 x 32 tiles, partial ones on MFMA
+    ],
+)
+def test_default_path_integer_exact(oracle, M, N, K, orient):
+    """The default path with transposed operands at shapes that select each tile
+    configuration: bit-exact on integer inputs."""
+    ta, tb = ORIENTATIONS[orient]
+    a = integer_matrix(M, K, -4, 4, seed=M + K)
+    b = integer_matrix(K, N, -4, 4, seed=N + K)
+    c = integer_matrix(M, N, -4, 4, seed=M + N)
+    lda, ldb, ldc = min_ld(M, K, ta, False) + 4, min_ld(K, N, tb, False) + 8, N + 3
+    A, B, C = store(a, ta, False, lda, np.nan), store(b, tb, False, ldb, np.nan), pad_rows(c, ldc, C_PAD_SENTINEL)
+    out = run_op(ta, tb, M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, VARIANTS["auto"])
     ref, _ = oracle_logical(oracle, M, N, K, 2.0, a, b, -1.0, c)
     got = read_c(out, M, N, ldc, False).astype(np.float64)
     bad = np.argwhere(got != ref)
