@@ -59,6 +59,8 @@
 // MFMA tile: its last K-tile loads zeros past K.
 #pragma once
 
+#include <type_traits>
+
 #include "regblock_tile.h"
 
 namespace sgemm_impl {
@@ -109,7 +111,7 @@ struct Operand {
   long long ld;
   int lim;                     // rows of the slice inside the matrix (R for a full tile)
   int row[LOADS], col[LOADS];  // KROWS: (r, chunk); else (k, 4 * r-quad)
-  float4 reg[LOADS];
+  float4 reg[2][LOADS];  // two register sets for a prefetch distance of two K-tiles
 
   __device__ __forceinline__ void init(const float* X, long long ldx, int r0, int rows_left, int t) {
     ld = ldx;
@@ -124,37 +126,39 @@ struct Operand {
   }
   // full K-tile starting at k0.  GUARD: the slice may reach past the matrix (lim < R):
   // zeros there (a float4 along r that is only partly inside is read element by element)
-  template <bool VEC, bool GUARD>
+  template <bool VEC, bool GUARD, int SET = 0>
   __device__ __forceinline__ void load_full(int k0) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       if (KROWS)
-        reg[i] = (!GUARD || row[i] < lim) ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], 4)
+        reg[SET][i] = (!GUARD || row[i] < lim) ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], 4)
                                           : make_float4(0.f, 0.f, 0.f, 0.f);
       else
-        reg[i] = GUARD ? load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], lim - col[i])
-                       : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
+        reg[SET][i] = GUARD ? load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], lim - col[i])
+                            : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
     }
   }
   // last K-tile: kl = K - k0 < BK valid k; zeros past K (and past the matrix, GUARD)
-  template <bool VEC, bool GUARD>
+  template <bool VEC, bool GUARD, int SET = 0>
   __device__ __forceinline__ void load_tail(int k0, int kl) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       if (KROWS)
-        reg[i] = (!GUARD || row[i] < lim) ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], kl - 4 * col[i])
+        reg[SET][i] = (!GUARD || row[i] < lim) ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], kl - 4 * col[i])
                                           : make_float4(0.f, 0.f, 0.f, 0.f);
       else if (row[i] >= kl)
-        reg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        reg[SET][i] = make_float4(0.f, 0.f, 0.f, 0.f);
       else
-        reg[i] = GUARD ? load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], lim - col[i])
-                       : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
+        reg[SET][i] = GUARD ? load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], lim - col[i])
+                            : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
     }
   }
+  template <int SET = 0>
   __device__ __forceinline__ void store(float* stage) const {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : row[i] * STRIDE + col[i])) = reg[i];
+      *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : row[i] * STRIDE + col[i])) =
+          reg[SET][i];
   }
   // out[e] = X(rr, 16g + 8lh + e), e = 0..7: this lane's values for the 8 MFMA steps of k-group g
   __device__ __forceinline__ static void read(const float* stage, int rr, int g, int lh, float (&out)[8]) {
@@ -195,7 +199,7 @@ struct TileMap {
 
 // One BM x BN tile of C at (m0, n0).  GUARD: the tile reaches past M or N; loads read
 // zeros there and stores skip it.
-template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool VEC, bool GUARD>
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool VEC, bool GUARD, int PF>
 __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, float* smem) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   using OpA = typename Cfg::OpA;
@@ -226,26 +230,20 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, floa
 
   const int nfull = p.K / BK;  // K-tiles with no element past K
   const int ntiles = (p.K + BK - 1) / BK;
-  // global -> registers for K-tile kt; the guarded form (the last, partial K-tile
-  // only) loads zeros past K and is kept out of the steady-state loop
-  auto load = [&](int kt) {
+  // global -> registers (set SET) for K-tile kt; the guarded form (the last, partial
+  // K-tile only) loads zeros past K and is kept out of the steady-state loop
+  auto load = [&](auto set, int kt) {
+    constexpr int SET = decltype(set)::value;
     if (kt < nfull) {
-      opa.template load_full<VEC, GUARD>(kt * BK);
-      opb.template load_full<VEC, GUARD>(kt * BK);
+      opa.template load_full<VEC, GUARD, SET>(kt * BK);
+      opb.template load_full<VEC, GUARD, SET>(kt * BK);
     } else {
-      opa.template load_tail<VEC, GUARD>(kt * BK, p.K - kt * BK);
-      opb.template load_tail<VEC, GUARD>(kt * BK, p.K - kt * BK);
+      opa.template load_tail<VEC, GUARD, SET>(kt * BK, p.K - kt * BK);
+      opb.template load_tail<VEC, GUARD, SET>(kt * BK, p.K - kt * BK);
     }
   };
-
-  load(0);
-  opa.store(a_stage(0));
-  opb.store(b_stage(0));
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < ntiles) load(kt + 1);
+  // the MFMAs of K-tile kt from stage s; `mid` runs half-way through the last k-group
+  auto multiply = [&](int s, auto mid) {
 #pragma unroll
     for (int r = 0; r < KG; ++r) {
       const int g = ks * KG + r;  // 16-deep k-group of this K-tile
@@ -264,13 +262,56 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, floa
         // store the next tile into the other stage half-way through the last k-group's MFMAs
         // (that stage was last read before the previous barrier), so that the LDS writes
         // overlap MFMAs instead of bunching up before the barrier: +1.5% at 4096^3
-        if (e == 3 && r == KG - 1 && kt + 1 < ntiles) {
+        if (e == 3 && r == KG - 1) mid();
+      }
+    }
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+
+  if constexpr (PF == 1) {
+    // prefetch distance one: tile kt+1 is loaded while tile kt is multiplied
+    load(Set0{}, 0);
+    opa.store(a_stage(0));
+    opb.store(b_stage(0));
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int s = kt & 1;
+      const bool more = kt + 1 < ntiles;
+      if (more) load(Set0{}, kt + 1);
+      multiply(s, [&] {
+        if (more) {
           opa.store(a_stage(s ^ 1));
           opb.store(b_stage(s ^ 1));
         }
-      }
+      });
+      __syncthreads();
     }
+  } else {
+    // prefetch distance two: tile j's registers are set j % 2; tile kt+2 is loaded while
+    // tile kt is multiplied and tile kt+1 (loaded one step earlier) is stored to LDS, so
+    // each load has two K-tiles of MFMAs to arrive
+    static_assert(PF == 2, "prefetch distance one or two");
+    load(Set0{}, 0);
+    opa.template store<0>(a_stage(0));
+    opb.template store<0>(b_stage(0));
+    if (ntiles > 1) load(Set1{}, 1);
     __syncthreads();
+    auto step = [&](auto set, int kt) {  // set = kt % 2, also the LDS stage of tile kt
+      constexpr int P = decltype(set)::value;
+      if (kt + 2 < ntiles) load(set, kt + 2);
+      multiply(P, [&] {
+        if (kt + 1 < ntiles) {
+          opa.template store<P ^ 1>(a_stage(P ^ 1));
+          opb.template store<P ^ 1>(b_stage(P ^ 1));
+        }
+      });
+      __syncthreads();
+    };
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      step(Set0{}, kt);
+      if (kt + 1 < ntiles) step(Set1{}, kt + 1);
+    }
   }
 
   const bool beta0 = p.beta == 0.0f;
@@ -370,7 +411,7 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // MFMA_EDGES: the tiles reaching past M or N are guarded MFMA tiles of the same grid
 // (tiles_m x tiles_n covers the whole matrix) instead of scalar edge tiles.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          bool MFMA_EDGES, bool VEC>
+          bool MFMA_EDGES, int PF, bool VEC>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
@@ -387,9 +428,9 @@ void mfma_kernel(Problem p, TileMap map) {
     tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
     const int m0 = bm * BM, n0 = bn * BN;
     if (!MFMA_EDGES || (m0 + BM <= p.M && n0 + BN <= p.N))
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false>(p, m0, n0, smem);
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false, PF>(p, m0, n0, smem);
     else
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, true>(p, m0, n0, smem);
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, true, PF>(p, m0, n0, smem);
     return;
   }
   if constexpr (!MFMA_EDGES) {
@@ -408,7 +449,7 @@ void mfma_kernel(Problem p, TileMap map) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          bool MFMA_EDGES = false>
+          bool MFMA_EDGES = false, int PF = 1>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   static_assert(BM % kEdge == 0 && BN % kEdge == 0, "edge tiles of the right strip end at Mf");
   TileMap map;
@@ -437,11 +478,11 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks, batch), block(WM * WN * KS * 64);
   if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, true>), grid,
-                       block, 0, stream, p, map);
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, PF, true>),
+                       grid, block, 0, stream, p, map);
   else
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false>), grid,
-                       block, 0, stream, p, map);
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, PF, false>),
+                       grid, block, 0, stream, p, map);
   return hipGetLastError();
 }
 
@@ -453,6 +494,9 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
 //        256 threads; four workgroups per CU.  Partial tiles are guarded MFMA tiles
 //        (the other configurations send them to the scalar edge-tile path).
+// The 64 and 32 configurations load two K-tiles ahead (each K-tile is short there:
+// 8 MFMAs per wavefront), which gains 4-10%; the 256 and 128 ones load one ahead
+// (two ahead costs them 3-6%).
 template <bool TA, bool TB>
 hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles) {
   switch (tiles) {
@@ -461,10 +505,11 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles)
     case 128:
       return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
     case 64:
-      return launch_cfg<64, 64, 64, 2, 2, 4, TA, TB, 8, 2>(p, batch, stream);
+      return launch_cfg<64, 64, 64, 2, 2, 4, TA, TB, 8, 2, false, 2>(p, batch, stream);
     case 32:
-      if (p.M % 32 == 0 && p.N % 32 == 0) return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4>(p, batch, stream);
-      return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, true>(p, batch, stream);
+      if (p.M % 32 == 0 && p.N % 32 == 0)
+        return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, false, 2>(p, batch, stream);
+      return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, true, 2>(p, batch, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -19,7 +19,7 @@ struct TileCost {
   int side;  // tile side: 256, 128, 64 or 32
   double u1, u2;
 };
-constexpr TileCost kTileCosts[] = {{256, 242.0, 242.0}, {128, 69.3, 69.3}, {64, 18.8, 17.9}, {32, 6.1, 5.4}};
+constexpr TileCost kTileCosts[] = {{256, 242.0, 242.0}, {128, 69.3, 69.3}, {64, 17.1, 17.0}, {32, 5.7, 5.2}};
 
 // M, N, K, batch > 0.
 inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {

@@ -228,7 +228,6 @@ def test_plan_tiles(lib):
     assert lib.sgemm_rm_plan_tiles(0, 4, 4, 1) == 0 and lib.sgemm_rm_plan_tiles(4, 4, 4, 0) == 0
     assert sgemm_rm_plan_tiles(4096, 4096, 4096) == 256
     assert sgemm_rm_plan_tiles(8192, 8192, 8192) == 256
-    assert sgemm_rm_plan_tiles(2048, 2048, 2048) == 128
     assert sgemm_rm_plan_tiles(1024, 1024, 1024) == 64
     assert sgemm_rm_plan_tiles(256, 256, 256) == 32
     assert sgemm_rm_plan_tiles(1000, 1030, 999) == 32
