@@ -25,8 +25,9 @@
 // SIMD a single wavefront, run 4 wavefronts per SIMD and hide LDS, barrier and
 // MFMA latencies.
 //
-// LDS, two stages (one barrier per K-tile; the global loads of tile t+1 are in
-// flight while tile t is multiplied and are stored half-way through its MFMAs):
+// LDS, two stages (one barrier per K-tile; the global loads of tile t+2 are issued as
+// tile t's MFMAs start, into the second of two register sets, and tile t+1's registers
+// are stored half-way through those MFMAs):
 //   A tile, BM rows of BK floats (BK/4 16-byte chunks), no padding.  For
 //     BK = 16, chunk c of row r is stored at chunk position c ^ ((r/4) % 4).  On
 //     gfx950 a 128-bit LDS access serves 16 lanes per cycle from 64 banks of 4
@@ -199,7 +200,7 @@ struct TileMap {
 
 // One BM x BN tile of C at (m0, n0).  GUARD: the tile reaches past M or N; loads read
 // zeros there and stores skip it.
-template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool VEC, bool GUARD, int PF>
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool VEC, bool GUARD>
 __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, float* smem) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   using OpA = typename Cfg::OpA;
@@ -259,59 +260,57 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, floa
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][e], bf[j][e], acc[i][j], 0, 0, 0);
-        // store the next tile into the other stage half-way through the last k-group's MFMAs
-        // (that stage was last read before the previous barrier), so that the LDS writes
-        // overlap MFMAs instead of bunching up before the barrier: +1.5% at 4096^3
+        // store the next tile's registers into the other stage half-way through the last
+        // k-group's MFMAs (that stage was last read before the previous barrier), so that
+        // the LDS writes overlap MFMAs instead of bunching up before the barrier: +1.5%
         if (e == 3 && r == KG - 1) mid();
       }
     }
   };
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
-
-  if constexpr (PF == 1) {
-    // prefetch distance one: tile kt+1 is loaded while tile kt is multiplied
-    load(Set0{}, 0);
-    opa.store(a_stage(0));
-    opb.store(b_stage(0));
+  // Prefetch distance two: tile j's registers are set j % 2; tile kt+2 is loaded while
+  // tile kt is multiplied and tile kt+1 (loaded one step earlier) is stored to LDS, so
+  // each load has two K-tiles of MFMAs to arrive (one K-tile ahead is 2-10% slower;
+  // 4096^3: 141.0 against 143.7 TFLOP/s).  The steady-state loop issues the same loads
+  // and stores on every path, so that the compiler's wait before the LDS store covers
+  // only the older register set (a wait on the newest loads would undo the prefetch);
+  // the last steps run the general form.
+  load(Set0{}, 0);
+  opa.template store<0>(a_stage(0));
+  opb.template store<0>(b_stage(0));
+  if (ntiles > 1) load(Set1{}, 1);
+  __syncthreads();
+  auto steady = [&](auto set, int kt) {  // set = kt % 2, also the LDS stage of tile kt
+    constexpr int P = decltype(set)::value;
+    opa.template load_full<VEC, GUARD, P>((kt + 2) * BK);
+    opb.template load_full<VEC, GUARD, P>((kt + 2) * BK);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    multiply(P, [&] {
+      opa.template store<P ^ 1>(a_stage(P ^ 1));
+      opb.template store<P ^ 1>(b_stage(P ^ 1));
+    });
     __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-      const int s = kt & 1;
-      const bool more = kt + 1 < ntiles;
-      if (more) load(Set0{}, kt + 1);
-      multiply(s, [&] {
-        if (more) {
-          opa.store(a_stage(s ^ 1));
-          opb.store(b_stage(s ^ 1));
-        }
-      });
-      __syncthreads();
-    }
-  } else {
-    // prefetch distance two: tile j's registers are set j % 2; tile kt+2 is loaded while
-    // tile kt is multiplied and tile kt+1 (loaded one step earlier) is stored to LDS, so
-    // each load has two K-tiles of MFMAs to arrive
-    static_assert(PF == 2, "prefetch distance one or two");
-    load(Set0{}, 0);
-    opa.template store<0>(a_stage(0));
-    opb.template store<0>(b_stage(0));
-    if (ntiles > 1) load(Set1{}, 1);
+  };
+  auto step = [&](auto set, int kt) {
+    constexpr int P = decltype(set)::value;
+    if (kt + 2 < ntiles) load(set, kt + 2);
+    multiply(P, [&] {
+      if (kt + 1 < ntiles) {
+        opa.template store<P ^ 1>(a_stage(P ^ 1));
+        opb.template store<P ^ 1>(b_stage(P ^ 1));
+      }
+    });
     __syncthreads();
-    auto step = [&](auto set, int kt) {  // set = kt % 2, also the LDS stage of tile kt
-      constexpr int P = decltype(set)::value;
-      if (kt + 2 < ntiles) load(set, kt + 2);
-      multiply(P, [&] {
-        if (kt + 1 < ntiles) {
-          opa.template store<P ^ 1>(a_stage(P ^ 1));
-          opb.template store<P ^ 1>(b_stage(P ^ 1));
-        }
-      });
-      __syncthreads();
-    };
-    for (int kt = 0; kt < ntiles; kt += 2) {
-      step(Set0{}, kt);
-      if (kt + 1 < ntiles) step(Set1{}, kt + 1);
-    }
+  };
+  int kt = 0;
+  for (; kt + 3 < nfull; kt += 2) {  // tiles kt+2 and kt+3 are full
+    steady(Set0{}, kt);
+    steady(Set1{}, kt + 1);
+  }
+  for (; kt < ntiles; kt += 2) {
+    step(Set0{}, kt);
+    if (kt + 1 < ntiles) step(Set1{}, kt + 1);
   }
 
   const bool beta0 = p.beta == 0.0f;
@@ -411,7 +410,7 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // MFMA_EDGES: the tiles reaching past M or N are guarded MFMA tiles of the same grid
 // (tiles_m x tiles_n covers the whole matrix) instead of scalar edge tiles.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          bool MFMA_EDGES, int PF, bool VEC>
+          bool MFMA_EDGES, bool VEC>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
@@ -428,9 +427,9 @@ void mfma_kernel(Problem p, TileMap map) {
     tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
     const int m0 = bm * BM, n0 = bn * BN;
     if (!MFMA_EDGES || (m0 + BM <= p.M && n0 + BN <= p.N))
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false, PF>(p, m0, n0, smem);
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false>(p, m0, n0, smem);
     else
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, true, PF>(p, m0, n0, smem);
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, true>(p, m0, n0, smem);
     return;
   }
   if constexpr (!MFMA_EDGES) {
@@ -449,7 +448,7 @@ void mfma_kernel(Problem p, TileMap map) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          bool MFMA_EDGES = false, int PF = 1>
+          bool MFMA_EDGES = false>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   static_assert(BM % kEdge == 0 && BN % kEdge == 0, "edge tiles of the right strip end at Mf");
   TileMap map;
@@ -478,10 +477,10 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks, batch), block(WM * WN * KS * 64);
   if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, PF, true>),
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, true>),
                        grid, block, 0, stream, p, map);
   else
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, PF, false>),
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false>),
                        grid, block, 0, stream, p, map);
   return hipGetLastError();
 }
@@ -494,9 +493,6 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
 //        256 threads; four workgroups per CU.  Partial tiles are guarded MFMA tiles
 //        (the other configurations send them to the scalar edge-tile path).
-// The 64 and 32 configurations load two K-tiles ahead (each K-tile is short there:
-// 8 MFMAs per wavefront), which gains 4-10%; the 256 and 128 ones load one ahead
-// (two ahead costs them 3-6%).
 template <bool TA, bool TB>
 hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles) {
   switch (tiles) {
@@ -505,11 +501,10 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles)
     case 128:
       return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
     case 64:
-      return launch_cfg<64, 64, 64, 2, 2, 4, TA, TB, 8, 2, false, 2>(p, batch, stream);
+      return launch_cfg<64, 64, 64, 2, 2, 4, TA, TB, 8, 2>(p, batch, stream);
     case 32:
-      if (p.M % 32 == 0 && p.N % 32 == 0)
-        return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, false, 2>(p, batch, stream);
-      return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, true, 2>(p, batch, stream);
+      if (p.M % 32 == 0 && p.N % 32 == 0) return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4>(p, batch, stream);
+      return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, true>(p, batch, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -6,8 +6,8 @@
 // tile and unit of K on a CU that holds one tile (u1) or several (u2); the model
 // picks the configuration with the least time.  The per-configuration figures come
 // from a sweep of square and rectangular shapes on MI355X (microseconds per 1024 of
-// K per tile-layer); they reproduce the measured times of every configuration within
-// about 10% above a few microseconds of launch cost.  Transposed operands use the
+// K per tile-layer, net of about 5 us of launch cost); they reproduce the measured
+// times of every configuration within about 10%.  Transposed operands use the
 // same figures.
 #pragma once
 
@@ -19,7 +19,7 @@ struct TileCost {
   int side;  // tile side: 256, 128, 64 or 32
   double u1, u2;
 };
-constexpr TileCost kTileCosts[] = {{256, 242.0, 242.0}, {128, 69.3, 69.3}, {64, 17.1, 17.0}, {32, 5.7, 5.2}};
+constexpr TileCost kTileCosts[] = {{256, 237.0, 237.0}, {128, 64.7, 64.7}, {64, 17.1, 17.6}, {32, 5.4, 4.95}};
 
 // M, N, K, batch > 0.
 inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
