@@ -301,3 +301,31 @@ def test_offsets_past_2_pow_31(oracle, variant, N):
     np.testing.assert_array_equal(got, ref)
     del dA
     torch.cuda.empty_cache()
+
+
+# K-tile depth of each tile configuration (the K loop runs a steady state over pairs of
+# full K-tiles and a general tail; these K values put its boundaries in every place).
+TILE_BK = {256: 16, 128: 32, 64: 64, 32: 64}
+
+
+@pytest.mark.parametrize("tiles", [256, 128, 64, 32])
+def test_k_loop_boundaries_integer_exact(oracle, tiles):
+    """K from 1 to nine K-tiles (full, ragged, odd and even tile counts) for each forced
+    tile configuration, on a shape with full and partial tiles: bit-exact."""
+    from fp32_gemm_rm_amd import TILE_VARIANTS
+
+    bk = TILE_BK[tiles]
+    M, N = tiles + 40, tiles + 24
+    for K in sorted({1, 3, bk - 1, bk, bk + 1, 2 * bk, 2 * bk + 5, 3 * bk - 1, 3 * bk, 4 * bk, 4 * bk + 1,
+                     5 * bk, 5 * bk + 7, 6 * bk, 7 * bk + 3, 8 * bk, 9 * bk - 2}):
+        lda, ldb, ldc = K + 3, N + 5, N + 2
+        a = integer_matrix(M, K, -4, 4, seed=3 * K + 1)
+        b = integer_matrix(K, N, -4, 4, seed=3 * K + 2)
+        c = integer_matrix(M, N, -4, 4, seed=3 * K + 3)
+        A, B, C = pad_rows(a, lda, np.nan), pad_rows(b, ldb, np.nan), pad_rows(c, ldc, C_PAD_SENTINEL)
+        out = run_gemm(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, TILE_VARIANTS[tiles])
+        ref, _ = oracle.full(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc)
+        got = c_window(out, M, N, ldc).astype(np.float64)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"tiles {tiles} K {K}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+        check_padding(out, C, M, N, ldc)

@@ -127,7 +127,8 @@ def test_ragged_random_bound(oracle, variant, orient):
 
 # Small shapes per forced MFMA tile configuration: several full tiles plus partial ones,
 # and (for 32) full tiles only.
-TILE_SHAPES = [(256, 600, 520, 77), (128, 300, 290, 77), (64, 200, 150, 77), (32, 100, 70, 77), (32, 96, 64, 77)]
+TILE_SHAPES = [(256, 600, 520, 77), (256, 300, 270, 160), (128, 300, 290, 77), (128, 140, 290, 257),
+               (64, 200, 150, 77), (64, 130, 70, 450), (32, 100, 70, 77), (32, 96, 64, 77), (32, 40, 70, 449)]
 
 
 @pytest.mark.parametrize("orient", ["nt", "tn", "tt"])
