@@ -488,8 +488,8 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
 // The tile configurations (tile_plan.h), by tile side.
 //   256: 256 x 256 tiles, 4 x 4 wavefronts of 64 x 64, BK 16: one workgroup per CU.
 //   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64 and a 2-way K split, BK 32.
-//   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 4-way K split, BK 64; two
-//        workgroups per CU.
+//   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32; three
+//        workgroups per CU (a 4-way split with BK 64 is 2-7% slower).
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
 //        256 threads; four workgroups per CU.  Partial tiles are guarded MFMA tiles
 //        (the other configurations send them to the scalar edge-tile path).
@@ -501,7 +501,7 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles)
     case 128:
       return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
     case 64:
-      return launch_cfg<64, 64, 64, 2, 2, 4, TA, TB, 8, 2>(p, batch, stream);
+      return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 3>(p, batch, stream);
     case 32:
       if (p.M % 32 == 0 && p.N % 32 == 0) return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4>(p, batch, stream);
       return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, true>(p, batch, stream);
