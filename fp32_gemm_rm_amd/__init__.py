@@ -27,12 +27,15 @@ from .binding import (  # noqa: F401
     sgemm_batched,
     sgemm_cm,
     sgemm_cm_strided_batched_ex,
+    sgemm_cm_strided_batched_ws,
     sgemm_rm,
     sgemm_rm_ex,
     sgemm_rm_op,
     sgemm_rm_op_strided_batched_ex,
+    sgemm_rm_op_strided_batched_ws,
     sgemm_rm_plan_tiles,
     sgemm_rm_strerror,
     sgemm_rm_strided_batched,
     sgemm_rm_strided_batched_ex,
+    sgemm_rm_workspace_size,
 )

@@ -44,6 +44,7 @@ _lib = None
 #: Names the header declares; the CPU tests check that the library exports each.
 EXPORTED_SYMBOLS = ("sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex",
                     "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex", "sgemm_cm", "sgemm_cm_strided_batched_ex",
+                    "sgemm_rm_op_strided_batched_ws", "sgemm_cm_strided_batched_ws", "sgemm_rm_workspace_size",
                     "sgemm_rm_plan_tiles", "sgemm_rm_strerror", "sgemm_rm_version")
 
 
@@ -90,6 +91,13 @@ def load_library():
         for name in ("sgemm_rm_op_strided_batched_ex", "sgemm_cm_strided_batched_ex"):
             getattr(lib, name).argtypes = obargs
             getattr(lib, name).restype = ctypes.c_int
+        wargs = [ctypes.c_int, ctypes.c_int] + bargs[:-1] + [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p,
+                                                           ctypes.c_int]
+        for name in ("sgemm_rm_op_strided_batched_ws", "sgemm_cm_strided_batched_ws"):
+            getattr(lib, name).argtypes = wargs
+            getattr(lib, name).restype = ctypes.c_int
+        lib.sgemm_rm_workspace_size.argtypes = [ctypes.c_int] * 4
+        lib.sgemm_rm_workspace_size.restype = ctypes.c_longlong
         lib.sgemm_rm_plan_tiles.argtypes = [ctypes.c_int] * 4
         lib.sgemm_rm_plan_tiles.restype = ctypes.c_int
         lib.sgemm_rm_strerror.argtypes = [ctypes.c_int]
@@ -98,6 +106,53 @@ def load_library():
         lib.sgemm_rm_version.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def sgemm_rm_op_strided_batched_ws(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                                   strideC, batch, workspace, workspace_bytes, stream=0,
+                                   variant=SGEMM_RM_VARIANT_AUTO):
+    """The general row-major call with a stream-K workspace (device pointer and bytes)."""
+    lib = load_library()
+    return _check(lib.sgemm_rm_op_strided_batched_ws(
+        int(transA), int(transB), int(M), int(N), int(K), float(alpha), A or None, int(lda), int(strideA),
+        B or None, int(ldb), int(strideB), float(beta), C or None, int(ldc), int(strideC), int(batch),
+        workspace or None, int(workspace_bytes), stream or None, int(variant)))
+
+
+def sgemm_cm_strided_batched_ws(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                                strideC, batch, workspace, workspace_bytes, stream=0, variant=SGEMM_RM_VARIANT_AUTO):
+    """The column-major form of ``sgemm_rm_op_strided_batched_ws``."""
+    lib = load_library()
+    return _check(lib.sgemm_cm_strided_batched_ws(
+        int(transA), int(transB), int(M), int(N), int(K), float(alpha), A or None, int(lda), int(strideA),
+        B or None, int(ldb), int(strideB), float(beta), C or None, int(ldc), int(strideC), int(batch),
+        workspace or None, int(workspace_bytes), stream or None, int(variant)))
+
+
+def sgemm_rm_workspace_size(M, N, K, batch=1) -> int:
+    """Workspace bytes with which the _ws calls use stream-K for the shape (0: none); host only."""
+    code = load_library().sgemm_rm_workspace_size(int(M), int(N), int(K), int(batch))
+    if code < 0:
+        raise SgemmError(int(code), sgemm_rm_strerror(int(code)))
+    return int(code)
+
+
+_workspaces = {}
+
+
+def _workspace_for(M, N, K, device, stream):
+    """(pointer, bytes) of a cached device workspace for the calls on `stream`, or (None, 0)."""
+    import torch
+
+    need = sgemm_rm_workspace_size(M, N, K, 1)
+    if need == 0:
+        return None, 0
+    key = (device.index, stream.cuda_stream)
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < need:
+        buf = torch.empty(need, dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf.data_ptr(), buf.numel()
 
 
 def sgemm_rm_plan_tiles(M, N, K, batch=1) -> int:
@@ -247,11 +302,13 @@ def sgemm_batched(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, s
                                        C.stride(0), nb, s, variant)
 
 
-def sgemm(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, stream=None):
+def sgemm(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, stream=None, workspace=True):
     """C := alpha*A@B + beta*C in place on 2-D float32 device tensors, on torch's current
     stream unless ``stream`` is given.  C is a row-major view (leading dimension =
     stride(0)); A and B may be row-major views or transposed ones (``X.t()`` of a
-    row-major X), which run as the transposed-operand forms without a copy."""
+    row-major X), which run as the transposed-operand forms without a copy.  With
+    ``workspace`` the call gets a cached per-stream device workspace where the library's
+    cost model chooses stream-K for the shape."""
     import torch
 
     if isinstance(variant, str):
@@ -263,6 +320,7 @@ def sgemm(A, B, C, alpha=1.0, beta=0.0, variant=SGEMM_RM_VARIANT_AUTO, stream=No
     a, lda, ta = _operand_view(A, "A")
     b, ldb, tb = _operand_view(B, "B")
     c, ldc = _matrix_view(C, "C")
-    s = (stream if stream is not None else torch.cuda.current_stream(C.device)).cuda_stream
-    return sgemm_rm_op_strided_batched_ex(ta, tb, M, N, K, alpha, a, lda, 0, b, ldb, 0, beta, c, ldc, 0, 1, s,
-                                          variant)
+    st = stream if stream is not None else torch.cuda.current_stream(C.device)
+    ws, ws_bytes = _workspace_for(M, N, K, C.device, st) if workspace else (None, 0)
+    return sgemm_rm_op_strided_batched_ws(ta, tb, M, N, K, alpha, a, lda, 0, b, ldb, 0, beta, c, ldc, 0, 1, ws,
+                                          ws_bytes, st.cuda_stream, variant)

@@ -63,14 +63,20 @@ hipError_t launch_regblock(const Problem& p, int batch, hipStream_t stream);
 // tiles (the scalar edge-tile path) for the strips past them, in one launch; one
 // instantiation per operand orientation (p.ta, p.tb), dispatched by launch_mfma.
 // tiles: the tile configuration by its side (256, 128, 64 or 32; see tile_plan.h).
-hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream, int tiles);
-hipError_t launch_mfma_nt(const Problem& p, int batch, hipStream_t stream, int tiles);
-hipError_t launch_mfma_tn(const Problem& p, int batch, hipStream_t stream, int tiles);
-hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream, int tiles);
-inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream, int tiles) {
-  if (p.ta) return p.tb ? launch_mfma_tt(p, batch, stream, tiles) : launch_mfma_tn(p, batch, stream, tiles);
-  return p.tb ? launch_mfma_nt(p, batch, stream, tiles) : launch_mfma_nn(p, batch, stream, tiles);
+// ws: nullptr, or kStreamKBytes of device memory for stream-K (256 configuration, batch 1).
+hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
+hipError_t launch_mfma_nt(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
+hipError_t launch_mfma_tn(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
+hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
+inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr) {
+  if (p.ta) return p.tb ? launch_mfma_tt(p, batch, stream, tiles, ws) : launch_mfma_tn(p, batch, stream, tiles, ws);
+  return p.tb ? launch_mfma_nt(p, batch, stream, tiles, ws) : launch_mfma_nn(p, batch, stream, tiles, ws);
 }
+
+// Stream-K for the 256 x 256 configuration: the workgroups that share the last waves of
+// tiles, and the workspace their partial tiles need (two 256 x 256 slots each, 128 MiB).
+constexpr int kStreamKWgs = 256;
+constexpr long long kStreamKBytes = 2LL * kStreamKWgs * 256 * 256 * 4;
 // C := beta*C on the M x N window (zeros when beta == 0; C is then not read).
 hipError_t launch_scale(const Problem& p, int batch, hipStream_t stream);
 

@@ -3,8 +3,8 @@
 
 namespace sgemm_impl {
 
-hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream, int tiles) {
-  return mfma_detail::launch_op<true, true>(p, batch, stream, tiles);
+hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws) {
+  return mfma_detail::launch_op<true, true>(p, batch, stream, tiles, ws);
 }
 
 }  // namespace sgemm_impl

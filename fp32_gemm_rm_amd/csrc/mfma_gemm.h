@@ -21,7 +21,8 @@
 // KS of them share each such block and split every K-tile of BK = 16*KS*KG
 // between them (KG 16-deep k-groups each).  Their partial sums are added through
 // LDS in the fixed order ks = 0, 1, ..., KS-1, so results are deterministic; each
-// of the KS wavefronts then finishes 1/KS of the block (sum, alpha/beta, store).  KS > 1 lets small problems, whose output alone would give each
+// of the KS wavefronts then finishes 1/KS of the block (sum, alpha/beta, store).
+// KS > 1 lets small problems, whose output alone would give each
 // SIMD a single wavefront, run 4 wavefronts per SIMD and hide LDS, barrier and
 // MFMA latencies.
 //
@@ -56,8 +57,16 @@
 // NT/256 groups of 256 threads split the tile's K range (all groups run the same
 // number of K-steps, so their barriers match) and add their partial sums through
 // LDS in the fixed group order.  Edge workgroups take the highest block ids of
-// the same launch, so they run beside the MFMA tiles instead of after them.  Ragged K is handled inside every
-// MFMA tile: its last K-tile loads zeros past K.
+// the same launch, so they run beside the MFMA tiles instead of after them.  Ragged K
+// is handled inside every MFMA tile: its last K-tile loads zeros past K.
+//
+// Stream-K (256 x 256 tiles, batch 1, with a caller workspace): when the full tiles do
+// not fill whole waves of 256 workgroups, the last partial wave and the full wave before
+// it are not run one tile per workgroup; their K-tiles, taken tile by tile, are cut into
+// 256 equal contiguous ranges, one per workgroup (after "Stream-K" work decomposition;
+// the pages' kernels all run one tile per thread block).  Pieces of a tile that fall in
+// different ranges go to the workspace and a fix-up kernel adds them in range order,
+// so the result is deterministic (its summation order differs from the one-tile path).
 #pragma once
 
 #include <type_traits>
@@ -145,8 +154,9 @@ struct Operand {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       if (KROWS)
-        reg[SET][i] = (!GUARD || row[i] < lim) ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], kl - 4 * col[i])
-                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        reg[SET][i] = (!GUARD || row[i] < lim)
+                          ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], kl - 4 * col[i])
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
       else if (row[i] >= kl)
         reg[SET][i] = make_float4(0.f, 0.f, 0.f, 0.f);
       else
@@ -196,12 +206,36 @@ struct TileMap {
   int Mf, Nf;              // extent they cover
   int right_m, right_n;    // 32 x 32 edge tiles in columns [Nf, N) of rows [0, Mf)
   int bottom_m, bottom_n;  // 32 x 32 edge tiles in rows [Mf, M)
+  // stream-K (sk_wgs > 0): MFMA tiles [0, dp_tiles) run one per workgroup; the K-tiles of
+  // tiles [dp_tiles, tiles_m * tiles_n) are split evenly over sk_wgs workgroups (see
+  // StreamK); partial tiles go to ws
+  int dp_tiles, sk_wgs;
+  float* ws;
 };
 
-// One BM x BN tile of C at (m0, n0).  GUARD: the tile reaches past M or N; loads read
-// zeros there and stores skip it.
+// The stream-K split: the K-tiles ("iterations") of the stream-K tiles, tile-major, are
+// cut into sk_wgs equal contiguous ranges; range g is [start(g), start(g + 1)) with
+// start(g) = floor(g * W / G) for W iterations over G workgroups.  A workgroup writes a
+// tile that its range covers whole straight to C.  The pieces of a tile split between
+// ranges go to workspace slots: the first piece of range g to slot 2g, the last to slot
+// 2g + 1 (both BM x BN floats), and a fix-up pass adds them in range order.
+struct StreamK {
+  long long work;  // W = stream-K tiles x iters
+  int iters;       // K-tiles per tile
+  int wgs;         // G
+  __device__ __forceinline__ long long start(int g) const { return (long long)g * work / wgs; }
+  // the range holding iteration j (the last range starting at or before j; ranges are
+  // empty only when there are fewer iterations than workgroups)
+  __device__ __forceinline__ int owner(long long j) const { return (int)(((j + 1) * wgs - 1) / work); }
+};
+
+// K-tiles [kb, ke) of the BM x BN tile of C at (m0, n0).  part == nullptr: the range is
+// the whole K range and the result goes to C (alpha, beta); otherwise the raw sums go to
+// part, a BM x BN row-major block (a stream-K partial tile).  GUARD: the tile reaches
+// past M or N; loads read zeros there and stores skip it.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool VEC, bool GUARD>
-__device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, float* smem) {
+__device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
+                                          float* part = nullptr) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
@@ -230,7 +264,6 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, floa
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nfull = p.K / BK;  // K-tiles with no element past K
-  const int ntiles = (p.K + BK - 1) / BK;
   // global -> registers (set SET) for K-tile kt; the guarded form (the last, partial
   // K-tile only) loads zeros past K and is kept out of the steady-state loop
   auto load = [&](auto set, int kt) {
@@ -276,12 +309,12 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, floa
   // and stores on every path, so that the compiler's wait before the LDS store covers
   // only the older register set (a wait on the newest loads would undo the prefetch);
   // the last steps run the general form.
-  load(Set0{}, 0);
+  load(Set0{}, kb);
   opa.template store<0>(a_stage(0));
   opb.template store<0>(b_stage(0));
-  if (ntiles > 1) load(Set1{}, 1);
+  if (kb + 1 < ke) load(Set1{}, kb + 1);
   __syncthreads();
-  auto steady = [&](auto set, int kt) {  // set = kt % 2, also the LDS stage of tile kt
+  auto steady = [&](auto set, int kt) {  // set = (kt - kb) % 2, also the LDS stage of tile kt
     constexpr int P = decltype(set)::value;
     opa.template load_full<VEC, GUARD, P>((kt + 2) * BK);
     opb.template load_full<VEC, GUARD, P>((kt + 2) * BK);
@@ -294,27 +327,32 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, floa
   };
   auto step = [&](auto set, int kt) {
     constexpr int P = decltype(set)::value;
-    if (kt + 2 < ntiles) load(set, kt + 2);
+    if (kt + 2 < ke) load(set, kt + 2);
     multiply(P, [&] {
-      if (kt + 1 < ntiles) {
+      if (kt + 1 < ke) {
         opa.template store<P ^ 1>(a_stage(P ^ 1));
         opb.template store<P ^ 1>(b_stage(P ^ 1));
       }
     });
     __syncthreads();
   };
-  int kt = 0;
-  for (; kt + 3 < nfull; kt += 2) {  // tiles kt+2 and kt+3 are full
+  int kt = kb;
+  const int steady_end = min(ke, nfull);
+  for (; kt + 3 < steady_end; kt += 2) {  // tiles kt+2 and kt+3 are full and in range
     steady(Set0{}, kt);
     steady(Set1{}, kt + 1);
   }
-  for (; kt < ntiles; kt += 2) {
+  for (; kt < ke; kt += 2) {
     step(Set0{}, kt);
-    if (kt + 1 < ntiles) step(Set1{}, kt + 1);
+    if (kt + 1 < ke) step(Set1{}, kt + 1);
   }
 
   const bool beta0 = p.beta == 0.0f;
   auto store_c = [&](int row, int col, float x) {
+    if (part != nullptr) {  // stream-K partial tile (full tiles only)
+      part[(row - m0) * BN + (col - n0)] = x;
+      return;
+    }
     if (GUARD && (row >= p.M || col >= p.N)) return;
     float* c = p.C + (long long)row * p.ldc + col;
     *c = beta0 ? p.alpha * x : fmaf(p.alpha, x, p.beta * *c);
@@ -410,7 +448,7 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // MFMA_EDGES: the tiles reaching past M or N are guarded MFMA tiles of the same grid
 // (tiles_m x tiles_n covers the whole matrix) instead of scalar edge tiles.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          bool MFMA_EDGES, bool VEC>
+          bool MFMA_EDGES, bool STREAM_K, bool VEC>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
@@ -421,17 +459,39 @@ void mfma_kernel(Problem p, TileMap map) {
   static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
   const int nmfma = map.tiles_m * map.tiles_n;
-  int e = (int)blockIdx.x - nmfma;
-  if (e < 0) {
+  const int ndp = STREAM_K ? map.dp_tiles : nmfma;
+  const int iters = (p.K + BK - 1) / BK;
+  int e = (int)blockIdx.x - ndp;
+  if (e < 0) {  // one whole tile
     int bm, bn;
     tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
     const int m0 = bm * BM, n0 = bn * BN;
     if (!MFMA_EDGES || (m0 + BM <= p.M && n0 + BN <= p.N))
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false>(p, m0, n0, smem);
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false>(p, m0, n0, 0, iters, smem);
     else
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, true>(p, m0, n0, smem);
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, true>(p, m0, n0, 0, iters, smem);
     return;
   }
+  if (STREAM_K && e < map.sk_wgs) {  // one stream-K range (full tiles only)
+    const StreamK sk{(long long)(nmfma - map.dp_tiles) * iters, iters, map.sk_wgs};
+    const long long j0 = sk.start(e), j1 = sk.start(e + 1);
+    for (long long j = j0; j < j1;) {
+      const int u = (int)(j / iters);  // stream-K tile
+      const long long tile_end = (long long)(u + 1) * iters;
+      const long long seg_end = j1 < tile_end ? j1 : tile_end;
+      const int kb = (int)(j - (long long)u * iters), ke = (int)(seg_end - (long long)u * iters);
+      float* part = nullptr;
+      if (kb > 0 || ke < iters)
+        part = map.ws + (2LL * e + (j == j0 ? 0 : 1)) * (long long)(BM * BN);
+      int bm, bn;
+      tile_coords<GROUP_M>(map.dp_tiles + u, map.tiles_m, map.tiles_n, bm, bn);
+      if (j != j0) __syncthreads();  // the previous piece's epilogue may still read LDS
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false>(p, bm * BM, bn * BN, kb, ke, smem, part);
+      j = seg_end;
+    }
+    return;
+  }
+  if (STREAM_K) e -= map.sk_wgs;
   if constexpr (!MFMA_EDGES) {
     int m0, n0;
     const int n_right = map.right_m * map.right_n;
@@ -447,11 +507,52 @@ void mfma_kernel(Problem p, TileMap map) {
   }
 }
 
+// Stream-K fix-up: one workgroup per stream-K tile that was split between ranges; adds
+// the pieces in range order and applies alpha and beta.  Tiles that one range covered
+// whole were written by the main kernel.
+template <int BM, int BN, int BK, int GROUP_M>
+__global__ __launch_bounds__(256) void sk_fixup_kernel(Problem p, TileMap map) {
+  const int nmfma = map.tiles_m * map.tiles_n;
+  const int iters = (p.K + BK - 1) / BK;
+  const StreamK sk{(long long)(nmfma - map.dp_tiles) * iters, iters, map.sk_wgs};
+  const int u = blockIdx.x;
+  const int g0 = sk.owner((long long)u * iters), g1 = sk.owner((long long)(u + 1) * iters - 1);
+  if (g0 == g1) return;
+  int bm, bn;
+  tile_coords<GROUP_M>(map.dp_tiles + u, map.tiles_m, map.tiles_n, bm, bn);
+  const int m0 = bm * BM, n0 = bn * BN;
+  const bool beta0 = p.beta == 0.0f;
+  constexpr int kQuads = BN / 4;  // float4 per row
+  for (int q = threadIdx.x; q < BM * kQuads; q += 256) {
+    const int r = q / kQuads, c = (q % kQuads) * 4;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int g = g0; g <= g1; ++g) {
+      if (sk.start(g) == sk.start(g + 1)) continue;  // empty range (fewer iterations than workgroups)
+      const long long slot = 2LL * g + (sk.start(g) / iters == u ? 0 : 1);
+      const float4 v = *reinterpret_cast<const float4*>(map.ws + slot * (BM * BN) + r * BN + c);
+      if (g == g0) {
+        sum = v;
+      } else {
+        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+      }
+    }
+    float* crow = p.C + (long long)(m0 + r) * p.ldc + n0 + c;
+    const float s4[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) crow[e] = beta0 ? p.alpha * s4[e] : fmaf(p.alpha, s4[e], p.beta * crow[e]);
+  }
+}
+
+// ws != nullptr (batch 1, configurations without MFMA_EDGES): stream-K over 256
+// workgroups for the last partial wave of tiles plus one full wave before it (the tiles
+// before those run one per workgroup); ws holds 2 * 256 * BM * BN floats.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
           bool MFMA_EDGES = false>
-hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
+hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws = nullptr) {
   static_assert(BM % kEdge == 0 && BN % kEdge == 0, "edge tiles of the right strip end at Mf");
   TileMap map;
+  map.dp_tiles = map.sk_wgs = 0;
+  map.ws = nullptr;
   if (MFMA_EDGES) {
     map.tiles_m = (p.M + BM - 1) / BM;
     map.tiles_n = (p.N + BN - 1) / BN;
@@ -472,15 +573,39 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
     map.bottom_m = (p.M - map.Mf + kEdge - 1) / kEdge;
     map.bottom_n = map.bottom_m > 0 ? (p.N + kEdge - 1) / kEdge : 0;
   }
+  const long long nmfma = (long long)map.tiles_m * map.tiles_n;
   const long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
-  const long long blocks = (long long)map.tiles_m * map.tiles_n + edge_tiles;
+  const dim3 block(WM * WN * KS * 64);
+  const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
+  if constexpr (!MFMA_EDGES && BM == 256 && BN == 256) {  // the workspace holds 256 x 256 slots
+    if (ws != nullptr && batch == 1 && nmfma % kStreamKWgs != 0) {
+      const long long sk_tiles = nmfma % kStreamKWgs + (nmfma > kStreamKWgs ? kStreamKWgs : 0);
+      map.dp_tiles = (int)(nmfma - sk_tiles);
+      map.sk_wgs = kStreamKWgs;
+      map.ws = ws;
+      const long long blocks = map.dp_tiles + map.sk_wgs + edge_tiles;
+      if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
+      if (vec)
+        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false, true, true>),
+                           dim3((unsigned)blocks), block, 0, stream, p, map);
+      else
+        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false, true, false>),
+                           dim3((unsigned)blocks), block, 0, stream, p, map);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL((sk_fixup_kernel<BM, BN, BK, GROUP_M>), dim3((unsigned)sk_tiles), dim3(256), 0, stream, p,
+                         map);
+      return hipGetLastError();
+    }
+  }
+  const long long blocks = nmfma + edge_tiles;
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks, batch), block(WM * WN * KS * 64);
-  if (vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb))
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, true>),
+  const dim3 grid((unsigned)blocks, batch);
+  if (vec)
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false, true>),
                        grid, block, 0, stream, p, map);
   else
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false>),
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false, false>),
                        grid, block, 0, stream, p, map);
   return hipGetLastError();
 }
@@ -493,11 +618,12 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
 //        256 threads; four workgroups per CU.  Partial tiles are guarded MFMA tiles
 //        (the other configurations send them to the scalar edge-tile path).
+// ws: stream-K workspace (kStreamKBytes) for the 256 configuration, or nullptr.
 template <bool TA, bool TB>
-hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles) {
+hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr) {
   switch (tiles) {
     case 256:
-      return launch_cfg<256, 256, 16, 4, 4, 1, TA, TB, 8, 1>(p, batch, stream);
+      return launch_cfg<256, 256, 16, 4, 4, 1, TA, TB, 8, 1>(p, batch, stream, ws);
     case 128:
       return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
     case 64:

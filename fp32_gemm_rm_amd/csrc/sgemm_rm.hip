@@ -14,12 +14,13 @@ using sgemm_impl::Problem;
 // such argument.  Every entry point lists its arguments in this relative order:
 // transA transB M N K alpha A lda strideA B ldb strideB beta C ldc strideC batch stream variant.
 struct Positions {
-  int ta, tb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, variant;
+  int ta, tb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ws, ws_bytes, variant;
 };
-constexpr Positions kPosRm = {0, 0, 1, 2, 3, 5, 6, 0, 7, 8, 0, 10, 11, 0, 0, 13};
-constexpr Positions kPosRmBatched = {0, 0, 1, 2, 3, 5, 6, 7, 8, 9, 10, 12, 13, 14, 15, 17};
-constexpr Positions kPosOp = {1, 2, 3, 4, 5, 7, 8, 0, 9, 10, 0, 12, 13, 0, 0, 0};
-constexpr Positions kPosOpBatched = {1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12, 14, 15, 16, 17, 19};
+constexpr Positions kPosRm = {0, 0, 1, 2, 3, 5, 6, 0, 7, 8, 0, 10, 11, 0, 0, 0, 0, 13};
+constexpr Positions kPosRmBatched = {0, 0, 1, 2, 3, 5, 6, 7, 8, 9, 10, 12, 13, 14, 15, 0, 0, 17};
+constexpr Positions kPosOp = {1, 2, 3, 4, 5, 7, 8, 0, 9, 10, 0, 12, 13, 0, 0, 0, 0, 0};
+constexpr Positions kPosOpBatched = {1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12, 14, 15, 16, 17, 0, 0, 19};
+constexpr Positions kPosOpBatchedWs = {1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12, 14, 15, 16, 17, 18, 19, 21};
 
 // One call in the caller's terms.  cm: column-major storage (element (i, j) of X at
 // X[j*ldX + i]); ta / tb: A is stored K x M / B is stored N x K (op = transpose).
@@ -37,7 +38,10 @@ struct Call {
   float* C;
   int ldc;
   long long sC;
-  int batch, variant;
+  int batch;
+  void* ws;  // stream-K workspace (nullptr: none)
+  long long ws_bytes;
+  int variant;
 };
 
 int at_least(int n) { return n > 1 ? n : 1; }
@@ -67,12 +71,16 @@ int check(const Call& c, const Positions& pos) {
     if (c.sC < 0 || (c.batch > 1 && c.M > 0 && c.N > 0 && c.sC < extent)) return -pos.sC;
   }
   if (pos.batch && c.batch < 0) return -pos.batch;
+  if (pos.ws && c.ws == nullptr && c.ws_bytes > 0) return -pos.ws;
+  if (pos.ws_bytes && c.ws_bytes < 0) return -pos.ws_bytes;
   if (pos.variant && (c.variant < SGEMM_RM_VARIANT_AUTO || c.variant > SGEMM_RM_VARIANT_MFMA_T32)) return -pos.variant;
   return 0;
 }
 
 // Enqueue `batch` problems spaced by p.sA, p.sB, p.sC (p already validated, M, N > 0).
-int launch(Problem p, int batch, hipStream_t stream, int variant) {
+// ws: a stream-K workspace of at least kStreamKBytes, or nullptr.
+int launch(Problem p, int batch, hipStream_t stream, int variant, float* ws) {
+  if (batch != 1) ws = nullptr;  // stream-K covers single products only
   while (batch > 0) {
     const int chunk = batch < sgemm_impl::kMaxBatch ? batch : sgemm_impl::kMaxBatch;
     hipError_t err;
@@ -90,8 +98,8 @@ int launch(Problem p, int batch, hipStream_t stream, int variant) {
         case SGEMM_RM_VARIANT_REGBLOCK:
           err = sgemm_impl::launch_regblock(p, chunk, stream);
           break;
-        case SGEMM_RM_VARIANT_MFMA_T256:
-          err = sgemm_impl::launch_mfma(p, chunk, stream, 256);
+        case SGEMM_RM_VARIANT_MFMA_T256:  // with a workspace: stream-K wherever the tiles leave a partial wave
+          err = sgemm_impl::launch_mfma(p, chunk, stream, 256, ws);
           break;
         case SGEMM_RM_VARIANT_MFMA_T128:
           err = sgemm_impl::launch_mfma(p, chunk, stream, 128);
@@ -104,9 +112,11 @@ int launch(Problem p, int batch, hipStream_t stream, int variant) {
           break;
         case SGEMM_RM_VARIANT_MFMA:
         case SGEMM_RM_VARIANT_AUTO:
-        default:
-          err = sgemm_impl::launch_mfma(p, chunk, stream, sgemm_impl::plan_tiles(p.M, p.N, p.K, chunk));
+        default: {
+          const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(p.M, p.N, p.K, chunk, ws != nullptr);
+          err = sgemm_impl::launch_mfma(p, chunk, stream, plan.side, plan.stream_k ? ws : nullptr);
           break;
+        }
       }
     }
     if (err != hipSuccess) return (int)err;
@@ -132,7 +142,8 @@ int run(const Call& c, const Positions& pos, hipStream_t stream) {
   } else {
     p = Problem{c.N, c.M, c.K, c.alpha, c.beta, c.B, c.ldb, c.A, c.lda, c.C, c.ldc, c.sB, c.sA, c.sC, c.tb, c.ta};
   }
-  return launch(p, c.batch, stream, c.variant);
+  float* ws = c.ws_bytes >= sgemm_impl::kStreamKBytes ? static_cast<float*>(c.ws) : nullptr;
+  return launch(p, c.batch, stream, c.variant, ws);
 }
 
 }  // namespace
@@ -141,34 +152,37 @@ extern "C" {
 
 int sgemm_rm(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
              float* C, int ldc, hipStream_t stream) {
-  return run({false, 0, 0, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, SGEMM_RM_VARIANT_AUTO}, kPosRm,
-             stream);
+  return run({false, 0, 0, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, nullptr, 0,
+              SGEMM_RM_VARIANT_AUTO},
+             kPosRm, stream);
 }
 
 int sgemm_rm_ex(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
                 float* C, int ldc, hipStream_t stream, int variant) {
-  return run({false, 0, 0, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, variant}, kPosRm, stream);
+  return run({false, 0, 0, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, nullptr, 0, variant}, kPosRm,
+             stream);
 }
 
 int sgemm_rm_strided_batched(int M, int N, int K, float alpha, const float* A, int lda, long long strideA,
                              const float* B, int ldb, long long strideB, float beta, float* C, int ldc,
                              long long strideC, int batch, hipStream_t stream) {
   return run({false, 0, 0, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
-              SGEMM_RM_VARIANT_AUTO},
+              nullptr, 0, SGEMM_RM_VARIANT_AUTO},
              kPosRmBatched, stream);
 }
 
 int sgemm_rm_strided_batched_ex(int M, int N, int K, float alpha, const float* A, int lda, long long strideA,
                                 const float* B, int ldb, long long strideB, float beta, float* C, int ldc,
                                 long long strideC, int batch, hipStream_t stream, int variant) {
-  return run({false, 0, 0, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch, variant},
+  return run({false, 0, 0, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch, nullptr,
+              0, variant},
              kPosRmBatched, stream);
 }
 
 int sgemm_rm_op(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda, const float* B,
                 int ldb, float beta, float* C, int ldc, hipStream_t stream) {
-  return run({false, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
-              SGEMM_RM_VARIANT_AUTO},
+  return run({false, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, nullptr,
+              0, SGEMM_RM_VARIANT_AUTO},
              kPosOp, stream);
 }
 
@@ -177,14 +191,14 @@ int sgemm_rm_op_strided_batched_ex(int transA, int transB, int M, int N, int K, 
                                    float beta, float* C, int ldc, long long strideC, int batch, hipStream_t stream,
                                    int variant) {
   return run({false, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
-              variant},
+              nullptr, 0, variant},
              kPosOpBatched, stream);
 }
 
 int sgemm_cm(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda, const float* B,
              int ldb, float beta, float* C, int ldc, hipStream_t stream) {
-  return run({true, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
-              SGEMM_RM_VARIANT_AUTO},
+  return run({true, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, nullptr,
+              0, SGEMM_RM_VARIANT_AUTO},
              kPosOp, stream);
 }
 
@@ -192,8 +206,35 @@ int sgemm_cm_strided_batched_ex(int transA, int transB, int M, int N, int K, flo
                                 long long strideA, const float* B, int ldb, long long strideB, float beta, float* C,
                                 int ldc, long long strideC, int batch, hipStream_t stream, int variant) {
   return run({true, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
-              variant},
+              nullptr, 0, variant},
              kPosOpBatched, stream);
+}
+
+int sgemm_rm_op_strided_batched_ws(int transA, int transB, int M, int N, int K, float alpha, const float* A,
+                                   int lda, long long strideA, const float* B, int ldb, long long strideB,
+                                   float beta, float* C, int ldc, long long strideC, int batch, void* workspace,
+                                   long long workspace_bytes, hipStream_t stream, int variant) {
+  return run({false, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+              workspace, workspace_bytes, variant},
+             kPosOpBatchedWs, stream);
+}
+
+int sgemm_cm_strided_batched_ws(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda,
+                                long long strideA, const float* B, int ldb, long long strideB, float beta, float* C,
+                                int ldc, long long strideC, int batch, void* workspace, long long workspace_bytes,
+                                hipStream_t stream, int variant) {
+  return run({true, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+              workspace, workspace_bytes, variant},
+             kPosOpBatchedWs, stream);
+}
+
+long long sgemm_rm_workspace_size(int M, int N, int K, int batch) {
+  if (M < 0) return -1;
+  if (N < 0) return -2;
+  if (K < 0) return -3;
+  if (batch < 0) return -4;
+  if (M == 0 || N == 0 || K == 0 || batch == 0) return 0;
+  return sgemm_impl::plan_tiles(M, N, K, batch, true).stream_k ? sgemm_impl::kStreamKBytes : 0;
 }
 
 int sgemm_rm_plan_tiles(int M, int N, int K, int batch) {
@@ -202,7 +243,7 @@ int sgemm_rm_plan_tiles(int M, int N, int K, int batch) {
   if (K < 0) return -3;
   if (batch < 0) return -4;
   if (M == 0 || N == 0 || K == 0 || batch == 0) return 0;
-  return sgemm_impl::plan_tiles(M, N, K, batch < sgemm_impl::kMaxBatch ? batch : sgemm_impl::kMaxBatch);
+  return sgemm_impl::plan_tiles(M, N, K, batch < sgemm_impl::kMaxBatch ? batch : sgemm_impl::kMaxBatch).side;
 }
 
 const char* sgemm_rm_strerror(int code) {
@@ -211,13 +252,14 @@ const char* sgemm_rm_strerror(int code) {
       "invalid argument 5",  "invalid argument 6",  "invalid argument 7",  "invalid argument 8",
       "invalid argument 9",  "invalid argument 10", "invalid argument 11", "invalid argument 12",
       "invalid argument 13", "invalid argument 14", "invalid argument 15", "invalid argument 16",
-      "invalid argument 17", "invalid argument 18", "invalid argument 19"};
+      "invalid argument 17", "invalid argument 18", "invalid argument 19", "invalid argument 20",
+      "invalid argument 21"};
   if (code == 0) return "success";
-  if (code < 0 && code >= -19) return kInvalid[-code - 1];
+  if (code < 0 && code >= -21) return kInvalid[-code - 1];
   if (code > 0) return hipGetErrorString((hipError_t)code);
   return "unknown error code";
 }
 
-int sgemm_rm_version(void) { return 300; }
+int sgemm_rm_version(void) { return 400; }
 
 }  // extern "C"

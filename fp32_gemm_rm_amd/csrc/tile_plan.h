@@ -21,20 +21,47 @@ struct TileCost {
 };
 constexpr TileCost kTileCosts[] = {{256, 237.0, 237.0}, {128, 64.7, 64.7}, {64, 16.2, 17.2}, {32, 5.4, 4.95}};
 
-// M, N, K, batch > 0.
+// Modelled microseconds; M, N, K, batch > 0.
 inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
   const long long tiles = ((long long)(M - 1) / c.side + 1) * ((long long)(N - 1) / c.side + 1) * batch;
   const long long layers = (tiles + 255) / 256;
-  return (double)layers * (layers > 1 ? c.u2 : c.u1) * (double)K;
+  return (double)layers * (layers > 1 ? c.u2 : c.u1) * (double)K / 1024.0;
 }
 
-// Tile side of the configuration with the least modelled time (ties: the larger tile).
-inline int plan_tiles(int M, int N, int K, int batch) {
-  int best = kTileCosts[0].side;
+// Stream-K (256 configuration, batch 1, with a workspace): the K-tiles of the last
+// partial wave of T full tiles and of one full wave before it are shared evenly by 256
+// workgroups, so the MFMA time is T/256 layers instead of ceil(T/256).  Overheads: the
+// fix-up pass (up to 2 x 256 partial tiles of 256 KB written and read back at about
+// 5 TB/s, plus a launch) and each workgroup's two partial pieces (pipeline fill and
+// partial-tile stores), about 15 us.  With fewer than 256 tiles every tile is split and
+// the pieces' overheads dominate (3072^3: 511 us against 473 us one tile per
+// workgroup), so stream-K is a candidate only past one full wave.  Measured: 5120^3
+// 2157 -> 1977 us, 6144^3 3479 -> 3324 us.  Returns a negative value where it does not
+// apply.
+inline double modelled_stream_k_time(int M, int N, int K, int batch) {
+  const long long tiles = (long long)(M / 256) * (N / 256);
+  if (batch != 1 || tiles <= kStreamKWgs || tiles % kStreamKWgs == 0) return -1.0;
+  const double overhead_us = 4.0 + 2.0 * (double)kStreamKBytes / 5.0e6 + 15.0;
+  return (double)tiles / kStreamKWgs * kTileCosts[0].u2 * (double)K / 1024.0 + overhead_us;
+}
+
+struct TilePlan {
+  int side;        // tile configuration
+  bool stream_k;   // stream-K over the last waves (side 256 only)
+};
+
+// The configuration with the least modelled time (ties: the larger tile); stream-K is a
+// candidate when a workspace is available.
+inline TilePlan plan_tiles(int M, int N, int K, int batch, bool workspace = false) {
+  TilePlan best{kTileCosts[0].side, false};
   double t = modelled_time(kTileCosts[0], M, N, K, batch);
   for (const TileCost& c : kTileCosts) {
     const double tc = modelled_time(c, M, N, K, batch);
-    if (tc < t) best = c.side, t = tc;
+    if (tc < t) best = TilePlan{c.side, false}, t = tc;
+  }
+  if (workspace) {
+    const double tsk = modelled_stream_k_time(M, N, K, batch);
+    if (tsk >= 0.0 && tsk < t) best = TilePlan{256, true}, t = tsk;
   }
   return best;
 }

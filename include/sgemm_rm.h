@@ -186,6 +186,44 @@ int sgemm_cm_strided_batched_ex(int transA, int transB, int M, int N, int K, flo
                                 int ldc, long long strideC, int batch, hipStream_t stream, int variant);
 
 /*
+ * The general row-major call with a caller-owned workspace: as
+ * sgemm_rm_op_strided_batched_ex, and where a single product's 256 x 256 tiles leave the
+ * last wave of 256 workgroups partly empty, the last waves run as "stream-K" (their
+ * K-tiles shared evenly by 256 workgroups; after the Stream-K work decomposition, not a
+ * technique of the pages) when the library's cost model expects it to be faster.
+ * Partial tiles go to `workspace` (device memory, at least sgemm_rm_workspace_size
+ * bytes; the library only writes and reads it during the call's kernels) and a second
+ * kernel adds them in a fixed order, so results are deterministic; their summation
+ * order, and so their rounding, differs from the call without a workspace.  With
+ * workspace NULL or workspace_bytes below the size needed, the call is exactly
+ * sgemm_rm_op_strided_batched_ex.  SGEMM_RM_VARIANT_MFMA_T256 with a large enough
+ * workspace uses stream-K whenever the tiles leave a partial wave (for tests and
+ * sweeps); the other forced variants ignore the workspace.  Calls that share a
+ * workspace must not overlap (same stream, or synchronised).  Return codes as
+ * sgemm_rm_op_strided_batched_ex, plus -18 workspace NULL with workspace_bytes > 0,
+ * -19 workspace_bytes < 0; the stream is argument 20 and -21 is an unknown variant.
+ */
+int sgemm_rm_op_strided_batched_ws(int transA, int transB, int M, int N, int K, float alpha, const float* A,
+                                   int lda, long long strideA, const float* B, int ldb, long long strideB,
+                                   float beta, float* C, int ldc, long long strideC, int batch, void* workspace,
+                                   long long workspace_bytes, hipStream_t stream, int variant);
+
+/* The column-major form of sgemm_rm_op_strided_batched_ws (rules of sgemm_cm). */
+int sgemm_cm_strided_batched_ws(int transA, int transB, int M, int N, int K, float alpha, const float* A, int lda,
+                                long long strideA, const float* B, int ldb, long long strideB, float beta, float* C,
+                                int ldc, long long strideC, int batch, void* workspace, long long workspace_bytes,
+                                hipStream_t stream, int variant);
+
+/*
+ * Workspace bytes with which the _ws calls run an M x N x K problem (repeated `batch`
+ * times) as stream-K, or 0 where the cost model keeps the one-tile-per-workgroup path.
+ * Currently 0 or 128 MiB (two 256 x 256 float partial tiles for each of 256
+ * workgroups).  -1 M < 0, -2 N < 0, -3 K < 0, -4 batch < 0.  Host only: no HIP call.
+ * The transpose flags and storage order do not change the answer.
+ */
+long long sgemm_rm_workspace_size(int M, int N, int K, int batch);
+
+/*
  * Tile side (256, 128, 64 or 32) of the MFMA configuration that SGEMM_RM_VARIANT_AUTO
  * and SGEMM_RM_VARIANT_MFMA use for an M x N x K problem repeated `batch` times (any
  * orientation or storage order; batches above 65535 are planned per launch of 65535).

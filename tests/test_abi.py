@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "sgemm_rm.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:long\s+long|\w+)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -26,10 +26,11 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["sgemm_cm", "sgemm_cm_strided_batched_ex", "sgemm_rm", "sgemm_rm_ex",
-                                     "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex", "sgemm_rm_plan_tiles",
-                                     "sgemm_rm_strerror",
-                                     "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex", "sgemm_rm_version"]
+    assert _declared_functions() == ["sgemm_cm", "sgemm_cm_strided_batched_ex", "sgemm_cm_strided_batched_ws",
+                                     "sgemm_rm", "sgemm_rm_ex", "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex",
+                                     "sgemm_rm_op_strided_batched_ws", "sgemm_rm_plan_tiles", "sgemm_rm_strerror",
+                                     "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex", "sgemm_rm_version",
+                                     "sgemm_rm_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(raw, name), name
     assert set(EXPORTED_SYMBOLS) == set(_declared_functions())
-    assert lib.sgemm_rm_version() == 300
+    assert lib.sgemm_rm_version() == 400
 
 
 F = 0x1000  # a non-null dummy pointer: never dereferenced, the calls return before any launch
@@ -89,7 +90,7 @@ def test_strerror(lib):
     from fp32_gemm_rm_amd import sgemm_rm_strerror
 
     assert sgemm_rm_strerror(0) == "success"
-    for code in range(-19, 0):
+    for code in range(-21, 0):
         assert sgemm_rm_strerror(code) == f"invalid argument {-code}"
     assert sgemm_rm_strerror(-99) == "unknown error code"
 
@@ -234,3 +235,36 @@ def test_plan_tiles(lib):
     assert sgemm_rm_plan_tiles(64, 64, 64, 1024) == 64
     for M, N, K, b in [(1, 1, 1, 1), (5000, 3, 7, 1), (3, 5000, 70000, 1), (65535, 65535, 1, 1000000)]:
         assert sgemm_rm_plan_tiles(M, N, K, b) in (256, 128, 64, 32)
+
+
+@pytest.mark.parametrize("cm", [False, True], ids=["rm", "cm"])
+def test_workspace_call_invalid_arguments(lib, cm):
+    """The _ws calls check the workspace pair (positions 18, 19) after batch and before the
+    variant (21); everything else as the _ex form, whose checks they share."""
+    fn = lib.sgemm_cm_strided_batched_ws if cm else lib.sgemm_rm_op_strided_batched_ws
+    lda, ldb, ldc = _min_lds(cm, 0, 0)
+    ok = [0, 0, M6, N5, K3, 0.0, F, lda, G, F, ldb, G, 1.0, F, ldc, G, 2, F, 1 << 27, None, 0]
+    assert fn(*ok) == 0  # alpha = 0, beta = 1: nothing launched
+    for pos, bad in [(1, 2), (3, -1), (8, lda - 1), (17, -1), (18, None), (19, -1), (21, 9), (21, -1)]:
+        args = list(ok)
+        args[pos - 1] = bad
+        assert fn(*args) == -pos, (pos, bad)
+    args = list(ok)
+    args[17], args[18] = None, 0  # no workspace at all is valid
+    assert fn(*args) == 0
+
+
+def test_workspace_size(lib):
+    from fp32_gemm_rm_amd import sgemm_rm_workspace_size
+
+    assert lib.sgemm_rm_workspace_size(-1, 4, 4, 1) == -1
+    assert lib.sgemm_rm_workspace_size(4, -1, 4, 1) == -2
+    assert lib.sgemm_rm_workspace_size(4, 4, -1, 1) == -3
+    assert lib.sgemm_rm_workspace_size(4, 4, 4, -1) == -4
+    assert sgemm_rm_workspace_size(0, 4, 4) == 0
+    # tiles filling whole waves of 256 workgroups, batches, shapes under one wave: no stream-K
+    for M, N, K, b in [(4096, 4096, 4096, 1), (8192, 8192, 8192, 1), (256, 256, 256, 1), (5120, 5120, 5120, 2),
+                       (1024, 1024, 1024, 1), (3072, 3072, 3072, 1)]:
+        assert sgemm_rm_workspace_size(M, N, K, b) == 0, (M, N, K, b)
+    # 5120^3: 400 tiles of 256^2, 1.56 waves: stream-K with two 256 KB slots per workgroup
+    assert sgemm_rm_workspace_size(5120, 5120, 5120) == 2 * 256 * 256 * 256 * 4
