@@ -54,7 +54,23 @@ def build_probes() -> list:
         if proc.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{proc.stdout}\n{proc.stderr}")
         built.append(exe)
+    built.append(build_c_client(out_dir))
     return built
+
+
+def build_c_client(out_dir: str) -> str:
+    """Compile the plain C client of the library (tests/c_client/sgemm_client.c) with gcc,
+    linked against the in-tree libsgemm_rm.so (found through a relative rpath)."""
+    src = os.path.join(ROOT, "tests", "c_client", "sgemm_client.c")
+    exe = os.path.join(out_dir, "sgemm_client")
+    rel = os.path.relpath(HERE, out_dir)
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           f"-I{INCLUDE}", src, "-o", exe, f"-L{HERE}", "-l:libsgemm_rm.so", "-L/opt/rocm/lib", "-lamdhip64",
+           f"-Wl,-rpath,$ORIGIN/{rel}", "-Wl,-rpath,/opt/rocm/lib"]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"gcc failed on {src}:\n{proc.stdout}\n{proc.stderr}")
+    return exe
 
 
 def build(verbose: bool = False) -> str:
