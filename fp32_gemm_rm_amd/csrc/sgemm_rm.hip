@@ -3,6 +3,8 @@
 // The operations and their return codes are specified in include/sgemm_rm.h.
 #include "sgemm_rm.h"
 
+#include <cstdint>
+
 #include "internal.h"
 #include "tile_plan.h"
 
@@ -12,7 +14,8 @@ using sgemm_impl::Problem;
 
 // 1-based positions of the arguments of one entry point; 0 = the entry point has no
 // such argument.  Every entry point lists its arguments in this relative order:
-// transA transB M N K alpha A lda strideA B ldb strideB beta C ldc strideC batch stream variant.
+// transA transB M N K alpha A lda strideA B ldb strideB beta C ldc strideC batch
+// workspace workspace_bytes stream variant.
 struct Positions {
   int ta, tb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ws, ws_bytes, variant;
 };
@@ -142,7 +145,9 @@ int run(const Call& c, const Positions& pos, hipStream_t stream) {
   } else {
     p = Problem{c.N, c.M, c.K, c.alpha, c.beta, c.B, c.ldb, c.A, c.lda, c.C, c.ldc, c.sB, c.sA, c.sC, c.tb, c.ta};
   }
-  float* ws = c.ws_bytes >= sgemm_impl::kStreamKBytes ? static_cast<float*>(c.ws) : nullptr;
+  // a workspace too small or not 16-byte aligned (the fix-up reads it as float4) is not used
+  const bool ws_ok = c.ws_bytes >= sgemm_impl::kStreamKBytes && reinterpret_cast<uintptr_t>(c.ws) % 16 == 0;
+  float* ws = ws_ok ? static_cast<float*>(c.ws) : nullptr;
   return launch(p, c.batch, stream, c.variant, ws);
 }
 

@@ -195,8 +195,8 @@ int sgemm_cm_strided_batched_ex(int transA, int transB, int M, int N, int K, flo
  * bytes; the library only writes and reads it during the call's kernels) and a second
  * kernel adds them in a fixed order, so results are deterministic; their summation
  * order, and so their rounding, differs from the call without a workspace.  With
- * workspace NULL or workspace_bytes below the size needed, the call is exactly
- * sgemm_rm_op_strided_batched_ex.  SGEMM_RM_VARIANT_MFMA_T256 with a large enough
+ * workspace NULL, not 16-byte aligned (hipMalloc gives 256) or workspace_bytes below
+ * the size needed, the call is exactly sgemm_rm_op_strided_batched_ex.  SGEMM_RM_VARIANT_MFMA_T256 with a large enough
  * workspace uses stream-K whenever the tiles leave a partial wave (for tests and
  * sweeps); the other forced variants ignore the workspace.  Calls that share a
  * workspace must not overlap (same stream, or synchronised).  Return codes as

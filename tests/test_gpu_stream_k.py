@@ -115,25 +115,26 @@ def test_stream_k_deterministic(workspace):
     assert np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
 
 
-def test_small_workspace_is_ignored(oracle, workspace):
-    """A workspace below the size needed leaves the call on the one-tile path: the same
-    bits as without a workspace."""
+def test_unusable_workspace_is_ignored(workspace):
+    """A workspace below the size needed, or not 16-byte aligned, leaves the call on the
+    one-tile path: the same bits as without a workspace."""
     import torch
 
     from fp32_gemm_rm_amd import sgemm_rm_op_strided_batched_ws
 
     M, N, K = 1280, 1536, 300
     A, B, C = make_inputs(M, N, K, K, N, N, "normal", seed=6)
+    big = torch.empty(WS_BYTES + 64, dtype=torch.uint8, device="cuda")
     outs = []
-    for nbytes in (0, WS_BYTES - 4):
+    for ptr, nbytes in ((None, 0), (workspace.data_ptr(), WS_BYTES - 4), (big.data_ptr() + 4, WS_BYTES)):
         dA, dB, dC = device(A), device(B), device(C)
         s = torch.cuda.current_stream()
         sgemm_rm_op_strided_batched_ws(0, 0, M, N, K, 1.0, dA.data_ptr(), K, 0, dB.data_ptr(), N, 0, 0.0,
-                                       dC.data_ptr(), N, 0, 1, workspace.data_ptr() if nbytes else None, nbytes,
-                                       s.cuda_stream, T256)
+                                       dC.data_ptr(), N, 0, 1, ptr, nbytes, s.cuda_stream, T256)
         s.synchronize()
         outs.append(dC.cpu().numpy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
 
 
 def test_default_path_5120_sampled(oracle, workspace):
