@@ -42,7 +42,9 @@ __device__ __forceinline__ float4 load4_guarded(const float* base, long long ld,
 // TA / TB: A stored K x M (element (i, k) at A[k*lda + i]) / B stored N x K.  A
 // transposed operand is read with the same coalesced float4 loads along its
 // contiguous dimension, and the four values are written down a column of the
-// As[m][k] / Bs[k][n] tile instead of along a row.
+// As[m][k] / Bs[k][n] tile instead of along a row.  Into the unpadded Bs those column
+// stores conflict (the 8 lanes of a row share a bank); this stage keeps the pages'
+// tile layout, and the orientations are tuned in the MFMA kernel instead.
 template <bool VEC, bool TA, bool TB>
 __global__ __launch_bounds__(256) void lds_tiled_kernel(Problem p, int col_blocks) {
   p = batch_entry(p);
