@@ -229,6 +229,69 @@ struct StreamK {
   __device__ __forceinline__ int owner(long long j) const { return (int)(((j + 1) * wgs - 1) / work); }
 };
 
+// C := alpha * x[u] + beta * C at the NV elements (row(u), col(u)) of this lane, given
+// by coord(u, row, col); C is not read when beta == 0, and with GUARD elements past M or
+// N are skipped.  Every C value of the batch is loaded before the first store: a load
+// after a store into the same array would wait for that store (the compiler cannot tell
+// that the addresses differ), which turns the epilogue into a chain of round trips.
+template <int NV, bool GUARD, typename Coord>
+__device__ __forceinline__ void finish_c(const Problem& p, const float (&x)[NV], Coord coord) {
+  auto inside = [&](int row, int col) { return !GUARD || (row < p.M && col < p.N); };
+  if (p.beta == 0.0f) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      int row, col;
+      coord(u, row, col);
+      if (inside(row, col)) p.C[(long long)row * p.ldc + col] = p.alpha * x[u];
+    }
+    return;
+  }
+  float c[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    int row, col;
+    coord(u, row, col);
+    c[u] = inside(row, col) ? p.C[(long long)row * p.ldc + col] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    int row, col;
+    coord(u, row, col);
+    if (inside(row, col)) p.C[(long long)row * p.ldc + col] = fmaf(p.alpha, x[u], p.beta * c[u]);
+  }
+}
+
+// The accumulators of one wavefront (FM x FN blocks of 32 x 32 at (m0 + wm0, n0 + wn0))
+// to C, one row of blocks at a time, or raw to a stream-K partial tile `part`.
+// Register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its block.
+template <int BM, int BN, int FM, int FN, bool GUARD>
+__device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM][FN], int m0, int n0, int wm0,
+                                          int wn0, int lr, int lh, float* part) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    float x[FN * 16];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[j * 16 + r] = acc[i][j][r];
+    auto coord = [&](int u, int& row, int& col) {
+      const int j = u / 16, r = u % 16;
+      row = m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+      col = n0 + wn0 + j * 32 + lr;
+    };
+    if (part != nullptr) {  // stream-K partial tile (full tiles only)
+#pragma unroll
+      for (int u = 0; u < FN * 16; ++u) {
+        int row, col;
+        coord(u, row, col);
+        part[(row - m0) * BN + (col - n0)] = x[u];
+      }
+      continue;
+    }
+    finish_c<FN * 16, GUARD>(p, x, coord);
+  }
+}
+
 // K-tiles [kb, ke) of the BM x BN tile of C at (m0, n0).  part == nullptr: the range is
 // the whole K range and the result goes to C (alpha, beta); otherwise the raw sums go to
 // part, a BM x BN row-major block (a stream-K partial tile).  GUARD: the tile reaches
@@ -347,17 +410,7 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
     if (kt + 1 < ke) step(Set1{}, kt + 1);
   }
 
-  const bool beta0 = p.beta == 0.0f;
-  auto store_c = [&](int row, int col, float x) {
-    if (part != nullptr) {  // stream-K partial tile (full tiles only)
-      part[(row - m0) * BN + (col - n0)] = x;
-      return;
-    }
-    if (GUARD && (row >= p.M || col >= p.N)) return;
-    float* c = p.C + (long long)row * p.ldc + col;
-    *c = beta0 ? p.alpha * x : fmaf(p.alpha, x, p.beta * *c);
-  };
-
+  // register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its 32 x 32 block
   if constexpr (KS > 1) {
     // The KS wavefronts of one output block pass their partial sums through LDS (free
     // after the last barrier); then each of them finishes 1/KS of the block's
@@ -375,27 +428,178 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
 #pragma unroll
         for (int r = 0; r < 16; ++r) mine[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
     __syncthreads();
-    const float* part = smem + sp * kPart + l;
+    const float* sums = smem + sp * kPart + l;
+    constexpr int kMine = kSlots / KS;
+    float x[kMine];
 #pragma unroll
-    for (int u = 0; u < kSlots / KS; ++u) {
-      const int s = ks * (kSlots / KS) + u;  // register (i, j, r) = (s / (16 FN), (s / 16) % FN, s % 16)
-      float x = part[s * 64];
+    for (int u = 0; u < kMine; ++u) {
+      const int s = ks * kMine + u;  // register (i, j, r) = (s / (16 FN), (s / 16) % FN, s % 16)
+      x[u] = sums[s * 64];
 #pragma unroll
-      for (int q = 1; q < KS; ++q) x += part[q * kStride + s * 64];
-      const int i = s / (FN * 16), j = (s / 16) % FN, r = s % 16;
-      store_c(m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4), n0 + wn0 + j * 32 + lr, x);
+      for (int q = 1; q < KS; ++q) x[u] += sums[q * kStride + s * 64];
     }
+    auto coord = [&](int u, int& row, int& col) {
+      const int s = ks * kMine + u, i = s / (FN * 16), j = (s / 16) % FN, r = s % 16;
+      row = m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+      col = n0 + wn0 + j * 32 + lr;
+    };
+    if (part != nullptr) {  // stream-K partial tile (full tiles only)
+#pragma unroll
+      for (int u = 0; u < kMine; ++u) {
+        int row, col;
+        coord(u, row, col);
+        part[(row - m0) * BN + (col - n0)] = x[u];
+      }
+      return;
+    }
+    finish_c<kMine, GUARD>(p, x, coord);
     return;
   }
 
-  // epilogue: register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its block
+  store_acc<BM, BN, FM, FN, GUARD>(p, acc, m0, n0, wm0, wn0, lr, lh, part);
+}
+
+// K-tiles [kb, ke) of the BM x BN tile at (m0, n0), as mfma_tile, for configurations with
+// BK = 16, no K split and large wavefront tiles (one wavefront per SIMD).  The MFMA
+// fragments are read from LDS one K-tile ahead into a second register set, so that no
+// MFMA waits for an LDS read: with fragments read after the barrier, right before the
+// MFMAs that use them, the wavefronts lose 3-6% of the matrix-core cycles to LDS
+// latency (probe: 150-146 against 155 TFLOP/s with no LDS reads).
+//   During K-tile t (register set P = (t - kb) % 2, LDS stage P):
+//     - the fragments of tile t+1 are read from stage P^1 into set P^1;
+//     - the global registers (tile t+2, loaded during tile t-1) are stored to stage P,
+//       whose fragments were read before the previous barrier;
+//     - tile t+3 is loaded into the global registers;
+//     - the MFMAs of tile t run on set P;
+//   and one barrier ends the K-tile.  A global load has one K-tile of MFMAs to arrive.
+template <int BM, int BN, int WM, int WN, bool TA, bool TB, bool VEC, bool GUARD>
+__device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
+                                             float* part = nullptr) {
+  constexpr int BK = 16;
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, 1, TA, TB>;
+  using OpA = typename Cfg::OpA;
+  using OpB = typename Cfg::OpB;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN;
+  auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
+  auto b_stage = [&](int s) { return smem + s * Cfg::kStageFloats + OpA::kStageFloats; };
+
+  const int t = threadIdx.x;
+  const int w = t / 64, l = t % 64;
+  const int lr = l % 32, lh = l / 32;
+  const int wm0 = (w / WN) * (BM / WM), wn0 = (w % WN) * (BN / WN);
+
+  OpA opa;
+  OpB opb;
+  opa.init(p.A, p.lda, m0, p.M - m0, t);
+  opb.init(p.B, p.ldb, n0, p.N - n0, t);
+
+  v16f acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        store_c(m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4), n0 + wn0 + j * 32 + lr, acc[i][j][r]);
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  float af[2][FM][8], bf[2][FN][8];
+
+  const int nfull = p.K / BK;
+  auto load = [&](int kt) {
+    if (kt < nfull) {
+      opa.template load_full<VEC, GUARD, 0>(kt * BK);
+      opb.template load_full<VEC, GUARD, 0>(kt * BK);
+    } else {
+      opa.template load_tail<VEC, GUARD, 0>(kt * BK, p.K - kt * BK);
+      opb.template load_tail<VEC, GUARD, 0>(kt * BK, p.K - kt * BK);
+    }
+  };
+  auto store = [&](int s) {
+    opa.template store<0>(a_stage(s));
+    opb.template store<0>(b_stage(s));
+  };
+  auto frags = [&](auto set, int s) {
+    constexpr int S = decltype(set)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) OpA::read(a_stage(s), wm0 + i * 32 + lr, 0, lh, af[S][i]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) OpB::read(b_stage(s), wn0 + j * 32 + lr, 0, lh, bf[S][j]);
+  };
+  auto mfmas = [&](auto set) {
+    constexpr int S = decltype(set)::value;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[S][i][e], bf[S][j][e], acc[i][j], 0, 0, 0);
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+
+  // prologue: stage 0 <- tile kb (read into set 0), stage 1 <- tile kb+1, registers <- tile kb+2
+  load(kb);
+  store(0);
+  if (kb + 1 < ke) load(kb + 1);
+  __syncthreads();
+  frags(Set0{}, 0);
+  if (kb + 1 < ke) store(1);
+  if (kb + 2 < ke) load(kb + 2);
+  __syncthreads();
+
+  // Instruction order of a steady K-tile: the MFMAs start right after the barrier and
+  // each of the first ones is followed by one memory instruction (LDS stores, then
+  // global loads, then fragment reads), so that the single wavefront of each SIMD issues
+  // its memory traffic in the shadow of the MFMAs; nothing moves across the barrier (the
+  // compiler would otherwise hoist the barrier, and its wait on the fragment reads, above
+  // the MFMAs).
+  constexpr int kStores = OpA::LOADS + OpB::LOADS;
+  constexpr int kFragReads = FM * (OpA::STRIDE == BK ? 2 : 8) + FN * (OpB::STRIDE == BK ? 2 : 8);
+  auto steady = [&](auto set, int kt) {  // tiles kt+1 .. kt+3 exist and kt+3 is full
+    constexpr int P = decltype(set)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    store(P);
+    opa.template load_full<VEC, GUARD, 0>((kt + 3) * BK);
+    opb.template load_full<VEC, GUARD, 0>((kt + 3) * BK);
+    frags(std::integral_constant<int, P ^ 1>{}, P ^ 1);
+    mfmas(set);
+#pragma unroll
+    for (int i = 0; i < kStores; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+    }
+#pragma unroll
+    for (int i = 0; i < kStores; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+    }
+#pragma unroll
+    for (int i = 0; i < kFragReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+  auto step = [&](auto set, int kt) {
+    constexpr int P = decltype(set)::value;
+    if (kt + 2 < ke) store(P);
+    if (kt + 3 < ke) load(kt + 3);
+    if (kt + 1 < ke) frags(std::integral_constant<int, P ^ 1>{}, P ^ 1);
+    mfmas(set);
+    __syncthreads();
+  };
+  int kt = kb;
+  const int steady_end = min(ke, nfull);
+  for (; kt + 4 < steady_end; kt += 2) {  // tiles kt+3 and kt+4 are full and in range
+    steady(Set0{}, kt);
+    steady(Set1{}, kt + 1);
+  }
+  for (; kt < ke; kt += 2) {
+    step(Set0{}, kt);
+    if (kt + 1 < ke) step(Set1{}, kt + 1);
+  }
+
+  store_acc<BM, BN, FM, FN, GUARD>(p, acc, m0, n0, wm0, wn0, lr, lh, part);
 }
 
 // Scalar edge-tile path: one 32 x 32 register-blocked VALU tile per workgroup; the
@@ -447,10 +651,12 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // MIN_BLOCKS workgroups must fit on one CU at once (a register budget for the compiler).
 // MFMA_EDGES: the tiles reaching past M or N are guarded MFMA tiles of the same grid
 // (tiles_m x tiles_n covers the whole matrix) instead of scalar edge tiles.
+// PF: the tiles run mfma_tile_pf (BK = 16, KS = 1) instead of mfma_tile.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          bool MFMA_EDGES, bool STREAM_K, bool VEC>
+          bool MFMA_EDGES, bool STREAM_K, bool VEC, bool PF>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
+  static_assert(!PF || (BK == 16 && KS == 1), "fragment prefetch: one 16-deep k-group per K-tile");
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   p = batch_entry(p);
   constexpr int kGroups = Cfg::kThreads / 256;
@@ -458,6 +664,13 @@ void mfma_kernel(Problem p, TileMap map) {
   constexpr int kFloats = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
   static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
+  auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
+    constexpr bool G = decltype(guard)::value;
+    if constexpr (PF)
+      mfma_tile_pf<BM, BN, WM, WN, TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
+    else
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
+  };
   const int nmfma = map.tiles_m * map.tiles_n;
   const int ndp = STREAM_K ? map.dp_tiles : nmfma;
   const int iters = (p.K + BK - 1) / BK;
@@ -467,9 +680,9 @@ void mfma_kernel(Problem p, TileMap map) {
     tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
     const int m0 = bm * BM, n0 = bn * BN;
     if (!MFMA_EDGES || (m0 + BM <= p.M && n0 + BN <= p.N))
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false>(p, m0, n0, 0, iters, smem);
+      tile(std::false_type{}, m0, n0, 0, iters, nullptr);
     else
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, true>(p, m0, n0, 0, iters, smem);
+      tile(std::true_type{}, m0, n0, 0, iters, nullptr);
     return;
   }
   if (STREAM_K && e < map.sk_wgs) {  // one stream-K range (full tiles only)
@@ -486,7 +699,7 @@ void mfma_kernel(Problem p, TileMap map) {
       int bm, bn;
       tile_coords<GROUP_M>(map.dp_tiles + u, map.tiles_m, map.tiles_n, bm, bn);
       if (j != j0) __syncthreads();  // the previous piece's epilogue may still read LDS
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, false>(p, bm * BM, bn * BN, kb, ke, smem, part);
+      tile(std::false_type{}, bm * BM, bn * BN, kb, ke, part);
       j = seg_end;
     }
     return;
@@ -547,7 +760,7 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(Problem p, TileMap map) {
 // workgroups for the last partial wave of tiles plus one full wave before it (the tiles
 // before those run one per workgroup); ws holds 2 * 256 * BM * BN floats.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          bool MFMA_EDGES = false>
+          bool MFMA_EDGES = false, bool PF = false>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws = nullptr) {
   static_assert(BM % kEdge == 0 && BN % kEdge == 0, "edge tiles of the right strip end at Mf");
   TileMap map;
@@ -586,10 +799,10 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
       const long long blocks = map.dp_tiles + map.sk_wgs + edge_tiles;
       if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
       if (vec)
-        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false, true, true>),
+        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false, true, true, PF>),
                            dim3((unsigned)blocks), block, 0, stream, p, map);
       else
-        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false, true, false>),
+        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false, true, false, PF>),
                            dim3((unsigned)blocks), block, 0, stream, p, map);
       const hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
@@ -602,16 +815,18 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks, batch);
   if (vec)
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false, true>),
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false, true, PF>),
                        grid, block, 0, stream, p, map);
   else
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false, false>),
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false, false, PF>),
                        grid, block, 0, stream, p, map);
   return hipGetLastError();
 }
 
 // The tile configurations (tile_plan.h), by tile side.
-//   256: 256 x 256 tiles, 4 x 4 wavefronts of 64 x 64, BK 16: one workgroup per CU.
+//   256: 256 x 256 tiles, 2 x 2 wavefronts of 128 x 128 (one per SIMD, 256 accumulator
+//        registers each), BK 16, fragments read one K-tile ahead (mfma_tile_pf): one
+//        workgroup per CU.
 //   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64 and a 2-way K split, BK 32.
 //   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32; three
 //        workgroups per CU (a 4-way split with BK 64 is 2-7% slower).
@@ -623,7 +838,7 @@ template <bool TA, bool TB>
 hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr) {
   switch (tiles) {
     case 256:
-      return launch_cfg<256, 256, 16, 4, 4, 1, TA, TB, 8, 1>(p, batch, stream, ws);
+      return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, false, true>(p, batch, stream, ws);
     case 128:
       return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
     case 64:

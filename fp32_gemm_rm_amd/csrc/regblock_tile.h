@@ -192,24 +192,32 @@ struct RegBlock {
     const int tm = (w / WAVES_N) * 8 + l / 8;
     const int tn = (w % WAVES_N) * 8 + l % 8;
     const int rows_left = p.M - m0, cols_left = p.N - n0;
+    // every C value of the thread is loaded before the first store: a load after a store
+    // into the same array would wait for that store
+    float cin[TM][TN];
     const bool beta0 = p.beta == 0.0f;
 #pragma unroll
-    for (int gi = 0; gi < GM; ++gi)
+    for (int pass = beta0 ? 1 : 0; pass < 2; ++pass)
 #pragma unroll
-      for (int vi = 0; vi < VM; ++vi) {
-        const int r = gi * (BM / GM) + tm * VM + vi;
-        if (GUARD && r >= rows_left) continue;
-        float* crow = p.C + (long long)(m0 + r) * p.ldc + n0;
+      for (int gi = 0; gi < GM; ++gi)
 #pragma unroll
-        for (int gj = 0; gj < GN; ++gj)
+        for (int vi = 0; vi < VM; ++vi) {
+          const int r = gi * (BM / GM) + tm * VM + vi;
+          if (GUARD && r >= rows_left) continue;
+          float* crow = p.C + (long long)(m0 + r) * p.ldc + n0;
 #pragma unroll
-          for (int vj = 0; vj < VN; ++vj) {
-            const int c = gj * (BN / GN) + tn * VN + vj;
-            if (GUARD && c >= cols_left) continue;
-            const float x = acc[gi * VM + vi][gj * VN + vj];
-            crow[c] = beta0 ? p.alpha * x : fmaf(p.alpha, x, p.beta * crow[c]);
-          }
-      }
+          for (int gj = 0; gj < GN; ++gj)
+#pragma unroll
+            for (int vj = 0; vj < VN; ++vj) {
+              const int c = gj * (BN / GN) + tn * VN + vj;
+              if (GUARD && c >= cols_left) continue;
+              const int i = gi * VM + vi, j = gj * VN + vj;
+              if (pass == 0)
+                cin[i][j] = crow[c];
+              else
+                crow[c] = beta0 ? p.alpha * acc[i][j] : fmaf(p.alpha, acc[i][j], p.beta * cin[i][j]);
+            }
+        }
   }
 
   // The whole tile: C[m0.., n0..] = alpha * op(A)[m0.., :] op(B)[:, n0..] + beta * C.
