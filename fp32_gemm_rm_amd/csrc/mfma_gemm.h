@@ -134,18 +134,24 @@ struct Operand {
       col[i] = KROWS ? q % KC : (q % (R / 4)) * 4;
     }
   }
-  // full K-tile starting at k0.  GUARD: the slice may reach past the matrix (lim < R):
-  // zeros there (a float4 along r that is only partly inside is read element by element)
+  // full K-tile starting at k0.  GUARD: the slice may reach past the matrix (lim < R).
+  // A row past the matrix (rows along k) is loaded unconditionally from the last row and
+  // store<true> writes zeros in its place: a load under a branch makes the compiler wait
+  // for it where the branches join, which would undo the prefetch of the guarded tiles of
+  // a partial tile row.  Along r (rows along m or n) a tile that is full there loads as an
+  // unguarded one; in the one partial tile column a float4 that is only partly inside is
+  // read element by element, with zeros past the matrix.
   template <bool VEC, bool GUARD, int SET = 0>
   __device__ __forceinline__ void load_full(int k0) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      if (KROWS)
-        reg[SET][i] = (!GUARD || row[i] < lim) ? load4<VEC>(base + (long long)row[i] * ld + k0 + 4 * col[i], 4)
-                                          : make_float4(0.f, 0.f, 0.f, 0.f);
-      else
-        reg[SET][i] = GUARD ? load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], lim - col[i])
-                            : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
+      if (KROWS) {
+        const int r = (!GUARD || row[i] < lim) ? row[i] : lim - 1;
+        reg[SET][i] = load4<VEC>(base + (long long)r * ld + k0 + 4 * col[i], 4);
+      } else {
+        const float* q = base + (long long)(k0 + row[i]) * ld + col[i];
+        reg[SET][i] = load4<VEC>(q, (!GUARD || lim == R) ? 4 : lim - col[i]);
+      }
     }
   }
   // last K-tile: kl = K - k0 < BK valid k; zeros past K (and past the matrix, GUARD)
@@ -164,12 +170,15 @@ struct Operand {
                             : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
     }
   }
-  template <int SET = 0>
+  // registers of set SET to an LDS stage; GUARD: zeros for rows past the matrix
+  template <bool GUARD, int SET = 0>
   __device__ __forceinline__ void store(float* stage) const {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : row[i] * STRIDE + col[i])) =
-          reg[SET][i];
+    for (int i = 0; i < LOADS; ++i) {
+      float4 v = reg[SET][i];
+      if (GUARD && KROWS && row[i] >= lim) v = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : row[i] * STRIDE + col[i])) = v;
+    }
   }
   // out[e] = X(rr, 16g + 8lh + e), e = 0..7: this lane's values for the 8 MFMA steps of k-group g
   __device__ __forceinline__ static void read(const float* stage, int rr, int g, int lh, float (&out)[8]) {
@@ -230,13 +239,13 @@ struct StreamK {
 };
 
 // C := alpha * x[u] + beta * C at the NV elements (row(u), col(u)) of this lane, given
-// by coord(u, row, col); C is not read when beta == 0, and with GUARD elements past M or
-// N are skipped.  Every C value of the batch is loaded before the first store: a load
+// by coord(u, row, col); C is not read when beta == 0.  GUARD (bit 0: rows, bit 1:
+// columns): elements past M or N are skipped.  Every C value of the batch is loaded before the first store: a load
 // after a store into the same array would wait for that store (the compiler cannot tell
 // that the addresses differ), which turns the epilogue into a chain of round trips.
-template <int NV, bool GUARD, typename Coord>
+template <int NV, int GUARD, typename Coord>
 __device__ __forceinline__ void finish_c(const Problem& p, const float (&x)[NV], Coord coord) {
-  auto inside = [&](int row, int col) { return !GUARD || (row < p.M && col < p.N); };
+  auto inside = [&](int row, int col) { return (!(GUARD & 1) || row < p.M) && (!(GUARD & 2) || col < p.N); };
   if (p.beta == 0.0f) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -264,7 +273,7 @@ __device__ __forceinline__ void finish_c(const Problem& p, const float (&x)[NV],
 // The accumulators of one wavefront (FM x FN blocks of 32 x 32 at (m0 + wm0, n0 + wn0))
 // to C, one row of blocks at a time, or raw to a stream-K partial tile `part`.
 // Register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its block.
-template <int BM, int BN, int FM, int FN, bool GUARD>
+template <int BM, int BN, int FM, int FN, int GUARD>
 __device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM][FN], int m0, int n0, int wm0,
                                           int wn0, int lr, int lh, float* part) {
 #pragma unroll
@@ -294,15 +303,16 @@ __device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM
 
 // K-tiles [kb, ke) of the BM x BN tile of C at (m0, n0).  part == nullptr: the range is
 // the whole K range and the result goes to C (alpha, beta); otherwise the raw sums go to
-// part, a BM x BN row-major block (a stream-K partial tile).  GUARD: the tile reaches
-// past M or N; loads read zeros there and stores skip it.
-template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool VEC, bool GUARD>
+// part, a BM x BN row-major block (a stream-K partial tile).  GUARD bit 0 (1): the tile
+// reaches past M, bit 1 (2): past N; // past M or N; loads read zeros there and stores skip it.
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool VEC, int GUARD>
 __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                           float* part = nullptr) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, KG = Cfg::KG;
+  constexpr bool GA = (GUARD & 1) != 0, GB = (GUARD & 2) != 0;  // A rows past M, B columns past N
   // stage s: A at smem + s * kStageFloats, B right after it
   auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
   auto b_stage = [&](int s) { return smem + s * Cfg::kStageFloats + OpA::kStageFloats; };
@@ -332,11 +342,11 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
   auto load = [&](auto set, int kt) {
     constexpr int SET = decltype(set)::value;
     if (kt < nfull) {
-      opa.template load_full<VEC, GUARD, SET>(kt * BK);
-      opb.template load_full<VEC, GUARD, SET>(kt * BK);
+      opa.template load_full<VEC, GA, SET>(kt * BK);
+      opb.template load_full<VEC, GB, SET>(kt * BK);
     } else {
-      opa.template load_tail<VEC, GUARD, SET>(kt * BK, p.K - kt * BK);
-      opb.template load_tail<VEC, GUARD, SET>(kt * BK, p.K - kt * BK);
+      opa.template load_tail<VEC, GA, SET>(kt * BK, p.K - kt * BK);
+      opb.template load_tail<VEC, GB, SET>(kt * BK, p.K - kt * BK);
     }
   };
   // the MFMAs of K-tile kt from stage s; `mid` runs half-way through the last k-group
@@ -373,18 +383,18 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
   // only the older register set (a wait on the newest loads would undo the prefetch);
   // the last steps run the general form.
   load(Set0{}, kb);
-  opa.template store<0>(a_stage(0));
-  opb.template store<0>(b_stage(0));
+  opa.template store<GA, 0>(a_stage(0));
+  opb.template store<GB, 0>(b_stage(0));
   if (kb + 1 < ke) load(Set1{}, kb + 1);
   __syncthreads();
   auto steady = [&](auto set, int kt) {  // set = (kt - kb) % 2, also the LDS stage of tile kt
     constexpr int P = decltype(set)::value;
-    opa.template load_full<VEC, GUARD, P>((kt + 2) * BK);
-    opb.template load_full<VEC, GUARD, P>((kt + 2) * BK);
+    opa.template load_full<VEC, GA, P>((kt + 2) * BK);
+    opb.template load_full<VEC, GB, P>((kt + 2) * BK);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
     multiply(P, [&] {
-      opa.template store<P ^ 1>(a_stage(P ^ 1));
-      opb.template store<P ^ 1>(b_stage(P ^ 1));
+      opa.template store<GA, P ^ 1>(a_stage(P ^ 1));
+      opb.template store<GB, P ^ 1>(b_stage(P ^ 1));
     });
     __syncthreads();
   };
@@ -393,8 +403,8 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
     if (kt + 2 < ke) load(set, kt + 2);
     multiply(P, [&] {
       if (kt + 1 < ke) {
-        opa.template store<P ^ 1>(a_stage(P ^ 1));
-        opb.template store<P ^ 1>(b_stage(P ^ 1));
+        opa.template store<GA, P ^ 1>(a_stage(P ^ 1));
+        opb.template store<GB, P ^ 1>(b_stage(P ^ 1));
       }
     });
     __syncthreads();
@@ -472,7 +482,7 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
 //     - tile t+3 is loaded into the global registers;
 //     - the MFMAs of tile t run on set P;
 //   and one barrier ends the K-tile.  A global load has one K-tile of MFMAs to arrive.
-template <int BM, int BN, int WM, int WN, bool TA, bool TB, bool VEC, bool GUARD>
+template <int BM, int BN, int WM, int WN, bool TA, bool TB, bool VEC, int GUARD>
 __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                              float* part = nullptr) {
   constexpr int BK = 16;
@@ -480,6 +490,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
   constexpr int FM = Cfg::FM, FN = Cfg::FN;
+  constexpr bool GA = (GUARD & 1) != 0, GB = (GUARD & 2) != 0;  // A rows past M, B columns past N
   auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
   auto b_stage = [&](int s) { return smem + s * Cfg::kStageFloats + OpA::kStageFloats; };
 
@@ -505,16 +516,16 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   const int nfull = p.K / BK;
   auto load = [&](int kt) {
     if (kt < nfull) {
-      opa.template load_full<VEC, GUARD, 0>(kt * BK);
-      opb.template load_full<VEC, GUARD, 0>(kt * BK);
+      opa.template load_full<VEC, GA, 0>(kt * BK);
+      opb.template load_full<VEC, GB, 0>(kt * BK);
     } else {
-      opa.template load_tail<VEC, GUARD, 0>(kt * BK, p.K - kt * BK);
-      opb.template load_tail<VEC, GUARD, 0>(kt * BK, p.K - kt * BK);
+      opa.template load_tail<VEC, GA, 0>(kt * BK, p.K - kt * BK);
+      opb.template load_tail<VEC, GB, 0>(kt * BK, p.K - kt * BK);
     }
   };
   auto store = [&](int s) {
-    opa.template store<0>(a_stage(s));
-    opb.template store<0>(b_stage(s));
+    opa.template store<GA, 0>(a_stage(s));
+    opb.template store<GB, 0>(b_stage(s));
   };
   auto frags = [&](auto set, int s) {
     constexpr int S = decltype(set)::value;
@@ -558,8 +569,8 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
     constexpr int P = decltype(set)::value;
     __builtin_amdgcn_sched_barrier(0);
     store(P);
-    opa.template load_full<VEC, GUARD, 0>((kt + 3) * BK);
-    opb.template load_full<VEC, GUARD, 0>((kt + 3) * BK);
+    opa.template load_full<VEC, GA, 0>((kt + 3) * BK);
+    opb.template load_full<VEC, GB, 0>((kt + 3) * BK);
     frags(std::integral_constant<int, P ^ 1>{}, P ^ 1);
     mfmas(set);
 #pragma unroll
@@ -649,23 +660,26 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 }
 
 // MIN_BLOCKS workgroups must fit on one CU at once (a register budget for the compiler).
-// MFMA_EDGES: the tiles reaching past M or N are guarded MFMA tiles of the same grid
-// (tiles_m x tiles_n covers the whole matrix) instead of scalar edge tiles.
+// EDGE_MIN: 0, the tiles cover [0, Mf) x [0, Nf) with Mf, Nf multiples of BM, BN and the
+// strips past them are scalar edge tiles; otherwise a strip at least EDGE_MIN rows
+// (columns) wide is covered by guarded MFMA tiles of the same grid and only a thinner one
+// goes to the scalar edge tiles (EDGE_MIN = 1: every partial tile is an MFMA tile).
 // PF: the tiles run mfma_tile_pf (BK = 16, KS = 1) instead of mfma_tile.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          bool MFMA_EDGES, bool STREAM_K, bool VEC, bool PF>
+          int EDGE_MIN, bool STREAM_K, bool VEC, bool PF>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   static_assert(!PF || (BK == 16 && KS == 1), "fragment prefetch: one 16-deep k-group per K-tile");
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   p = batch_entry(p);
   constexpr int kGroups = Cfg::kThreads / 256;
-  constexpr int kEdgeFloats = MFMA_EDGES ? 0 : kGroups * EdgeTile::kLdsFloats;  // >= its reduction floats
+  constexpr bool kEdges = EDGE_MIN != 1;  // scalar edge tiles may exist
+  constexpr int kEdgeFloats = kEdges ? kGroups * EdgeTile::kLdsFloats : 0;  // >= its reduction floats
   constexpr int kFloats = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
   static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
   auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
-    constexpr bool G = decltype(guard)::value;
+    constexpr int G = decltype(guard)::value;
     if constexpr (PF)
       mfma_tile_pf<BM, BN, WM, WN, TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
     else
@@ -679,10 +693,15 @@ void mfma_kernel(Problem p, TileMap map) {
     int bm, bn;
     tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
     const int m0 = bm * BM, n0 = bn * BN;
-    if (!MFMA_EDGES || (m0 + BM <= p.M && n0 + BN <= p.N))
-      tile(std::false_type{}, m0, n0, 0, iters, nullptr);
+    const bool past_m = EDGE_MIN != 0 && m0 + BM > p.M, past_n = EDGE_MIN != 0 && n0 + BN > p.N;
+    if (!past_m && !past_n)
+      tile(std::integral_constant<int, 0>{}, m0, n0, 0, iters, nullptr);
+    else if (!past_n)
+      tile(std::integral_constant<int, 1>{}, m0, n0, 0, iters, nullptr);
+    else if (!past_m)
+      tile(std::integral_constant<int, 2>{}, m0, n0, 0, iters, nullptr);
     else
-      tile(std::true_type{}, m0, n0, 0, iters, nullptr);
+      tile(std::integral_constant<int, 3>{}, m0, n0, 0, iters, nullptr);
     return;
   }
   if (STREAM_K && e < map.sk_wgs) {  // one stream-K range (full tiles only)
@@ -699,13 +718,13 @@ void mfma_kernel(Problem p, TileMap map) {
       int bm, bn;
       tile_coords<GROUP_M>(map.dp_tiles + u, map.tiles_m, map.tiles_n, bm, bn);
       if (j != j0) __syncthreads();  // the previous piece's epilogue may still read LDS
-      tile(std::false_type{}, bm * BM, bn * BN, kb, ke, part);
+      tile(std::integral_constant<int, 0>{}, bm * BM, bn * BN, kb, ke, part);
       j = seg_end;
     }
     return;
   }
   if (STREAM_K) e -= map.sk_wgs;
-  if constexpr (!MFMA_EDGES) {
+  if constexpr (kEdges) {
     int m0, n0;
     const int n_right = map.right_m * map.right_n;
     if (e < n_right) {
@@ -756,41 +775,35 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(Problem p, TileMap map) {
   }
 }
 
-// ws != nullptr (batch 1, configurations without MFMA_EDGES): stream-K over 256
+// ws != nullptr (batch 1, configurations with EDGE_MIN = 0): stream-K over 256
 // workgroups for the last partial wave of tiles plus one full wave before it (the tiles
 // before those run one per workgroup); ws holds 2 * 256 * BM * BN floats.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          bool MFMA_EDGES = false, bool PF = false>
+          int EDGE_MIN = 0, bool PF = false>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws = nullptr) {
-  static_assert(BM % kEdge == 0 && BN % kEdge == 0, "edge tiles of the right strip end at Mf");
+  static_assert(BM == BN && BM % kEdge == 0, "square tiles whose sides are multiples of the edge tile");
   TileMap map;
   map.dp_tiles = map.sk_wgs = 0;
   map.ws = nullptr;
-  if (MFMA_EDGES) {
-    map.tiles_m = (p.M + BM - 1) / BM;
-    map.tiles_n = (p.N + BN - 1) / BN;
-    map.Mf = p.M;
-    map.Nf = p.N;
-    map.right_m = map.right_n = map.bottom_m = map.bottom_n = 0;
-  } else {
-    map.Mf = (p.M / BM) * BM;
-    map.Nf = (p.N / BN) * BN;
-    map.tiles_m = map.Mf / BM;
-    map.tiles_n = map.Nf / BN;
-    if (map.tiles_m == 0 || map.tiles_n == 0) {  // no full tile: everything is edge
-      map.tiles_m = map.tiles_n = 0;
-      map.Mf = map.Nf = 0;
-    }
-    map.right_m = (map.Nf < p.N) ? map.Mf / kEdge : 0;
-    map.right_n = (map.Nf < p.N) ? (p.N - map.Nf + kEdge - 1) / kEdge : 0;
-    map.bottom_m = (p.M - map.Mf + kEdge - 1) / kEdge;
-    map.bottom_n = map.bottom_m > 0 ? (p.N + kEdge - 1) / kEdge : 0;
+  // extent of the MFMA tiles: rows [0, Mf), columns [0, Nf) (mfma_extent, tile_plan.h uses
+  // the same rule); the strips past it are scalar edge tiles
+  map.Mf = mfma_extent(p.M, BM, EDGE_MIN);
+  map.Nf = mfma_extent(p.N, BN, EDGE_MIN);
+  map.tiles_m = (map.Mf + BM - 1) / BM;
+  map.tiles_n = (map.Nf + BN - 1) / BN;
+  if (map.tiles_m == 0 || map.tiles_n == 0) {  // no MFMA tile: everything is edge
+    map.tiles_m = map.tiles_n = 0;
+    map.Mf = map.Nf = 0;
   }
+  map.right_m = (map.Nf < p.N) ? (map.Mf + kEdge - 1) / kEdge : 0;
+  map.right_n = (map.Nf < p.N) ? (p.N - map.Nf + kEdge - 1) / kEdge : 0;
+  map.bottom_m = (p.M - map.Mf + kEdge - 1) / kEdge;
+  map.bottom_n = map.bottom_m > 0 ? (p.N + kEdge - 1) / kEdge : 0;
   const long long nmfma = (long long)map.tiles_m * map.tiles_n;
   const long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
   const dim3 block(WM * WN * KS * 64);
   const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
-  if constexpr (!MFMA_EDGES && BM == 256 && BN == 256) {  // the workspace holds 256 x 256 slots
+  if constexpr (EDGE_MIN == 0 && BM == 256 && BN == 256) {  // the workspace holds 256 x 256 slots
     if (ws != nullptr && batch == 1 && nmfma % kStreamKWgs != 0) {
       const long long sk_tiles = nmfma % kStreamKWgs + (nmfma > kStreamKWgs ? kStreamKWgs : 0);
       map.dp_tiles = (int)(nmfma - sk_tiles);
@@ -799,10 +812,10 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
       const long long blocks = map.dp_tiles + map.sk_wgs + edge_tiles;
       if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
       if (vec)
-        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false, true, true, PF>),
+        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, 0, true, true, PF>),
                            dim3((unsigned)blocks), block, 0, stream, p, map);
       else
-        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, false, true, false, PF>),
+        hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, 0, true, false, PF>),
                            dim3((unsigned)blocks), block, 0, stream, p, map);
       const hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
@@ -815,10 +828,10 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks, batch);
   if (vec)
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false, true, PF>),
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF>),
                        grid, block, 0, stream, p, map);
   else
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, MFMA_EDGES, false, false, PF>),
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, false, PF>),
                        grid, block, 0, stream, p, map);
   return hipGetLastError();
 }
@@ -831,21 +844,24 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
 //   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32; three
 //        workgroups per CU (a 4-way split with BK 64 is 2-7% slower).
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
-//        256 threads; four workgroups per CU.  Partial tiles are guarded MFMA tiles
-//        (the other configurations send them to the scalar edge-tile path).
+//        256 threads; four workgroups per CU.
+// Partial tiles (mfma_edge_min): guarded MFMA tiles of the same grid in the 128, 64 and
+// 32 configurations, the scalar edge-tile path in the 256 configuration.
 // ws: stream-K workspace (kStreamKBytes) for the 256 configuration, or nullptr.
 template <bool TA, bool TB>
 hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr) {
   switch (tiles) {
     case 256:
-      return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, false, true>(p, batch, stream, ws);
+      return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(256), true>(p, batch, stream, ws);
     case 128:
-      return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
+      if (p.M % 128 == 0 && p.N % 128 == 0) return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
+      return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1, mfma_edge_min(128)>(p, batch, stream);
     case 64:
-      return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 3>(p, batch, stream);
+      if (p.M % 64 == 0 && p.N % 64 == 0) return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 3>(p, batch, stream);
+      return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 3, mfma_edge_min(64)>(p, batch, stream);
     case 32:
       if (p.M % 32 == 0 && p.N % 32 == 0) return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4>(p, batch, stream);
-      return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, true>(p, batch, stream);
+      return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, mfma_edge_min(32)>(p, batch, stream);
     default:
       return hipErrorInvalidValue;
   }

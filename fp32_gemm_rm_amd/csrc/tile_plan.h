@@ -21,9 +21,14 @@ struct TileCost {
 };
 constexpr TileCost kTileCosts[] = {{256, 237.0, 237.0}, {128, 64.7, 64.7}, {64, 16.2, 17.2}, {32, 5.4, 4.95}};
 
+// MFMA tiles along one dimension of n: a partial strip counts as a tile row (column),
+// whether it runs as guarded MFMA tiles or, in the 256 configuration, as scalar edge
+// tiles (which take at least as long).
+inline long long modelled_tiles(int n, int side) { return (n + side - 1) / side; }
+
 // Modelled microseconds; M, N, K, batch > 0.
 inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
-  const long long tiles = ((long long)(M - 1) / c.side + 1) * ((long long)(N - 1) / c.side + 1) * batch;
+  const long long tiles = modelled_tiles(M, c.side) * modelled_tiles(N, c.side) * batch;
   const long long layers = (tiles + 255) / 256;
   return (double)layers * (layers > 1 ? c.u2 : c.u1) * (double)K / 1024.0;
 }

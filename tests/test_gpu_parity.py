@@ -262,6 +262,36 @@ def test_tile_configs_integer_exact(oracle, tiles, M, N, K):
         check_padding(out, C, M, N, ldc)
 
 
+# Partial tiles of the 128 and 64 configurations run as guarded MFMA tiles, guarded along
+# M only, along N only, or both (separate code paths).  Shapes give wide and thin remainders
+# in either dimension and matrices smaller than one tile.
+PARTIAL_SHAPES = {
+    128: [(3 * 128 + 32, 2 * 128 + 31, 70), (3 * 128 + 31, 2 * 128 + 32, 70), (128 + 31, 128 + 31, 70),
+          (128 + 32, 128 + 32, 33), (100, 300, 70), (20, 300, 45), (300, 20, 45)],
+    64: [(5 * 64 + 16, 4 * 64 + 15, 70), (5 * 64 + 15, 4 * 64 + 16, 70), (64 + 15, 64 + 15, 70),
+         (1000, 1030, 99), (40, 200, 45), (10, 200, 45), (200, 10, 45)],
+}
+
+
+@pytest.mark.parametrize("tiles,M,N,K", [(t, *s) for t, shapes in PARTIAL_SHAPES.items() for s in shapes])
+def test_partial_tile_forms_integer_exact(oracle, tiles, M, N, K):
+    """Full and guarded MFMA tiles side by side (forced tile configuration): bit-exact on
+    integer inputs, NaN padding in A/B, sentinel in C."""
+    from fp32_gemm_rm_amd import TILE_VARIANTS
+
+    lda, ldb, ldc = K + 4, N + 4, N + 1
+    a = integer_matrix(M, K, -4, 4, seed=M + 2 * K)
+    b = integer_matrix(K, N, -4, 4, seed=N + 2 * K)
+    c = integer_matrix(M, N, -4, 4, seed=M + 2 * N)
+    A, B, C = pad_rows(a, lda, np.nan), pad_rows(b, ldb, np.nan), pad_rows(c, ldc, C_PAD_SENTINEL)
+    ref, _ = oracle.full(M, N, K, -1.5, A, lda, B, ldb, 0.5, C, ldc)
+    out = run_gemm(M, N, K, -1.5, A, lda, B, ldb, 0.5, C, ldc, TILE_VARIANTS[tiles])
+    got = c_window(out, M, N, ldc).astype(np.float64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"tiles {tiles} {M}x{N}x{K}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+    check_padding(out, C, M, N, ldc)
+
+
 @pytest.mark.parametrize("tiles", [256, 128, 64, 32])
 def test_tile_configs_random_bound(oracle, tiles):
     """Each forced tile configuration on the ragged 1000 x 1030 x 999 workload (alpha 1.5,
