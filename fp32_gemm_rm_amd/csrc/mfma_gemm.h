@@ -26,9 +26,15 @@
 // SIMD a single wavefront, run 4 wavefronts per SIMD and hide LDS, barrier and
 // MFMA latencies.
 //
-// LDS, two stages (one barrier per K-tile; the global loads of tile t+2 are issued as
-// tile t's MFMAs start, into the second of two register sets, and tile t+1's registers
-// are stored half-way through those MFMAs):
+// Pipelines (one barrier per K-tile, two LDS stages):
+//   mfma_tile (128, 64 and 32 configurations): the global loads of tile t+2 are issued as
+//     tile t's MFMAs start, into the second of two register sets, and tile t+1's
+//     registers are stored half-way through those MFMAs; fragments are read from LDS
+//     at the start of each k-group.
+//   mfma_tile_pf (256 configuration, one wavefront per SIMD): fragments are read one
+//     K-tile ahead into a second register set, so no MFMA waits for LDS; the global
+//     loads, LDS stores and fragment reads are interleaved one per MFMA.
+// LDS layout:
 //   A tile, BM rows of BK floats (BK/4 16-byte chunks), no padding.  For
 //     BK = 16, chunk c of row r is stored at chunk position c ^ ((r/4) % 4).  On
 //     gfx950 a 128-bit LDS access serves 16 lanes per cycle from 64 banks of 4
@@ -49,16 +55,18 @@
 // the run walks GROUP_M tile-rows at a time, so the A and B panels of the
 // tiles in flight on one XCD share its L2.
 //
-// Edge tiles: the MFMA tiles cover [0, Mf) x [0, Nf) with Mf, Nf the largest
-// multiples of BM, BN.  The strips past them (columns [Nf, N) of rows [0, Mf),
-// then rows [Mf, M) in full) are cut into 32 x 32 tiles computed by the
-// bounds-checked register-blocked VALU tile (regblock_tile.h, 256 threads, 2 x 2
-// outputs each): the scalar edge-tile path.  One edge tile per workgroup; its
-// NT/256 groups of 256 threads split the tile's K range (all groups run the same
-// number of K-steps, so their barriers match) and add their partial sums through
-// LDS in the fixed group order.  Edge workgroups take the highest block ids of
-// the same launch, so they run beside the MFMA tiles instead of after them.  Ragged K
-// is handled inside every MFMA tile: its last K-tile loads zeros past K.
+// Partial tiles.  In the 128, 64 and 32 configurations the tile grid covers the whole
+// matrix and the tiles that reach past M or N are guarded MFMA tiles, dispatched on
+// which side they cross (past M, past N, or both), so that a tile past M only loads B
+// as a full tile does.  In the 256 configuration the MFMA tiles cover [0, Mf) x [0, Nf)
+// with Mf, Nf the largest multiples of 256, and the strips past them (columns [Nf, N)
+// of rows [0, Mf), then rows [Mf, M) in full) are cut into 32 x 32 tiles computed by
+// the bounds-checked register-blocked VALU tile (regblock_tile.h, 256 threads, 2 x 2
+// outputs each): the scalar edge-tile path.  One edge tile per workgroup; its NT/256
+// groups of 256 threads split the tile's K range (all groups run the same number of
+// K-steps, so their barriers match) and add their partial sums through LDS in the
+// fixed group order.  Edge workgroups take the highest block ids of the same launch.
+// Ragged K is handled inside every MFMA tile: its last K-tile loads zeros past K.
 //
 // Stream-K (256 x 256 tiles, batch 1, with a caller workspace): when the full tiles do
 // not fill whole waves of 256 workgroups, the last partial wave and the full wave before
