@@ -27,13 +27,14 @@
 // MFMA latencies.
 //
 // Pipelines (one barrier per K-tile, two LDS stages):
-//   mfma_tile (128, 64 and 32 configurations): the global loads of tile t+2 are issued as
+//   mfma_tile (64 and 32 configurations): the global loads of tile t+2 are issued as
 //     tile t's MFMAs start, into the second of two register sets, and tile t+1's
 //     registers are stored half-way through those MFMAs; fragments are read from LDS
 //     at the start of each k-group.
-//   mfma_tile_pf (256 configuration, one wavefront per SIMD): fragments are read one
-//     K-tile ahead into a second register set, so no MFMA waits for LDS; the global
-//     loads, LDS stores and fragment reads are interleaved one per MFMA.
+//   mfma_tile_pf (256 and 128 configurations, one wavefront per SIMD and workgroup):
+//     fragments are read one K-tile ahead into a second register set, so no MFMA waits
+//     for LDS; the global loads, LDS stores and fragment reads are interleaved one per
+//     MFMA.
 // LDS layout:
 //   A tile, BM rows of BK floats (BK/4 16-byte chunks), no padding.  For
 //     BK = 16, chunk c of row r is stored at chunk position c ^ ((r/4) % 4).  On
@@ -848,7 +849,8 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
 //   256: 256 x 256 tiles, 2 x 2 wavefronts of 128 x 128 (one per SIMD, 256 accumulator
 //        registers each), BK 16, fragments read one K-tile ahead (mfma_tile_pf): one
 //        workgroup per CU.
-//   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64 and a 2-way K split, BK 32.
+//   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64, BK 16, fragments read one K-tile
+//        ahead (mfma_tile_pf); two workgroups per CU (three spill registers).
 //   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32; three
 //        workgroups per CU (a 4-way split with BK 64 is 2-7% slower).
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
@@ -862,8 +864,9 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
     case 256:
       return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(256), true>(p, batch, stream, ws);
     case 128:
-      if (p.M % 128 == 0 && p.N % 128 == 0) return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1>(p, batch, stream);
-      return launch_cfg<128, 128, 32, 2, 2, 2, TA, TB, 8, 1, mfma_edge_min(128)>(p, batch, stream);
+      if (p.M % 128 == 0 && p.N % 128 == 0)
+        return launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true>(p, batch, stream);
+      return launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, mfma_edge_min(128), true>(p, batch, stream);
     case 64:
       if (p.M % 64 == 0 && p.N % 64 == 0) return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 3>(p, batch, stream);
       return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 3, mfma_edge_min(64)>(p, batch, stream);

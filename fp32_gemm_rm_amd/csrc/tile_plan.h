@@ -19,7 +19,7 @@ struct TileCost {
   int side;  // tile side: 256, 128, 64 or 32
   double u1, u2;
 };
-constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0}, {128, 64.7, 64.7}, {64, 16.2, 17.2}, {32, 5.4, 4.95}};
+constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0}, {128, 62.0, 59.5}, {64, 16.2, 17.2}, {32, 5.4, 4.95}};
 
 // MFMA tiles along one dimension of n: a partial strip counts as a tile row (column),
 // whether it runs as guarded MFMA tiles or, in the 256 configuration, as scalar edge

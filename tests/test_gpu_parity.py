@@ -335,7 +335,7 @@ def test_offsets_past_2_pow_31(oracle, variant, N):
 
 # K-tile depth of each tile configuration (the K loop runs a steady state over pairs of
 # full K-tiles and a general tail; these K values put its boundaries in every place).
-TILE_BK = {256: 16, 128: 32, 64: 32, 32: 64}
+TILE_BK = {256: 16, 128: 16, 64: 32, 32: 64}
 
 
 @pytest.mark.parametrize("tiles", [256, 128, 64, 32])
