@@ -40,14 +40,17 @@ inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
 // 5 TB/s, plus a launch) and each workgroup's two partial pieces (pipeline fill and
 // partial-tile stores), about 15 us.  With fewer than 256 tiles every tile is split and
 // the pieces' overheads dominate (3072^3: 511 us against 473 us one tile per
-// workgroup), so stream-K is a candidate only past one full wave.  Measured: 5120^3
-// 2157 -> 1977 us, 6144^3 3479 -> 3324 us.  Returns a negative value where it does not
-// apply.
+// workgroup), so stream-K is a candidate only past one full wave.  The stream-K kernel
+// is a separate instantiation of the 256 configuration that spills registers (its range
+// bookkeeping around the tile code), about 9% slower per K-tile than the one-tile kernel:
+// kStreamKCost.  Measured: 5120^3 2005 us (2100 us on 128 x 128 tiles), 6144^3 3377 us
+// (3221 us on 128 x 128 tiles).  Returns a negative value where it does not apply.
+constexpr double kStreamKCost = 252.0;  // us per 1024 of K per layer of 256 tiles
 inline double modelled_stream_k_time(int M, int N, int K, int batch) {
   const long long tiles = (long long)(M / 256) * (N / 256);
   if (batch != 1 || tiles <= kStreamKWgs || tiles % kStreamKWgs == 0) return -1.0;
   const double overhead_us = 4.0 + 2.0 * (double)kStreamKBytes / 5.0e6 + 15.0;
-  return (double)tiles / kStreamKWgs * kTileCosts[0].u2 * (double)K / 1024.0 + overhead_us;
+  return (double)tiles / kStreamKWgs * kStreamKCost * (double)K / 1024.0 + overhead_us;
 }
 
 struct TilePlan {
