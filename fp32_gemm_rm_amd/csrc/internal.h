@@ -78,14 +78,13 @@ inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream, i
 constexpr int kStreamKWgs = 256;
 constexpr long long kStreamKBytes = 2LL * kStreamKWgs * 256 * 256 * 4;
 // Partial MFMA tiles.  A strip of rows (columns) past the last full tile that is at least
-// mfma_edge_min(side) wide runs as guarded MFMA tiles of the same grid; a thinner one goes
-// to the scalar edge tiles (32 x 32 register-blocked VALU tiles).  0: never MFMA.  The
-// scalar edge tile is a latency-bound chain of K-steps (a 32 x 32 tile with K = 999 takes
-// about 24 us on its own, longer than the whole 960 x 1024 x 999 product on 64 x 64 MFMA
-// tiles), so every strip is an MFMA strip (1), except in the 256 configuration (0): its
-// workgroups fill a CU's register file, a guarded tile there costs a whole 256 x 256
-// tile, and the cost model steers ragged shapes to the smaller configurations.
-constexpr int mfma_edge_min(int side) { return side == 256 ? 0 : 1; }
+// mfma_edge_min(side) wide runs as guarded MFMA tiles of the same grid; a thinner one runs
+// as thin strips (128 and 64 configurations: 16, below which a strip would pay for a whole
+// tile row or column of MFMA work) or, in the 256 configuration (0: never MFMA), as
+// scalar edge tiles (its workgroups fill a CU's register file and a guarded tile there
+// costs a whole 256 x 256 tile; the cost model steers ragged shapes to the smaller
+// configurations).  The 32 configuration (1) covers every strip with MFMA tiles.
+constexpr int mfma_edge_min(int side) { return side == 256 ? 0 : side == 32 ? 1 : 16; }
 // The extent [0, result) of rows (columns) that MFMA tiles of this side cover, out of n.
 constexpr int mfma_extent(int n, int side, int edge_min) {
   return (edge_min > 0 && n % side >= edge_min) ? n : n - n % side;

@@ -656,6 +656,59 @@ __device__ __forceinline__ void edge_tile(const Problem& p, int m0, int n0, floa
   EdgeTile::template store<true>(p, m0, n0, tid, acc);
 }
 
+// Thin strips (configurations with EDGE_MIN > 1): columns [lo, lo + width) of rows
+// [first, first + nlines) when `cols`, else rows [lo, lo + width) of columns [first,
+// first + nlines); width < EDGE_MIN <= 16 and nlines <= 16.  A strip that thin would cost
+// a whole MFMA tile row or column (on 64 x 64 tiles a 17th tile column turns one wave of
+// tiles into two), so it runs beside the MFMA tiles as 16 x 16 blocks on
+// v_mfma_f32_16x16x4_f32: each wavefront of the workgroup takes a K slice, every lane
+// loads its two operands straight from global memory (clamped addresses, masked to zero
+// outside the strip, so the loads are unconditional), and the wavefronts' partial blocks
+// are added through LDS in wavefront order.  16x16x4 lane layout: lane l supplies
+// X(l % 16, l / 16) and Y(l / 16, l % 16); accumulator register r of lane l holds
+// D(4 * (l / 16) + r, l % 16).  D(i, j) is (line i, output j) when `cols`, (output i,
+// line j) otherwise.
+constexpr int kThinMax = 16;    // widest thin strip, and lines per workgroup
+template <int NT, bool TA, bool TB>
+__device__ __forceinline__ void thin_strip(const Problem& p, bool cols, int first, int nlines, int lo, int width,
+                                           float* smem) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  constexpr int W = NT / 64;
+  static_assert(NT >= 256, "one thread per output of the 16 x 16 block in the final sums");
+  const int t = threadIdx.x, wv = t / 64, l = t % 64, i16 = l % 16, kq = l / 16;
+  const int kc = ((p.K + W - 1) / W + 3) & ~3;  // K slice of a wavefront, a multiple of 4
+  const int k0 = min(wv * kc, p.K), k1 = min(k0 + kc, p.K);
+  // this lane's row of op(A) (X operand) and column of op(B) (Y operand), clamped
+  const int nx = cols ? nlines : width, ny = cols ? width : nlines;
+  const int am = (cols ? first : lo) + min(i16, nx - 1), bn = (cols ? lo : first) + min(i16, ny - 1);
+  const bool x_in = i16 < nx, y_in = i16 < ny;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int k = k0; k < k1; k += 4) {
+    const int kx = k + kq, kcl = min(kx, p.K - 1);
+    const float av = TA ? p.A[(long long)kcl * p.lda + am] : p.A[(long long)am * p.lda + kcl];
+    const float bv = TB ? p.B[(long long)bn * p.ldb + kcl] : p.B[(long long)kcl * p.ldb + bn];
+    const bool kin = kx < k1;
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x_in && kin ? av : 0.f, y_in && kin ? bv : 0.f, acc, 0, 0, 0);
+  }
+  float* red = smem;  // [wavefront][register][lane]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(wv * 4 + r) * 64 + l] = acc[r];
+  __syncthreads();
+  if (t < 256) {
+    const int i = t / 16, j = t % 16, lane = 16 * (i / 4) + j, r = i % 4;
+    const int line = cols ? i : j, out = cols ? j : i;
+    if (line < nlines && out < width) {
+      float x = red[r * 64 + lane];
+#pragma unroll
+      for (int q = 1; q < W; ++q) x += red[(q * 4 + r) * 64 + lane];
+      const int row = cols ? first + line : lo + out, col = cols ? lo + out : first + line;
+      float* c = p.C + (long long)row * p.ldc + col;
+      *c = p.beta == 0.0f ? p.alpha * x : fmaf(p.alpha, x, p.beta * *c);
+    }
+  }
+}
+
 // Tile (bm, bn) of MFMA workgroup `bid`: XCD-contiguous, GROUP_M-row-major order.
 template <int GROUP_M>
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& bm, int& bn) {
@@ -671,8 +724,8 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // MIN_BLOCKS workgroups must fit on one CU at once (a register budget for the compiler).
 // EDGE_MIN: 0, the tiles cover [0, Mf) x [0, Nf) with Mf, Nf multiples of BM, BN and the
 // strips past them are scalar edge tiles; otherwise a strip at least EDGE_MIN rows
-// (columns) wide is covered by guarded MFMA tiles of the same grid and only a thinner one
-// goes to the scalar edge tiles (EDGE_MIN = 1: every partial tile is an MFMA tile).
+// (columns) wide is covered by guarded MFMA tiles of the same grid and a thinner one runs
+// as thin strips (EDGE_MIN = 1: every partial tile is an MFMA tile).
 // PF: the tiles run mfma_tile_pf (BK = 16, KS = 1) instead of mfma_tile.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
           int EDGE_MIN, bool STREAM_K, bool VEC, bool PF>
@@ -682,8 +735,10 @@ void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   p = batch_entry(p);
   constexpr int kGroups = Cfg::kThreads / 256;
-  constexpr bool kEdges = EDGE_MIN != 1;  // scalar edge tiles may exist
-  constexpr int kEdgeFloats = kEdges ? kGroups * EdgeTile::kLdsFloats : 0;  // >= its reduction floats
+  constexpr bool kEdges = EDGE_MIN == 0, kThin = EDGE_MIN > 1;  // scalar edge tiles / thin strips may exist
+  static_assert(EDGE_MIN <= kThinMax, "thin strips are at most kThinMax wide");
+  constexpr int kEdgeFloats = kEdges ? kGroups * EdgeTile::kLdsFloats  // >= its reduction floats
+                                     : kThin ? Cfg::kThreads / 64 * 4 * 64 : 0;
   constexpr int kFloats = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
   static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
@@ -746,6 +801,16 @@ void mfma_kernel(Problem p, TileMap map) {
     }
     edge_tile<kGroups, TA, TB, VEC>(p, m0, n0, smem);
   }
+  if constexpr (kThin) {
+    const int n_right = map.right_m;  // right strip: columns [Nf, N) of rows [0, Mf)
+    if (e < n_right) {
+      const int first = e * kThinMax;
+      thin_strip<Cfg::kThreads, TA, TB>(p, true, first, min(kThinMax, map.Mf - first), map.Nf, p.N - map.Nf, smem);
+    } else {  // bottom strip: rows [Mf, M) of columns [0, N)
+      const int first = (e - n_right) * kThinMax;
+      thin_strip<Cfg::kThreads, TA, TB>(p, false, first, min(kThinMax, p.N - first), map.Mf, p.M - map.Mf, smem);
+    }
+  }
 }
 
 // Stream-K fix-up: one workgroup per stream-K tile that was split between ranges; adds
@@ -795,19 +860,29 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   map.dp_tiles = map.sk_wgs = 0;
   map.ws = nullptr;
   // extent of the MFMA tiles: rows [0, Mf), columns [0, Nf) (mfma_extent, tile_plan.h uses
-  // the same rule); the strips past it are scalar edge tiles
+  // the same rule); the strips past it (columns [Nf, N) of rows [0, Mf), then rows [Mf, M)
+  // of every column) are scalar edge tiles or thin strips
   map.Mf = mfma_extent(p.M, BM, EDGE_MIN);
   map.Nf = mfma_extent(p.N, BN, EDGE_MIN);
   map.tiles_m = (map.Mf + BM - 1) / BM;
   map.tiles_n = (map.Nf + BN - 1) / BN;
-  if (map.tiles_m == 0 || map.tiles_n == 0) {  // no MFMA tile: everything is edge
+  if (map.tiles_m == 0 || map.tiles_n == 0) {  // no MFMA tile
     map.tiles_m = map.tiles_n = 0;
-    map.Mf = map.Nf = 0;
+    // scalar edge tiles: everything is the bottom strip; thin strips: M or N is thinner
+    // than EDGE_MIN and the strips as defined cover the matrix
+    if (EDGE_MIN <= 1) map.Mf = map.Nf = 0;
   }
-  map.right_m = (map.Nf < p.N) ? (map.Mf + kEdge - 1) / kEdge : 0;
-  map.right_n = (map.Nf < p.N) ? (p.N - map.Nf + kEdge - 1) / kEdge : 0;
-  map.bottom_m = (p.M - map.Mf + kEdge - 1) / kEdge;
-  map.bottom_n = map.bottom_m > 0 ? (p.N + kEdge - 1) / kEdge : 0;
+  if constexpr (EDGE_MIN > 1) {  // thin strips, in workgroups of kThinMax lines
+    map.right_m = (map.Nf < p.N) ? (map.Mf + kThinMax - 1) / kThinMax : 0;
+    map.right_n = map.right_m > 0 ? 1 : 0;
+    map.bottom_n = (map.Mf < p.M) ? (p.N + kThinMax - 1) / kThinMax : 0;
+    map.bottom_m = map.bottom_n > 0 ? 1 : 0;
+  } else {
+    map.right_m = (map.Nf < p.N) ? (map.Mf + kEdge - 1) / kEdge : 0;
+    map.right_n = (map.Nf < p.N) ? (p.N - map.Nf + kEdge - 1) / kEdge : 0;
+    map.bottom_m = (p.M - map.Mf + kEdge - 1) / kEdge;
+    map.bottom_n = map.bottom_m > 0 ? (p.N + kEdge - 1) / kEdge : 0;
+  }
   const long long nmfma = (long long)map.tiles_m * map.tiles_n;
   const long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
   const dim3 block(WM * WN * KS * 64);
@@ -856,7 +931,8 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
 //        256 threads; four workgroups per CU.
 // Partial tiles (mfma_edge_min): guarded MFMA tiles of the same grid in the 128, 64 and
-// 32 configurations, the scalar edge-tile path in the 256 configuration.
+// 32 configurations, except strips thinner than 16 in the 128 and 64 configurations
+// (thin strips); the scalar edge-tile path in the 256 configuration.
 // ws: stream-K workspace (kStreamKBytes) for the 256 configuration, or nullptr.
 template <bool TA, bool TB>
 hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr) {

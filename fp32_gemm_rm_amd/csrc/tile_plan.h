@@ -21,10 +21,14 @@ struct TileCost {
 };
 constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0}, {128, 62.0, 59.5}, {64, 16.2, 17.2}, {32, 5.4, 4.95}};
 
-// MFMA tiles along one dimension of n: a partial strip counts as a tile row (column),
-// whether it runs as guarded MFMA tiles or, in the 256 configuration, as scalar edge
-// tiles (which take at least as long).
-inline long long modelled_tiles(int n, int side) { return (n + side - 1) / side; }
+// MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
+// counts as a tile row (column), and so does any strip of the 256 configuration (its
+// scalar edge tiles take at least as long); a thin strip, which runs beside the MFMA
+// tiles, does not.
+inline long long modelled_tiles(int n, int side) {
+  const int edge_min = mfma_edge_min(side) > 0 ? mfma_edge_min(side) : 1;
+  return (mfma_extent(n, side, edge_min) + side - 1) / side;
+}
 
 // Modelled microseconds; M, N, K, batch > 0.
 inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {

@@ -125,10 +125,12 @@ def test_ragged_random_bound(oracle, variant, orient):
     print(f"[transposed] ragged {orient} {variant} max err/bound {r:.3g}", flush=True)
 
 
-# Small shapes per forced MFMA tile configuration: several full tiles plus partial ones,
-# and (for 32) full tiles only.
+# Small shapes per forced MFMA tile configuration: several full tiles plus partial ones
+# (for 128 and 64 also strips thinner than 16, which run as thin strips), and (for 32)
+# full tiles only.
 TILE_SHAPES = [(256, 600, 520, 77), (256, 300, 270, 160), (128, 300, 290, 77), (128, 140, 290, 257),
-               (64, 200, 150, 77), (64, 130, 70, 450), (32, 100, 70, 77), (32, 96, 64, 77), (32, 40, 70, 449)]
+               (128, 143, 265, 77), (64, 200, 150, 77), (64, 130, 70, 450), (64, 199, 141, 450),
+               (32, 100, 70, 77), (32, 96, 64, 77), (32, 40, 70, 449)]
 
 
 @pytest.mark.parametrize("orient", ["nt", "tn", "tt"])
@@ -158,7 +160,7 @@ def test_tile_configs_integer_exact(oracle, tiles, M, N, K, orient):
         (2048, 2048, 300),   # 128 x 128 tiles
         (4196, 4132, 77),    # 64 x 64 tiles plus edge strips, ragged K
         (4096, 4096, 17),    # 256 x 256 tiles, K just past one K-tile
-        (1000, 1030, 99),    # 32 x 32 tiles, partial ones on MFMA
+        (1000, 1030, 99),    # 64 x 64 tiles, guarded partial rows, thin column strip
     ],
 )
 def test_default_path_integer_exact(oracle, M, N, K, orient):
