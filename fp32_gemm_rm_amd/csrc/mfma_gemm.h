@@ -27,14 +27,14 @@
 // MFMA latencies.
 //
 // Pipelines (one barrier per K-tile, two LDS stages):
-//   mfma_tile (64 and 32 configurations): the global loads of tile t+2 are issued as
-//     tile t's MFMAs start, into the second of two register sets, and tile t+1's
-//     registers are stored half-way through those MFMAs; fragments are read from LDS
-//     at the start of each k-group.
-//   mfma_tile_pf (256 and 128 configurations, one wavefront per SIMD and workgroup):
-//     fragments are read one K-tile ahead into a second register set, so no MFMA waits
-//     for LDS; the global loads, LDS stores and fragment reads are interleaved one per
-//     MFMA.
+//   mfma_tile (32 configuration): the global loads of tile t+2 are issued as tile t's
+//     MFMAs start, into the second of two register sets, and tile t+1's registers are
+//     stored half-way through those MFMAs; fragments are read from LDS at the start of
+//     each k-group.
+//   mfma_tile_pf (256, 128 and 64 configurations, one 16-deep k-group per wavefront and
+//     K-tile): fragments are read one K-tile ahead into a second register set, so no
+//     MFMA waits for LDS; the global loads (one or two K-tiles ahead of their LDS
+//     stores), LDS stores and fragment reads are interleaved with the MFMAs.
 // LDS layout:
 //   A tile, BM rows of BK floats (BK/4 16-byte chunks), no padding.  For
 //     BK = 16, chunk c of row r is stored at chunk position c ^ ((r/4) % 4).  On
@@ -310,6 +310,64 @@ __device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM
   }
 }
 
+// The end of a tile: with no K split, store_acc; with KS > 1 the KS wavefronts of one
+// output block pass their partial sums through LDS (free after the K loop's last
+// barrier); then each of them finishes 1/KS of the block's accumulator registers,
+// adding the partials in the fixed order 0, 1, ..., KS-1, so that the epilogue's C
+// traffic is spread over all wavefronts.
+template <int BM, int BN, int WM, int WN, int KS, int FM, int FN, int GUARD>
+__device__ __forceinline__ void finish_acc(const Problem& p, const v16f (&acc)[FM][FN], float* smem, int m0, int n0,
+                                           float* part) {
+  const int w = threadIdx.x / 64, l = threadIdx.x % 64;
+  const int lr = l % 32, lh = l / 32;
+  // K-group and spatial position of this wavefront (compile-time zero K-group without a
+  // K split, which keeps the fragment-read addresses foldable)
+  const int ks = KS == 1 ? 0 : w / (WM * WN), sp = KS == 1 ? w : w % (WM * WN);
+  const int wm0 = (sp / WN) * (BM / WM), wn0 = (sp % WN) * (BN / WN);
+  if constexpr (KS == 1) {
+    store_acc<BM, BN, FM, FN, GUARD>(p, acc, m0, n0, wm0, wn0, lr, lh, part);
+  } else {
+    // register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its 32 x 32 block
+    constexpr int kSlots = FM * FN * 16;      // accumulator registers per lane
+    constexpr int kPart = kSlots * 64;        // floats per wavefront
+    constexpr int kStride = WM * WN * kPart;  // between the partials of consecutive K-groups
+    static_assert(kSlots % KS == 0, "registers split evenly over the K-groups");
+    float* mine = smem + (ks * (WM * WN) + sp) * kPart + l;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+    __syncthreads();
+    const float* sums = smem + sp * kPart + l;
+    constexpr int kMine = kSlots / KS;
+    float x[kMine];
+#pragma unroll
+    for (int u = 0; u < kMine; ++u) {
+      const int s = ks * kMine + u;  // register (i, j, r) = (s / (16 FN), (s / 16) % FN, s % 16)
+      x[u] = sums[s * 64];
+#pragma unroll
+      for (int q = 1; q < KS; ++q) x[u] += sums[q * kStride + s * 64];
+    }
+    auto coord = [&](int u, int& row, int& col) {
+      const int s = ks * kMine + u, i = s / (FN * 16), j = (s / 16) % FN, r = s % 16;
+      row = m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+      col = n0 + wn0 + j * 32 + lr;
+    };
+    if (part != nullptr) {  // stream-K partial tile (full tiles only)
+#pragma unroll
+      for (int u = 0; u < kMine; ++u) {
+        int row, col;
+        coord(u, row, col);
+        part[(row - m0) * BN + (col - n0)] = x[u];
+      }
+      return;
+    }
+    finish_c<kMine, GUARD>(p, x, coord);
+  }
+}
+
 // K-tiles [kb, ke) of the BM x BN tile of C at (m0, n0).  part == nullptr: the range is
 // the whole K range and the result goes to C (alpha, beta); otherwise the raw sums go to
 // part, a BM x BN row-major block (a stream-K partial tile).  GUARD bit 0 (1): the tile
@@ -329,7 +387,9 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
   const int t = threadIdx.x;
   const int w = t / 64, l = t % 64;
   const int lr = l % 32, lh = l / 32;
-  const int ks = w / (WM * WN), sp = w % (WM * WN);  // K-group and spatial position of this wavefront
+  // K-group and spatial position of this wavefront (compile-time zero K-group without a
+  // K split, which keeps the fragment-read addresses foldable)
+  const int ks = KS == 1 ? 0 : w / (WM * WN), sp = KS == 1 ? w : w % (WM * WN);
   const int wm0 = (sp / WN) * (BM / WM), wn0 = (sp % WN) * (BN / WN);
 
   OpA opa;
@@ -429,76 +489,53 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
     if (kt + 1 < ke) step(Set1{}, kt + 1);
   }
 
-  // register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its 32 x 32 block
-  if constexpr (KS > 1) {
-    // The KS wavefronts of one output block pass their partial sums through LDS (free
-    // after the last barrier); then each of them finishes 1/KS of the block's
-    // accumulator registers, adding the partials in the fixed order 0, 1, ..., KS-1,
-    // so that the epilogue's C traffic is spread over all wavefronts.
-    constexpr int kSlots = FM * FN * 16;   // accumulator registers per lane
-    constexpr int kPart = kSlots * 64;     // floats per wavefront
-    constexpr int kStride = WM * WN * kPart;  // between the partials of consecutive K-groups
-    static_assert(kSlots % KS == 0, "registers split evenly over the K-groups");
-    float* mine = smem + (ks * (WM * WN) + sp) * kPart + l;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mine[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
-    __syncthreads();
-    const float* sums = smem + sp * kPart + l;
-    constexpr int kMine = kSlots / KS;
-    float x[kMine];
-#pragma unroll
-    for (int u = 0; u < kMine; ++u) {
-      const int s = ks * kMine + u;  // register (i, j, r) = (s / (16 FN), (s / 16) % FN, s % 16)
-      x[u] = sums[s * 64];
-#pragma unroll
-      for (int q = 1; q < KS; ++q) x[u] += sums[q * kStride + s * 64];
-    }
-    auto coord = [&](int u, int& row, int& col) {
-      const int s = ks * kMine + u, i = s / (FN * 16), j = (s / 16) % FN, r = s % 16;
-      row = m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-      col = n0 + wn0 + j * 32 + lr;
-    };
-    if (part != nullptr) {  // stream-K partial tile (full tiles only)
-#pragma unroll
-      for (int u = 0; u < kMine; ++u) {
-        int row, col;
-        coord(u, row, col);
-        part[(row - m0) * BN + (col - n0)] = x[u];
-      }
-      return;
-    }
-    finish_c<kMine, GUARD>(p, x, coord);
-    return;
-  }
+  finish_acc<BM, BN, WM, WN, KS, FM, FN, GUARD>(p, acc, smem, m0, n0, part);
+}
 
-  store_acc<BM, BN, FM, FN, GUARD>(p, acc, m0, n0, wm0, wn0, lr, lh, part);
+// Scheduling groups for one K-tile of mfma_tile_pf: each of its NM MFMAs is followed by
+// PER of its T memory instructions, in the order NW LDS writes, NL global loads, then
+// the LDS fragment reads (sched_group_barrier masks 0x008 MFMA, 0x200 LDS write, 0x020
+// global load, 0x100 LDS read).
+template <int O, int E, int NW, int NL>
+__device__ __forceinline__ void sched_mem_ops() {
+  if constexpr (O < E) {
+    __builtin_amdgcn_sched_group_barrier(O < NW ? 0x200 : O < NW + NL ? 0x020 : 0x100, 1, 0);
+    sched_mem_ops<O + 1, E, NW, NL>();
+  }
+}
+template <int I, int NM, int PER, int T, int NW, int NL>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (I < NM && I * PER < T) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    sched_mem_ops<I * PER, (I * PER + PER < T ? I * PER + PER : T), NW, NL>();
+    sched_interleave<I + 1, NM, PER, T, NW, NL>();
+  }
 }
 
 // K-tiles [kb, ke) of the BM x BN tile at (m0, n0), as mfma_tile, for configurations with
-// BK = 16, no K split and large wavefront tiles (one wavefront per SIMD).  The MFMA
-// fragments are read from LDS one K-tile ahead into a second register set, so that no
-// MFMA waits for an LDS read: with fragments read after the barrier, right before the
-// MFMAs that use them, the wavefronts lose 3-6% of the matrix-core cycles to LDS
-// latency (probe: 150-146 against 155 TFLOP/s with no LDS reads).
-//   During K-tile t (register set P = (t - kb) % 2, LDS stage P):
+// one 16-deep k-group per wavefront and K-tile (BK = 16 KS).  The MFMA fragments are read
+// from LDS one K-tile ahead into a second register set, so that no MFMA waits for an LDS
+// read: with fragments read after the barrier, right before the MFMAs that use them, the
+// wavefronts lose 3-6% of the matrix-core cycles to LDS latency (probe: 150-146 against
+// 155 TFLOP/s with no LDS reads), and more where a K-tile holds few MFMAs.
+//   During K-tile t (fragment set P = (t - kb) % 2, LDS stage P):
 //     - the fragments of tile t+1 are read from stage P^1 into set P^1;
-//     - the global registers (tile t+2, loaded during tile t-1) are stored to stage P,
-//       whose fragments were read before the previous barrier;
-//     - tile t+3 is loaded into the global registers;
+//     - the global registers of tile t+2 are stored to stage P, whose fragments were
+//       read before the previous barrier;
+//     - tile t+2+NSETS is loaded into global register set P % NSETS, the one just stored;
 //     - the MFMAs of tile t run on set P;
-//   and one barrier ends the K-tile.  A global load has one K-tile of MFMAs to arrive.
-template <int BM, int BN, int WM, int WN, bool TA, bool TB, bool VEC, int GUARD>
+//   and one barrier ends the K-tile.  A global load has NSETS K-tiles of MFMAs to
+//   arrive: one for the large tiles (whose K-tile is 32 or 128 MFMAs per wavefront and
+//   whose registers are spoken for), two for the K-split tiles (8 MFMAs per wavefront).
+template <int BM, int BN, int BK, int WM, int WN, int KS, int NSETS, bool TA, bool TB, bool VEC, int GUARD>
 __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                              float* part = nullptr) {
-  constexpr int BK = 16;
-  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, 1, TA, TB>;
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
   constexpr int FM = Cfg::FM, FN = Cfg::FN;
+  static_assert(Cfg::KG == 1, "one k-group per wavefront and K-tile");
+  static_assert(NSETS == 1 || NSETS == 2, "global register sets");
   constexpr bool GA = (GUARD & 1) != 0, GB = (GUARD & 2) != 0;  // A rows past M, B columns past N
   auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
   auto b_stage = [&](int s) { return smem + s * Cfg::kStageFloats + OpA::kStageFloats; };
@@ -506,7 +543,10 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   const int t = threadIdx.x;
   const int w = t / 64, l = t % 64;
   const int lr = l % 32, lh = l / 32;
-  const int wm0 = (w / WN) * (BM / WM), wn0 = (w % WN) * (BN / WN);
+  // K-group and spatial position of this wavefront (compile-time zero K-group without a
+  // K split, which keeps the fragment-read addresses foldable)
+  const int ks = KS == 1 ? 0 : w / (WM * WN), sp = KS == 1 ? w : w % (WM * WN);
+  const int wm0 = (sp / WN) * (BM / WM), wn0 = (sp % WN) * (BN / WN);
 
   OpA opa;
   OpB opb;
@@ -523,25 +563,27 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   float af[2][FM][8], bf[2][FN][8];
 
   const int nfull = p.K / BK;
-  auto load = [&](int kt) {
+  auto load = [&](auto set, int kt) {
+    constexpr int R = decltype(set)::value % NSETS;
     if (kt < nfull) {
-      opa.template load_full<VEC, GA, 0>(kt * BK);
-      opb.template load_full<VEC, GB, 0>(kt * BK);
+      opa.template load_full<VEC, GA, R>(kt * BK);
+      opb.template load_full<VEC, GB, R>(kt * BK);
     } else {
-      opa.template load_tail<VEC, GA, 0>(kt * BK, p.K - kt * BK);
-      opb.template load_tail<VEC, GB, 0>(kt * BK, p.K - kt * BK);
+      opa.template load_tail<VEC, GA, R>(kt * BK, p.K - kt * BK);
+      opb.template load_tail<VEC, GB, R>(kt * BK, p.K - kt * BK);
     }
   };
-  auto store = [&](int s) {
-    opa.template store<GA, 0>(a_stage(s));
-    opb.template store<GB, 0>(b_stage(s));
+  auto store = [&](auto set, int s) {
+    constexpr int R = decltype(set)::value % NSETS;
+    opa.template store<GA, R>(a_stage(s));
+    opb.template store<GB, R>(b_stage(s));
   };
   auto frags = [&](auto set, int s) {
     constexpr int S = decltype(set)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) OpA::read(a_stage(s), wm0 + i * 32 + lr, 0, lh, af[S][i]);
+    for (int i = 0; i < FM; ++i) OpA::read(a_stage(s), wm0 + i * 32 + lr, ks, lh, af[S][i]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) OpB::read(b_stage(s), wn0 + j * 32 + lr, 0, lh, bf[S][j]);
+    for (int j = 0; j < FN; ++j) OpB::read(b_stage(s), wn0 + j * 32 + lr, ks, lh, bf[S][j]);
   };
   auto mfmas = [&](auto set) {
     constexpr int S = decltype(set)::value;
@@ -555,62 +597,58 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   };
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
+  constexpr int D = 2 + NSETS;  // load distance in K-tiles, counted from the tile being multiplied
 
-  // prologue: stage 0 <- tile kb (read into set 0), stage 1 <- tile kb+1, registers <- tile kb+2
-  load(kb);
-  store(0);
-  if (kb + 1 < ke) load(kb + 1);
+  // prologue: stage 0 <- tile kb (read into fragment set 0), stage 1 <- tile kb+1, global
+  // registers <- tiles kb+2 .. kb+D-1
+  load(Set0{}, kb);
+  if constexpr (NSETS == 2)
+    if (kb + 1 < ke) load(Set1{}, kb + 1);
+  store(Set0{}, 0);
+  if constexpr (NSETS == 1) {
+    if (kb + 1 < ke) load(Set1{}, kb + 1);
+  } else {
+    if (kb + 2 < ke) load(Set0{}, kb + 2);
+  }
   __syncthreads();
   frags(Set0{}, 0);
-  if (kb + 1 < ke) store(1);
-  if (kb + 2 < ke) load(kb + 2);
+  if (kb + 1 < ke) store(Set1{}, 1);
+  if (kb + D - 1 < ke) load(std::integral_constant<int, D - 1>{}, kb + D - 1);
   __syncthreads();
 
   // Instruction order of a steady K-tile: the MFMAs start right after the barrier and
-  // each of the first ones is followed by one memory instruction (LDS stores, then
-  // global loads, then fragment reads), so that the single wavefront of each SIMD issues
-  // its memory traffic in the shadow of the MFMAs; nothing moves across the barrier (the
+  // each of the first ones is followed by its share of the memory instructions (LDS
+  // stores, then global loads, then fragment reads), so that the wavefronts issue their
+  // memory traffic in the shadow of the MFMAs; nothing moves across the barrier (the
   // compiler would otherwise hoist the barrier, and its wait on the fragment reads, above
   // the MFMAs).
   constexpr int kStores = OpA::LOADS + OpB::LOADS;
   constexpr int kFragReads = FM * (OpA::STRIDE == BK ? 2 : 8) + FN * (OpB::STRIDE == BK ? 2 : 8);
-  auto steady = [&](auto set, int kt) {  // tiles kt+1 .. kt+3 exist and kt+3 is full
+  constexpr int kMfmas = 8 * FM * FN, kMemOps = 2 * kStores + kFragReads;
+  constexpr int kPer = (kMemOps + kMfmas - 1) / kMfmas;
+  auto steady = [&](auto set, int kt) {  // tiles kt+1 .. kt+D exist and kt+D is full
     constexpr int P = decltype(set)::value;
     __builtin_amdgcn_sched_barrier(0);
-    store(P);
-    opa.template load_full<VEC, GA, 0>((kt + 3) * BK);
-    opb.template load_full<VEC, GB, 0>((kt + 3) * BK);
+    store(set, P);
+    opa.template load_full<VEC, GA, P % NSETS>((kt + D) * BK);
+    opb.template load_full<VEC, GB, P % NSETS>((kt + D) * BK);
     frags(std::integral_constant<int, P ^ 1>{}, P ^ 1);
     mfmas(set);
-#pragma unroll
-    for (int i = 0; i < kStores; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
-    }
-#pragma unroll
-    for (int i = 0; i < kStores; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
-    }
-#pragma unroll
-    for (int i = 0; i < kFragReads; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    }
+    sched_interleave<0, kMfmas, kPer, kMemOps, kStores, kStores>();
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   };
   auto step = [&](auto set, int kt) {
     constexpr int P = decltype(set)::value;
-    if (kt + 2 < ke) store(P);
-    if (kt + 3 < ke) load(kt + 3);
+    if (kt + 2 < ke) store(set, P);
+    if (kt + D < ke) load(set, kt + D);
     if (kt + 1 < ke) frags(std::integral_constant<int, P ^ 1>{}, P ^ 1);
     mfmas(set);
     __syncthreads();
   };
   int kt = kb;
   const int steady_end = min(ke, nfull);
-  for (; kt + 4 < steady_end; kt += 2) {  // tiles kt+3 and kt+4 are full and in range
+  for (; kt + D + 1 < steady_end; kt += 2) {  // tiles kt+D and kt+D+1 are full and in range
     steady(Set0{}, kt);
     steady(Set1{}, kt + 1);
   }
@@ -619,7 +657,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
     if (kt + 1 < ke) step(Set1{}, kt + 1);
   }
 
-  store_acc<BM, BN, FM, FN, GUARD>(p, acc, m0, n0, wm0, wn0, lr, lh, part);
+  finish_acc<BM, BN, WM, WN, KS, FM, FN, GUARD>(p, acc, smem, m0, n0, part);
 }
 
 // Scalar edge-tile path: one 32 x 32 register-blocked VALU tile per workgroup; the
@@ -682,15 +720,47 @@ __device__ __forceinline__ void thin_strip(const Problem& p, bool cols, int firs
   const int nx = cols ? nlines : width, ny = cols ? width : nlines;
   const int am = (cols ? first : lo) + min(i16, nx - 1), bn = (cols ? lo : first) + min(i16, ny - 1);
   const bool x_in = i16 < nx, y_in = i16 < ny;
+  // The slice runs in chunks of U MFMA steps whose loads are issued one chunk ahead (two
+  // register sets), so that a wavefront keeps 2U loads per lane in flight instead of
+  // waiting out the memory latency every few steps; U = 16 (64 loads, the most the
+  // memory counter tracks) for long slices, 4 for short ones, whose steps past the slice
+  // would otherwise dominate.  Those steps (the last chunks) load clamped addresses and
+  // contribute zeros.
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int k = k0; k < k1; k += 4) {
-    const int kx = k + kq, kcl = min(kx, p.K - 1);
-    const float av = TA ? p.A[(long long)kcl * p.lda + am] : p.A[(long long)am * p.lda + kcl];
-    const float bv = TB ? p.B[(long long)bn * p.ldb + kcl] : p.B[(long long)kcl * p.ldb + bn];
-    const bool kin = kx < k1;
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x_in && kin ? av : 0.f, y_in && kin ? bv : 0.f, acc, 0, 0, 0);
-  }
+  auto slice = [&](auto chunk) {
+    constexpr int U = decltype(chunk)::value;
+    float xv[2][U], yv[2][U];
+    auto fetch = [&](auto set, int kbase) {
+      constexpr int S = decltype(set)::value;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kx = kbase + 4 * u + kq, kcl = min(kx, p.K - 1);
+        const float av = TA ? p.A[(long long)kcl * p.lda + am] : p.A[(long long)am * p.lda + kcl];
+        const float bv = TB ? p.B[(long long)bn * p.ldb + kcl] : p.B[(long long)kcl * p.ldb + bn];
+        const bool kin = kx < k1;
+        xv[S][u] = x_in && kin ? av : 0.f;
+        yv[S][u] = y_in && kin ? bv : 0.f;
+      }
+    };
+    auto steps = [&](auto set) {
+      constexpr int S = decltype(set)::value;
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[S][u], yv[S][u], acc, 0, 0, 0);
+    };
+    using Set0 = std::integral_constant<int, 0>;
+    using Set1 = std::integral_constant<int, 1>;
+    fetch(Set0{}, k0);
+    for (int k = k0; k < k1; k += 8 * U) {
+      fetch(Set1{}, k + 4 * U);
+      steps(Set0{});
+      fetch(Set0{}, k + 8 * U);
+      steps(Set1{});
+    }
+  };
+  if (k1 - k0 >= 4 * 64)  // 64 steps or more
+    slice(std::integral_constant<int, 16>{});
+  else
+    slice(std::integral_constant<int, 4>{});
   float* red = smem;  // [wavefront][register][lane]
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[(wv * 4 + r) * 64 + l] = acc[r];
@@ -726,12 +796,12 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // strips past them are scalar edge tiles; otherwise a strip at least EDGE_MIN rows
 // (columns) wide is covered by guarded MFMA tiles of the same grid and a thinner one runs
 // as thin strips (EDGE_MIN = 1: every partial tile is an MFMA tile).
-// PF: the tiles run mfma_tile_pf (BK = 16, KS = 1) instead of mfma_tile.
+// PF: the tiles run mfma_tile_pf (one k-group per wavefront and K-tile) instead of mfma_tile.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
           int EDGE_MIN, bool STREAM_K, bool VEC, bool PF>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
-  static_assert(!PF || (BK == 16 && KS == 1), "fragment prefetch: one 16-deep k-group per K-tile");
+  static_assert(!PF || BK == 16 * KS, "fragment prefetch: one 16-deep k-group per wavefront and K-tile");
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   p = batch_entry(p);
   constexpr int kGroups = Cfg::kThreads / 256;
@@ -745,7 +815,7 @@ void mfma_kernel(Problem p, TileMap map) {
   auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
     constexpr int G = decltype(guard)::value;
     if constexpr (PF)
-      mfma_tile_pf<BM, BN, WM, WN, TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
+      mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM >= 256 ? 1 : 2), TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
     else
       mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
   };
@@ -944,8 +1014,8 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
         return launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true>(p, batch, stream);
       return launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, mfma_edge_min(128), true>(p, batch, stream);
     case 64:
-      if (p.M % 64 == 0 && p.N % 64 == 0) return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 3>(p, batch, stream);
-      return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 3, mfma_edge_min(64)>(p, batch, stream);
+      if (p.M % 64 == 0 && p.N % 64 == 0) return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true>(p, batch, stream);
+      return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, mfma_edge_min(64), true>(p, batch, stream);
     case 32:
       if (p.M % 32 == 0 && p.N % 32 == 0) return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4>(p, batch, stream);
       return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, mfma_edge_min(32)>(p, batch, stream);
