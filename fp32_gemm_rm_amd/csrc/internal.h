@@ -62,7 +62,7 @@ hipError_t launch_regblock(const Problem& p, int batch, hipStream_t stream);
 // MFMA tiles for the full BM x BN tiles plus bounds-checked register-blocked
 // tiles (the scalar edge-tile path) for the strips past them, in one launch; one
 // instantiation per operand orientation (p.ta, p.tb), dispatched by launch_mfma.
-// tiles: the tile configuration by its side (256, 128, 64 or 32; see tile_plan.h).
+// tiles: the tile configuration by its side (256, 192, 128, 64 or 32; see tile_plan.h).
 // ws: nullptr, or kStreamKBytes of device memory for stream-K (256 configuration, batch 1).
 hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
 hipError_t launch_mfma_nt(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
@@ -79,8 +79,8 @@ constexpr int kStreamKWgs = 256;
 constexpr long long kStreamKBytes = 2LL * kStreamKWgs * 256 * 256 * 4;
 // Partial MFMA tiles.  A strip of rows (columns) past the last full tile that is at least
 // mfma_edge_min(side) wide runs as guarded MFMA tiles of the same grid; a thinner one runs
-// as thin strips (128 and 64 configurations: 16, below which a strip would pay for a whole
-// tile row or column of MFMA work) or, in the 256 configuration (0: never MFMA), as
+// as thin strips (192, 128 and 64 configurations: 16, below which a strip would pay for a
+// whole tile row or column of MFMA work) or, in the 256 configuration (0: never MFMA), as
 // scalar edge tiles (its workgroups fill a CU's register file and a guarded tile there
 // costs a whole 256 x 256 tile; the cost model steers ragged shapes to the smaller
 // configurations).  The 32 configuration (1) covers every strip with MFMA tiles.

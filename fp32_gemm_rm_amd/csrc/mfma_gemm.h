@@ -31,8 +31,8 @@
 //     MFMAs start, into the second of two register sets, and tile t+1's registers are
 //     stored half-way through those MFMAs; fragments are read from LDS at the start of
 //     each k-group.
-//   mfma_tile_pf (256, 128 and 64 configurations, one 16-deep k-group per wavefront and
-//     K-tile): fragments are read one K-tile ahead into a second register set, so no
+//   mfma_tile_pf (256, 192, 128 and 64 configurations, one 16-deep k-group per wavefront
+//     and K-tile): fragments are read one K-tile ahead into a second register set, so no
 //     MFMA waits for LDS; the global loads (one or two K-tiles ahead of their LDS
 //     stores), LDS stores and fragment reads are interleaved with the MFMAs.
 // LDS layout:
@@ -56,7 +56,7 @@
 // the run walks GROUP_M tile-rows at a time, so the A and B panels of the
 // tiles in flight on one XCD share its L2.
 //
-// Partial tiles.  In the 128, 64 and 32 configurations the tile grid covers the whole
+// Partial tiles.  In the 192, 128, 64 and 32 configurations the tile grid covers the whole
 // matrix and the tiles that reach past M or N are guarded MFMA tiles, dispatched on
 // which side they cross (past M, past N, or both), so that a tile past M only loads B
 // as a full tile does.  In the 256 configuration the MFMA tiles cover [0, Mf) x [0, Nf)
@@ -144,12 +144,13 @@ struct Operand {
     }
   }
   // full K-tile starting at k0.  GUARD: the slice may reach past the matrix (lim < R).
-  // A row past the matrix (rows along k) is loaded unconditionally from the last row and
-  // store<true> writes zeros in its place: a load under a branch makes the compiler wait
-  // for it where the branches join, which would undo the prefetch of the guarded tiles of
-  // a partial tile row.  Along r (rows along m or n) a tile that is full there loads as an
-  // unguarded one; in the one partial tile column a float4 that is only partly inside is
-  // read element by element, with zeros past the matrix.
+  // Every load is unconditional: a load under a branch makes the compiler wait for it
+  // where the branches join, which would undo the prefetch of the guarded tiles.  A row
+  // of A or B^T past the matrix (rows along k) is loaded from the last row and store<true>
+  // writes zeros in its place; along r (rows along m or n: B, or A^T) each element past
+  // the matrix is loaded from the last column.  Values past M or N only ever reach rows or
+  // columns of the product that are not stored (output (i, j) takes row i of op(A) and
+  // column j of op(B) alone), so the clamped loads only have to stay inside the matrix.
   template <bool VEC, bool GUARD, int SET = 0>
   __device__ __forceinline__ void load_full(int k0) {
 #pragma unroll
@@ -157,12 +158,18 @@ struct Operand {
       if (KROWS) {
         const int r = (!GUARD || row[i] < lim) ? row[i] : lim - 1;
         reg[SET][i] = load4<VEC>(base + (long long)r * ld + k0 + 4 * col[i], 4);
+      } else if (!GUARD) {
+        reg[SET][i] = load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
       } else {
-        const float* q = base + (long long)(k0 + row[i]) * ld + col[i];
-        reg[SET][i] = load4<VEC>(q, (!GUARD || lim == R) ? 4 : lim - col[i]);
+        const float* q = base + (long long)(k0 + row[i]) * ld;
+        reg[SET][i] = make_float4(q[min(col[i], lim - 1)], q[min(col[i] + 1, lim - 1)], q[min(col[i] + 2, lim - 1)],
+                                  q[min(col[i] + 3, lim - 1)]);
       }
     }
   }
+  // global load instructions of one load_full
+  template <bool VEC, bool GUARD>
+  static constexpr int kLoadInstrs = (VEC && (KROWS || !GUARD)) ? LOADS : 4 * LOADS;
   // last K-tile: kl = K - k0 < BK valid k; zeros past K (and past the matrix, GUARD)
   template <bool VEC, bool GUARD, int SET = 0>
   __device__ __forceinline__ void load_tail(int k0, int kl) {
@@ -525,8 +532,9 @@ __device__ __forceinline__ void sched_interleave() {
 //     - tile t+2+NSETS is loaded into global register set P % NSETS, the one just stored;
 //     - the MFMAs of tile t run on set P;
 //   and one barrier ends the K-tile.  A global load has NSETS K-tiles of MFMAs to
-//   arrive: one for the large tiles (whose K-tile is 32 or 128 MFMAs per wavefront and
-//   whose registers are spoken for), two for the K-split tiles (8 MFMAs per wavefront).
+//   arrive: one in the 256 and 192 configurations (128 and 72 MFMAs per wavefront and
+//   K-tile; the 256 configuration has no registers to spare, and a second set measured
+//   no better in the 192 one), two in the 128 and 64 configurations (32 and 8).
 template <int BM, int BN, int BK, int WM, int WN, int KS, int NSETS, bool TA, bool TB, bool VEC, int GUARD>
 __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                              float* part = nullptr) {
@@ -623,8 +631,9 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   // compiler would otherwise hoist the barrier, and its wait on the fragment reads, above
   // the MFMAs).
   constexpr int kStores = OpA::LOADS + OpB::LOADS;
+  constexpr int kLoads = OpA::template kLoadInstrs<VEC, GA> + OpB::template kLoadInstrs<VEC, GB>;
   constexpr int kFragReads = FM * (OpA::STRIDE == BK ? 2 : 8) + FN * (OpB::STRIDE == BK ? 2 : 8);
-  constexpr int kMfmas = 8 * FM * FN, kMemOps = 2 * kStores + kFragReads;
+  constexpr int kMfmas = 8 * FM * FN, kMemOps = kStores + kLoads + kFragReads;
   constexpr int kPer = (kMemOps + kMfmas - 1) / kMfmas;
   auto steady = [&](auto set, int kt) {  // tiles kt+1 .. kt+D exist and kt+D is full
     constexpr int P = decltype(set)::value;
@@ -634,7 +643,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
     opb.template load_full<VEC, GB, P % NSETS>((kt + D) * BK);
     frags(std::integral_constant<int, P ^ 1>{}, P ^ 1);
     mfmas(set);
-    sched_interleave<0, kMfmas, kPer, kMemOps, kStores, kStores>();
+    sched_interleave<0, kMfmas, kPer, kMemOps, kStores, kLoads>();
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   };
@@ -815,7 +824,7 @@ void mfma_kernel(Problem p, TileMap map) {
   auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
     constexpr int G = decltype(guard)::value;
     if constexpr (PF)
-      mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM >= 256 ? 1 : 2), TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
+      mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM >= 192 ? 1 : 2), TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
     else
       mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
   };
@@ -990,25 +999,32 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   return hipGetLastError();
 }
 
-// The tile configurations (tile_plan.h), by tile side.
+// The tile configurations (tile_plan.h), by tile side.  All but the 32 configuration run
+// mfma_tile_pf (fragments read one K-tile ahead).
 //   256: 256 x 256 tiles, 2 x 2 wavefronts of 128 x 128 (one per SIMD, 256 accumulator
-//        registers each), BK 16, fragments read one K-tile ahead (mfma_tile_pf): one
-//        workgroup per CU.
-//   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64, BK 16, fragments read one K-tile
-//        ahead (mfma_tile_pf); two workgroups per CU (three spill registers).
-//   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32; three
-//        workgroups per CU (a 4-way split with BK 64 is 2-7% slower).
+//        registers each), BK 16, one global register set: one workgroup per CU.
+//   192: 192 x 192 tiles, 2 x 2 wavefronts of 96 x 96 (144 accumulator registers), BK 16,
+//        one global register set: one workgroup per CU.  Its tile counts fill whole waves
+//        where the others do not (3072^3: 256 tiles).
+//   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64, BK 16, two global register sets;
+//        two workgroups per CU (three spill registers).
+//   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32, two
+//        global register sets; two workgroups per CU.
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
-//        256 threads; four workgroups per CU.
-// Partial tiles (mfma_edge_min): guarded MFMA tiles of the same grid in the 128, 64 and
-// 32 configurations, except strips thinner than 16 in the 128 and 64 configurations
-// (thin strips); the scalar edge-tile path in the 256 configuration.
+//        256 threads, mfma_tile; four workgroups per CU.
+// Partial tiles (mfma_edge_min): guarded MFMA tiles of the same grid in the 192, 128, 64
+// and 32 configurations, except strips thinner than 16 in the 192, 128 and 64
+// configurations (thin strips); the scalar edge-tile path in the 256 configuration.
 // ws: stream-K workspace (kStreamKBytes) for the 256 configuration, or nullptr.
 template <bool TA, bool TB>
 hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr) {
   switch (tiles) {
     case 256:
       return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(256), true>(p, batch, stream, ws);
+    case 192:
+      if (p.M % 192 == 0 && p.N % 192 == 0)
+        return launch_cfg<192, 192, 16, 2, 2, 1, TA, TB, 8, 1, 0, true>(p, batch, stream);
+      return launch_cfg<192, 192, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(192), true>(p, batch, stream);
     case 128:
       if (p.M % 128 == 0 && p.N % 128 == 0)
         return launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true>(p, batch, stream);

@@ -76,7 +76,7 @@ int check(const Call& c, const Positions& pos) {
   if (pos.batch && c.batch < 0) return -pos.batch;
   if (pos.ws && c.ws == nullptr && c.ws_bytes > 0) return -pos.ws;
   if (pos.ws_bytes && c.ws_bytes < 0) return -pos.ws_bytes;
-  if (pos.variant && (c.variant < SGEMM_RM_VARIANT_AUTO || c.variant > SGEMM_RM_VARIANT_MFMA_T32)) return -pos.variant;
+  if (pos.variant && (c.variant < SGEMM_RM_VARIANT_AUTO || c.variant > SGEMM_RM_VARIANT_MFMA_T192)) return -pos.variant;
   return 0;
 }
 
@@ -103,6 +103,9 @@ int launch(Problem p, int batch, hipStream_t stream, int variant, float* ws) {
           break;
         case SGEMM_RM_VARIANT_MFMA_T256:  // with a workspace: stream-K wherever the tiles leave a partial wave
           err = sgemm_impl::launch_mfma(p, chunk, stream, 256, ws);
+          break;
+        case SGEMM_RM_VARIANT_MFMA_T192:
+          err = sgemm_impl::launch_mfma(p, chunk, stream, 192);
           break;
         case SGEMM_RM_VARIANT_MFMA_T128:
           err = sgemm_impl::launch_mfma(p, chunk, stream, 128);

@@ -19,10 +19,11 @@
 namespace sgemm_impl {
 
 struct TileCost {
-  int side;  // tile side: 256, 128, 64 or 32
+  int side;  // tile side: 256, 192, 128, 64 or 32
   double u1, u2;
 };
-constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0}, {128, 60.5, 59.5}, {64, 15.3, 16.0}, {32, 5.4, 4.95}};
+constexpr TileCost kTileCosts[] = {
+    {256, 231.0, 231.0}, {192, 134.0, 133.3}, {128, 60.5, 59.5}, {64, 15.3, 16.0}, {32, 5.4, 4.95}};
 
 // MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
 // counts as a tile row (column), and so does any strip of the 256 configuration (its

@@ -235,6 +235,7 @@ def test_single_hip_runtime():
 # and full tiles plus partial ones (scalar edge tiles, or guarded MFMA tiles for 32).
 TILE_SHAPES = {
     256: [(4096, 4096, 17), (4000, 3900, 77)],
+    192: [(3072, 3072, 300), (2000, 1950, 129)],
     128: [(2048, 2048, 300), (2000, 1950, 129)],
     64: [(1024, 1024, 129), (1000, 990, 129)],
     32: [(512, 512, 300), (1000, 1030, 99)],
@@ -262,13 +263,15 @@ def test_tile_configs_integer_exact(oracle, tiles, M, N, K):
         check_padding(out, C, M, N, ldc)
 
 
-# Partial tiles of the 128 and 64 configurations: a remainder of 16 or more rows (columns)
+# Partial tiles of the 192, 128 and 64 configurations: a remainder of 16 or more rows (columns)
 # runs as guarded MFMA tiles (guarded along M only, along N only, or both: separate code
 # paths), a thinner one as thin strips.  Shapes put remainders on both sides of 16, in
 # either dimension, and cover matrices smaller than one tile or thinner than 16; the
 # long-K cases give every wavefront of a thin strip 64 or more MFMA steps (its long-slice
 # form).
 PARTIAL_SHAPES = {
+    192: [(2 * 192 + 32, 192 + 31, 70), (192 + 15, 2 * 192 + 16, 45), (3 * 192 + 5, 192 + 3, 1100), (100, 300, 70),
+          (12, 300, 45)],
     128: [(3 * 128 + 32, 2 * 128 + 31, 70), (3 * 128 + 31, 2 * 128 + 32, 70), (128 + 16, 128 + 15, 70),
           (128 + 15, 128 + 16, 33), (2 * 128 + 7, 3 * 128 + 1, 70), (100, 300, 70), (20, 300, 45), (300, 20, 45),
           (12, 300, 45), (300, 12, 45), (9, 7, 45), (2 * 128 + 5, 128 + 3, 1100)],
@@ -297,7 +300,7 @@ def test_partial_tile_forms_integer_exact(oracle, tiles, M, N, K):
     check_padding(out, C, M, N, ldc)
 
 
-@pytest.mark.parametrize("tiles", [256, 128, 64, 32])
+@pytest.mark.parametrize("tiles", [256, 192, 128, 64, 32])
 def test_tile_configs_random_bound(oracle, tiles):
     """Each forced tile configuration on the ragged 1000 x 1030 x 999 workload (alpha 1.5,
     beta -0.5, padded leading dimensions), within the bound."""
@@ -340,10 +343,10 @@ def test_offsets_past_2_pow_31(oracle, variant, N):
 
 # K-tile depth of each tile configuration (the K loop runs a steady state over pairs of
 # full K-tiles and a general tail; these K values put its boundaries in every place).
-TILE_BK = {256: 16, 128: 16, 64: 32, 32: 64}
+TILE_BK = {256: 16, 192: 16, 128: 16, 64: 32, 32: 64}
 
 
-@pytest.mark.parametrize("tiles", [256, 128, 64, 32])
+@pytest.mark.parametrize("tiles", [256, 192, 128, 64, 32])
 def test_k_loop_boundaries_integer_exact(oracle, tiles):
     """K from 1 to nine K-tiles (full, ragged, odd and even tile counts) for each forced
     tile configuration, on a shape with full and partial tiles: bit-exact."""

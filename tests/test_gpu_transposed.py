@@ -126,9 +126,10 @@ def test_ragged_random_bound(oracle, variant, orient):
 
 
 # Small shapes per forced MFMA tile configuration: several full tiles plus partial ones
-# (for 128 and 64 also strips thinner than 16, which run as thin strips), and (for 32)
+# (for 192, 128 and 64 also strips thinner than 16, which run as thin strips), and (for 32)
 # full tiles only.
-TILE_SHAPES = [(256, 600, 520, 77), (256, 300, 270, 160), (128, 300, 290, 77), (128, 140, 290, 257),
+TILE_SHAPES = [(256, 600, 520, 77), (256, 300, 270, 160), (192, 400, 390, 77), (192, 3 * 192 + 7, 232, 300),
+               (128, 300, 290, 77), (128, 140, 290, 257),
                (128, 143, 265, 77), (64, 200, 150, 77), (64, 130, 70, 450), (64, 199, 141, 450), (64, 67, 73, 2100),
                (32, 100, 70, 77), (32, 96, 64, 77), (32, 40, 70, 449)]
 
