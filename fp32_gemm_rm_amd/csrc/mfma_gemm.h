@@ -146,11 +146,11 @@ struct Operand {
   // full K-tile starting at k0.  GUARD: the slice may reach past the matrix (lim < R).
   // Every load is unconditional: a load under a branch makes the compiler wait for it
   // where the branches join, which would undo the prefetch of the guarded tiles.  A row
-  // of A or B^T past the matrix (rows along k) is loaded from the last row and store<true>
-  // writes zeros in its place; along r (rows along m or n: B, or A^T) each element past
-  // the matrix is loaded from the last column.  Values past M or N only ever reach rows or
-  // columns of the product that are not stored (output (i, j) takes row i of op(A) and
-  // column j of op(B) alone), so the clamped loads only have to stay inside the matrix.
+  // of A or B^T past the matrix (rows along k) is loaded from the last row; along r (rows
+  // along m or n: B, or A^T) each element past the matrix is loaded from the last column.
+  // Values past M or N only ever reach rows or columns of the product that are not stored
+  // (output (i, j) takes row i of op(A) and column j of op(B) alone), so the clamped loads
+  // only have to stay inside the matrix, and they are stored to LDS as loaded.
   template <bool VEC, bool GUARD, int SET = 0>
   __device__ __forceinline__ void load_full(int k0) {
 #pragma unroll
@@ -186,15 +186,13 @@ struct Operand {
                             : load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
     }
   }
-  // registers of set SET to an LDS stage; GUARD: zeros for rows past the matrix
-  template <bool GUARD, int SET = 0>
+  // registers of set SET to an LDS stage
+  template <int SET = 0>
   __device__ __forceinline__ void store(float* stage) const {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      float4 v = reg[SET][i];
-      if (GUARD && KROWS && row[i] >= lim) v = make_float4(0.f, 0.f, 0.f, 0.f);
-      *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : row[i] * STRIDE + col[i])) = v;
-    }
+    for (int i = 0; i < LOADS; ++i)
+      *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : row[i] * STRIDE + col[i])) =
+          reg[SET][i];
   }
   // out[e] = X(rr, 16g + 8lh + e), e = 0..7: this lane's values for the 8 MFMA steps of k-group g
   __device__ __forceinline__ static void read(const float* stage, int rr, int g, int lh, float (&out)[8]) {
@@ -459,8 +457,8 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
   // only the older register set (a wait on the newest loads would undo the prefetch);
   // the last steps run the general form.
   load(Set0{}, kb);
-  opa.template store<GA, 0>(a_stage(0));
-  opb.template store<GB, 0>(b_stage(0));
+  opa.template store<0>(a_stage(0));
+  opb.template store<0>(b_stage(0));
   if (kb + 1 < ke) load(Set1{}, kb + 1);
   __syncthreads();
   auto steady = [&](auto set, int kt) {  // set = (kt - kb) % 2, also the LDS stage of tile kt
@@ -469,8 +467,8 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
     opb.template load_full<VEC, GB, P>((kt + 2) * BK);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
     multiply(P, [&] {
-      opa.template store<GA, P ^ 1>(a_stage(P ^ 1));
-      opb.template store<GB, P ^ 1>(b_stage(P ^ 1));
+      opa.template store<P ^ 1>(a_stage(P ^ 1));
+      opb.template store<P ^ 1>(b_stage(P ^ 1));
     });
     __syncthreads();
   };
@@ -479,8 +477,8 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
     if (kt + 2 < ke) load(set, kt + 2);
     multiply(P, [&] {
       if (kt + 1 < ke) {
-        opa.template store<GA, P ^ 1>(a_stage(P ^ 1));
-        opb.template store<GB, P ^ 1>(b_stage(P ^ 1));
+        opa.template store<P ^ 1>(a_stage(P ^ 1));
+        opb.template store<P ^ 1>(b_stage(P ^ 1));
       }
     });
     __syncthreads();
@@ -583,8 +581,8 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   };
   auto store = [&](auto set, int s) {
     constexpr int R = decltype(set)::value % NSETS;
-    opa.template store<GA, R>(a_stage(s));
-    opb.template store<GB, R>(b_stage(s));
+    opa.template store<R>(a_stage(s));
+    opb.template store<R>(b_stage(s));
   };
   auto frags = [&](auto set, int s) {
     constexpr int S = decltype(set)::value;
