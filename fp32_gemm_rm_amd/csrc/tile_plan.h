@@ -26,37 +26,39 @@ constexpr TileCost kTileCosts[] = {
     {256, 231.0, 231.0}, {192, 134.0, 133.3}, {128, 60.5, 59.5}, {64, 15.3, 16.0}, {32, 5.4, 4.95}};
 
 // MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
-// counts as a tile row (column), and so does any strip of the 256 configuration (its
-// scalar edge tiles take at least as long); a thin strip, which runs beside the MFMA
-// tiles, does not.
+// counts as a tile row (column); a thin strip, which runs beside the MFMA tiles, does not.
 inline long long modelled_tiles(int n, int side) {
-  const int edge_min = mfma_edge_min(side) > 0 ? mfma_edge_min(side) : 1;
-  return (mfma_extent(n, side, edge_min) + side - 1) / side;
+  return (mfma_extent(n, side, mfma_edge_min(side)) + side - 1) / side;
 }
 
-// Modelled microseconds; M, N, K, batch > 0.
+// Modelled microseconds; M, N, K, batch > 0.  The 256 configuration is a candidate only
+// where its tiles cover the matrix: the strips past them run as scalar edge tiles, which
+// cannot share a CU with its workgroups and are latency-bound chains of K-steps (4000^3:
+// 1434 us, against 949 us on 128 x 128 tiles; 4090^3: 1887 against 1021 us).
 inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
+  if (mfma_edge_min(c.side) == 0 && (M % c.side != 0 || N % c.side != 0)) return 1e30;
   const long long tiles = modelled_tiles(M, c.side) * modelled_tiles(N, c.side) * batch;
   const long long layers = (tiles + 255) / 256;
   return (double)layers * (layers > 1 ? c.u2 : c.u1) * (double)K / 1024.0;
 }
 
-// Stream-K (256 configuration, batch 1, with a workspace): the K-tiles of the last
-// partial wave of T full tiles and of one full wave before it are shared evenly by 256
-// workgroups, so the MFMA time is T/256 layers instead of ceil(T/256).  Overheads: the
-// fix-up pass (up to 2 x 256 partial tiles of 256 KB written and read back at about
-// 5 TB/s, plus a launch) and each workgroup's two partial pieces (pipeline fill and
-// partial-tile stores), about 15 us.  With fewer than 256 tiles every tile is split and
-// the pieces' overheads dominate (3072^3: 511 us against 473 us one tile per
-// workgroup), so stream-K is a candidate only past one full wave.  The stream-K kernel
-// is a separate instantiation of the 256 configuration that spills registers (its range
-// bookkeeping around the tile code), about 9% slower per K-tile than the one-tile kernel:
+// Stream-K (256 configuration, batch 1, with a workspace, full tiles only): the K-tiles of
+// the last partial wave of T full tiles and of one full wave before it are shared evenly
+// by 256 workgroups, so the MFMA time is T/256 layers instead of ceil(T/256).  Overheads:
+// the fix-up pass (up to 2 x 256 partial tiles of 256 KB written and read back at about
+// 5 TB/s, plus a launch) and each workgroup's two partial pieces (pipeline fill and partial-
+// tile stores), about 15 us.  With fewer than 256 tiles every tile is split and the
+// pieces' overheads dominate (3072^3: 511 us against 473 us one tile per workgroup), so
+// stream-K is a candidate only past one full wave.  The stream-K kernel is a separate
+// instantiation of the 256 configuration that spills registers (its range bookkeeping
+// around the tile code), about 9% slower per K-tile than the one-tile kernel:
 // kStreamKCost.  Measured: 5120^3 2005 us (2100 us on 128 x 128 tiles), 6144^3 3377 us
 // (3221 us on 128 x 128 tiles).  Returns a negative value where it does not apply.
 constexpr double kStreamKCost = 252.0;  // us per 1024 of K per layer of 256 tiles
 inline double modelled_stream_k_time(int M, int N, int K, int batch) {
   const long long tiles = (long long)(M / 256) * (N / 256);
-  if (batch != 1 || tiles <= kStreamKWgs || tiles % kStreamKWgs == 0) return -1.0;
+  if (batch != 1 || M % 256 != 0 || N % 256 != 0) return -1.0;
+  if (tiles <= kStreamKWgs || tiles % kStreamKWgs == 0) return -1.0;
   const double overhead_us = 4.0 + 2.0 * (double)kStreamKBytes / 5.0e6 + 15.0;
   return (double)tiles / kStreamKWgs * kStreamKCost * (double)K / 1024.0 + overhead_us;
 }

@@ -232,6 +232,10 @@ def test_plan_tiles(lib):
     assert sgemm_rm_plan_tiles(1024, 1024, 1024) == 64
     assert sgemm_rm_plan_tiles(256, 256, 256) == 32
     assert sgemm_rm_plan_tiles(3072, 3072, 3072) == 192  # 256 tiles of 192^2: one whole wave
+    # 256 x 256 tiles only where they cover the matrix: strips past them would run as scalar edge tiles
+    for n in (4000, 4090, 3900, 8000):
+        assert sgemm_rm_plan_tiles(n, n, n) != 256, n
+    assert sgemm_rm_plan_tiles(4096, 4000, 4096) != 256
     assert sgemm_rm_plan_tiles(1000, 1030, 999) == 64  # 6-column thin strip beside 64 x 64 tiles
     assert sgemm_rm_plan_tiles(64, 64, 64, 1024) == 64
     for M, N, K, b in [(1, 1, 1, 1), (5000, 3, 7, 1), (3, 5000, 70000, 1), (65535, 65535, 1, 1000000)]:
@@ -269,5 +273,7 @@ def test_workspace_size(lib):
         assert sgemm_rm_workspace_size(M, N, K, b) == 0, (M, N, K, b)
     # 4608^3: 324 tiles of 256^2, 1.27 waves: stream-K with two 256 KB slots per workgroup
     assert sgemm_rm_workspace_size(4608, 4608, 4608) == 2 * 256 * 256 * 256 * 4
-    # 5120^3 (400 tiles, 1.56 waves): the 64 x 64 tiles are modelled faster than stream-K
+    # 5120^3 (400 tiles, 1.56 waves): the 192 x 192 tiles are modelled faster than stream-K
     assert sgemm_rm_workspace_size(5120, 5120, 5120) == 0
+    # stream-K covers full 256 x 256 tiles only
+    assert sgemm_rm_workspace_size(4600, 4608, 4608) == 0
