@@ -80,11 +80,11 @@ constexpr long long kStreamKBytes = 2LL * kStreamKWgs * 256 * 256 * 4;
 // Partial MFMA tiles.  A strip of rows (columns) past the last full tile that is at least
 // mfma_edge_min(side) wide runs as guarded MFMA tiles of the same grid; a thinner one runs
 // as thin strips (192, 128 and 64 configurations: 16, below which a strip would pay for a
-// whole tile row or column of MFMA work) or, in the 256 configuration (0: never MFMA), as
-// scalar edge tiles (its workgroups fill a CU's register file and a guarded tile there
-// costs a whole 256 x 256 tile; the cost model steers ragged shapes to the smaller
-// configurations).  The 32 configuration (1) covers every strip with MFMA tiles.
-constexpr int mfma_edge_min(int side) { return side == 256 ? 0 : side == 32 ? 1 : 16; }
+// whole tile row or column of MFMA work; 32 configuration: 4) or, in the 256 configuration
+// (0: never MFMA), as scalar edge tiles (its workgroups fill a CU's register file and a
+// guarded tile there costs a whole 256 x 256 tile; the cost model steers ragged shapes to
+// the smaller configurations).
+constexpr int mfma_edge_min(int side) { return side == 256 ? 0 : side == 32 ? 4 : 16; }
 // The extent [0, result) of rows (columns) that MFMA tiles of this side cover, out of n.
 constexpr int mfma_extent(int n, int side, int edge_min) {
   return (edge_min > 0 && n % side >= edge_min) ? n : n - n % side;

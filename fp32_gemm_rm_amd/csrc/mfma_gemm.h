@@ -150,7 +150,9 @@ struct Operand {
   // along m or n: B, or A^T) each element past the matrix is loaded from the last column.
   // Values past M or N only ever reach rows or columns of the product that are not stored
   // (output (i, j) takes row i of op(A) and column j of op(B) alone), so the clamped loads
-  // only have to stay inside the matrix, and they are stored to LDS as loaded.
+  // only have to stay inside the matrix, and they are stored to LDS as loaded.  Along r the
+  // limit is a multiple of 4 (launch_cfg leaves the last 1-3 rows or columns to the thin
+  // strips), so no float4 straddles the edge, and one past it loads the last float4 inside.
   template <bool VEC, bool GUARD, int SET = 0>
   __device__ __forceinline__ void load_full(int k0) {
 #pragma unroll
@@ -158,18 +160,14 @@ struct Operand {
       if (KROWS) {
         const int r = (!GUARD || row[i] < lim) ? row[i] : lim - 1;
         reg[SET][i] = load4<VEC>(base + (long long)r * ld + k0 + 4 * col[i], 4);
-      } else if (!GUARD) {
-        reg[SET][i] = load4<VEC>(base + (long long)(k0 + row[i]) * ld + col[i], 4);
       } else {
-        const float* q = base + (long long)(k0 + row[i]) * ld;
-        reg[SET][i] = make_float4(q[min(col[i], lim - 1)], q[min(col[i] + 1, lim - 1)], q[min(col[i] + 2, lim - 1)],
-                                  q[min(col[i] + 3, lim - 1)]);
+        const int c = GUARD ? min(col[i], lim - 4) : col[i];
+        reg[SET][i] = load4<VEC>(base + (long long)(k0 + row[i]) * ld + c, 4);
       }
     }
   }
   // global load instructions of one load_full
-  template <bool VEC, bool GUARD>
-  static constexpr int kLoadInstrs = (VEC && (KROWS || !GUARD)) ? LOADS : 4 * LOADS;
+  static constexpr int kLoadInstrs(bool vec) { return vec ? LOADS : 4 * LOADS; }
   // last K-tile: kl = K - k0 < BK valid k; zeros past K (and past the matrix, GUARD)
   template <bool VEC, bool GUARD, int SET = 0>
   __device__ __forceinline__ void load_tail(int k0, int kl) {
@@ -376,7 +374,8 @@ __device__ __forceinline__ void finish_acc(const Problem& p, const v16f (&acc)[F
 // K-tiles [kb, ke) of the BM x BN tile of C at (m0, n0).  part == nullptr: the range is
 // the whole K range and the result goes to C (alpha, beta); otherwise the raw sums go to
 // part, a BM x BN row-major block (a stream-K partial tile).  GUARD bit 0 (1): the tile
-// reaches past M, bit 1 (2): past N; // past M or N; loads read zeros there and stores skip it.
+// reaches past M, bit 1 (2): past N (loads stay inside the matrix, stores skip what is
+// past it).
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool VEC, int GUARD>
 __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                           float* part = nullptr) {
@@ -629,7 +628,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   // compiler would otherwise hoist the barrier, and its wait on the fragment reads, above
   // the MFMAs).
   constexpr int kStores = OpA::LOADS + OpB::LOADS;
-  constexpr int kLoads = OpA::template kLoadInstrs<VEC, GA> + OpB::template kLoadInstrs<VEC, GB>;
+  constexpr int kLoads = OpA::kLoadInstrs(VEC) + OpB::kLoadInstrs(VEC);
   constexpr int kFragReads = FM * (OpA::STRIDE == BK ? 2 : 8) + FN * (OpB::STRIDE == BK ? 2 : 8);
   constexpr int kMfmas = 8 * FM * FN, kMemOps = kStores + kLoads + kFragReads;
   constexpr int kPer = (kMemOps + kMfmas - 1) / kMfmas;
@@ -802,7 +801,8 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // EDGE_MIN: 0, the tiles cover [0, Mf) x [0, Nf) with Mf, Nf multiples of BM, BN and the
 // strips past them are scalar edge tiles; otherwise a strip at least EDGE_MIN rows
 // (columns) wide is covered by guarded MFMA tiles of the same grid and a thinner one runs
-// as thin strips (EDGE_MIN = 1: every partial tile is an MFMA tile).
+// as thin strips.  Edge tiles and thin strips take the block ids after the tiles (thin
+// strips dispatched first measured slower: 1000 x 1030 x 999 24.8 -> 28.4 us).
 // PF: the tiles run mfma_tile_pf (one k-group per wavefront and K-tile) instead of mfma_tile.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
           int EDGE_MIN, bool STREAM_K, bool VEC, bool PF>
@@ -819,12 +819,16 @@ void mfma_kernel(Problem p, TileMap map) {
   constexpr int kFloats = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
   static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
+  // the MFMA tiles see the matrix as [0, Mf) x [0, Nf): what lies past it is the strips'
+  Problem pt = p;
+  pt.M = map.Mf;
+  pt.N = map.Nf;
   auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
     constexpr int G = decltype(guard)::value;
     if constexpr (PF)
-      mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM >= 192 ? 1 : 2), TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
+      mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM >= 192 ? 1 : 2), TA, TB, VEC, G>(pt, m0, n0, kb, ke, smem, part);
     else
-      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, G>(p, m0, n0, kb, ke, smem, part);
+      mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, G>(pt, m0, n0, kb, ke, smem, part);
   };
   const int nmfma = map.tiles_m * map.tiles_n;
   const int ndp = STREAM_K ? map.dp_tiles : nmfma;
@@ -834,7 +838,7 @@ void mfma_kernel(Problem p, TileMap map) {
     int bm, bn;
     tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
     const int m0 = bm * BM, n0 = bn * BN;
-    const bool past_m = EDGE_MIN != 0 && m0 + BM > p.M, past_n = EDGE_MIN != 0 && n0 + BN > p.N;
+    const bool past_m = EDGE_MIN != 0 && m0 + BM > pt.M, past_n = EDGE_MIN != 0 && n0 + BN > pt.N;
     if (!past_m && !past_n)
       tile(std::integral_constant<int, 0>{}, m0, n0, 0, iters, nullptr);
     else if (!past_n)
@@ -941,6 +945,13 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   // of every column) are scalar edge tiles or thin strips
   map.Mf = mfma_extent(p.M, BM, EDGE_MIN);
   map.Nf = mfma_extent(p.N, BN, EDGE_MIN);
+  if constexpr (EDGE_MIN > 1) {
+    // Guarded tiles load an operand stored along m or n (A^T, B) in whole float4s, so its
+    // limit must be a multiple of 4: the last 1-3 rows (columns) join the thin strips (the
+    // tile count does not change: a guarded remainder is at least 4 wide).
+    if (TA) map.Mf &= ~3;
+    if (!TB) map.Nf &= ~3;
+  }
   map.tiles_m = (map.Mf + BM - 1) / BM;
   map.tiles_n = (map.Nf + BN - 1) / BN;
   if (map.tiles_m == 0 || map.tiles_n == 0) {  // no MFMA tile

@@ -263,9 +263,10 @@ def test_tile_configs_integer_exact(oracle, tiles, M, N, K):
         check_padding(out, C, M, N, ldc)
 
 
-# Partial tiles of the 192, 128 and 64 configurations: a remainder of 16 or more rows (columns)
-# runs as guarded MFMA tiles (guarded along M only, along N only, or both: separate code
-# paths), a thinner one as thin strips.  Shapes put remainders on both sides of 16, in
+# Partial tiles: a remainder of 16 or more rows (columns; 4 in the 32 configuration) runs as
+# guarded MFMA tiles (guarded along M only, along N only, or both: separate code paths), a
+# thinner one as thin strips; so do the last 1-3 columns of B (rows of A^T) when the guarded
+# remainder is not a multiple of 4.  Shapes put remainders on both sides of 16, in
 # either dimension, and cover matrices smaller than one tile or thinner than 16; the
 # long-K cases give every wavefront of a thin strip 64 or more MFMA steps (its long-slice
 # form).
@@ -275,6 +276,8 @@ PARTIAL_SHAPES = {
     128: [(3 * 128 + 32, 2 * 128 + 31, 70), (3 * 128 + 31, 2 * 128 + 32, 70), (128 + 16, 128 + 15, 70),
           (128 + 15, 128 + 16, 33), (2 * 128 + 7, 3 * 128 + 1, 70), (100, 300, 70), (20, 300, 45), (300, 20, 45),
           (12, 300, 45), (300, 12, 45), (9, 7, 45), (2 * 128 + 5, 128 + 3, 1100)],
+    32: [(3 * 32 + 2, 2 * 32 + 3, 70), (3 * 32 + 5, 2 * 32 + 7, 45), (1, 40, 33), (40, 1, 33), (3, 3, 5),
+         (2 * 32 + 6, 3 * 32 + 6, 300)],
     64: [(5 * 64 + 16, 4 * 64 + 15, 70), (5 * 64 + 15, 4 * 64 + 16, 70), (64 + 15, 64 + 15, 70),
          (1000, 1030, 99), (40, 200, 45), (10, 200, 45), (200, 10, 45), (1, 1, 300), (3 * 64 + 1, 2 * 64 + 14, 1),
          (64 + 3, 2 * 64 + 9, 2100)],
