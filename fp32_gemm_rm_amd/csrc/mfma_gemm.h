@@ -713,60 +713,93 @@ __device__ __forceinline__ void edge_tile(const Problem& p, int m0, int n0, floa
 // D(4 * (l / 16) + r, l % 16).  D(i, j) is (line i, output j) when `cols`, (output i,
 // line j) otherwise.
 constexpr int kThinMax = 16;    // widest thin strip, and lines per workgroup
-template <int NT, bool TA, bool TB>
+template <int NT, bool TA, bool TB, bool VEC>
 __device__ __forceinline__ void thin_strip(const Problem& p, bool cols, int first, int nlines, int lo, int width,
                                            float* smem) {
   typedef float v4f __attribute__((ext_vector_type(4)));
   constexpr int W = NT / 64;
   static_assert(NT >= 256, "one thread per output of the 16 x 16 block in the final sums");
+  // An operand stored along k (A, or B^T) is read as float4s of 4 consecutive k when its
+  // rows are 16-byte aligned: lane quad kq takes k = kb + 4 kq + s in MFMA step s of each
+  // group of 4 steps (16 k), so a lane's 4 values are adjacent.  The other operand (A^T,
+  // or B) is read element by element, 16 adjacent values per row across the lanes.
+  constexpr bool VX = VEC && !TA, VY = VEC && TB;
   const int t = threadIdx.x, wv = t / 64, l = t % 64, i16 = l % 16, kq = l / 16;
-  const int kc = ((p.K + W - 1) / W + 3) & ~3;  // K slice of a wavefront, a multiple of 4
-  const int k0 = min(wv * kc, p.K), k1 = min(k0 + kc, p.K);
   // this lane's row of op(A) (X operand) and column of op(B) (Y operand), clamped
   const int nx = cols ? nlines : width, ny = cols ? width : nlines;
   const int am = (cols ? first : lo) + min(i16, nx - 1), bn = (cols ? lo : first) + min(i16, ny - 1);
   const bool x_in = i16 < nx, y_in = i16 < ny;
-  // The slice runs in chunks of U MFMA steps whose loads are issued one chunk ahead (two
-  // register sets), so that a wavefront keeps 2U loads per lane in flight instead of
-  // waiting out the memory latency every few steps; U = 16 (64 loads, the most the
-  // memory counter tracks) for long slices, 4 for short ones, whose steps past the slice
-  // would otherwise dominate.  Those steps (the last chunks) load clamped addresses and
-  // contribute zeros.
+  const float* arow = TA ? p.A + am : p.A + (long long)am * p.lda;  // element k at arow[k * (TA ? lda : 1)]
+  const float* bcol = TB ? p.B + (long long)bn * p.ldb : p.B + bn;  // element k at bcol[k * (TB ? 1 : ldb)]
+  auto xk = [&](int k) { return TA ? arow[(long long)k * p.lda] : arow[k]; };
+  auto yk = [&](int k) { return TB ? bcol[k] : bcol[(long long)k * p.ldb]; };
+  // [0, K16) in groups of 16 k, each wavefront a contiguous slice of whole groups; the
+  // last 0-15 k (the tail) are one wavefront's extra steps.
+  const int K16 = p.K & ~15;
+  const int kc = ((K16 / 16 + W - 1) / W) * 16;
+  const int k0 = min(wv * kc, K16), k1 = min(k0 + kc, K16);
+  // The slice runs in chunks of U groups whose loads are issued one chunk ahead (two
+  // register sets), so that a wavefront keeps up to 64 loads per lane in flight instead
+  // of waiting out the memory latency every few steps; U = 4 for long slices, 1 for short
+  // ones, whose groups past the slice would otherwise dominate.  Those groups (the last
+  // chunks) load clamped addresses and contribute zeros.
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   auto slice = [&](auto chunk) {
     constexpr int U = decltype(chunk)::value;
-    float xv[2][U], yv[2][U];
+    float xv[2][U][4], yv[2][U][4];
     auto fetch = [&](auto set, int kbase) {
       constexpr int S = decltype(set)::value;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int kx = kbase + 4 * u + kq, kcl = min(kx, p.K - 1);
-        const float av = TA ? p.A[(long long)kcl * p.lda + am] : p.A[(long long)am * p.lda + kcl];
-        const float bv = TB ? p.B[(long long)bn * p.ldb + kcl] : p.B[(long long)kcl * p.ldb + bn];
-        const bool kin = kx < k1;
-        xv[S][u] = x_in && kin ? av : 0.f;
-        yv[S][u] = y_in && kin ? bv : 0.f;
+        const int kg = kbase + 16 * u;
+        const bool kin = kg < k1;
+        const int kl = min(kg, K16 - 16) + 4 * kq;  // inside [0, K16)
+        float4 x, y;
+        if (VX)
+          x = *reinterpret_cast<const float4*>(arow + kl);
+        else
+          x = make_float4(xk(kl), xk(kl + 1), xk(kl + 2), xk(kl + 3));
+        if (VY)
+          y = *reinterpret_cast<const float4*>(bcol + kl);
+        else
+          y = make_float4(yk(kl), yk(kl + 1), yk(kl + 2), yk(kl + 3));
+        const bool xo = x_in && kin, yo = y_in && kin;
+        xv[S][u][0] = xo ? x.x : 0.f; xv[S][u][1] = xo ? x.y : 0.f; xv[S][u][2] = xo ? x.z : 0.f; xv[S][u][3] = xo ? x.w : 0.f;
+        yv[S][u][0] = yo ? y.x : 0.f; yv[S][u][1] = yo ? y.y : 0.f; yv[S][u][2] = yo ? y.z : 0.f; yv[S][u][3] = yo ? y.w : 0.f;
       }
     };
     auto steps = [&](auto set) {
       constexpr int S = decltype(set)::value;
 #pragma unroll
-      for (int u = 0; u < U; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[S][u], yv[S][u], acc, 0, 0, 0);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[S][u][q], yv[S][u][q], acc, 0, 0, 0);
     };
     using Set0 = std::integral_constant<int, 0>;
     using Set1 = std::integral_constant<int, 1>;
     fetch(Set0{}, k0);
-    for (int k = k0; k < k1; k += 8 * U) {
-      fetch(Set1{}, k + 4 * U);
+    for (int k = k0; k < k1; k += 32 * U) {
+      fetch(Set1{}, k + 16 * U);
       steps(Set0{});
-      fetch(Set0{}, k + 8 * U);
+      fetch(Set0{}, k + 32 * U);
       steps(Set1{});
     }
   };
-  if (k1 - k0 >= 4 * 64)  // 64 steps or more
-    slice(std::integral_constant<int, 16>{});
-  else
-    slice(std::integral_constant<int, 4>{});
+  if (K16 > 0) {
+    if (k1 - k0 >= 16 * 16)  // 16 groups or more
+      slice(std::integral_constant<int, 4>{});
+    else
+      slice(std::integral_constant<int, 1>{});
+  }
+  if (wv == W - 1 && K16 < p.K) {  // the tail: k = K16 + 4 u + kq in step u
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kx = K16 + 4 * u + kq, kcl = min(kx, p.K - 1);
+      const float av = xk(kcl), bv = yk(kcl);
+      const bool kin = kx < p.K;
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x_in && kin ? av : 0.f, y_in && kin ? bv : 0.f, acc, 0, 0, 0);
+    }
+  }
   float* red = smem;  // [wavefront][register][lane]
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[(wv * 4 + r) * 64 + l] = acc[r];
@@ -886,10 +919,10 @@ void mfma_kernel(Problem p, TileMap map) {
     const int n_right = map.right_m;  // right strip: columns [Nf, N) of rows [0, Mf)
     if (e < n_right) {
       const int first = e * kThinMax;
-      thin_strip<Cfg::kThreads, TA, TB>(p, true, first, min(kThinMax, map.Mf - first), map.Nf, p.N - map.Nf, smem);
+      thin_strip<Cfg::kThreads, TA, TB, VEC>(p, true, first, min(kThinMax, map.Mf - first), map.Nf, p.N - map.Nf, smem);
     } else {  // bottom strip: rows [Mf, M) of columns [0, N)
       const int first = (e - n_right) * kThinMax;
-      thin_strip<Cfg::kThreads, TA, TB>(p, false, first, min(kThinMax, p.N - first), map.Mf, p.M - map.Mf, smem);
+      thin_strip<Cfg::kThreads, TA, TB, VEC>(p, false, first, min(kThinMax, p.N - first), map.Mf, p.M - map.Mf, smem);
     }
   }
 }
