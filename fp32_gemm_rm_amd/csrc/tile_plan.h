@@ -21,14 +21,33 @@ namespace sgemm_impl {
 struct TileCost {
   int side;  // tile side: 256, 192, 128, 64 or 32
   double u1, u2;
+  double thin;  // us per 1024 of K per 256 thin-strip workgroups
 };
-constexpr TileCost kTileCosts[] = {
-    {256, 231.0, 231.0}, {192, 134.0, 133.3}, {128, 60.5, 59.5}, {64, 15.3, 16.0}, {32, 5.4, 4.95}};
+// Thin strips are priced only in the 32 configuration: its tiles fill all four workgroup
+// slots of a CU, so the strips run after them (a strip workgroup takes about 3.3 us per
+// 1024 of K on its own); beside the larger tiles they overlap.  Fitted together with the
+// tile costs against forced-configuration timings of 75 shapes (squares, skinny, long-K,
+// ragged, batched, and 40 seeded random ones): the choice costs 0.5% on average against
+// the fastest configuration of each shape.
+constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 0.0},
+                                   {192, 134.0, 133.3, 0.0},
+                                   {128, 60.5, 59.5, 0.0},
+                                   {64, 15.3, 16.0, 0.0},
+                                   {32, 5.4, 4.95, 4.0}};
 
 // MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
 // counts as a tile row (column); a thin strip, which runs beside the MFMA tiles, does not.
 inline long long modelled_tiles(int n, int side) {
   return (mfma_extent(n, side, mfma_edge_min(side)) + side - 1) / side;
+}
+
+// Thin-strip workgroups (16 lines each) of one product, for B stored along n (the last
+// 1-3 columns of a guarded remainder that is not a multiple of 4 are thin too).
+inline long long modelled_thin_wgs(int M, int N, int side) {
+  const int em = mfma_edge_min(side);
+  if (em <= 1) return 0;
+  const int Mf = mfma_extent(M, side, em), Nf = mfma_extent(N, side, em) & ~3;
+  return (Nf < N ? (Mf + 15) / 16 : 0) + (Mf < M ? (N + 15) / 16 : 0);
 }
 
 // Modelled microseconds; M, N, K, batch > 0.  The 256 configuration is a candidate only
@@ -39,7 +58,8 @@ inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
   if (mfma_edge_min(c.side) == 0 && (M % c.side != 0 || N % c.side != 0)) return 1e30;
   const long long tiles = modelled_tiles(M, c.side) * modelled_tiles(N, c.side) * batch;
   const long long layers = (tiles + 255) / 256;
-  return (double)layers * (layers > 1 ? c.u2 : c.u1) * (double)K / 1024.0;
+  const long long thin_rounds = (modelled_thin_wgs(M, N, c.side) * batch + 255) / 256;
+  return ((double)layers * (layers > 1 ? c.u2 : c.u1) + (double)thin_rounds * c.thin) * (double)K / 1024.0;
 }
 
 // Stream-K (256 configuration, batch 1, with a workspace, full tiles only): the K-tiles of
