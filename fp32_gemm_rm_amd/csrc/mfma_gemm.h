@@ -927,11 +927,20 @@ void mfma_kernel(Problem p, TileMap map) {
   }
 }
 
-// Stream-K fix-up: one workgroup per stream-K tile that was split between ranges; adds
-// the pieces in range order and applies alpha and beta.  Tiles that one range covered
-// whole were written by the main kernel.
+// Stream-K fix-up: kFixSlices workgroups per stream-K tile that was split between ranges,
+// each over BM / kFixSlices rows; adds the pieces in range order and applies alpha and
+// beta.  Tiles that one range covered whole were written by the main kernel.  Each thread
+// takes kFixQuads float4s of the slice and issues all of their loads (every piece, then
+// C) before its first store, so that the memory-bound pass keeps many loads in flight
+// (one workgroup per tile, each thread walking its float4s one by one, took 87 us for
+// 272 tiles at 4352 x 4096).
+constexpr int kFixSlices = 8;
 template <int BM, int BN, int BK, int GROUP_M>
 __global__ __launch_bounds__(256) void sk_fixup_kernel(Problem p, TileMap map) {
+  constexpr int kQuads = BN / 4;                         // float4 per row
+  constexpr int kSliceQuads = BM / kFixSlices * kQuads;  // float4 per slice
+  constexpr int kFixQuads = kSliceQuads / 256;           // float4 per thread
+  static_assert(kFixQuads * 256 == kSliceQuads, "even split of a slice over 256 threads");
   const int nmfma = map.tiles_m * map.tiles_n;
   const int iters = (p.K + BK - 1) / BK;
   const StreamK sk{(long long)(nmfma - map.dp_tiles) * iters, iters, map.sk_wgs};
@@ -940,26 +949,52 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(Problem p, TileMap map) {
   if (g0 == g1) return;
   int bm, bn;
   tile_coords<GROUP_M>(map.dp_tiles + u, map.tiles_m, map.tiles_n, bm, bn);
-  const int m0 = bm * BM, n0 = bn * BN;
-  const bool beta0 = p.beta == 0.0f;
-  constexpr int kQuads = BN / 4;  // float4 per row
-  for (int q = threadIdx.x; q < BM * kQuads; q += 256) {
-    const int r = q / kQuads, c = (q % kQuads) * 4;
-    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int g = g0; g <= g1; ++g) {
-      if (sk.start(g) == sk.start(g + 1)) continue;  // empty range (fewer iterations than workgroups)
-      const long long slot = 2LL * g + (sk.start(g) / iters == u ? 0 : 1);
-      const float4 v = *reinterpret_cast<const float4*>(map.ws + slot * (BM * BN) + r * BN + c);
-      if (g == g0) {
-        sum = v;
+  const int m0 = bm * BM, n0 = bn * BN, r0 = blockIdx.y * (BM / kFixSlices);
+  float4 sum[kFixQuads];
+  bool first = true;
+  for (int g = g0; g <= g1; ++g) {
+    if (sk.start(g) == sk.start(g + 1)) continue;  // empty range (fewer iterations than workgroups)
+    const long long slot = 2LL * g + (sk.start(g) / iters == u ? 0 : 1);
+    const float* piece = map.ws + slot * (BM * BN) + r0 * BN;
+#pragma unroll
+    for (int i = 0; i < kFixQuads; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(piece + 4 * (threadIdx.x + 256 * i));
+      if (first) {
+        sum[i] = v;
       } else {
-        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+        sum[i].x += v.x; sum[i].y += v.y; sum[i].z += v.z; sum[i].w += v.w;
       }
     }
-    float* crow = p.C + (long long)(m0 + r) * p.ldc + n0 + c;
-    const float s4[4] = {sum.x, sum.y, sum.z, sum.w};
+    first = false;
+  }
+  const bool vec_c = reinterpret_cast<uintptr_t>(p.C) % 16 == 0 && p.ldc % 4 == 0;
+  auto crow = [&](int i) {
+    const int q = threadIdx.x + 256 * i;
+    return p.C + (long long)(m0 + r0 + q / kQuads) * p.ldc + n0 + (q % kQuads) * 4;
+  };
+  float4 c[kFixQuads];
+  if (p.beta != 0.0f) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) crow[e] = beta0 ? p.alpha * s4[e] : fmaf(p.alpha, s4[e], p.beta * crow[e]);
+    for (int i = 0; i < kFixQuads; ++i) {
+      const float* q = crow(i);
+      c[i] = vec_c ? *reinterpret_cast<const float4*>(q) : make_float4(q[0], q[1], q[2], q[3]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kFixQuads; ++i) {
+    float4 o;
+    if (p.beta == 0.0f) {
+      o = make_float4(p.alpha * sum[i].x, p.alpha * sum[i].y, p.alpha * sum[i].z, p.alpha * sum[i].w);
+    } else {
+      o = make_float4(fmaf(p.alpha, sum[i].x, p.beta * c[i].x), fmaf(p.alpha, sum[i].y, p.beta * c[i].y),
+                      fmaf(p.alpha, sum[i].z, p.beta * c[i].z), fmaf(p.alpha, sum[i].w, p.beta * c[i].w));
+    }
+    float* q = crow(i);
+    if (vec_c) {
+      *reinterpret_cast<float4*>(q) = o;
+    } else {
+      q[0] = o.x; q[1] = o.y; q[2] = o.z; q[3] = o.w;
+    }
   }
 }
 
@@ -1024,8 +1059,8 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
                            dim3((unsigned)blocks), block, 0, stream, p, map);
       const hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
-      hipLaunchKernelGGL((sk_fixup_kernel<BM, BN, BK, GROUP_M>), dim3((unsigned)sk_tiles), dim3(256), 0, stream, p,
-                         map);
+      hipLaunchKernelGGL((sk_fixup_kernel<BM, BN, BK, GROUP_M>), dim3((unsigned)sk_tiles, kFixSlices), dim3(256), 0,
+                         stream, p, map);
       return hipGetLastError();
     }
   }

@@ -64,23 +64,22 @@ inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
 
 // Stream-K (256 configuration, batch 1, with a workspace, full tiles only): the K-tiles of
 // the last partial wave of T full tiles and of one full wave before it are shared evenly
-// by 256 workgroups, so the MFMA time is T/256 layers instead of ceil(T/256).  Overheads:
-// the fix-up pass (up to 2 x 256 partial tiles of 256 KB written and read back at about
-// 5 TB/s, plus a launch) and each workgroup's two partial pieces (pipeline fill and partial-
-// tile stores), about 15 us.  With fewer than 256 tiles every tile is split and the
-// pieces' overheads dominate (3072^3: 511 us against 473 us one tile per workgroup), so
-// stream-K is a candidate only past one full wave.  The stream-K kernel is a separate
-// instantiation of the 256 configuration that spills registers (its range bookkeeping
-// around the tile code), about 9% slower per K-tile than the one-tile kernel:
-// kStreamKCost.  Measured: 5120^3 2005 us (2100 us on 128 x 128 tiles), 6144^3 3377 us
-// (3221 us on 128 x 128 tiles).  Returns a negative value where it does not apply.
-constexpr double kStreamKCost = 252.0;  // us per 1024 of K per layer of 256 tiles
+// by 256 workgroups, so the MFMA time is T/256 layers instead of ceil(T/256), at
+// kStreamKCost (the stream-K instantiation runs the tile code as an outlined function,
+// about 2% slower per K-tile than the one-tile kernel), plus a fixed cost of about 110 us:
+// each workgroup's two partial pieces (pipeline fill and 256 KB partial-tile stores) and
+// the fix-up pass (about 45 us for 300 split tiles).  Measured (us, stream-K against the
+// model): 4352 x 4096 x 4096 1094 / 1113, x 8192 2098 / 2116, 4608^3 1457 / 1454, 5120^3
+// 1959 / 1954, 6144^3 3318 / 3296.  With fewer than 256 tiles every tile is split and the
+// pieces' overheads dominate, so stream-K is a candidate only past one full wave.
+// Returns a negative value where it does not apply.
+constexpr double kStreamKCost = 236.0;     // us per 1024 of K per layer of 256 tiles
+constexpr double kStreamKOverhead = 110.0;  // us
 inline double modelled_stream_k_time(int M, int N, int K, int batch) {
   const long long tiles = (long long)(M / 256) * (N / 256);
   if (batch != 1 || M % 256 != 0 || N % 256 != 0) return -1.0;
   if (tiles <= kStreamKWgs || tiles % kStreamKWgs == 0) return -1.0;
-  const double overhead_us = 4.0 + 2.0 * (double)kStreamKBytes / 5.0e6 + 15.0;
-  return (double)tiles / kStreamKWgs * kStreamKCost * (double)K / 1024.0 + overhead_us;
+  return (double)tiles / kStreamKWgs * kStreamKCost * (double)K / 1024.0 + kStreamKOverhead;
 }
 
 struct TilePlan {

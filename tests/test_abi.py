@@ -273,7 +273,9 @@ def test_workspace_size(lib):
         assert sgemm_rm_workspace_size(M, N, K, b) == 0, (M, N, K, b)
     # 4608^3: 324 tiles of 256^2, 1.27 waves: stream-K with two 256 KB slots per workgroup
     assert sgemm_rm_workspace_size(4608, 4608, 4608) == 2 * 256 * 256 * 256 * 4
-    # 5120^3 (400 tiles, 1.56 waves): the 192 x 192 tiles are modelled faster than stream-K
-    assert sgemm_rm_workspace_size(5120, 5120, 5120) == 0
+    # 5120^3 (400 tiles, 1.56 waves): stream-K, modelled (and measured) faster than 192 x 192 tiles
+    assert sgemm_rm_workspace_size(5120, 5120, 5120) == 2 * 256 * 256 * 256 * 4
+    # 6144^3 (576 tiles, 2.25 waves): 1024 tiles of 192^2 fill four waves and beat stream-K
+    assert sgemm_rm_workspace_size(6144, 6144, 6144) == 0
     # stream-K covers full 256 x 256 tiles only
     assert sgemm_rm_workspace_size(4600, 4608, 4608) == 0
