@@ -40,12 +40,91 @@ __device__ __forceinline__ void finish_c(const Problem& p, const float (&x)[NV],
   }
 }
 
+template <int V>
+using fvec = float __attribute__((ext_vector_type(V)));
+
+// finish_c for V adjacent columns per element: x[u] holds columns col(u) .. col(u) + V - 1,
+// read and written as one V-float vector.  The caller has checked that C's rows and
+// leading dimension are V-float aligned and, with GUARD bit 1, that N is a multiple of V
+// (a vector is then wholly inside or wholly past N).
+template <int NV, int V, int GUARD, typename Coord>
+__device__ __forceinline__ void finish_c_vec(const Problem& p, const fvec<V> (&x)[NV], Coord coord) {
+  auto inside = [&](int row, int col) { return (!(GUARD & 1) || row < p.M) && (!(GUARD & 2) || col < p.N); };
+  auto at = [&](int row, int col) { return reinterpret_cast<fvec<V>*>(p.C + (long long)row * p.ldc + col); };
+  if (p.beta == 0.0f) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      int row, col;
+      coord(u, row, col);
+      if (inside(row, col)) *at(row, col) = p.alpha * x[u];
+    }
+    return;
+  }
+  fvec<V> c[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    int row, col;
+    coord(u, row, col);
+    c[u] = inside(row, col) ? *at(row, col) : fvec<V>(0.f);
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    int row, col;
+    coord(u, row, col);
+    if (inside(row, col)) *at(row, col) = p.alpha * x[u] + p.beta * c[u];
+  }
+}
+
+// Output (row, column) of register r of lane (lr, lh) in block (i, j) of a wavefront
+// whose tile starts at (r0, c0): the MFMA puts it at row 8*(r/4) + 4*lh + r%4 and column
+// lr of the block, i.e. at the A line and B line of those lanes (frag_line).
+template <int VA, int VB>
+__device__ __forceinline__ void acc_coord(int i, int j, int r, int lr, int lh, int r0, int c0, int& row, int& col) {
+  row = r0 + frag_line<VA>(i, 8 * (r / 4) + 4 * lh + (r % 4));
+  col = c0 + frag_line<VB>(j, lr);
+}
+
 // The accumulators of one wavefront (FM x FN blocks of 32 x 32 at (m0 + wm0, n0 + wn0))
 // to C, one row of blocks at a time, or raw to a stream-K partial tile `part`.
-// Register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its block.
-template <int BM, int BN, int FM, int FN, int GUARD>
+// With B's lines in groups of VB > 1 (frag_line), a lane holds VB adjacent columns of
+// each of its rows and stores them as one vector where C allows it (scattered 32-bit
+// stores, 16 bytes apart across the lanes, cost 4x the cache-line writes).
+template <int BM, int BN, int FM, int FN, int VA, int VB, int GUARD>
 __device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM][FN], int m0, int n0, int wm0,
                                           int wn0, int lr, int lh, float* part) {
+  if constexpr (VB > 1) {
+    // partial tiles: BN-float rows in a 16-byte aligned workspace
+    const bool vec = part != nullptr ||
+                     (((reinterpret_cast<unsigned long long>(p.C) | (unsigned long long)p.ldc * 4) % (4 * VB)) == 0 &&
+                      (!(GUARD & 2) || p.N % VB == 0));
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        constexpr int NV = FN / VB * 16;
+        fvec<VB> x[NV];  // x[q * 16 + r]: register r of blocks VB q .. VB q + VB - 1
+#pragma unroll
+        for (int q = 0; q < FN / VB; ++q)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int v = 0; v < VB; ++v) x[q * 16 + r][v] = acc[i][VB * q + v][r];
+        auto coord = [&](int u, int& row, int& col) {
+          acc_coord<VA, VB>(i, VB * (u / 16), u % 16, lr, lh, m0 + wm0, n0 + wn0, row, col);
+        };
+        if (part != nullptr) {  // stream-K partial tile (full tiles only)
+#pragma unroll
+          for (int u = 0; u < NV; ++u) {
+            int row, col;
+            coord(u, row, col);
+            *reinterpret_cast<fvec<VB>*>(part + (row - m0) * BN + (col - n0)) = x[u];
+          }
+          continue;
+        }
+        finish_c_vec<NV, VB, GUARD>(p, x, coord);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     float x[FN * 16];
@@ -54,9 +133,7 @@ __device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[j * 16 + r] = acc[i][j][r];
     auto coord = [&](int u, int& row, int& col) {
-      const int j = u / 16, r = u % 16;
-      row = m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-      col = n0 + wn0 + j * 32 + lr;
+      acc_coord<VA, VB>(i, u / 16, u % 16, lr, lh, m0 + wm0, n0 + wn0, row, col);
     };
     if (part != nullptr) {  // stream-K partial tile (full tiles only)
 #pragma unroll
@@ -76,7 +153,7 @@ __device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM
 // barrier); then each of them finishes 1/KS of the block's accumulator registers,
 // adding the partials in the fixed order 0, 1, ..., KS-1, so that the epilogue's C
 // traffic is spread over all wavefronts.
-template <int BM, int BN, int WM, int WN, int KS, int FM, int FN, int GUARD>
+template <int BM, int BN, int WM, int WN, int KS, int FM, int FN, int VA, int VB, int GUARD>
 __device__ __forceinline__ void finish_acc(const Problem& p, const v16f (&acc)[FM][FN], float* smem, int m0, int n0,
                                            float* part) {
   const int w = threadIdx.x / 64, l = threadIdx.x % 64;
@@ -86,9 +163,8 @@ __device__ __forceinline__ void finish_acc(const Problem& p, const v16f (&acc)[F
   const int ks = KS == 1 ? 0 : w / (WM * WN), sp = KS == 1 ? w : w % (WM * WN);
   const int wm0 = (sp / WN) * (BM / WM), wn0 = (sp % WN) * (BN / WN);
   if constexpr (KS == 1) {
-    store_acc<BM, BN, FM, FN, GUARD>(p, acc, m0, n0, wm0, wn0, lr, lh, part);
+    store_acc<BM, BN, FM, FN, VA, VB, GUARD>(p, acc, m0, n0, wm0, wn0, lr, lh, part);
   } else {
-    // register r of lane l is row 8*(r/4) + 4*lh + r%4, column lr of its 32 x 32 block
     constexpr int kSlots = FM * FN * 16;      // accumulator registers per lane
     constexpr int kPart = kSlots * 64;        // floats per wavefront
     constexpr int kStride = WM * WN * kPart;  // between the partials of consecutive K-groups
@@ -112,9 +188,8 @@ __device__ __forceinline__ void finish_acc(const Problem& p, const v16f (&acc)[F
       for (int q = 1; q < KS; ++q) x[u] += sums[q * kStride + s * 64];
     }
     auto coord = [&](int u, int& row, int& col) {
-      const int s = ks * kMine + u, i = s / (FN * 16), j = (s / 16) % FN, r = s % 16;
-      row = m0 + wm0 + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-      col = n0 + wn0 + j * 32 + lr;
+      const int s = ks * kMine + u;
+      acc_coord<VA, VB>(s / (FN * 16), (s / 16) % FN, s % 16, lr, lh, m0 + wm0, n0 + wn0, row, col);
     };
     if (part != nullptr) {  // stream-K partial tile (full tiles only)
 #pragma unroll

@@ -161,7 +161,7 @@ void mfma_kernel(Problem p, TileMap map) {
   auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
     constexpr int G = decltype(guard)::value;
     if constexpr (PF)
-      mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM >= 192 ? 1 : 2), TA, TB, VEC, G>(pt, m0, n0, kb, ke, smem, part);
+      mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G>(pt, m0, n0, kb, ke, smem, part);
     else
       mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, G>(pt, m0, n0, kb, ke, smem, part);
   };

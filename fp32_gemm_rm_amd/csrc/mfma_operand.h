@@ -40,7 +40,7 @@ __device__ __forceinline__ float4 load4(const float* p, int left) {
 // MFMA fragments.  KROWS: the operand's rows in memory run along k (A, or B^T):
 // the stage holds R rows of BK floats with swizzled 16-byte chunks and a fragment
 // is two 128-bit reads.  Otherwise (A^T, or B) the stage holds BK rows of R floats
-// with stride R + 4 and a fragment is eight 32-bit reads.
+// with stride R + 4, and the fragments of V blocks (frag_line) are eight V-float reads.
 template <int R, int BK, int NT, bool KROWS>
 struct Operand {
   static constexpr int KC = BK / 4;
@@ -115,6 +115,25 @@ struct Operand {
       *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : row[i] * STRIDE + col[i])) =
           reg[SET][i];
   }
+  // out[f0 + v][e] = X(c + v, 16g + 8lh + e), v < V, e = 0..7 (stage along m or n only):
+  // the values of V blocks for the 8 MFMA steps of k-group g as V-float vectors (c is a
+  // multiple of V, rows start on 16-byte boundaries)
+  template <int V, int F>
+  __device__ __forceinline__ static void read_vec(const float* stage, int c, int g, int lh, int f0,
+                                                  float (&out)[F][8]) {
+    static_assert(!KROWS && (V == 2 || V == 4), "vector fragment reads along m or n");
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float* q = stage + (16 * g + 8 * lh + e) * STRIDE + c;
+      if constexpr (V == 4) {
+        const float4 x = *reinterpret_cast<const float4*>(q);
+        out[f0][e] = x.x; out[f0 + 1][e] = x.y; out[f0 + 2][e] = x.z; out[f0 + 3][e] = x.w;
+      } else {
+        const float2 x = *reinterpret_cast<const float2*>(q);
+        out[f0][e] = x.x; out[f0 + 1][e] = x.y;
+      }
+    }
+  }
   // out[e] = X(rr, 16g + 8lh + e), e = 0..7: this lane's values for the 8 MFMA steps of k-group g
   __device__ __forceinline__ static void read(const float* stage, int rr, int g, int lh, float (&out)[8]) {
     if constexpr (KROWS) {
@@ -129,6 +148,29 @@ struct Operand {
   }
 };
 
+// Lanes and lines of a wavefront's F blocks along m (A) or n (B).  With vector width V,
+// blocks V*q .. V*q+V-1 share 32 V consecutive lines and lane lr of block V*q + v takes
+// line 32 V q + V lr + v: a lane's V lines are adjacent, so an operand stored along m or
+// n gives it one V-float LDS read per k for V blocks (V = 1: line 32 f + lr).
+template <int V>
+__device__ __forceinline__ constexpr int frag_line(int f, int lr) {
+  return 32 * V * (f / V) + V * lr + f % V;
+}
+constexpr int frag_vec(bool along_k, int F) { return along_k ? 1 : F % 4 == 0 ? 4 : F % 2 == 0 ? 2 : 1; }
+
+// The fragments of k-group g of a wavefront's F blocks, whose lines start at w0:
+// out[f][e] = X(w0 + frag_line<V>(f, lr), 16g + 8lh + e)
+template <typename Op, int F, int V>
+__device__ __forceinline__ void read_frags(const float* stage, int w0, int g, int lr, int lh, float (&out)[F][8]) {
+  if constexpr (V == 1) {
+#pragma unroll
+    for (int f = 0; f < F; ++f) Op::read(stage, w0 + 32 * f + lr, g, lh, out[f]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < F / V; ++q) Op::template read_vec<V>(stage, w0 + 32 * V * q + V * lr, g, lh, V * q, out);
+  }
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB>
 struct MfmaCfg {
   static constexpr int KG = BK / (16 * KS);  // 16-deep k-groups per wavefront per K-tile
@@ -136,6 +178,10 @@ struct MfmaCfg {
   static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;  // 32x32 blocks per wavefront
   using OpA = Operand<BM, BK, kThreads, !TA>;
   using OpB = Operand<BN, BK, kThreads, TB>;
+  // fragment vector widths (frag_line) of A along m and B along n
+  static constexpr int VA = frag_vec(!TA, FM), VB = frag_vec(TB, FN);
+  // LDS fragment-read instructions of one wavefront per 16-deep k-group
+  static constexpr int kFragReads = (TA ? 8 * FM / VA : 2 * FM) + (TB ? 2 * FN : 8 * FN / VB);
   static constexpr int kStageFloats = OpA::kStageFloats + OpB::kStageFloats;
   static constexpr int kReduceFloats = KS > 1 ? KS * BM * BN : 0;
   static constexpr int kLdsFloats = 2 * kStageFloats > kReduceFloats ? 2 * kStageFloats : kReduceFloats;

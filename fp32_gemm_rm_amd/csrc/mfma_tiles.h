@@ -66,10 +66,8 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
     for (int r = 0; r < KG; ++r) {
       const int g = ks * KG + r;  // 16-deep k-group of this K-tile
       float af[FM][8], bf[FN][8];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) OpA::read(a_stage(s), wm0 + i * 32 + lr, g, lh, af[i]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) OpB::read(b_stage(s), wn0 + j * 32 + lr, g, lh, bf[j]);
+      read_frags<OpA, FM, Cfg::VA>(a_stage(s), wm0, g, lr, lh, af);
+      read_frags<OpB, FN, Cfg::VB>(b_stage(s), wn0, g, lr, lh, bf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
 #pragma unroll
@@ -131,7 +129,7 @@ __device__ __forceinline__ void mfma_tile(const Problem& p, int m0, int n0, int 
     if (kt + 1 < ke) step(Set1{}, kt + 1);
   }
 
-  finish_acc<BM, BN, WM, WN, KS, FM, FN, GUARD>(p, acc, smem, m0, n0, part);
+  finish_acc<BM, BN, WM, WN, KS, FM, FN, Cfg::VA, Cfg::VB, GUARD>(p, acc, smem, m0, n0, part);
 }
 
 // Scheduling groups for one K-tile of mfma_tile_pf: each of its NM MFMAs is followed by
@@ -167,9 +165,10 @@ __device__ __forceinline__ void sched_interleave() {
 //     - tile t+2+NSETS is loaded into global register set P % NSETS, the one just stored;
 //     - the MFMAs of tile t run on set P;
 //   and one barrier ends the K-tile.  A global load has NSETS K-tiles of MFMAs to
-//   arrive: one in the 256 and 192 configurations (128 and 72 MFMAs per wavefront and
-//   K-tile; the 256 configuration has no registers to spare, and a second set measured
-//   no better in the 192 one), two in the 128 and 64 configurations (32 and 8).
+//   arrive: one in the 192 configuration (72 MFMAs per wavefront and K-tile; a second
+//   set measured no better), two in the 256, 128 and 64 configurations (128, 32 and 8;
+//   in the 256 one the second set fits beside the 128 fragment registers once B's
+//   fragments are read as 128-bit vectors, and it spills only outside the K loop).
 template <int BM, int BN, int BK, int WM, int WN, int KS, int NSETS, bool TA, bool TB, bool VEC, int GUARD>
 __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                              float* part = nullptr) {
@@ -223,10 +222,8 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   };
   auto frags = [&](auto set, int s) {
     constexpr int S = decltype(set)::value;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) OpA::read(a_stage(s), wm0 + i * 32 + lr, ks, lh, af[S][i]);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) OpB::read(b_stage(s), wn0 + j * 32 + lr, ks, lh, bf[S][j]);
+    read_frags<OpA, FM, Cfg::VA>(a_stage(s), wm0, ks, lr, lh, af[S]);
+    read_frags<OpB, FN, Cfg::VB>(b_stage(s), wn0, ks, lr, lh, bf[S]);
   };
   auto mfmas = [&](auto set) {
     constexpr int S = decltype(set)::value;
@@ -243,21 +240,35 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   constexpr int D = 2 + NSETS;  // load distance in K-tiles, counted from the tile being multiplied
 
   // prologue: stage 0 <- tile kb (read into fragment set 0), stage 1 <- tile kb+1, global
-  // registers <- tiles kb+2 .. kb+D-1
-  load(Set0{}, kb);
-  if constexpr (NSETS == 2)
-    if (kb + 1 < ke) load(Set1{}, kb + 1);
-  store(Set0{}, 0);
-  if constexpr (NSETS == 1) {
-    if (kb + 1 < ke) load(Set1{}, kb + 1);
-  } else {
-    if (kb + 2 < ke) load(Set0{}, kb + 2);
-  }
-  __syncthreads();
-  frags(Set0{}, 0);
-  if (kb + 1 < ke) store(Set1{}, 1);
-  if (kb + D - 1 < ke) load(std::integral_constant<int, D - 1>{}, kb + D - 1);
-  __syncthreads();
+  // registers <- tiles kb+2 .. kb+D-1.  FULL: tiles kb .. kb+D+1 exist and are full, and the
+  // loads are unconditional: the steady loop's entry then leaves exactly the loads that its
+  // back edge leaves in flight, so the compiler's wait before each LDS store covers only
+  // the older register set (merged with a prologue whose loads may be skipped, it waits on
+  // some of the newest loads too).
+  auto prologue = [&](auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    auto ld = [&](auto set, int kt) {
+      if constexpr (FULL) {
+        constexpr int R = decltype(set)::value % NSETS;
+        opa.template load_full<VEC, GA, R>(kt * BK);
+        opb.template load_full<VEC, GB, R>(kt * BK);
+      } else if (kt < ke) {
+        load(set, kt);
+      }
+    };
+    ld(Set0{}, kb);
+    if constexpr (NSETS == 2) ld(Set1{}, kb + 1);
+    store(Set0{}, 0);
+    if constexpr (NSETS == 1)
+      ld(Set1{}, kb + 1);
+    else
+      ld(Set0{}, kb + 2);
+    __syncthreads();
+    frags(Set0{}, 0);
+    if (FULL || kb + 1 < ke) store(Set1{}, 1);
+    ld(std::integral_constant<int, D - 1>{}, kb + D - 1);
+    __syncthreads();
+  };
 
   // Instruction order of a steady K-tile: the MFMAs start right after the barrier and
   // each of the first ones is followed by its share of the memory instructions (LDS
@@ -267,8 +278,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   // the MFMAs).
   constexpr int kStores = OpA::LOADS + OpB::LOADS;
   constexpr int kLoads = OpA::kLoadInstrs(VEC) + OpB::kLoadInstrs(VEC);
-  constexpr int kFragReads = FM * (OpA::STRIDE == BK ? 2 : 8) + FN * (OpB::STRIDE == BK ? 2 : 8);
-  constexpr int kMfmas = 8 * FM * FN, kMemOps = kStores + kLoads + kFragReads;
+  constexpr int kMfmas = 8 * FM * FN, kMemOps = kStores + kLoads + Cfg::kFragReads;
   constexpr int kPer = (kMemOps + kMfmas - 1) / kMfmas;
   auto steady = [&](auto set, int kt) {  // tiles kt+1 .. kt+D exist and kt+D is full
     constexpr int P = decltype(set)::value;
@@ -292,16 +302,21 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   };
   int kt = kb;
   const int steady_end = min(ke, nfull);
-  for (; kt + D + 1 < steady_end; kt += 2) {  // tiles kt+D and kt+D+1 are full and in range
-    steady(Set0{}, kt);
-    steady(Set1{}, kt + 1);
+  if (kb + D + 1 < steady_end) {
+    prologue(std::true_type{});
+    for (; kt + D + 1 < steady_end; kt += 2) {  // tiles kt+D and kt+D+1 are full and in range
+      steady(Set0{}, kt);
+      steady(Set1{}, kt + 1);
+    }
+  } else {
+    prologue(std::false_type{});
   }
   for (; kt < ke; kt += 2) {
     step(Set0{}, kt);
     if (kt + 1 < ke) step(Set1{}, kt + 1);
   }
 
-  finish_acc<BM, BN, WM, WN, KS, FM, FN, GUARD>(p, acc, smem, m0, n0, part);
+  finish_acc<BM, BN, WM, WN, KS, FM, FN, Cfg::VA, Cfg::VB, GUARD>(p, acc, smem, m0, n0, part);
 }
 
 }  // namespace mfma_detail
