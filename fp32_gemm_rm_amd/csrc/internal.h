@@ -73,9 +73,12 @@ inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream, i
   return p.tb ? launch_mfma_nt(p, batch, stream, tiles, ws) : launch_mfma_nn(p, batch, stream, tiles, ws);
 }
 
+// Compute units of an MI355X (8 XCDs of 32).
+constexpr int kCUs = 256;
 // Stream-K for the 256 x 256 configuration: the workgroups that share the last waves of
-// tiles, and the workspace their partial tiles need (two 256 x 256 slots each, 128 MiB).
-constexpr int kStreamKWgs = 256;
+// tiles (one per CU), and the workspace their partial tiles need (two 256 x 256 slots
+// each, 128 MiB).
+constexpr int kStreamKWgs = kCUs;
 constexpr long long kStreamKBytes = 2LL * kStreamKWgs * 256 * 256 * 4;
 // Partial MFMA tiles.  A strip of rows (columns) past the last full tile that is at least
 // mfma_edge_min(side) wide runs as guarded MFMA tiles of the same grid; a thinner one runs

@@ -153,7 +153,8 @@ __device__ __forceinline__ void sched_interleave() {
 }
 
 // K-tiles [kb, ke) of the BM x BN tile at (m0, n0), as mfma_tile, for configurations with
-// one 16-deep k-group per wavefront and K-tile (BK = 16 KS).  The MFMA fragments are read
+// KG 16-deep k-groups per wavefront and K-tile (BK = 16 KS KG; the fragments of a K-tile
+// take 2 KG (FM + FN) 8 registers per lane).  The MFMA fragments are read
 // from LDS one K-tile ahead into a second register set, so that no MFMA waits for an LDS
 // read: with fragments read after the barrier, right before the MFMAs that use them, the
 // wavefronts lose 3-6% of the matrix-core cycles to LDS latency (probe: 150-146 against
@@ -175,8 +176,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
-  constexpr int FM = Cfg::FM, FN = Cfg::FN;
-  static_assert(Cfg::KG == 1, "one k-group per wavefront and K-tile");
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, KG = Cfg::KG;
   static_assert(NSETS == 1 || NSETS == 2, "global register sets");
   constexpr bool GA = (GUARD & 1) != 0, GB = (GUARD & 2) != 0;  // A rows past M, B columns past N
   auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
@@ -202,7 +202,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  float af[2][FM][8], bf[2][FN][8];
+  float af[2][KG][FM][8], bf[2][KG][FN][8];
 
   const int nfull = p.K / BK;
   auto load = [&](auto set, int kt) {
@@ -222,18 +222,23 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   };
   auto frags = [&](auto set, int s) {
     constexpr int S = decltype(set)::value;
-    read_frags<OpA, FM, Cfg::VA>(a_stage(s), wm0, ks, lr, lh, af[S]);
-    read_frags<OpB, FN, Cfg::VB>(b_stage(s), wn0, ks, lr, lh, bf[S]);
+#pragma unroll
+    for (int r = 0; r < KG; ++r) {
+      read_frags<OpA, FM, Cfg::VA>(a_stage(s), wm0, ks * KG + r, lr, lh, af[S][r]);
+      read_frags<OpB, FN, Cfg::VB>(b_stage(s), wn0, ks * KG + r, lr, lh, bf[S][r]);
+    }
   };
   auto mfmas = [&](auto set) {
     constexpr int S = decltype(set)::value;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int r = 0; r < KG; ++r)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[S][i][e], bf[S][j][e], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[S][r][i][e], bf[S][r][j][e], acc[i][j], 0, 0, 0);
   };
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
@@ -278,7 +283,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   // the MFMAs).
   constexpr int kStores = OpA::LOADS + OpB::LOADS;
   constexpr int kLoads = OpA::kLoadInstrs(VEC) + OpB::kLoadInstrs(VEC);
-  constexpr int kMfmas = 8 * FM * FN, kMemOps = kStores + kLoads + Cfg::kFragReads;
+  constexpr int kMfmas = 8 * KG * FM * FN, kMemOps = kStores + kLoads + KG * Cfg::kFragReads;
   constexpr int kPer = (kMemOps + kMfmas - 1) / kMfmas;
   auto steady = [&](auto set, int kt) {  // tiles kt+1 .. kt+D exist and kt+D is full
     constexpr int P = decltype(set)::value;

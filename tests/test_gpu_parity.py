@@ -236,7 +236,7 @@ def test_single_hip_runtime():
 TILE_SHAPES = {
     256: [(4096, 4096, 17), (4000, 3900, 77)],
     192: [(3072, 3072, 300), (2000, 1950, 129)],
-    128: [(2048, 2048, 300), (2000, 1950, 129)],
+    128: [(2048, 2048, 300), (2176, 2048, 300), (2000, 1950, 129)],  # one layer, 272 tiles, guarded
     64: [(1024, 1024, 129), (1000, 990, 129)],
     32: [(512, 512, 300), (1000, 1030, 99)],
 }
@@ -349,14 +349,18 @@ def test_offsets_past_2_pow_31(oracle, variant, N):
 TILE_BK = {256: 16, 192: 16, 128: 16, 64: 32, 32: 64}
 
 
-@pytest.mark.parametrize("tiles", [256, 192, 128, 64, 32])
-def test_k_loop_boundaries_integer_exact(oracle, tiles):
+@pytest.mark.parametrize(
+    "tiles,M,N,bk",
+    [(t, t + 40, t + 24, TILE_BK[t]) for t in (256, 192, 128, 64, 32)]
+    # exact 128 x 128 tiles, at most one per CU: the BK 32 form
+    + [(128, 256, 384, 32)],
+)
+def test_k_loop_boundaries_integer_exact(oracle, tiles, M, N, bk):
     """K from 1 to nine K-tiles (full, ragged, odd and even tile counts) for each forced
-    tile configuration, on a shape with full and partial tiles: bit-exact."""
+    tile configuration, on a shape with full and partial tiles (and on full tiles only for
+    the one-layer form of the 128 configuration): bit-exact."""
     from fp32_gemm_rm_amd import TILE_VARIANTS
 
-    bk = TILE_BK[tiles]
-    M, N = tiles + 40, tiles + 24
     for K in sorted({1, 3, bk - 1, bk, bk + 1, 2 * bk, 2 * bk + 5, 3 * bk - 1, 3 * bk, 4 * bk, 4 * bk + 1,
                      5 * bk, 5 * bk + 7, 6 * bk, 7 * bk + 3, 8 * bk, 9 * bk - 2}):
         lda, ldb, ldc = K + 3, N + 5, N + 2
