@@ -86,13 +86,16 @@ __device__ __forceinline__ void acc_coord(int i, int j, int r, int lr, int lh, i
 
 // The accumulators of one wavefront (FM x FN blocks of 32 x 32 at (m0 + wm0, n0 + wn0))
 // to C, one row of blocks at a time, or raw to a stream-K partial tile `part`.
-// With B's lines in groups of VB > 1 (frag_line), a lane holds VB adjacent columns of
-// each of its rows and stores them as one vector where C allows it (scattered 32-bit
-// stores, 16 bytes apart across the lanes, cost 4x the cache-line writes).
+// With B's lines in groups of VB = 4 (frag_line), a lane holds 4 adjacent columns of
+// each of its rows and stores them as one 128-bit vector where C allows it: 32-bit stores
+// 16 bytes apart across the lanes cost 4x the cache-line writes (4096^3 on 256 x 256
+// tiles: 972 against 929 us).  With VB = 2 the 64-bit stores serve launches of full tiles
+// only (GUARD bit 2; 2048^3: 125.4 against 127.4 us); with partial tiles in the launch
+// they made it slower (2000 x 1950 x 1000: 80.0 against 70.1 us).
 template <int BM, int BN, int FM, int FN, int VA, int VB, int GUARD>
 __device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM][FN], int m0, int n0, int wm0,
                                           int wn0, int lr, int lh, float* part) {
-  if constexpr (VB > 1) {
+  if constexpr (VB == 4 || (VB == 2 && (GUARD & 4))) {
     // partial tiles: BN-float rows in a 16-byte aligned workspace
     const bool vec = part != nullptr ||
                      (((reinterpret_cast<unsigned long long>(p.C) | (unsigned long long)p.ldc * 4) % (4 * VB)) == 0 &&

@@ -159,7 +159,8 @@ void mfma_kernel(Problem p, TileMap map) {
   pt.M = map.Mf;
   pt.N = map.Nf;
   auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
-    constexpr int G = decltype(guard)::value;
+    // guard bits 0-1 (the tile's partial sides), bit 2: the launch has full tiles only
+    constexpr int G = decltype(guard)::value | (EDGE_MIN == 0 ? 4 : 0);
     if constexpr (PF)
       mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G>(pt, m0, n0, kb, ke, smem, part);
     else
