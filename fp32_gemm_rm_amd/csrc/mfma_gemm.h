@@ -75,8 +75,9 @@
 // Ragged K is handled inside every MFMA tile: its last K-tile loads zeros past K.
 //
 // Stream-K (256 x 256 tiles, batch 1, with a caller workspace): when the full tiles do
-// not fill whole waves of 256 workgroups, the last partial wave and the full wave before
-// it are not run one tile per workgroup; their K-tiles, taken tile by tile, are cut into
+// not fill whole waves of 256 workgroups, the last partial wave (and the full wave before
+// it, where the partial one holds fewer than 32 tiles) is not run one tile per workgroup;
+// its K-tiles, taken tile by tile, are cut into
 // 256 equal contiguous ranges, one per workgroup (after "Stream-K" work decomposition;
 // the pages' kernels all run one tile per thread block).  Pieces of a tile that fall in
 // different ranges go to the workspace and a fix-up kernel adds them in range order,
@@ -302,8 +303,11 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(Problem p, TileMap map) {
 }
 
 // ws != nullptr (batch 1, configurations with EDGE_MIN = 0): stream-K over 256
-// workgroups for the last partial wave of tiles plus one full wave before it (the tiles
-// before those run one per workgroup); ws holds 2 * 256 * BM * BN floats.
+// workgroups for the last partial wave of tiles, plus the full wave before it where the
+// partial one holds fewer than 32 tiles (the tiles before those run one per workgroup);
+// ws holds 2 * 256 * BM * BN floats.  Measured, us, partial wave alone against with the
+// wave before it: 5120^3 1911 / 1923, 4608^3 1423 / 1440, 6144^3 3227 / 3247,
+// 5120 x 5120 x 2048 823 / 833; 4352 x 4096 x 4096 (16 tiles in the partial wave) 1095 / 1079.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
           int EDGE_MIN = 0, bool PF = false>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws = nullptr) {
@@ -348,7 +352,10 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
   if constexpr (EDGE_MIN == 0 && BM == 256 && BN == 256) {  // the workspace holds 256 x 256 slots
     if (ws != nullptr && batch == 1 && nmfma % kStreamKWgs != 0) {
-      const long long sk_tiles = nmfma % kStreamKWgs + (nmfma > kStreamKWgs ? kStreamKWgs : 0);
+      // the partial wave, and the full wave before it where the partial one is under 1/8
+      // of a wave (its pieces would be too short to fill the pipeline)
+      const long long rem = nmfma % kStreamKWgs;
+      const long long sk_tiles = rem + (nmfma > kStreamKWgs && rem < kStreamKWgs / 8 ? kStreamKWgs : 0);
       map.dp_tiles = (int)(nmfma - sk_tiles);
       map.sk_wgs = kStreamKWgs;
       map.ws = ws;

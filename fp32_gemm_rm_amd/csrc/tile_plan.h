@@ -63,14 +63,15 @@ inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
 }
 
 // Stream-K (256 configuration, batch 1, with a workspace, full tiles only): the K-tiles of
-// the last partial wave of T full tiles and of one full wave before it are shared evenly
-// by 256 workgroups, so the MFMA time is T/256 layers instead of ceil(T/256), at
+// the last partial wave of T full tiles (and of the full wave before it where the partial
+// one holds fewer than 32 tiles) are shared evenly by 256 workgroups, so the MFMA time is
+// T/256 layers instead of ceil(T/256), at
 // kStreamKCost (the stream-K instantiation runs the tile code as an outlined function,
 // about 2% slower per K-tile than the one-tile kernel), plus a fixed cost of about 110 us:
 // each workgroup's two partial pieces (pipeline fill and 256 KB partial-tile stores) and
 // the fix-up pass (about 45 us for 300 split tiles).  Measured (us, stream-K against the
-// model): 4352 x 4096 x 4096 1094 / 1113, x 8192 2098 / 2116, 4608^3 1457 / 1454, 5120^3
-// 1959 / 1954, 6144^3 3318 / 3296.  With fewer than 256 tiles every tile is split and the
+// model): 4352 x 4096 x 4096 1079 / 1113, x 8192 2067 / 2116, 4608^3 1423 / 1454, 5120^3
+// 1911 / 1954, 6144^3 3227 / 3296.  With fewer than 256 tiles every tile is split and the
 // pieces' overheads dominate, so stream-K is a candidate only past one full wave.
 // Returns a negative value where it does not apply.
 constexpr double kStreamKCost = 236.0;     // us per 1024 of K per layer of 256 tiles

@@ -59,9 +59,11 @@ def run_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant, ws, ta=0, tb=0
         (512, 768, 300),      # 6 tiles: 256 ranges of under one K-tile, most of them empty
         (512, 768, 4000),     # 6 tiles, long K: each tile split over ~43 ranges
         (1024, 1280, 77),     # 20 tiles, ragged K
-        (4352, 4352, 77),     # 289 tiles: two stream-K waves, ranges over two tiles
+        (4352, 4352, 77),     # 289 tiles: 256 one-tile workgroups, 33 stream-K tiles (the partial wave)
         (4352 + 37, 4352 + 19, 40),  # the same with scalar edge tiles around them
-        (6144, 5632, 40),     # 528 tiles: 256 one-tile workgroups, then 272 stream-K tiles
+        (4096, 4608, 200),    # 288 tiles: 32 in the partial wave, which alone is stream-K
+        (1792, 10496, 200),   # 287 tiles: 31 in the partial wave, stream-K with the wave before it
+        (6144, 5632, 40),     # 528 tiles: 256 one-tile workgroups, then 272 stream-K tiles (16 + 256)
     ],
 )
 def test_stream_k_integer_exact(oracle, workspace, M, N, K):
