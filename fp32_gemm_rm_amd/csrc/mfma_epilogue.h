@@ -43,20 +43,29 @@ __device__ __forceinline__ void finish_c(const Problem& p, const float (&x)[NV],
 template <int V>
 using fvec = float __attribute__((ext_vector_type(V)));
 
-// finish_c for V adjacent columns per element: x[u] holds columns col(u) .. col(u) + V - 1,
-// read and written as one V-float vector.  The caller has checked that C's rows and
-// leading dimension are V-float aligned and, with GUARD bit 1, that N is a multiple of V
-// (a vector is then wholly inside or wholly past N).
-template <int NV, int V, int GUARD, typename Coord>
+// finish_c for V adjacent columns per element: x[u] holds columns col(u) .. col(u) + V - 1.
+// vec (the caller's uniform choice): C's rows and leading dimension are V-float aligned and, with GUARD bit 1, N is a
+// multiple of V (a vector is then wholly inside or wholly past N): each element is read
+// and written as one V-float vector; otherwise component by component, each guarded.
+template <int NV, int V, int GUARD, bool vec, typename Coord>
 __device__ __forceinline__ void finish_c_vec(const Problem& p, const fvec<V> (&x)[NV], Coord coord) {
   auto inside = [&](int row, int col) { return (!(GUARD & 1) || row < p.M) && (!(GUARD & 2) || col < p.N); };
-  auto at = [&](int row, int col) { return reinterpret_cast<fvec<V>*>(p.C + (long long)row * p.ldc + col); };
+  auto at = [&](int row, int col) { return p.C + (long long)row * p.ldc + col; };
+  auto put = [&](int row, int col, const fvec<V>& v) {
+    if constexpr (vec) {
+      if (inside(row, col)) *reinterpret_cast<fvec<V>*>(at(row, col)) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (inside(row, col + e)) at(row, col)[e] = v[e];
+    }
+  };
   if (p.beta == 0.0f) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       int row, col;
       coord(u, row, col);
-      if (inside(row, col)) *at(row, col) = p.alpha * x[u];
+      put(row, col, p.alpha * x[u]);
     }
     return;
   }
@@ -65,13 +74,18 @@ __device__ __forceinline__ void finish_c_vec(const Problem& p, const fvec<V> (&x
   for (int u = 0; u < NV; ++u) {
     int row, col;
     coord(u, row, col);
-    c[u] = inside(row, col) ? *at(row, col) : fvec<V>(0.f);
+    if constexpr (vec) {
+      c[u] = inside(row, col) ? *reinterpret_cast<const fvec<V>*>(at(row, col)) : fvec<V>(0.f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) c[u][e] = inside(row, col + e) ? at(row, col)[e] : 0.f;
+    }
   }
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     int row, col;
     coord(u, row, col);
-    if (inside(row, col)) *at(row, col) = p.alpha * x[u] + p.beta * c[u];
+    put(row, col, p.alpha * x[u] + p.beta * c[u]);
   }
 }
 
@@ -96,37 +110,38 @@ template <int BM, int BN, int FM, int FN, int VA, int VB, int GUARD>
 __device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM][FN], int m0, int n0, int wm0,
                                           int wn0, int lr, int lh, float* part) {
   if constexpr (VB == 4 || (VB == 2 && (GUARD & 4))) {
-    // partial tiles: BN-float rows in a 16-byte aligned workspace
-    const bool vec = part != nullptr ||
-                     (((reinterpret_cast<unsigned long long>(p.C) | (unsigned long long)p.ldc * 4) % (4 * VB)) == 0 &&
+    // vector access to C (stream-K partial tiles, BN-float rows in a 16-byte aligned
+    // workspace, always take it)
+    const bool vec = (((reinterpret_cast<unsigned long long>(p.C) | (unsigned long long)p.ldc * 4) % (4 * VB)) == 0 &&
                       (!(GUARD & 2) || p.N % VB == 0));
-    if (vec) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        constexpr int NV = FN / VB * 16;
-        fvec<VB> x[NV];  // x[q * 16 + r]: register r of blocks VB q .. VB q + VB - 1
+    for (int i = 0; i < FM; ++i) {
+      constexpr int NV = FN / VB * 16;
+      fvec<VB> x[NV];  // x[q * 16 + r]: register r of blocks VB q .. VB q + VB - 1
 #pragma unroll
-        for (int q = 0; q < FN / VB; ++q)
+      for (int q = 0; q < FN / VB; ++q)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < 16; ++r)
 #pragma unroll
-            for (int v = 0; v < VB; ++v) x[q * 16 + r][v] = acc[i][VB * q + v][r];
-        auto coord = [&](int u, int& row, int& col) {
-          acc_coord<VA, VB>(i, VB * (u / 16), u % 16, lr, lh, m0 + wm0, n0 + wn0, row, col);
-        };
-        if (part != nullptr) {  // stream-K partial tile (full tiles only)
+          for (int v = 0; v < VB; ++v) x[q * 16 + r][v] = acc[i][VB * q + v][r];
+      auto coord = [&](int u, int& row, int& col) {
+        acc_coord<VA, VB>(i, VB * (u / 16), u % 16, lr, lh, m0 + wm0, n0 + wn0, row, col);
+      };
+      if (part != nullptr) {  // stream-K partial tile (full tiles only)
 #pragma unroll
-          for (int u = 0; u < NV; ++u) {
-            int row, col;
-            coord(u, row, col);
-            *reinterpret_cast<fvec<VB>*>(part + (row - m0) * BN + (col - n0)) = x[u];
-          }
-          continue;
+        for (int u = 0; u < NV; ++u) {
+          int row, col;
+          coord(u, row, col);
+          *reinterpret_cast<fvec<VB>*>(part + (row - m0) * BN + (col - n0)) = x[u];
         }
-        finish_c_vec<NV, VB, GUARD>(p, x, coord);
+        continue;
       }
-      return;
+      if (vec)  // uniform: one of two copies of the stores, not a branch per store
+        finish_c_vec<NV, VB, GUARD, true>(p, x, coord);
+      else
+        finish_c_vec<NV, VB, GUARD, false>(p, x, coord);
     }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {

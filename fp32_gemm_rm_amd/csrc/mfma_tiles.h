@@ -170,7 +170,7 @@ __device__ __forceinline__ void sched_interleave() {
 //   arrive: one in the 192 configuration (72 MFMAs per wavefront and K-tile; a second
 //   set measured no better), two in the 256, 128 and 64 configurations (128, 32 and 8;
 //   in the 256 one the second set fits beside the 128 fragment registers once B's
-//   fragments are read as 128-bit vectors, and it spills only outside the K loop).
+//   fragments are read as 128-bit vectors).
 template <int BM, int BN, int BK, int WM, int WN, int KS, int NSETS, bool TA, bool TB, bool VEC, int GUARD>
 __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                              float* part = nullptr) {
