@@ -352,8 +352,8 @@ TILE_BK = {256: 16, 192: 16, 128: 16, 64: 32, 32: 64}
 @pytest.mark.parametrize(
     "tiles,M,N,bk",
     [(t, t + 40, t + 24, TILE_BK[t]) for t in (256, 192, 128, 64, 32)]
-    # exact 128 x 128 tiles, at most one per CU: the BK 32 form
-    + [(128, 256, 384, 32)],
+    # exact 128 x 128 tiles, at most one per CU: the one-layer form (4 x 2 wavefronts)
+    + [(128, 256, 384, 16)],
 )
 def test_k_loop_boundaries_integer_exact(oracle, tiles, M, N, bk):
     """K from 1 to nine K-tiles (full, ragged, odd and even tile counts) for each forced
