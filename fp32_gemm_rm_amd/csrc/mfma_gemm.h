@@ -394,8 +394,8 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
 //        one global register set: one workgroup per CU.  Its tile counts fill whole waves
 //        where the others do not (3072^3: 256 tiles).
 //   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64, BK 16, two global register sets;
-//        two workgroups per CU.  Exact tiles, at most one per CU: 4 x 2 wavefronts of
-//        32 x 64, one workgroup per CU.
+//        two workgroups per CU.  At most one tile per CU: 4 x 2 wavefronts of 32 x 64,
+//        one workgroup per CU.
 //   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32, two
 //        global register sets; two workgroups per CU.
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
@@ -413,19 +413,23 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
       if (p.M % 192 == 0 && p.N % 192 == 0)
         return launch_cfg<192, 192, 16, 2, 2, 1, TA, TB, 8, 1, 0, true>(p, batch, stream);
       return launch_cfg<192, 192, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(192), true>(p, batch, stream);
-    case 128:
-      if (p.M % 128 == 0 && p.N % 128 == 0) {
-        // At most one tile per CU: the second workgroup slot of a CU would stay empty, so
-        // the tile takes 4 x 2 wavefronts of 32 x 64, two per SIMD, each covering the
-        // other's barrier waits (2048^3: 123.0 us, against 125.2 with 2 x 2 wavefronts and
-        // BK 32, and 127.7 with the two-workgroup form).  With more tiles, or guarded ones,
-        // the two-workgroup form is as fast or faster (4000^3: 941 against 956 us for BK 32
-        // at one workgroup per CU).
-        if ((long long)(p.M / 128) * (p.N / 128) * batch <= kCUs)
-          return launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, 0, true>(p, batch, stream);
-        return launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true>(p, batch, stream);
-      }
-      return launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, mfma_edge_min(128), true>(p, batch, stream);
+    case 128: {
+      // At most one tile per CU: the second workgroup slot of a CU would stay empty, so
+      // the tile takes 4 x 2 wavefronts of 32 x 64, two per SIMD, each covering the
+      // other's barrier waits (2048^3: 123.0 us, against 125.2 with 2 x 2 wavefronts and
+      // BK 32, and 127.7 with the two-workgroup form; guarded tiles, 1900^3: 116.1 against
+      // 121.0 us).  With more tiles the two-workgroup form is as fast or faster (4000^3:
+      // 941 against 956 us for BK 32 at one workgroup per CU).
+      constexpr int em = mfma_edge_min(128);
+      const bool exact = p.M % 128 == 0 && p.N % 128 == 0;
+      const long long tiles = (long long)((mfma_extent(p.M, 128, exact ? 0 : em) + 127) / 128) *
+                              ((mfma_extent(p.N, 128, exact ? 0 : em) + 127) / 128) * batch;
+      if (tiles <= kCUs)
+        return exact ? launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, 0, true>(p, batch, stream)
+                     : launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, em, true>(p, batch, stream);
+      return exact ? launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true>(p, batch, stream)
+                   : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true>(p, batch, stream);
+    }
     case 64:
       if (p.M % 64 == 0 && p.N % 64 == 0) return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true>(p, batch, stream);
       return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, mfma_edge_min(64), true>(p, batch, stream);

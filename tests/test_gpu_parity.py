@@ -236,7 +236,7 @@ def test_single_hip_runtime():
 TILE_SHAPES = {
     256: [(4096, 4096, 17), (4000, 3900, 77)],
     192: [(3072, 3072, 300), (2000, 1950, 129)],
-    128: [(2048, 2048, 300), (2176, 2048, 300), (2000, 1950, 129)],  # one layer, 272 tiles, guarded
+    128: [(2048, 2048, 300), (2176, 2048, 300), (2000, 1950, 129)],  # one layer, 272 tiles, guarded one layer
     64: [(1024, 1024, 129), (1000, 990, 129)],
     32: [(512, 512, 300), (1000, 1030, 99)],
 }
@@ -275,7 +275,8 @@ PARTIAL_SHAPES = {
           (12, 300, 45)],
     128: [(3 * 128 + 32, 2 * 128 + 31, 70), (3 * 128 + 31, 2 * 128 + 32, 70), (128 + 16, 128 + 15, 70),
           (128 + 15, 128 + 16, 33), (2 * 128 + 7, 3 * 128 + 1, 70), (100, 300, 70), (20, 300, 45), (300, 20, 45),
-          (12, 300, 45), (300, 12, 45), (9, 7, 45), (2 * 128 + 5, 128 + 3, 1100)],
+          (12, 300, 45), (300, 12, 45), (9, 7, 45), (2 * 128 + 5, 128 + 3, 1100),
+          (2100, 2090, 77)],  # 289 guarded tiles: the two-workgroup form (smaller grids: 4 x 2 wavefronts)
     32: [(3 * 32 + 2, 2 * 32 + 3, 70), (3 * 32 + 5, 2 * 32 + 7, 45), (1, 40, 33), (40, 1, 33), (3, 3, 5),
          (2 * 32 + 6, 3 * 32 + 6, 300)],
     64: [(5 * 64 + 16, 4 * 64 + 15, 70), (5 * 64 + 15, 4 * 64 + 16, 70), (64 + 15, 64 + 15, 70),
