@@ -60,7 +60,9 @@ def _check_entries(oracle, out, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C,
 @pytest.mark.parametrize("variant", list(VARIANTS))
 @pytest.mark.parametrize(
     "M,N,K,batch,share_b",
-    [(64, 64, 64, 37, False), (70, 33, 129, 5, False), (130, 257, 17, 3, True), (5, 300, 64, 9, False)],
+    [(64, 64, 64, 37, False), (70, 33, 129, 5, False), (130, 257, 17, 3, True), (5, 300, 64, 9, False),
+     # 9 guarded 128^2 tiles x 30 entries = 270 > 256: the 128 configuration's two-workgroup form
+     (300, 300, 33, 30, False)],
 )
 def test_batched_parity(oracle, variant, M, N, K, batch, share_b):
     lda, ldb, ldc = K + 3, N + 1, N + 2
