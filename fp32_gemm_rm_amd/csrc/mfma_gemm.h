@@ -36,10 +36,10 @@
 //     stored half-way through those MFMAs; fragments are read from LDS at the start of
 //     each k-group.
 //   mfma_tile_pf (256, 192, 128 and 64 configurations, one 16-deep k-group per wavefront
-//     and K-tile): fragments are read one K-tile ahead
-//     into a second register set, so no
-//     MFMA waits for LDS; the global loads (one or two K-tiles ahead of their LDS
-//     stores), LDS stores and fragment reads are interleaved with the MFMAs.
+//     and K-tile): fragments are read one K-tile ahead into a second register set, so
+//     no MFMA waits for LDS; the global loads (one K-tile ahead of their LDS stores in
+//     the 192 configuration, two in the others), LDS stores and fragment reads are
+//     interleaved with the MFMAs.
 // LDS layout:
 //   A tile, BM rows of BK floats (BK/4 16-byte chunks), no padding.  For
 //     BK = 16, chunk c of row r is stored at chunk position c ^ ((r/4) % 4).  On
