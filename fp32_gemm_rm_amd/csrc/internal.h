@@ -88,6 +88,11 @@ constexpr long long kStreamKBytes = 2LL * kStreamKWgs * 256 * 256 * 4;
 // guarded tile there costs a whole 256 x 256 tile; the cost model steers ragged shapes to
 // the smaller configurations).
 constexpr int mfma_edge_min(int side) { return side == 256 ? 0 : side == 32 ? 4 : 16; }
+// The 256 configuration's thin-strip form: where both remainders past its full tiles are
+// thinner than kThin256, they run as thin strips (same launch, after the tiles) instead of
+// scalar edge tiles; a 256 x 256 tile is never guarded.
+constexpr int kThin256 = 16;
+constexpr bool thin256(int M, int N) { return M % 256 < kThin256 && N % 256 < kThin256; }
 // The extent [0, result) of rows (columns) that MFMA tiles of this side cover, out of n.
 constexpr int mfma_extent(int n, int side, int edge_min) {
   return (edge_min > 0 && n % side >= edge_min) ? n : n - n % side;

@@ -149,6 +149,11 @@ void mfma_kernel(Problem p, TileMap map) {
   p = batch_entry(p);
   constexpr int kGroups = Cfg::kThreads / 256;
   constexpr bool kEdges = EDGE_MIN == 0, kThin = EDGE_MIN > 1;  // scalar edge tiles / thin strips may exist
+  // guarded MFMA tiles may exist (the 256 configuration's thin-strip form has none: its
+  // launches have remainders thinner than kThin256 only)
+  constexpr bool kGuarded = EDGE_MIN != 0 && BM != 256;
+  static_assert(BM != 256 || EDGE_MIN == 0 || EDGE_MIN == kThin256, "256 tiles: scalar edges or thin strips");
+  static_assert(kThin256 == kThinMax, "the 256 thin-strip form's remainders fit one thin strip");
   static_assert(EDGE_MIN <= kThinMax, "thin strips are at most kThinMax wide");
   constexpr int kEdgeFloats = kEdges ? kGroups * EdgeTile::kLdsFloats  // >= its reduction floats
                                      : kThin ? Cfg::kThreads / 64 * 4 * 64 : 0;
@@ -161,7 +166,7 @@ void mfma_kernel(Problem p, TileMap map) {
   pt.N = map.Nf;
   auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
     // guard bits 0-1 (the tile's partial sides), bit 2: the launch has full tiles only
-    constexpr int G = decltype(guard)::value | (EDGE_MIN == 0 ? 4 : 0);
+    constexpr int G = decltype(guard)::value | (kGuarded ? 0 : 4);
     if constexpr (PF)
       mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G>(pt, m0, n0, kb, ke, smem, part);
     else
@@ -175,15 +180,19 @@ void mfma_kernel(Problem p, TileMap map) {
     int bm, bn;
     tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
     const int m0 = bm * BM, n0 = bn * BN;
-    const bool past_m = EDGE_MIN != 0 && m0 + BM > pt.M, past_n = EDGE_MIN != 0 && n0 + BN > pt.N;
-    if (!past_m && !past_n)
+    if constexpr (kGuarded) {
+      const bool past_m = m0 + BM > pt.M, past_n = n0 + BN > pt.N;
+      if (!past_m && !past_n)
+        tile(std::integral_constant<int, 0>{}, m0, n0, 0, iters, nullptr);
+      else if (!past_n)
+        tile(std::integral_constant<int, 1>{}, m0, n0, 0, iters, nullptr);
+      else if (!past_m)
+        tile(std::integral_constant<int, 2>{}, m0, n0, 0, iters, nullptr);
+      else
+        tile(std::integral_constant<int, 3>{}, m0, n0, 0, iters, nullptr);
+    } else {
       tile(std::integral_constant<int, 0>{}, m0, n0, 0, iters, nullptr);
-    else if (!past_n)
-      tile(std::integral_constant<int, 1>{}, m0, n0, 0, iters, nullptr);
-    else if (!past_m)
-      tile(std::integral_constant<int, 2>{}, m0, n0, 0, iters, nullptr);
-    else
-      tile(std::integral_constant<int, 3>{}, m0, n0, 0, iters, nullptr);
+    }
     return;
   }
   if (STREAM_K && e < map.sk_wgs) {  // one stream-K range (full tiles only)
@@ -408,6 +417,10 @@ template <bool TA, bool TB>
 hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr) {
   switch (tiles) {
     case 256:
+      // remainders thinner than kThin256 past the full tiles: thin strips after the tiles
+      // (4100^3: see tile_plan.h); wider ones: scalar edge tiles
+      if ((p.M % 256 != 0 || p.N % 256 != 0) && thin256(p.M, p.N))
+        return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, kThin256, true>(p, batch, stream);
       return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(256), true>(p, batch, stream, ws);
     case 192:
       if (p.M % 192 == 0 && p.N % 192 == 0)

@@ -23,13 +23,14 @@ struct TileCost {
   double u1, u2;
   double thin;  // us per 1024 of K per 256 thin-strip workgroups
 };
-// Thin strips are priced only in the 32 configuration: its tiles fill all four workgroup
-// slots of a CU, so the strips run after them (a strip workgroup takes about 3.3 us per
-// 1024 of K on its own); beside the larger tiles they overlap.  Fitted together with the
+// Thin strips are priced in the 32 configuration, whose tiles fill all four workgroup slots
+// of a CU, and in the 256 one, whose workgroups each take a whole CU: there the strips run
+// after the tiles (a strip workgroup takes about 3.3 us per 1024 of K on its own); beside
+// the other configurations' tiles they overlap.  Fitted together with the
 // tile costs against forced-configuration timings of 75 shapes (squares, skinny, long-K,
 // ragged, batched, and 40 seeded random ones): the choice costs 0.5% on average against
 // the fastest configuration of each shape.
-constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 0.0},
+constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 4.0},
                                    {192, 134.0, 133.3, 0.0},
                                    {128, 60.5, 59.5, 0.0},
                                    {64, 15.3, 16.0, 0.0},
@@ -44,20 +45,26 @@ inline long long modelled_tiles(int n, int side) {
 // Thin-strip workgroups (16 lines each) of one product, for B stored along n (the last
 // 1-3 columns of a guarded remainder that is not a multiple of 4 are thin too).
 inline long long modelled_thin_wgs(int M, int N, int side) {
-  const int em = mfma_edge_min(side);
+  const int em = side == 256 ? kThin256 : mfma_edge_min(side);
   if (em <= 1) return 0;
   const int Mf = mfma_extent(M, side, em), Nf = mfma_extent(N, side, em) & ~3;
   return (Nf < N ? (Mf + 15) / 16 : 0) + (Mf < M ? (N + 15) / 16 : 0);
 }
 
 // Modelled microseconds; M, N, K, batch > 0.  The 256 configuration is a candidate only
-// where its tiles cover the matrix: the strips past them run as scalar edge tiles, which
-// cannot share a CU with its workgroups and are latency-bound chains of K-steps (4000^3:
-// 1434 us, against 949 us on 128 x 128 tiles; 4090^3: 1887 against 1021 us).
+// where its tiles cover the matrix, or leave remainders thinner than kThin256 over one
+// layer of tiles (thin strips after the tiles: 4096 x 4100 x 4096 940 us against 969 on
+// 128 x 128 tiles; 4100^3 980 against 993, which the model still gives to 128).  Wider
+// strips would run as scalar edge tiles, which cannot share a CU with its workgroups and
+// are latency-bound chains of K-steps (4000^3: 1434 us, against 949 us on 128 x 128 tiles;
+// 4090^3: 1887 against 1021 us).
 inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
-  if (mfma_edge_min(c.side) == 0 && (M % c.side != 0 || N % c.side != 0)) return 1e30;
+  if (c.side == 256 && !thin256(M, N)) return 1e30;
   const long long tiles = modelled_tiles(M, c.side) * modelled_tiles(N, c.side) * batch;
   const long long layers = (tiles + 255) / 256;
+  // the 256 thin-strip form only over one layer of tiles: past it the strips' workgroups,
+  // each on a whole CU, add up (8200^3: 7809 against 7773 us on 128 x 128 tiles)
+  if (c.side == 256 && (M % 256 != 0 || N % 256 != 0) && layers > 1) return 1e30;
   const long long thin_rounds = (modelled_thin_wgs(M, N, c.side) * batch + 255) / 256;
   return ((double)layers * (layers > 1 ? c.u2 : c.u1) + (double)thin_rounds * c.thin) * (double)K / 1024.0;
 }

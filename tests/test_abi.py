@@ -232,10 +232,13 @@ def test_plan_tiles(lib):
     assert sgemm_rm_plan_tiles(1024, 1024, 1024) == 64
     assert sgemm_rm_plan_tiles(256, 256, 256) == 32
     assert sgemm_rm_plan_tiles(3072, 3072, 3072) == 192  # 256 tiles of 192^2: one whole wave
-    # 256 x 256 tiles only where they cover the matrix: strips past them would run as scalar edge tiles
+    # 256 x 256 tiles only where they cover the matrix, or leave strips thinner than 16 over one
+    # layer of tiles (thin strips after the tiles); wider strips would run as scalar edge tiles
     for n in (4000, 4090, 3900, 8000):
         assert sgemm_rm_plan_tiles(n, n, n) != 256, n
     assert sgemm_rm_plan_tiles(4096, 4000, 4096) != 256
+    assert sgemm_rm_plan_tiles(4096, 4100, 4096) == 256  # 256 tiles and a 4-column thin strip
+    assert sgemm_rm_plan_tiles(8200, 8200, 8200) != 256  # thin strips past four layers of tiles
     assert sgemm_rm_plan_tiles(1000, 1030, 999) == 64  # 6-column thin strip beside 64 x 64 tiles
     assert sgemm_rm_plan_tiles(64, 64, 64, 1024) == 64
     for M, N, K, b in [(1, 1, 1, 1), (5000, 3, 7, 1), (3, 5000, 70000, 1), (65535, 65535, 1, 1000000)]:

@@ -271,6 +271,10 @@ def test_tile_configs_integer_exact(oracle, tiles, M, N, K):
 # long-K cases give every wavefront of a thin strip 64 or more MFMA steps (its long-slice
 # form).
 PARTIAL_SHAPES = {
+    # 256: remainders thinner than 16 run as thin strips after the full tiles, wider ones as
+    # scalar edge tiles (TILE_SHAPES)
+    256: [(2 * 256 + 4, 256 + 3, 70), (256 + 15, 2 * 256, 45), (2 * 256, 256 + 1, 33), (12, 9, 40),
+          (256 + 7, 256 + 12, 1100)],
     192: [(2 * 192 + 32, 192 + 31, 70), (192 + 15, 2 * 192 + 16, 45), (3 * 192 + 5, 192 + 3, 1100), (100, 300, 70),
           (12, 300, 45)],
     128: [(3 * 128 + 32, 2 * 128 + 31, 70), (3 * 128 + 31, 2 * 128 + 32, 70), (128 + 16, 128 + 15, 70),
@@ -353,6 +357,8 @@ TILE_BK = {256: 16, 192: 16, 128: 16, 64: 32, 32: 64}
 @pytest.mark.parametrize(
     "tiles,M,N,bk",
     [(t, t + 40, t + 24, TILE_BK[t]) for t in (256, 192, 128, 64, 32)]
+    # the 256 configuration's thin-strip form
+    + [(256, 2 * 256 + 5, 256 + 3, 16)]
     # exact 128 x 128 tiles, at most one per CU: the one-layer form (4 x 2 wavefronts)
     + [(128, 256, 384, 16)],
 )

@@ -130,7 +130,7 @@ def test_ragged_random_bound(oracle, variant, orient):
 # of a guarded remainder that is not a multiple of 4), and full tiles only (96 x 64; for
 # 128, one layer of exact tiles (4 x 2 wavefronts), and 272 exact or 289 guarded ones (the
 # two-workgroup form)).
-TILE_SHAPES = [(256, 600, 520, 77), (256, 300, 270, 160), (192, 400, 390, 77), (192, 3 * 192 + 7, 232, 300),
+TILE_SHAPES = [(256, 600, 520, 77), (256, 300, 270, 160), (256, 516, 259, 77), (192, 400, 390, 77), (192, 3 * 192 + 7, 232, 300),
                (128, 300, 290, 77), (128, 140, 290, 257), (128, 256, 384, 77), (128, 2176, 2048, 45),
                (128, 2100, 2090, 45),
                (128, 143, 265, 77), (64, 200, 150, 77), (64, 130, 70, 450), (64, 199, 141, 450), (64, 67, 73, 2100),
