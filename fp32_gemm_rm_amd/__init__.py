@@ -21,7 +21,9 @@ from .binding import (  # noqa: F401
     SGEMM_RM_VARIANT_REGBLOCK,
     TILE_VARIANTS,
     VARIANTS,
+    SgemmArgumentError,
     SgemmError,
+    SgemmLaunchError,
     library_path,
     load_library,
     sgemm,

@@ -50,12 +50,27 @@ EXPORTED_SYMBOLS = ("sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strided_batched", "sgem
                     "sgemm_rm_plan_tiles", "sgemm_rm_strerror", "sgemm_rm_version")
 
 
-class SgemmError(RuntimeError):
-    """A nonzero return code of the library."""
+class SgemmError(Exception):
+    """A nonzero return code of the library (``code``)."""
 
     def __init__(self, code: int, message: str):
         super().__init__(f"sgemm_rm error {code}: {message}")
         self.code = code
+
+
+class SgemmArgumentError(SgemmError, ValueError):
+    """A negative return code: argument -code of the call is invalid (checked before any HIP call)."""
+
+
+class SgemmLaunchError(SgemmError, RuntimeError):
+    """A positive return code: the hipError_t of a launch (e.g. hipErrorInvalidConfiguration)."""
+
+
+def error_for(code: int) -> SgemmError:
+    """The exception for a nonzero return code: ValueError for an invalid argument,
+    RuntimeError for a HIP error."""
+    cls = SgemmArgumentError if code < 0 else SgemmLaunchError
+    return cls(int(code), sgemm_rm_strerror(int(code)))
 
 
 def library_path() -> str:
@@ -135,7 +150,7 @@ def sgemm_rm_workspace_size(M, N, K, batch=1) -> int:
     """Workspace bytes with which the _ws calls use stream-K for the shape (0: none); host only."""
     code = load_library().sgemm_rm_workspace_size(int(M), int(N), int(K), int(batch))
     if code < 0:
-        raise SgemmError(int(code), sgemm_rm_strerror(int(code)))
+        raise error_for(int(code))
     return int(code)
 
 
@@ -161,7 +176,7 @@ def sgemm_rm_plan_tiles(M, N, K, batch=1) -> int:
     """Tile side of the MFMA configuration the library picks for the shape (host only)."""
     code = load_library().sgemm_rm_plan_tiles(int(M), int(N), int(K), int(batch))
     if code < 0:
-        raise SgemmError(code, sgemm_rm_strerror(code))
+        raise error_for(code)
     return code
 
 
@@ -171,12 +186,13 @@ def sgemm_rm_strerror(code: int) -> str:
 
 def _check(code: int) -> int:
     if code != 0:
-        raise SgemmError(code, sgemm_rm_strerror(code))
+        raise error_for(code)
     return code
 
 
 def sgemm_rm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0):
-    """C := alpha*A*B + beta*C on raw device pointers (ints); raises SgemmError on failure."""
+    """C := alpha*A*B + beta*C on raw device pointers (ints); raises SgemmArgumentError (a ValueError) on an
+    invalid argument and SgemmLaunchError (a RuntimeError) on a HIP error."""
     lib = load_library()
     return _check(lib.sgemm_rm(int(M), int(N), int(K), float(alpha), A or None, int(lda), B or None,
                                int(ldb), float(beta), C or None, int(ldc), stream or None))

@@ -38,7 +38,7 @@ def _compile(src: str) -> str:
 
 
 PROBE_DIR = os.path.join(ROOT, "tests", "probes")
-PROBES = ["mfma_layout_probe.hip", "lds_bank_probe.hip", "mfma_peak_probe.hip", "mfma_schedule_probe.hip"]
+PROBES = ["mfma_layout_probe.hip", "lds_bank_probe.hip"]
 
 
 def build_probes() -> list:

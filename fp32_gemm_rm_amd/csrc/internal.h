@@ -36,13 +36,16 @@ __device__ __forceinline__ Problem batch_entry(Problem p) {
   return p;
 }
 
-// Sub-problem covering rows [m0, m0+rows) and columns [n0, n0+cols) of C.
+// Sub-problem covering rows [m0, m0+rows) and columns [n0, n0+cols) of C: the same
+// leading dimensions and batch strides, the operands moved to row m0 of op(A) (a
+// column offset when A is stored transposed) and column n0 of op(B) (a row offset
+// when B is).
 inline Problem sub_problem(const Problem& p, int m0, int n0, int rows, int cols) {
   Problem q = p;
   q.M = rows;
   q.N = cols;
-  q.A = p.A + (long long)m0 * p.lda;
-  q.B = p.B + n0;
+  q.A = p.A + (p.ta ? (long long)m0 : (long long)m0 * p.lda);
+  q.B = p.B + (p.tb ? (long long)n0 * p.ldb : (long long)n0);
   q.C = p.C + (long long)m0 * p.ldc + n0;
   return q;
 }
@@ -51,6 +54,13 @@ inline Problem sub_problem(const Problem& p, int m0, int n0, int rows, int cols)
 // stay 16-byte aligned: the base is 16-byte aligned and ld is a multiple of 4.
 inline bool vec4_ok(const void* x, long long ld) {
   return ((uintptr_t)x % 16 == 0) && (ld % 4 == 0);
+}
+
+// True when every entry of a batch of `batch` problems may take 128-bit loads of A and
+// B: entry b reads from A + b*sA and B + b*sB, so past the first entry the batch strides
+// must keep the 16-byte alignment too.
+inline bool vec_loads_ok(const Problem& p, int batch) {
+  return vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb) && (batch <= 1 || (p.sA % 4 == 0 && p.sB % 4 == 0));
 }
 
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the launch status.
@@ -101,8 +111,23 @@ constexpr int mfma_extent(int n, int side, int edge_min) {
 // C := beta*C on the M x N window (zeros when beta == 0; C is then not read).
 hipError_t launch_scale(const Problem& p, int batch, hipStream_t stream);
 
-// Largest grid the launchers use: x counts tiles, y counts batch entries.
+// Largest grid the launchers use: x counts tiles, y counts batch entries.  A dispatch
+// counts its work-items per dimension in 32 bits, so blocks times threads per block
+// along x must stay below 2^32 as well (grid_fits).
 constexpr long long kMaxGrid = 0x7fffffffLL;
+constexpr long long kMaxWorkItems = 0xffffffffLL;
 constexpr int kMaxBatch = 65535;
+inline bool grid_fits(long long blocks, int threads) {
+  return blocks <= kMaxGrid && blocks * threads <= kMaxWorkItems;
+}
+// The one-thread-per-element kernels (naive, scale) cap their grid at this many blocks and
+// stride over the rest, so that any M x N fits one launch.
+constexpr long long kStrideBlocks = 1LL << 20;
+// Largest output window one tiled launch covers: a larger C runs as row (and column) bands
+// of at most this many elements, each band a launch of its own on the same stream, so that
+// every launcher's grid stays within 32-bit work-item counts.  Band sides are multiples of
+// kBandAlign (a multiple of every tile side: 256, 192, 128, 64, 32).
+constexpr long long kBandElems = 1LL << 32;
+constexpr int kBandAlign = 768;
 
 }  // namespace sgemm_impl

@@ -113,8 +113,8 @@ __global__ __launch_bounds__(256) void lds_tiled_kernel(Problem p, int col_block
 hipError_t launch_lds_tiled(const Problem& p, int batch, hipStream_t stream) {
   const long long cb = (p.N + T - 1) / T;
   const long long rb = (p.M + T - 1) / T;
-  if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
-  const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
+  if (!grid_fits(cb * rb, 256)) return hipErrorInvalidConfiguration;
+  const bool vec = vec_loads_ok(p, batch);
   const dim3 grid((unsigned)(cb * rb), batch), block(256);
 #define SGEMM_LAUNCH_TILED(V, TA_, TB_) \
   hipLaunchKernelGGL((lds_tiled_kernel<V, TA_, TB_>), grid, block, 0, stream, p, (int)cb)

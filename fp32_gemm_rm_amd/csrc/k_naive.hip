@@ -18,34 +18,48 @@ constexpr int kNaiveCols = 64;  // one wavefront across columns
 constexpr int kNaiveRows = 4;
 
 // TA / TB: A stored K x M (element (i, k) at A[k*lda + i]) / B stored N x K.
+// Block id q (0 <= q < blocks) covers rows 4*(q / col_blocks) .. +3 and columns
+// 64*(q % col_blocks) .. +63; the grid is capped at kStrideBlocks and strides over the
+// block ids, so the work-item count of the dispatch stays within 32 bits for any M x N.
 template <bool TA, bool TB>
-__global__ __launch_bounds__(kNaiveCols* kNaiveRows) void naive_kernel(Problem p, int col_blocks) {
+__global__ __launch_bounds__(kNaiveCols* kNaiveRows) void naive_kernel(Problem p, long long col_blocks,
+                                                                       long long blocks) {
   p = batch_entry(p);
-  const int bm = blockIdx.x / col_blocks;
-  const int bn = blockIdx.x - bm * col_blocks;
-  const int i = bm * kNaiveRows + threadIdx.y;
-  const int j = bn * kNaiveCols + threadIdx.x;
-  if (i >= p.M || j >= p.N) return;
-  const float* a = TA ? p.A + i : p.A + (long long)i * p.lda;
-  const float* b = TB ? p.B + (long long)j * p.ldb : p.B + j;
   const long long sa = TA ? p.lda : 1, sb = TB ? 1 : p.ldb;  // steps along k
-  float acc = 0.0f;
-  for (int k = 0; k < p.K; ++k) acc = fmaf(a[k * sa], b[k * sb], acc);
-  float* c = p.C + (long long)i * p.ldc + j;
-  *c = (p.beta == 0.0f) ? p.alpha * acc : fmaf(p.alpha, acc, p.beta * *c);
+  for (long long q = blockIdx.x; q < blocks; q += gridDim.x) {
+    const long long bm = q / col_blocks;
+    const long long bn = q - bm * col_blocks;
+    const long long i = bm * kNaiveRows + threadIdx.y;
+    const long long j = bn * kNaiveCols + threadIdx.x;
+    if (i >= p.M || j >= p.N) continue;
+    const float* a = TA ? p.A + i : p.A + i * p.lda;
+    const float* b = TB ? p.B + j * p.ldb : p.B + j;
+    float acc = 0.0f;
+    for (int k = 0; k < p.K; ++k) acc = fmaf(a[k * sa], b[k * sb], acc);
+    float* c = p.C + i * p.ldc + j;
+    *c = (p.beta == 0.0f) ? p.alpha * acc : fmaf(p.alpha, acc, p.beta * *c);
+  }
 }
 
-// C := beta*C (zeros when beta == 0, without reading C).  One thread per element.
+// C := beta*C (zeros when beta == 0, without reading C).  One thread per element, with
+// the same block map and grid stride as naive_kernel.
 __global__ __launch_bounds__(256) void scale_kernel(float* C, long long ldc, long long sC, int M, int N,
-                                                    float beta, int col_blocks) {
+                                                    float beta, long long col_blocks, long long blocks) {
   C += blockIdx.y * sC;
-  const int bm = blockIdx.x / col_blocks;
-  const int bn = blockIdx.x - bm * col_blocks;
-  const int i = bm * 4 + threadIdx.y;
-  const int j = bn * 64 + threadIdx.x;
-  if (i >= M || j >= N) return;
-  float* c = C + (long long)i * ldc + j;
-  *c = (beta == 0.0f) ? 0.0f : beta * *c;
+  for (long long q = blockIdx.x; q < blocks; q += gridDim.x) {
+    const long long bm = q / col_blocks;
+    const long long bn = q - bm * col_blocks;
+    const long long i = bm * 4 + threadIdx.y;
+    const long long j = bn * 64 + threadIdx.x;
+    if (i >= M || j >= N) continue;
+    float* c = C + i * ldc + j;
+    *c = (beta == 0.0f) ? 0.0f : beta * *c;
+  }
+}
+
+// Blocks of the one-thread-per-element grid: capped at kStrideBlocks.
+inline unsigned stride_grid(long long blocks) {
+  return (unsigned)(blocks < kStrideBlocks ? blocks : kStrideBlocks);
 }
 
 }  // namespace
@@ -53,25 +67,25 @@ __global__ __launch_bounds__(256) void scale_kernel(float* C, long long ldc, lon
 hipError_t launch_naive(const Problem& p, int batch, hipStream_t stream) {
   const long long cb = (p.N + kNaiveCols - 1) / kNaiveCols;
   const long long rb = (p.M + kNaiveRows - 1) / kNaiveRows;
-  if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)(cb * rb), batch), block(kNaiveCols, kNaiveRows);
+  const long long blocks = cb * rb;
+  const dim3 grid(stride_grid(blocks), batch), block(kNaiveCols, kNaiveRows);
   if (p.ta && p.tb)
-    hipLaunchKernelGGL((naive_kernel<true, true>), grid, block, 0, stream, p, (int)cb);
+    hipLaunchKernelGGL((naive_kernel<true, true>), grid, block, 0, stream, p, cb, blocks);
   else if (p.ta)
-    hipLaunchKernelGGL((naive_kernel<true, false>), grid, block, 0, stream, p, (int)cb);
+    hipLaunchKernelGGL((naive_kernel<true, false>), grid, block, 0, stream, p, cb, blocks);
   else if (p.tb)
-    hipLaunchKernelGGL((naive_kernel<false, true>), grid, block, 0, stream, p, (int)cb);
+    hipLaunchKernelGGL((naive_kernel<false, true>), grid, block, 0, stream, p, cb, blocks);
   else
-    hipLaunchKernelGGL((naive_kernel<false, false>), grid, block, 0, stream, p, (int)cb);
+    hipLaunchKernelGGL((naive_kernel<false, false>), grid, block, 0, stream, p, cb, blocks);
   return hipGetLastError();
 }
 
 hipError_t launch_scale(const Problem& p, int batch, hipStream_t stream) {
   const long long cb = (p.N + 63) / 64;
   const long long rb = (p.M + 3) / 4;
-  if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)(cb * rb), batch), dim3(64, 4), 0, stream, p.C, p.ldc, p.sC, p.M,
-                     p.N, p.beta, (int)cb);
+  const long long blocks = cb * rb;
+  hipLaunchKernelGGL(scale_kernel, dim3(stride_grid(blocks), batch), dim3(64, 4), 0, stream, p.C, p.ldc, p.sC, p.M,
+                     p.N, p.beta, cb, blocks);
   return hipGetLastError();
 }
 

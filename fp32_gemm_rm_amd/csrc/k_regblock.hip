@@ -26,9 +26,9 @@ template <int BM, int BN, int BK, int TM, int TN, int PAD_A>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream) {
   const long long cb = (p.N + BN - 1) / BN;
   const long long rb = (p.M + BM - 1) / BM;
-  if (cb * rb > kMaxGrid) return hipErrorInvalidConfiguration;
+  if (!grid_fits(cb * rb, 256)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(cb * rb), batch), block(256);
-  const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
+  const bool vec = vec_loads_ok(p, batch);
 #define SGEMM_LAUNCH_RB(V, TA_, TB_) \
   hipLaunchKernelGGL((regblock_kernel<BM, BN, BK, TM, TN, PAD_A, V, TA_, TB_>), grid, block, 0, stream, p, (int)cb)
   if (vec) {

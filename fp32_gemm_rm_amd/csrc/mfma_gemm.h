@@ -358,7 +358,7 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   const long long nmfma = (long long)map.tiles_m * map.tiles_n;
   const long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
   const dim3 block(WM * WN * KS * 64);
-  const bool vec = vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb);
+  const bool vec = vec_loads_ok(p, batch);
   if constexpr (EDGE_MIN == 0 && BM == 256 && BN == 256) {  // the workspace holds 256 x 256 slots
     if (ws != nullptr && batch == 1 && nmfma % kStreamKWgs != 0) {
       // the partial wave, and the full wave before it where the partial one is under 1/8
@@ -369,7 +369,7 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
       map.sk_wgs = kStreamKWgs;
       map.ws = ws;
       const long long blocks = map.dp_tiles + map.sk_wgs + edge_tiles;
-      if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
+      if (!grid_fits(blocks, block.x)) return hipErrorInvalidConfiguration;
       if (vec)
         hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, 0, true, true, PF>),
                            dim3((unsigned)blocks), block, 0, stream, p, map);
@@ -384,7 +384,7 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
     }
   }
   const long long blocks = nmfma + edge_tiles;
-  if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
+  if (!grid_fits(blocks, block.x)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks, batch);
   if (vec)
     hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF>),

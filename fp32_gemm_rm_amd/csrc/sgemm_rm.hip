@@ -80,9 +80,10 @@ int check(const Call& c, const Positions& pos) {
   return 0;
 }
 
-// Enqueue `batch` problems spaced by p.sA, p.sB, p.sC (p already validated, M, N > 0).
-// ws: a stream-K workspace of at least kStreamKBytes, or nullptr.
-int launch(Problem p, int batch, hipStream_t stream, int variant, float* ws) {
+// Enqueue `batch` problems spaced by p.sA, p.sB, p.sC (p already validated, M, N > 0),
+// in launches of at most kMaxBatch entries.  ws: a stream-K workspace of at least
+// kStreamKBytes, or nullptr.
+int launch_batches(Problem p, int batch, hipStream_t stream, int variant, float* ws) {
   if (batch != 1) ws = nullptr;  // stream-K covers single products only
   while (batch > 0) {
     const int chunk = batch < sgemm_impl::kMaxBatch ? batch : sgemm_impl::kMaxBatch;
@@ -131,6 +132,31 @@ int launch(Problem p, int batch, hipStream_t stream, int variant, float* ws) {
     p.B += (long long)chunk * p.sB;
     p.C += (long long)chunk * p.sC;
   }
+  return 0;
+}
+
+// As launch_batches, with a C window of more than kBandElems elements cut into bands of
+// rows (and of columns, for rows wider than kBandElems / kBandAlign) that each launch on
+// their own, in order on the same stream: a tiled launcher's work-item count then stays
+// within 32 bits.  The one-thread-per-element kernels (naive, and the scale pass of
+// alpha == 0 or K == 0) stride over any grid and take the window whole.
+int launch(const Problem& p, int batch, hipStream_t stream, int variant, float* ws) {
+  using sgemm_impl::kBandAlign;
+  using sgemm_impl::kBandElems;
+  const bool strided = variant == SGEMM_RM_VARIANT_NAIVE || p.alpha == 0.0f || p.K == 0;
+  if (strided || (long long)p.M * p.N <= kBandElems) return launch_batches(p, batch, stream, variant, ws);
+  const int bn = (long long)p.N * kBandAlign <= kBandElems
+                     ? p.N
+                     : (int)(kBandElems / kBandAlign / kBandAlign * kBandAlign);
+  const long long rows = kBandElems / bn / kBandAlign * kBandAlign;
+  const int bm = rows > kBandAlign ? (int)(rows < p.M ? rows : p.M) : kBandAlign;
+  for (long long m0 = 0; m0 < p.M; m0 += bm)
+    for (long long n0 = 0; n0 < p.N; n0 += bn) {
+      const int rows_b = (int)(bm < p.M - m0 ? bm : p.M - m0), cols_b = (int)(bn < p.N - n0 ? bn : p.N - n0);
+      const int rc = launch_batches(sgemm_impl::sub_problem(p, (int)m0, (int)n0, rows_b, cols_b), batch, stream,
+                                    variant, ws);
+      if (rc != 0) return rc;
+    }
   return 0;
 }
 

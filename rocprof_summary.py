@@ -2,7 +2,7 @@
 
 Reads the CSV files that ``rocprofv3 --kernel-trace --stats`` and ``rocprofv3 --pmc``
 write (``-o run --output-format csv``) and prints the figures the profile summaries
-quote; with ``--traffic-json`` it also writes the per-launch HBM traffic record that
+quote; with ``--traffic-json`` it also writes the per-launch fabric traffic record that
 ``bench.py`` reports as ``roofline.traffic``.
 
 Layout under ``--prof-dir`` (one directory per run, as bench.py's profiling commands
@@ -17,7 +17,7 @@ Counter passes run bench.py with ``--calibrate-copy``: a 256 MiB device copy
 against its known size give the factor that turns each counter into bytes.
 
 Usage (from the repository root):
-  python -m fp32_gemm_rm_amd.rocprof_summary --prof-dir gpurun_out/prof --workload sgemm_4096 \\
+  python rocprof_summary.py --prof-dir gpurun_out/prof --workload sgemm_4096 \\
       [--traffic-json profiles/traffic_mfma_sgemm_4096.json]
 """
 from __future__ import annotations
@@ -29,7 +29,7 @@ import os
 import statistics
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
@@ -152,12 +152,14 @@ def main(argv=None) -> int:
             "workload": args.workload,
             "kernel": kernels[0] if len(kernels) == 1 else kernels,
             "kernel_source_sha256_16": bench.source_digest(),
-            "hbm_bytes_per_launch": round(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]),
+            "fabric_bytes_per_launch": round(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]),
             "fetch_bytes_per_launch": round(rec["fetch_bytes_per_launch"]),
             "write_bytes_per_launch": round(rec["write_bytes_per_launch"]),
             "fetch_calibration": round(rec["fetch_calibration"], 4),
             "write_calibration": round(rec["write_calibration"], 4),
             "calibration": f"FETCH_SIZE and WRITE_SIZE of a 256 MiB {COPY_KERNEL} in the same process",
+            "counters": "FETCH_SIZE and WRITE_SIZE count traffic between the L2 caches and the memory fabric; "
+                        "hits in the last-level cache in front of HBM are included",
             "dispatches": rec["dispatches"],
         }
         with open(args.traffic_json, "w") as f:

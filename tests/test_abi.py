@@ -96,11 +96,30 @@ def test_strerror(lib):
 
 
 def test_binding_raises_on_invalid_arguments(lib):
-    from fp32_gemm_rm_amd import SgemmError, sgemm_rm
+    """A negative return code (an invalid argument) raises a ValueError, not a RuntimeError."""
+    from fp32_gemm_rm_amd import SgemmArgumentError, SgemmError, sgemm_rm, sgemm_rm_plan_tiles
 
-    with pytest.raises(SgemmError) as e:
+    with pytest.raises(ValueError) as e:
         sgemm_rm(4, 4, 4, 1.0, F, 2, F, 4, 0.0, F, 4)
     assert e.value.code == -6
+    assert isinstance(e.value, SgemmArgumentError) and isinstance(e.value, SgemmError)
+    assert not isinstance(e.value, RuntimeError)
+    with pytest.raises(ValueError) as e:
+        sgemm_rm_plan_tiles(4, -2, 4)
+    assert e.value.code == -2
+
+
+def test_binding_raises_runtime_error_on_hip_errors(lib):
+    """A positive return code (the hipError_t of a launch) raises a RuntimeError, not a
+    ValueError; the message is the HIP runtime's text for the code."""
+    from fp32_gemm_rm_amd import SgemmLaunchError, binding
+
+    hip_error_invalid_configuration = 9
+    with pytest.raises(RuntimeError) as e:
+        binding._check(hip_error_invalid_configuration)
+    assert isinstance(e.value, SgemmLaunchError) and not isinstance(e.value, ValueError)
+    assert e.value.code == hip_error_invalid_configuration
+    assert binding._check(0) == 0
 
 
 G = 1 << 20  # a batch stride large enough for the 4 x 4 problems below
@@ -282,3 +301,4 @@ def test_workspace_size(lib):
     assert sgemm_rm_workspace_size(6144, 6144, 6144) == 0
     # stream-K covers full 256 x 256 tiles only
     assert sgemm_rm_workspace_size(4600, 4608, 4608) == 0
+

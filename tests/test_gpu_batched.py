@@ -75,6 +75,19 @@ def test_batched_parity(oracle, variant, M, N, K, batch, share_b):
     _check_entries(oracle, out, M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, range(batch))
 
 
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_batched_aligned_rows_odd_strides(oracle, variant):
+    """Leading dimensions that are multiples of 4 on 16-byte aligned buffers, with batch
+    strides that are not: entry 0 would allow 128-bit loads, entries 1.. do not, so every
+    launcher must take the scalar loads for the whole batch."""
+    M, N, K, batch = 70, 96, 132, 4
+    lda, ldb, ldc = K, N, N
+    sA, sB, sC = M * lda + 1, K * ldb + 3, M * ldc + 5
+    A, B, C = make_batched_inputs(batch, M, N, K, lda, ldb, ldc, sA, sB, sC, "uniform", seed=77, c_init="random")
+    out = _run_batched(M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, batch, VARIANTS[variant])
+    _check_entries(oracle, out, M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, range(batch))
+
+
 def test_batched_more_entries_than_one_launch(oracle):
     """70000 entries: two launches (65535 + 4465); integer inputs, checked bit for bit at the seams."""
     import torch

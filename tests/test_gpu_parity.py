@@ -1,11 +1,10 @@
 """GPU parity: every kernel family against the CPU oracle, through the C ABI.
 
-Small and mid-size workloads (256^3, 1024^3, the ragged 1000 x 1030 x 999 with
-padded leading dimensions) are compared element by element; 4096^3 and
-8192^3 are compared on sampled entries (whole rows and columns at tile
-boundaries plus random entries) in the launch configuration the benchmark
-times.  Closed forms that float32 must reproduce exactly are compared bit for
-bit.
+Every workload (256^3, 1024^3, the ragged 1000 x 1030 x 999 with padded
+leading dimensions, 4096^3 and 8192^3) is compared element by element over
+all of its outputs, the full-size ones in the launch configuration the
+benchmark times.  Closed forms that float32 must reproduce exactly are
+compared bit for bit.
 """
 import numpy as np
 import pytest
@@ -19,7 +18,7 @@ from fp32_gemm_rm_amd.workloads import (
     workload_inputs,
 )
 
-from .parity import assert_within_bound, c_window, check_padding, device, edge_shapes, run_gemm, sample_entries
+from .parity import assert_within_bound, c_window, check_padding, device, edge_shapes, run_gemm
 
 pytestmark = pytest.mark.gpu
 
@@ -52,33 +51,48 @@ def test_workload_full(oracle, name, variant):
 
 
 @pytest.mark.parametrize("name", ["sgemm_4096", "sgemm_8192"])
-def test_workload_sampled(oracle, name):
-    """Full-size workloads on the default (benchmarked) path, checked at sampled entries."""
+def test_workload_full_size(oracle, name):
+    """The full-size workloads on the default path, in the call the benchmark times
+    (sgemm_rm_ex, variant auto): every one of the M x N outputs against the oracle, within
+    the bound, and C's padding (none here) untouched."""
     w = WORKLOAD_BY_NAME[name]
-    print(f"[parity] {name} sampled", flush=True)
+    print(f"[parity] {name} full", flush=True)
     A, B, C = workload_inputs(w)
     out = run_gemm(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, 0)
-    rows, cols = sample_entries(w.M, w.N, seed=w.seed)
-    ref, S = oracle.entries(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, rows, cols)
-    got = c_window(out, w.M, w.N, w.ldc)[rows, cols]
-    r = assert_within_bound(got, ref, S, name)
-    assert np.all(np.isfinite(c_window(out, w.M, w.N, w.ldc)))
-    print(f"[parity] {name} sampled max err/bound {r:.3g}", flush=True)
+    print(f"[parity] {name}: GPU done, oracle on {oracle.threads()} threads", flush=True)
+    ref, S = oracle.full(w.M, w.N, w.K, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc)
+    r = assert_within_bound(c_window(out, w.M, w.N, w.ldc), ref, S, name)
+    check_padding(out, C, w.M, w.N, w.ldc)
+    print(f"[parity] {name} full: {w.M * w.N} outputs, max err/bound {r:.3g}", flush=True)
 
 
-@pytest.mark.parametrize("variant", list(VARIANTS))
-def test_integer_exact_full_size(oracle, variant):
-    """Integer inputs at 4096^3 make every summation order exact: sampled entries bit-exact."""
-    M = N = K = 4096 if variant in ("mfma", "auto", "regblock") else 1024
+@pytest.fixture(scope="module")
+def integer_4096(oracle):
+    """Integer inputs in [-4, 4] at 4096^3 (C NaN: beta = 0 must not read it) and the
+    oracle's full result, shared by the variants below."""
+    M = N = K = 4096
     a = integer_matrix(M, K, -4, 4, seed=41)
     b = integer_matrix(K, N, -4, 4, seed=42)
     A, B = a.reshape(-1), b.reshape(-1)
     C = np.full(M * N, np.nan, np.float32)
-    out = run_gemm(M, N, K, 1.0, A, K, B, N, 0.0, C, N, VARIANTS[variant])
-    rows, cols = sample_entries(M, N, seed=43, n_random=2048)
-    ref, _ = oracle.entries(M, N, K, 1.0, A, K, B, N, 0.0, C, N, rows, cols)
-    got = out.reshape(M, N)[rows, cols].astype(np.float64)
-    np.testing.assert_array_equal(got, ref)
+    ref, _ = oracle.full(M, N, K, 1.0, A, K, B, N, 0.0, C, N, with_absab=False)
+    return A, B, C, ref
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_integer_exact_full_size(oracle, integer_4096, variant):
+    """Integer inputs make every summation order exact: at 4096^3 every output is
+    bit-exact for the MFMA, default and register-blocked paths; the slower families run
+    the 1024^3 corner of the same inputs, every output bit-exact."""
+    A, B, C, ref = integer_4096
+    n = 4096 if variant in ("mfma", "auto", "regblock") else 1024
+    print(f"[parity] integer {n}^3 variant={variant}", flush=True)
+    # the n x n x n leading corner: A rows of 4096 floats (lda = 4096), B rows likewise
+    out = run_gemm(n, n, n, 1.0, A, 4096, B, 4096, 0.0, C[: n * n], n, VARIANTS[variant])
+    want = ref if n == 4096 else oracle.full(n, n, n, 1.0, A, 4096, B, 4096, 0.0, None, n, with_absab=False)[0]
+    got = out.reshape(n, n).astype(np.float64)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{variant}: {len(bad)} of {n * n} outputs differ, first at {bad[:3].tolist()}"
 
 
 @pytest.mark.parametrize("variant", list(VARIANTS))

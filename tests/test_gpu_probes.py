@@ -69,20 +69,3 @@ def test_lds_bank_behaviour():
     assert cyc[(1, 32)] > 8 * cyc[(1, 1)]
     assert cyc[(1, 33)] < 1.5 * cyc[(1, 1)]
     assert cyc[(1, 17)] < 1.5 * cyc[(1, 1)]
-
-
-def test_mfma_schedule_costs():
-    """The K-tile schedule probe runs every configuration; with neither a barrier nor LDS
-    reads each one keeps the matrix cores near their peak (the configurations differ only in
-    how the same MFMAs are spread over wavefronts), and LDS fragment reads issued right
-    before the MFMAs that use them cost throughput in every configuration."""
-    out = _run(["mfma_schedule_probe"], timeout=120)
-    print(out)
-    rows = re.findall(r"waves/SIMD=(\d+) acc_blocks=\s*(\d+) barrier=(\d) lds=(\d)\s+\S+ ms\s+(\S+) TFLOP/s", out)
-    assert len(rows) == 20, out
-    tf = {(int(w), int(a), int(b), int(l)): float(t) for w, a, b, l, t in rows}
-    bare = [t for (w, a, b, l), t in tf.items() if b == 0 and l == 0]
-    assert min(bare) > 0.9 * max(bare) and max(bare) < 160.0
-    for (w, a, b, l), t in tf.items():
-        if l == 1 and b == 0:
-            assert t < tf[(w, a, 0, 0)], (w, a, t)
