@@ -35,6 +35,7 @@ from .binding import (  # noqa: F401
     sgemm_rm_ex,
     sgemm_rm_op,
     sgemm_rm_op_strided_batched_ex,
+    sgemm_rm_op_strided_batched_noalloc,
     sgemm_rm_op_strided_batched_ws,
     sgemm_rm_plan_tiles,
     sgemm_rm_strerror,

@@ -47,7 +47,12 @@ _lib = None
 EXPORTED_SYMBOLS = ("sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex",
                     "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex", "sgemm_cm", "sgemm_cm_strided_batched_ex",
                     "sgemm_rm_op_strided_batched_ws", "sgemm_cm_strided_batched_ws", "sgemm_rm_workspace_size",
-                    "sgemm_rm_plan_tiles", "sgemm_rm_strerror", "sgemm_rm_version")
+                    "sgemm_rm_plan_tiles", "sgemm_rm_strerror", "sgemm_rm_version",
+                    "sgemm_rm_op_strided_batched_noalloc")
+#: Bytes of the library's static device scratch (SGEMM_RM_SCRATCH_BYTES) and the code of a
+#: call that would need more (SGEMM_RM_ERR_SCRATCH_LIMIT).
+SGEMM_RM_SCRATCH_BYTES = 128 << 20
+SGEMM_RM_ERR_SCRATCH_LIMIT = -100
 
 
 class SgemmError(Exception):
@@ -113,6 +118,8 @@ def load_library():
         for name in ("sgemm_rm_op_strided_batched_ws", "sgemm_cm_strided_batched_ws"):
             getattr(lib, name).argtypes = wargs
             getattr(lib, name).restype = ctypes.c_int
+        lib.sgemm_rm_op_strided_batched_noalloc.argtypes = obargs
+        lib.sgemm_rm_op_strided_batched_noalloc.restype = ctypes.c_int
         lib.sgemm_rm_workspace_size.argtypes = [ctypes.c_int] * 4
         lib.sgemm_rm_workspace_size.restype = ctypes.c_longlong
         lib.sgemm_rm_plan_tiles.argtypes = [ctypes.c_int] * 4
@@ -144,6 +151,17 @@ def sgemm_cm_strided_batched_ws(transA, transB, M, N, K, alpha, A, lda, strideA,
         int(transA), int(transB), int(M), int(N), int(K), float(alpha), A or None, int(lda), int(strideA),
         B or None, int(ldb), int(strideB), float(beta), C or None, int(ldc), int(strideC), int(batch),
         workspace or None, int(workspace_bytes), stream or None, int(variant)))
+
+
+def sgemm_rm_op_strided_batched_noalloc(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C,
+                                        ldc, strideC, batch, stream=0, variant=SGEMM_RM_VARIANT_AUTO):
+    """The general row-major call with the library's static scratch as its workspace (no
+    allocation; calls that overlap on one GPU race on the scratch)."""
+    lib = load_library()
+    return _check(lib.sgemm_rm_op_strided_batched_noalloc(
+        int(transA), int(transB), int(M), int(N), int(K), float(alpha), A or None, int(lda), int(strideA),
+        B or None, int(ldb), int(strideB), float(beta), C or None, int(ldc), int(strideC), int(batch),
+        stream or None, int(variant)))
 
 
 def sgemm_rm_workspace_size(M, N, K, batch=1) -> int:

@@ -4,6 +4,7 @@
 #include "sgemm_rm.h"
 
 #include <cstdint>
+#include <mutex>
 
 #include "internal.h"
 #include "tile_plan.h"
@@ -11,6 +12,46 @@
 namespace {
 
 using sgemm_impl::Problem;
+
+// The scratch of sgemm_rm_op_strided_batched_noalloc: the stream-K workspace kept in the
+// library's own static device memory, so that the call allocates nothing.  Each GPU the
+// library runs on holds its own copy from the code object's load until the process ends.
+// In host code `scratch` only names the symbol: its device address, per device, comes
+// from hipGetSymbolAddress (scratch_on), and only that address reaches a kernel.
+constexpr long long kScratchBytes = SGEMM_RM_SCRATCH_BYTES;
+static_assert(kScratchBytes >= sgemm_impl::kStreamKBytes, "the scratch holds a stream-K workspace");
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The address of `scratch` on the device that `stream` belongs to, looked up on the
+// first call for that device with that device current (the caller's current device is
+// restored).
+hipError_t scratch_on(hipStream_t stream, float** out) {
+  hipDevice_t dev = 0;
+  hipError_t err = hipStreamGetDevice(stream, &dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    int cur = 0;
+    err = hipGetDevice(&cur);
+    if (err != hipSuccess) return err;
+    if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return err;
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (err == hipSuccess) err = back;
+    }
+    if (err != hipSuccess) return err;
+    g_scratch[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
 
 // 1-based positions of the arguments of one entry point; 0 = the entry point has no
 // such argument.  Every entry point lists its arguments in this relative order:
@@ -160,11 +201,23 @@ int launch(const Problem& p, int batch, hipStream_t stream, int variant, float* 
   return 0;
 }
 
+// Workspace bytes that a call's kernels may use given a large enough workspace (0: none
+// of them can): stream-K, single products only, where the default path's cost model picks
+// it, the 256 configuration is forced, or a banded window (launch) leaves the choice to
+// each band.  An over-estimate only costs the scratch lookup; the launchers decide.
+long long workspace_need(const Problem& p, int batch, int variant) {
+  if (batch != 1 || p.alpha == 0.0f || p.K == 0) return 0;
+  if (variant == SGEMM_RM_VARIANT_MFMA_T256) return sgemm_impl::kStreamKBytes;
+  if (variant != SGEMM_RM_VARIANT_AUTO && variant != SGEMM_RM_VARIANT_MFMA) return 0;
+  if ((long long)p.M * p.N > sgemm_impl::kBandElems) return sgemm_impl::kStreamKBytes;
+  return sgemm_impl::plan_tiles(p.M, p.N, p.K, 1, true).stream_k ? sgemm_impl::kStreamKBytes : 0;
+}
+
 // Validate, then run as a row-major problem.  A column-major product C = op(A) op(B)
 // is the row-major product C^T = op(B)^T op(A)^T over the same memory: a column-major
 // X is the row-major X^T with the same leading dimension, so the operands and M, N
 // swap and each operand keeps its transpose flag.
-int run(const Call& c, const Positions& pos, hipStream_t stream) {
+int run(const Call& c, const Positions& pos, hipStream_t stream, bool use_scratch = false) {
   const int bad = check(c, pos);
   if (bad != 0) return bad;
   if (c.M == 0 || c.N == 0 || c.batch == 0) return 0;
@@ -177,6 +230,17 @@ int run(const Call& c, const Positions& pos, hipStream_t stream) {
   // a workspace too small or not 16-byte aligned (the fix-up reads it as float4) is not used
   const bool ws_ok = c.ws_bytes >= sgemm_impl::kStreamKBytes && reinterpret_cast<uintptr_t>(c.ws) % 16 == 0;
   float* ws = ws_ok ? static_cast<float*>(c.ws) : nullptr;
+  if (use_scratch) {
+    // the library's static scratch stands in for the caller's workspace, for the calls
+    // whose kernels use one (a call that launches nothing, or no stream-K, touches no
+    // scratch and makes no lookup)
+    const long long need = workspace_need(p, c.batch, c.variant);
+    if (need > kScratchBytes) return SGEMM_RM_ERR_SCRATCH_LIMIT;
+    if (need > 0) {
+      const hipError_t err = scratch_on(stream, &ws);
+      if (err != hipSuccess) return (int)err;
+    }
+  }
   return launch(p, c.batch, stream, c.variant, ws);
 }
 
@@ -262,6 +326,15 @@ int sgemm_cm_strided_batched_ws(int transA, int transB, int M, int N, int K, flo
              kPosOpBatchedWs, stream);
 }
 
+int sgemm_rm_op_strided_batched_noalloc(int transA, int transB, int M, int N, int K, float alpha, const float* A,
+                                        int lda, long long strideA, const float* B, int ldb, long long strideB,
+                                        float beta, float* C, int ldc, long long strideC, int batch,
+                                        hipStream_t stream, int variant) {
+  return run({false, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+              nullptr, 0, variant},
+             kPosOpBatched, stream, true);
+}
+
 long long sgemm_rm_workspace_size(int M, int N, int K, int batch) {
   if (M < 0) return -1;
   if (N < 0) return -2;
@@ -290,6 +363,7 @@ const char* sgemm_rm_strerror(int code) {
       "invalid argument 21"};
   if (code == 0) return "success";
   if (code < 0 && code >= -21) return kInvalid[-code - 1];
+  if (code == SGEMM_RM_ERR_SCRATCH_LIMIT) return "the problem needs more scratch than SGEMM_RM_SCRATCH_BYTES";
   if (code > 0) return hipGetErrorString((hipError_t)code);
   return "unknown error code";
 }

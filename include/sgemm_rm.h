@@ -222,6 +222,37 @@ int sgemm_cm_strided_batched_ws(int transA, int transB, int M, int N, int K, flo
                                 hipStream_t stream, int variant);
 
 /*
+ * Size of the library's static device scratch (128 MiB per GPU), and the return code of a
+ * call that would need more scratch than that.
+ */
+#define SGEMM_RM_SCRATCH_BYTES (128LL << 20)
+#define SGEMM_RM_ERR_SCRATCH_LIMIT (-100)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sgemm_rm_op_strided_batched_ws with
+ * the library's own static scratch as the workspace.  Same arguments, rules and return
+ * codes as sgemm_rm_op_strided_batched_ex (the stream is argument 18, -19 an unknown
+ * variant); the kernels, and so the results, are those of sgemm_rm_op_strided_batched_ws
+ * given a workspace of SGEMM_RM_SCRATCH_BYTES (stream-K where that call would run it).
+ * The call allocates nothing: the scratch is a static __device__ array of
+ * SGEMM_RM_SCRATCH_BYTES that each GPU the library runs on holds from the first call
+ * until the process ends; its address on a device is looked up (hipGetSymbolAddress)
+ * on the first call for that device, with that device made current for the lookup.
+ * A problem whose kernels would need more than SGEMM_RM_SCRATCH_BYTES returns
+ * SGEMM_RM_ERR_SCRATCH_LIMIT before any launch (every current kernel needs at most
+ * that much).  Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents; nothing in it has to start at zero.  Calls that may overlap on one
+ * GPU (different streams not synchronised, or several host threads) race on the
+ * scratch and must be serialised by the caller.  A positive value is a hipError_t
+ * (of the lookup or a launch).
+ */
+int sgemm_rm_op_strided_batched_noalloc(int transA, int transB, int M, int N, int K, float alpha, const float* A,
+                                        int lda, long long strideA, const float* B, int ldb, long long strideB,
+                                        float beta, float* C, int ldc, long long strideC, int batch,
+                                        hipStream_t stream, int variant);
+
+/*
  * Workspace bytes with which the _ws calls run an M x N x K problem (repeated `batch`
  * times) as stream-K, or 0 where the cost model keeps the one-tile-per-workgroup path.
  * Currently 0 or 128 MiB (two 256 x 256 float partial tiles for each of 256

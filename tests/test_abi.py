@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["sgemm_cm", "sgemm_cm_strided_batched_ex", "sgemm_cm_strided_batched_ws",
                                      "sgemm_rm", "sgemm_rm_ex", "sgemm_rm_op", "sgemm_rm_op_strided_batched_ex",
-                                     "sgemm_rm_op_strided_batched_ws", "sgemm_rm_plan_tiles", "sgemm_rm_strerror",
+                                     "sgemm_rm_op_strided_batched_noalloc", "sgemm_rm_op_strided_batched_ws", "sgemm_rm_plan_tiles", "sgemm_rm_strerror",
                                      "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex", "sgemm_rm_version",
                                      "sgemm_rm_workspace_size"]
 
@@ -302,3 +302,27 @@ def test_workspace_size(lib):
     # stream-K covers full 256 x 256 tiles only
     assert sgemm_rm_workspace_size(4600, 4608, 4608) == 0
 
+
+def test_noalloc_invalid_arguments_before_any_hip_call(lib):
+    """The allocation-free call checks its arguments (positions as the _ex call) before it
+    looks up its scratch or launches anything."""
+    args = [0, 0, 4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2, None, 0]
+    fn = lib.sgemm_rm_op_strided_batched_noalloc
+    for pos, bad in ((1, 2), (3, -1), (4, -1), (5, -1), (8, 3), (9, -1), (11, 3), (12, -1), (15, 3), (16, 15),
+                     (17, -1), (19, 10)):
+        a = list(args)
+        a[pos - 1] = bad
+        assert fn(*a) == -pos, (pos, bad)
+    # quick returns touch no scratch and launch nothing
+    assert fn(0, 0, 0, 4, 4, 1.0, None, 4, 0, None, 4, 0, 0.0, None, 4, 0, 1, None, 0) == 0
+    assert fn(0, 0, 4, 4, 4, 0.0, None, 4, 0, None, 4, 0, 1.0, F, 4, 0, 1, None, 0) == 0
+
+
+def test_scratch_limit_code(lib):
+    from fp32_gemm_rm_amd import binding
+
+    assert binding.SGEMM_RM_SCRATCH_BYTES == 128 << 20
+    assert binding.sgemm_rm_strerror(binding.SGEMM_RM_ERR_SCRATCH_LIMIT).startswith("the problem needs more scratch")
+    text = open(HEADER).read()
+    assert "#define SGEMM_RM_SCRATCH_BYTES (128LL << 20)" in text
+    assert "#define SGEMM_RM_ERR_SCRATCH_LIMIT (-100)" in text
