@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     SGEMM_RM_VARIANT_LDS_TILED,
     SGEMM_RM_VARIANT_MFMA,
     SGEMM_RM_VARIANT_MFMA_T32,
+    SGEMM_RM_VARIANT_MFMA_T16,
     SGEMM_RM_VARIANT_MFMA_T192,
     SGEMM_RM_VARIANT_MFMA_T64,
     SGEMM_RM_VARIANT_MFMA_T128,

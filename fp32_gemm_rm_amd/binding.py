@@ -20,6 +20,7 @@ SGEMM_RM_VARIANT_MFMA_T128 = 6
 SGEMM_RM_VARIANT_MFMA_T64 = 7
 SGEMM_RM_VARIANT_MFMA_T32 = 8
 SGEMM_RM_VARIANT_MFMA_T192 = 9
+SGEMM_RM_VARIANT_MFMA_T16 = 10
 VARIANTS = {
     "auto": SGEMM_RM_VARIANT_AUTO,
     "naive": SGEMM_RM_VARIANT_NAIVE,
@@ -31,10 +32,11 @@ VARIANTS = {
     "mfma_t64": SGEMM_RM_VARIANT_MFMA_T64,
     "mfma_t32": SGEMM_RM_VARIANT_MFMA_T32,
     "mfma_t192": SGEMM_RM_VARIANT_MFMA_T192,
+    "mfma_t16": SGEMM_RM_VARIANT_MFMA_T16,
 }
 #: Forced MFMA tile configurations by tile side.
 TILE_VARIANTS = {256: SGEMM_RM_VARIANT_MFMA_T256, 192: SGEMM_RM_VARIANT_MFMA_T192, 128: SGEMM_RM_VARIANT_MFMA_T128,
-                 64: SGEMM_RM_VARIANT_MFMA_T64, 32: SGEMM_RM_VARIANT_MFMA_T32}
+                 64: SGEMM_RM_VARIANT_MFMA_T64, 32: SGEMM_RM_VARIANT_MFMA_T32, 16: SGEMM_RM_VARIANT_MFMA_T16}
 
 SGEMM_RM_OP_N = 0
 SGEMM_RM_OP_T = 1

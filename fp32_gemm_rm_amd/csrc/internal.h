@@ -96,8 +96,8 @@ constexpr long long kStreamKBytes = 2LL * kStreamKWgs * 256 * 256 * 4;
 // whole tile row or column of MFMA work; 32 configuration: 4) or, in the 256 configuration
 // (0: never MFMA), as scalar edge tiles (its workgroups fill a CU's register file and a
 // guarded tile there costs a whole 256 x 256 tile; the cost model steers ragged shapes to
-// the smaller configurations).
-constexpr int mfma_edge_min(int side) { return side == 256 ? 0 : side == 32 ? 4 : 16; }
+// the smaller configurations); in the 16 configuration every block is guarded (1).
+constexpr int mfma_edge_min(int side) { return side == 256 ? 0 : side == 32 ? 4 : side == 16 ? 1 : 16; }
 // The 256 configuration's thin-strip form: where both remainders past its full tiles are
 // thinner than kThin256, they run as thin strips (same launch, after the tiles) instead of
 // scalar edge tiles; a 256 x 256 tile is never guarded.

@@ -395,6 +395,35 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   return hipGetLastError();
 }
 
+// The 16 configuration: one 16 x 16 block of C per workgroup of NT threads, over the whole
+// K range split between its wavefronts, on 16 x 16 x 4 MFMA with operands loaded straight
+// from global memory (thin_strip's block form, for whole blocks).  For products whose
+// output is a few hundred such blocks: the larger tiles would run a handful of workgroups,
+// each a latency-bound chain of K-tiles (256^3: 3.6 us against 4.5 us on 32 x 32 tiles;
+// 256 x 256 x 1024: 5.8 against 8.7 us).  Block (bm, bn) is workgroup bm * blocks_n + bn.
+constexpr int kBlock16Threads = 512;
+template <int NT, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__(NT) void block16_kernel(Problem p, int blocks_n) {
+  p = batch_entry(p);
+  __shared__ __attribute__((aligned(16))) float smem[NT / 64 * 4 * 64];
+  const int bm = blockIdx.x / blocks_n, bn = blockIdx.x - (blockIdx.x / blocks_n) * blocks_n;
+  const int first = bm * kThinMax, lo = bn * kThinMax;
+  thin_strip<NT, TA, TB, VEC>(p, true, first, min(kThinMax, p.M - first), lo, min(kThinMax, p.N - lo), smem);
+}
+
+template <bool TA, bool TB>
+hipError_t launch_block16(const Problem& p, int batch, hipStream_t stream) {
+  constexpr int NT = kBlock16Threads;
+  const long long bm = (p.M + kThinMax - 1) / kThinMax, bn = (p.N + kThinMax - 1) / kThinMax;
+  if (!grid_fits(bm * bn, NT)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(bm * bn), batch), block(NT);
+  if (vec_loads_ok(p, batch))
+    hipLaunchKernelGGL((block16_kernel<NT, TA, TB, true>), grid, block, 0, stream, p, (int)bn);
+  else
+    hipLaunchKernelGGL((block16_kernel<NT, TA, TB, false>), grid, block, 0, stream, p, (int)bn);
+  return hipGetLastError();
+}
+
 // The tile configurations (tile_plan.h), by tile side.  All but the 32 configuration run
 // mfma_tile_pf (fragments read one K-tile ahead).
 //   256: 256 x 256 tiles, 2 x 2 wavefronts of 128 x 128 (one per SIMD, 256 accumulator
@@ -409,6 +438,8 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
 //        global register sets; two workgroups per CU.
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
 //        256 threads, mfma_tile; four workgroups per CU.
+//   16:  16 x 16 blocks on 16 x 16 x 4 MFMA, K split over 8 wavefronts, no LDS staging
+//        (block16_kernel).
 // Partial tiles (mfma_edge_min): guarded MFMA tiles of the same grid in the 192, 128, 64
 // and 32 configurations, except strips thinner than 16 in the 192, 128 and 64
 // configurations (thin strips); the scalar edge-tile path in the 256 configuration.
@@ -449,6 +480,8 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
     case 32:
       if (p.M % 32 == 0 && p.N % 32 == 0) return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4>(p, batch, stream);
       return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, mfma_edge_min(32)>(p, batch, stream);
+    case 16:
+      return launch_block16<TA, TB>(p, batch, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -45,7 +45,8 @@ __device__ __forceinline__ void edge_tile(const Problem& p, int m0, int n0, floa
 
 // Thin strips (configurations with EDGE_MIN > 1): columns [lo, lo + width) of rows
 // [first, first + nlines) when `cols`, else rows [lo, lo + width) of columns [first,
-// first + nlines); width < EDGE_MIN <= 16 and nlines <= 16.  A strip that thin would cost
+// first + nlines); width <= 16 (under EDGE_MIN for a strip, up to 16 for the whole
+// blocks of the 16 configuration) and nlines <= 16.  A strip that thin would cost
 // a whole MFMA tile row or column (on 64 x 64 tiles a 17th tile column turns one wave of
 // tiles into two), so it runs beside the MFMA tiles as 16 x 16 blocks on
 // v_mfma_f32_16x16x4_f32: each wavefront of the workgroup takes a K slice, every lane

@@ -117,7 +117,7 @@ int check(const Call& c, const Positions& pos) {
   if (pos.batch && c.batch < 0) return -pos.batch;
   if (pos.ws && c.ws == nullptr && c.ws_bytes > 0) return -pos.ws;
   if (pos.ws_bytes && c.ws_bytes < 0) return -pos.ws_bytes;
-  if (pos.variant && (c.variant < SGEMM_RM_VARIANT_AUTO || c.variant > SGEMM_RM_VARIANT_MFMA_T192)) return -pos.variant;
+  if (pos.variant && (c.variant < SGEMM_RM_VARIANT_AUTO || c.variant > SGEMM_RM_VARIANT_MFMA_T16)) return -pos.variant;
   return 0;
 }
 
@@ -157,6 +157,9 @@ int launch_batches(Problem p, int batch, hipStream_t stream, int variant, float*
           break;
         case SGEMM_RM_VARIANT_MFMA_T32:
           err = sgemm_impl::launch_mfma(p, chunk, stream, 32);
+          break;
+        case SGEMM_RM_VARIANT_MFMA_T16:
+          err = sgemm_impl::launch_mfma(p, chunk, stream, 16);
           break;
         case SGEMM_RM_VARIANT_MFMA:
         case SGEMM_RM_VARIANT_AUTO:

@@ -19,7 +19,7 @@
 namespace sgemm_impl {
 
 struct TileCost {
-  int side;  // tile side: 256, 192, 128, 64 or 32
+  int side;  // tile side: 256, 192, 128, 64, 32 or 16
   double u1, u2;
   double thin;  // us per 1024 of K per 256 thin-strip workgroups
 };
@@ -30,11 +30,16 @@ struct TileCost {
 // tile costs against forced-configuration timings of 75 shapes (squares, skinny, long-K,
 // ragged, batched, and 40 seeded random ones): the choice costs 0.5% on average against
 // the fastest configuration of each shape.
+// The 16 configuration's blocks (one per workgroup of 8 wavefronts, several workgroups per
+// CU) are priced per layer of 256 blocks: 2.6 us per 1024 of K for one layer, 2.8 for more
+// (256 x 256 x 1024: 5.8 us against 8.7 on 32 x 32 tiles; 512^3, four layers: 8.8 against
+// 6.5 us), so it is chosen for outputs of at most a few hundred blocks.
 constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 4.0},
                                    {192, 134.0, 133.3, 0.0},
                                    {128, 60.5, 59.5, 0.0},
                                    {64, 15.3, 16.0, 0.0},
-                                   {32, 5.4, 4.95, 4.0}};
+                                   {32, 5.4, 4.95, 4.0},
+                                   {16, 2.6, 2.8, 0.0}};
 
 // MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
 // counts as a tile row (column); a thin strip, which runs beside the MFMA tiles, does not.

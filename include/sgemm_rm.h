@@ -83,7 +83,8 @@ enum sgemm_rm_variant {
   SGEMM_RM_VARIANT_MFMA_T128 = 6, /* 128 x 128 tiles, 4 wavefronts of 64 x 64, two workgroups per CU */
   SGEMM_RM_VARIANT_MFMA_T64 = 7,  /* 64 x 64 tiles, 4 x 32 x 32 wavefronts, 2-way in-tile K split */
   SGEMM_RM_VARIANT_MFMA_T32 = 8,  /* 32 x 32 tiles, 4-way in-tile K split */
-  SGEMM_RM_VARIANT_MFMA_T192 = 9  /* 192 x 192 tiles, 4 wavefronts of 96 x 96, one workgroup per CU */
+  SGEMM_RM_VARIANT_MFMA_T192 = 9, /* 192 x 192 tiles, 4 wavefronts of 96 x 96, one workgroup per CU */
+  SGEMM_RM_VARIANT_MFMA_T16 = 10  /* 16 x 16 blocks on 16x16x4 MFMA, K split over 8 wavefronts */
 };
 
 /*
@@ -262,7 +263,7 @@ int sgemm_rm_op_strided_batched_noalloc(int transA, int transB, int M, int N, in
 long long sgemm_rm_workspace_size(int M, int N, int K, int batch);
 
 /*
- * Tile side (256, 192, 128, 64 or 32) of the MFMA configuration that SGEMM_RM_VARIANT_AUTO
+ * Tile side (256, 192, 128, 64, 32 or 16) of the MFMA configuration that SGEMM_RM_VARIANT_AUTO
  * and SGEMM_RM_VARIANT_MFMA use for an M x N x K problem repeated `batch` times (any
  * orientation or storage order; batches above 65535 are planned per launch of 65535).
  * 0 when nothing would be launched for the product (M, N, K or batch 0).  -1 M < 0,

@@ -68,7 +68,7 @@ def test_invalid_arguments(lib, args, code):
 
 
 def test_unknown_variant(lib):
-    assert lib.sgemm_rm_ex(4, 4, 4, 1.0, F, 4, F, 4, 0.0, F, 4, None, 10) == -13
+    assert lib.sgemm_rm_ex(4, 4, 4, 1.0, F, 4, F, 4, 0.0, F, 4, None, 11) == -13
     assert lib.sgemm_rm_ex(4, 4, 4, 1.0, F, 4, F, 4, 0.0, F, 4, None, -1) == -13
 
 
@@ -155,7 +155,7 @@ def test_batched_quick_returns_and_variant(lib):
     assert lib.sgemm_rm_strided_batched(0, 4, 4, 1.0, None, 4, 0, None, 4, 0, 0.0, None, 4, 0, 3, None) == 0
     # a single entry may use any strideC (nothing can overlap)
     assert lib.sgemm_rm_strided_batched(4, 4, 4, 0.0, None, 4, 0, None, 4, 0, 1.0, F, 4, 0, 1, None) == 0
-    assert lib.sgemm_rm_strided_batched_ex(4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2, None, 10) == -17
+    assert lib.sgemm_rm_strided_batched_ex(4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2, None, 11) == -17
 
 
 # Transposed and column-major forms.  M = 6, N = 5, K = 3 keep every leading-dimension
@@ -206,7 +206,7 @@ def test_op_invalid_arguments(lib, cm):
     bfn = lib.sgemm_cm_strided_batched_ex if cm else lib.sgemm_rm_op_strided_batched_ex
     bok = [0, 0, M6, N5, K3, 1.0, F, lda, G, F, ldb, G, 0.0, F, ldc, G, 2, None, 0]
     for pos, bad in [(1, 3), (2, -1), (3, -1), (4, -1), (5, -1), (7, None), (9, -1), (10, None), (12, -1),
-                     (14, None), (16, -1), (17, -1), (19, 10), (19, -1)]:
+                     (14, None), (16, -1), (17, -1), (19, 11), (19, -1)]:
         args = list(bok)
         args[pos - 1] = bad
         assert bfn(*args) == -pos, (pos, bad)
@@ -249,7 +249,8 @@ def test_plan_tiles(lib):
     assert sgemm_rm_plan_tiles(4096, 4096, 4096) == 256
     assert sgemm_rm_plan_tiles(8192, 8192, 8192) == 256
     assert sgemm_rm_plan_tiles(1024, 1024, 1024) == 64
-    assert sgemm_rm_plan_tiles(256, 256, 256) == 32
+    assert sgemm_rm_plan_tiles(256, 256, 256) == 16  # 256 blocks of 16^2
+    assert sgemm_rm_plan_tiles(512, 512, 512) == 32  # 1024 blocks of 16^2 would take four layers
     assert sgemm_rm_plan_tiles(3072, 3072, 3072) == 192  # 256 tiles of 192^2: one whole wave
     # 256 x 256 tiles only where they cover the matrix, or leave strips thinner than 16 over one
     # layer of tiles (thin strips after the tiles); wider strips would run as scalar edge tiles
@@ -261,7 +262,7 @@ def test_plan_tiles(lib):
     assert sgemm_rm_plan_tiles(1000, 1030, 999) == 64  # 6-column thin strip beside 64 x 64 tiles
     assert sgemm_rm_plan_tiles(64, 64, 64, 1024) == 64
     for M, N, K, b in [(1, 1, 1, 1), (5000, 3, 7, 1), (3, 5000, 70000, 1), (65535, 65535, 1, 1000000)]:
-        assert sgemm_rm_plan_tiles(M, N, K, b) in (256, 192, 128, 64, 32)
+        assert sgemm_rm_plan_tiles(M, N, K, b) in (256, 192, 128, 64, 32, 16)
 
 
 @pytest.mark.parametrize("cm", [False, True], ids=["rm", "cm"])
@@ -272,7 +273,7 @@ def test_workspace_call_invalid_arguments(lib, cm):
     lda, ldb, ldc = _min_lds(cm, 0, 0)
     ok = [0, 0, M6, N5, K3, 0.0, F, lda, G, F, ldb, G, 1.0, F, ldc, G, 2, F, 1 << 27, None, 0]
     assert fn(*ok) == 0  # alpha = 0, beta = 1: nothing launched
-    for pos, bad in [(1, 2), (3, -1), (8, lda - 1), (17, -1), (18, None), (19, -1), (21, 10), (21, -1)]:
+    for pos, bad in [(1, 2), (3, -1), (8, lda - 1), (17, -1), (18, None), (19, -1), (21, 11), (21, -1)]:
         args = list(ok)
         args[pos - 1] = bad
         assert fn(*args) == -pos, (pos, bad)
@@ -309,7 +310,7 @@ def test_noalloc_invalid_arguments_before_any_hip_call(lib):
     args = [0, 0, 4, 4, 4, 1.0, F, 4, G, F, 4, G, 0.0, F, 4, G, 2, None, 0]
     fn = lib.sgemm_rm_op_strided_batched_noalloc
     for pos, bad in ((1, 2), (3, -1), (4, -1), (5, -1), (8, 3), (9, -1), (11, 3), (12, -1), (15, 3), (16, 15),
-                     (17, -1), (19, 10)):
+                     (17, -1), (19, 11)):
         a = list(args)
         a[pos - 1] = bad
         assert fn(*a) == -pos, (pos, bad)

@@ -25,7 +25,7 @@ from .parity import assert_ieee_equal, c_window, check_padding, device
 pytestmark = pytest.mark.gpu
 
 FAMILIES = {"naive": 1, "lds_tiled": 2, "regblock": 3, "mfma": 4, "auto": 0}
-TILES = {256: 5, 128: 6, 64: 7, 32: 8, 192: 9}
+TILES = {256: 5, 128: 6, 64: 7, 32: 8, 192: 9, 16: 10}
 # per forced configuration: shapes with a guarded remainder (>= its partial-tile width)
 # along M and a thin one along N, and the reverse; the 256 configuration's thin-strip form
 # (both remainders under 16) and its scalar edge tiles (wider remainders)
@@ -35,6 +35,7 @@ SHAPES = {
     128: [(2 * 128 + 32, 128 + 5, 70), (128 + 7, 128 + 40, 45)],
     64: [(3 * 64 + 20, 64 + 6, 70), (64 + 9, 2 * 64 + 17, 99)],
     32: [(3 * 32 + 6, 2 * 32 + 2, 70), (2 * 32 + 1, 3 * 32 + 5, 45)],
+    16: [(3 * 16 + 6, 2 * 16 + 2, 70), (2 * 16 + 1, 3 * 16 + 5, 1045)],
 }
 FAMILY_SHAPES = [(300, 270, 145), (33, 65, 17)]
 

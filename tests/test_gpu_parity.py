@@ -253,6 +253,7 @@ TILE_SHAPES = {
     128: [(2048, 2048, 300), (2176, 2048, 300), (2000, 1950, 129)],  # one layer, 272 tiles, guarded one layer
     64: [(1024, 1024, 129), (1000, 990, 129)],
     32: [(512, 512, 300), (1000, 1030, 99)],
+    16: [(256, 256, 300), (100, 90, 129)],
 }
 
 
@@ -300,6 +301,9 @@ PARTIAL_SHAPES = {
     64: [(5 * 64 + 16, 4 * 64 + 15, 70), (5 * 64 + 15, 4 * 64 + 16, 70), (64 + 15, 64 + 15, 70),
          (1000, 1030, 99), (40, 200, 45), (10, 200, 45), (200, 10, 45), (1, 1, 300), (3 * 64 + 1, 2 * 64 + 14, 1),
          (64 + 3, 2 * 64 + 9, 2100)],
+    # 16: every block guarded where M or N is not a multiple of 16; K below one group, K
+    # slices of every length (long ones take the 4-group chunks), and the K tail
+    16: [(17, 33, 70), (1, 1, 5), (15, 300, 45), (300, 7, 1100), (5 * 16 + 3, 3 * 16 + 9, 4100)],
 }
 
 
@@ -322,7 +326,7 @@ def test_partial_tile_forms_integer_exact(oracle, tiles, M, N, K):
     check_padding(out, C, M, N, ldc)
 
 
-@pytest.mark.parametrize("tiles", [256, 192, 128, 64, 32])
+@pytest.mark.parametrize("tiles", [256, 192, 128, 64, 32, 16])
 def test_tile_configs_random_bound(oracle, tiles):
     """Each forced tile configuration on the ragged 1000 x 1030 x 999 workload (alpha 1.5,
     beta -0.5, padded leading dimensions), within the bound."""
@@ -365,12 +369,12 @@ def test_offsets_past_2_pow_31(oracle, variant, N):
 
 # K-tile depth of each tile configuration (the K loop runs a steady state over pairs of
 # full K-tiles and a general tail; these K values put its boundaries in every place).
-TILE_BK = {256: 16, 192: 16, 128: 16, 64: 32, 32: 64}
+TILE_BK = {256: 16, 192: 16, 128: 16, 64: 32, 32: 64, 16: 16}
 
 
 @pytest.mark.parametrize(
     "tiles,M,N,bk",
-    [(t, t + 40, t + 24, TILE_BK[t]) for t in (256, 192, 128, 64, 32)]
+    [(t, t + 40, t + 24, TILE_BK[t]) for t in (256, 192, 128, 64, 32, 16)]
     # the 256 configuration's thin-strip form
     + [(256, 2 * 256 + 5, 256 + 3, 16)]
     # exact 128 x 128 tiles, at most one per CU: the one-layer form (4 x 2 wavefronts)

@@ -16,7 +16,8 @@ from .parity import device
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9]  # auto, naive, lds_tiled, regblock, mfma, mfma with tiles 256/128/64/32/192
+# auto, naive, lds_tiled, regblock, mfma, mfma with tiles 256/128/64/32/192/16
+VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
 ALPHAS = [1.0, -1.0, 2.0, 0.5, 0.0]
 BETAS = [0.0, 1.0, -1.0, 0.5]
 WS_BYTES = 2 * 256 * 256 * 256 * 4

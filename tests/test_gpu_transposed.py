@@ -134,7 +134,8 @@ TILE_SHAPES = [(256, 600, 520, 77), (256, 300, 270, 160), (256, 516, 259, 77), (
                (128, 300, 290, 77), (128, 140, 290, 257), (128, 256, 384, 77), (128, 2176, 2048, 45),
                (128, 2100, 2090, 45),
                (128, 143, 265, 77), (64, 200, 150, 77), (64, 130, 70, 450), (64, 199, 141, 450), (64, 67, 73, 2100),
-               (32, 100, 70, 77), (32, 103, 70, 77), (32, 96, 64, 77), (32, 40, 70, 449)]
+               (32, 100, 70, 77), (32, 103, 70, 77), (32, 96, 64, 77), (32, 40, 70, 449),
+               (16, 100, 70, 77), (16, 33, 17, 1045)]
 
 
 @pytest.mark.parametrize("orient", ["nt", "tn", "tt"])
