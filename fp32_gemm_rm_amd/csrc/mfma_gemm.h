@@ -156,7 +156,7 @@ void mfma_kernel(Problem p, TileMap map) {
   static_assert(kThin256 == kThinMax, "the 256 thin-strip form's remainders fit one thin strip");
   static_assert(EDGE_MIN <= kThinMax, "thin strips are at most kThinMax wide");
   constexpr int kEdgeFloats = kEdges ? kGroups * EdgeTile::kLdsFloats  // >= its reduction floats
-                                     : kThin ? Cfg::kThreads / 64 * 4 * 64 : 0;
+                                     : kThin ? thin_red_floats<Cfg::kThreads>() : 0;
   constexpr int kFloats = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
   static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
@@ -405,7 +405,7 @@ constexpr int kBlock16Threads = 512;
 template <int NT, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(NT) void block16_kernel(Problem p, int blocks_n) {
   p = batch_entry(p);
-  __shared__ __attribute__((aligned(16))) float smem[NT / 64 * 4 * 64];
+  __shared__ __attribute__((aligned(16))) float smem[thin_red_floats<NT>()];
   const int bm = blockIdx.x / blocks_n, bn = blockIdx.x - (blockIdx.x / blocks_n) * blocks_n;
   const int first = bm * kThinMax, lo = bn * kThinMax;
   thin_strip<NT, TA, TB, VEC>(p, true, first, min(kThinMax, p.M - first), lo, min(kThinMax, p.N - lo), smem);

@@ -57,6 +57,12 @@ __device__ __forceinline__ void edge_tile(const Problem& p, int m0, int n0, floa
 // D(4 * (l / 16) + r, l % 16).  D(i, j) is (line i, output j) when `cols`, (output i,
 // line j) otherwise.
 constexpr int kThinMax = 16;    // widest thin strip, and lines per workgroup
+// Row stride (floats) of the thin strip's reduction buffer [wavefront][register][lane]: the
+// final sums read, per half-wavefront, 16 lanes of register r and 16 of register r + 1, and
+// a stride of 64 put both on the same 16 banks (2-way conflicts); 80 puts them 16 apart.
+constexpr int kThinRedStride = 80;
+template <int NT>
+constexpr int thin_red_floats() { return NT / 64 * 4 * kThinRedStride; }
 template <int NT, bool TA, bool TB, bool VEC>
 __device__ __forceinline__ void thin_strip(const Problem& p, bool cols, int first, int nlines, int lo, int width,
                                            float* smem) {
@@ -144,17 +150,17 @@ __device__ __forceinline__ void thin_strip(const Problem& p, bool cols, int firs
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x_in && kin ? av : 0.f, y_in && kin ? bv : 0.f, acc, 0, 0, 0);
     }
   }
-  float* red = smem;  // [wavefront][register][lane]
+  float* red = smem;  // [wavefront][register][lane], thin_red_floats<NT>() floats
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[(wv * 4 + r) * 64 + l] = acc[r];
+  for (int r = 0; r < 4; ++r) red[(wv * 4 + r) * kThinRedStride + l] = acc[r];
   __syncthreads();
   if (t < 256) {
     const int i = t / 16, j = t % 16, lane = 16 * (i / 4) + j, r = i % 4;
     const int line = cols ? i : j, out = cols ? j : i;
     if (line < nlines && out < width) {
-      float x = red[r * 64 + lane];
+      float x = red[r * kThinRedStride + lane];
 #pragma unroll
-      for (int q = 1; q < W; ++q) x += red[(q * 4 + r) * 64 + lane];
+      for (int q = 1; q < W; ++q) x += red[(q * 4 + r) * kThinRedStride + lane];
       const int row = cols ? first + line : lo + out, col = cols ? lo + out : first + line;
       float* c = p.C + (long long)row * p.ldc + col;
       *c = p.beta == 0.0f ? p.alpha * x : fmaf(p.alpha, x, p.beta * *c);
