@@ -7,14 +7,30 @@
 namespace sgemm_impl {
 namespace mfma_detail {
 
-// C := alpha * x[u] + beta * C at the NV elements (row(u), col(u)) of this lane, given
-// by coord(u, row, col); C is not read when beta == 0.  GUARD (bit 0: rows, bit 1:
-// columns): elements past M or N are skipped.  Every C value of the batch is loaded
-// before the first store: a load after a store into the same array would wait for that
-// store (the compiler cannot tell
-// that the addresses differ), which turns the epilogue into a chain of round trips.
+// The C values at the NV elements (row(u), col(u)) of this lane, given by coord(u, row,
+// col), into c; nothing is read when beta == 0.  Elements past M or N (GUARD bit 0: rows,
+// bit 1: columns), which are not stored, read C's first element instead: the loads stay
+// unconditional, with nothing that uses their values before the epilogue (a masked load
+// followed by a select makes the compiler wait for every load in flight right there).
 template <int NV, int GUARD, typename Coord>
-__device__ __forceinline__ void finish_c(const Problem& p, const float (&x)[NV], Coord coord) {
+__device__ __forceinline__ void load_c(const Problem& p, float (&c)[NV], Coord coord) {
+  if (p.beta == 0.0f) return;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    int row, col;
+    coord(u, row, col);
+    const bool inside = (!(GUARD & 1) || row < p.M) && (!(GUARD & 2) || col < p.N);
+    c[u] = p.C[inside ? (long long)row * p.ldc + col : 0];
+  }
+}
+
+// C := alpha * x[u] + beta * C at the same elements; elements past M or N (GUARD) are
+// skipped.  Every C value is loaded (load_c) before the first store: a load after a store
+// into the same array would wait for that store (the compiler cannot tell that the
+// addresses differ), which turns the epilogue into a chain of round trips.  c: NV floats
+// of the caller's for the loaded values.
+template <int NV, int GUARD, typename Coord>
+__device__ __forceinline__ void finish_c(const Problem& p, const float (&x)[NV], Coord coord, float (&c)[NV]) {
   auto inside = [&](int row, int col) { return (!(GUARD & 1) || row < p.M) && (!(GUARD & 2) || col < p.N); };
   if (p.beta == 0.0f) {
 #pragma unroll
@@ -25,13 +41,7 @@ __device__ __forceinline__ void finish_c(const Problem& p, const float (&x)[NV],
     }
     return;
   }
-  float c[NV];
-#pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    int row, col;
-    coord(u, row, col);
-    c[u] = inside(row, col) ? p.C[(long long)row * p.ldc + col] : 0.f;
-  }
+  load_c<NV, GUARD>(p, c, coord);
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     int row, col;
@@ -162,8 +172,22 @@ __device__ __forceinline__ void store_acc(const Problem& p, const v16f (&acc)[FM
       }
       continue;
     }
-    finish_c<FN * 16, GUARD>(p, x, coord);
+    float c[FN * 16];
+    finish_c<FN * 16, GUARD>(p, x, coord, c);
   }
+}
+
+// Output (row, column) of the u-th of the accumulator registers that a lane finishes after
+// the K-split reduction of finish_acc (KS > 1): 1/KS of its wavefront's registers, chosen by
+// its K-group.
+template <int BM, int BN, int WM, int WN, int KS, int FM, int FN, int VA, int VB>
+__device__ __forceinline__ void ksplit_coord(int u, int m0, int n0, int& row, int& col) {
+  const int w = threadIdx.x / 64, l = threadIdx.x % 64;
+  const int ks = w / (WM * WN), sp = w % (WM * WN);
+  const int wm0 = (sp / WN) * (BM / WM), wn0 = (sp % WN) * (BN / WN);
+  constexpr int kMine = FM * FN * 16 / KS;
+  const int s = ks * kMine + u;  // register (i, j, r) = (s / (16 FN), (s / 16) % FN, s % 16)
+  acc_coord<VA, VB>(s / (FN * 16), (s / 16) % FN, s % 16, l % 32, l / 32, m0 + wm0, n0 + wn0, row, col);
 }
 
 // The end of a tile: with no K split, store_acc; with KS > 1 the KS wavefronts of one
@@ -200,14 +224,13 @@ __device__ __forceinline__ void finish_acc(const Problem& p, const v16f (&acc)[F
     float x[kMine];
 #pragma unroll
     for (int u = 0; u < kMine; ++u) {
-      const int s = ks * kMine + u;  // register (i, j, r) = (s / (16 FN), (s / 16) % FN, s % 16)
+      const int s = ks * kMine + u;
       x[u] = sums[s * 64];
 #pragma unroll
       for (int q = 1; q < KS; ++q) x[u] += sums[q * kStride + s * 64];
     }
     auto coord = [&](int u, int& row, int& col) {
-      const int s = ks * kMine + u;
-      acc_coord<VA, VB>(s / (FN * 16), (s / 16) % FN, s % 16, lr, lh, m0 + wm0, n0 + wn0, row, col);
+      ksplit_coord<BM, BN, WM, WN, KS, FM, FN, VA, VB>(u, m0, n0, row, col);
     };
     if (part != nullptr) {  // stream-K partial tile (full tiles only)
 #pragma unroll
@@ -218,7 +241,8 @@ __device__ __forceinline__ void finish_acc(const Problem& p, const v16f (&acc)[F
       }
       return;
     }
-    finish_c<kMine, GUARD>(p, x, coord);
+    float c[kMine];
+    finish_c<kMine, GUARD>(p, x, coord, c);
   }
 }
 

@@ -141,8 +141,10 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // as thin strips.  Edge tiles and thin strips take the block ids after the tiles (thin
 // strips dispatched first measured slower: 1000 x 1030 x 999 24.8 -> 28.4 us).
 // PF: the tiles run mfma_tile_pf (one k-group per wavefront and K-tile) instead of mfma_tile.
+// FUSE: the right thin strip is computed inside the tiles (FusedStrip): tile (bm, bn) takes
+// strip rows [bm BM + 4 bn, + 4), and the launch holds no right-strip workgroups.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          int EDGE_MIN, bool STREAM_K, bool VEC, bool PF>
+          int EDGE_MIN, bool STREAM_K, bool VEC, bool PF, bool FUSE = false>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
@@ -157,18 +159,23 @@ void mfma_kernel(Problem p, TileMap map) {
   static_assert(EDGE_MIN <= kThinMax, "thin strips are at most kThinMax wide");
   constexpr int kEdgeFloats = kEdges ? kGroups * EdgeTile::kLdsFloats  // >= its reduction floats
                                      : kThin ? thin_red_floats<Cfg::kThreads>() : 0;
-  constexpr int kFloats = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
+  constexpr int kFuseFloats = FUSE ? 2 * Cfg::kStageFloats + 2 * FusedStrip<BK, Cfg::kThreads>::kStageFloats : 0;
+  constexpr int kFloats0 = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
+  constexpr int kFloats = kFloats0 > kFuseFloats ? kFloats0 : kFuseFloats;
   static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
   // the MFMA tiles see the matrix as [0, Mf) x [0, Nf): what lies past it is the strips'
   Problem pt = p;
   pt.M = map.Mf;
   pt.N = map.Nf;
+  // fused strip rows of the tile being run (FUSE; set by the one-tile branch below)
+  int srow0 = 0, srows = 0;
   auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
     // guard bits 0-1 (the tile's partial sides), bit 2: the launch has full tiles only
     constexpr int G = decltype(guard)::value | (kGuarded ? 0 : 4);
     if constexpr (PF)
-      mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G>(pt, m0, n0, kb, ke, smem, part);
+      mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G, FUSE>(
+          pt, m0, n0, kb, ke, smem, part, srow0, srows, map.Nf, p.N - map.Nf);
     else
       mfma_tile<BM, BN, BK, WM, WN, KS, TA, TB, VEC, G>(pt, m0, n0, kb, ke, smem, part);
   };
@@ -180,6 +187,11 @@ void mfma_kernel(Problem p, TileMap map) {
     int bm, bn;
     tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
     const int m0 = bm * BM, n0 = bn * BN;
+    if constexpr (FUSE) {
+      constexpr int SR = FusedStrip<BK, Cfg::kThreads>::SR;
+      srow0 = m0 + SR * bn;
+      srows = max(0, min(SR, min(m0 + BM, map.Mf) - srow0));
+    }
     if constexpr (kGuarded) {
       const bool past_m = m0 + BM > pt.M, past_n = n0 + BN > pt.N;
       if (!past_m && !past_n)
@@ -356,7 +368,7 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
     map.bottom_n = map.bottom_m > 0 ? (p.N + kEdge - 1) / kEdge : 0;
   }
   const long long nmfma = (long long)map.tiles_m * map.tiles_n;
-  const long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
+  long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
   const dim3 block(WM * WN * KS * 64);
   const bool vec = vec_loads_ok(p, batch);
   if constexpr (EDGE_MIN == 0 && BM == 256 && BN == 256) {  // the workspace holds 256 x 256 slots
@@ -383,9 +395,41 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
       return hipGetLastError();
     }
   }
+  // The right thin strip inside the tiles (FusedStrip, FUSE) in the 64 configuration, with
+  // operands stored row-major, at least BM / 4 tile columns so that every strip row has its
+  // tile, and K of at least kFuseMinK; otherwise the strip runs as thin-strip workgroups.
+  // Fused, the strip adds a little to every K-tile of every tile and about 0.7 us to each
+  // tile's end, against strip workgroups that take their own time per K (1000 x 1030 x 999:
+  // 23.0 against 24.0 us; x 4000: 70.5 against 74.9 us; x 300: 11.6 against 10.9 us;
+  // 1000 x 990 x 129: 8.6 against 7.8 us).  In the 128 configuration it measured slower
+  // (2048 x 4100 x 2048: 253 against 249 us), in the 192 one no faster.
+  constexpr int kFuseMinK = 640;
+  constexpr int kThreadsPerWg = WM * WN * KS * 64;
+  constexpr bool kCanFuse = BM == 64 && EDGE_MIN > 1 && PF && !TA && !TB && kThreadsPerWg == BK * 16;
+  bool fuse = false;
+  if constexpr (kCanFuse) {
+    fuse = map.right_m > 0 && (long long)map.tiles_n * FusedStrip<BK, kThreadsPerWg>::SR >= BM && p.K >= kFuseMinK;
+    if (fuse) {
+      edge_tiles -= (long long)map.right_m * map.right_n;
+      map.right_m = map.right_n = 0;
+    }
+  }
   const long long blocks = nmfma + edge_tiles;
   if (!grid_fits(blocks, block.x)) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks, batch);
+  if constexpr (kCanFuse) {
+    if (fuse) {
+      if (vec)
+        hipLaunchKernelGGL(
+            (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF, true>), grid,
+            block, 0, stream, p, map);
+      else
+        hipLaunchKernelGGL(
+            (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, false, PF, true>), grid,
+            block, 0, stream, p, map);
+      return hipGetLastError();
+    }
+  }
   if (vec)
     hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF>),
                        grid, block, 0, stream, p, map);

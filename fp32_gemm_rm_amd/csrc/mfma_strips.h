@@ -168,5 +168,110 @@ __device__ __forceinline__ void thin_strip(const Problem& p, bool cols, int firs
   }
 }
 
+// A right thin strip (columns [n0, n0 + w) of C, w < 16) fused into the MFMA tiles of the
+// 192, 128 and 64 configurations, for operands stored row-major (A along k, B along n): a
+// separate thin-strip workgroup on a CU beside a tile takes that tile's MFMA, LDS and load
+// slots for the strip's whole latency-bound K loop (1000 x 1030 x 999 on 64 x 64 tiles:
+// 23.8 us, against 21.5 us for the 1024 columns of tiles alone).  Fused, tile (bm, bn)
+// computes rows [bm BM + 4 bn, + 4) of the strip from the A rows its K-tiles already hold
+// in LDS and the strip's columns of B, which the workgroup stages beside them (BK x 16
+// floats per K-tile); that takes BM / 4 tile columns per tile row.  Per K-tile each thread
+// loads one value of B's strip, stores it with the tile's LDS stores, reads its operands
+// (SK values of one A row and of one strip column) with the tile's fragment reads one
+// K-tile ahead, and adds SK products on the VALU during the next K-tile's MFMAs.  The SS
+// k-slices of each output are added through LDS in slice order at the end.  The loads are
+// unconditional (a masked load compiles to a branch whose join waits for every load in
+// flight): columns past the strip load the last strip column and only reach outputs that
+// are not stored; in the last, partial K-tile the rows past K load row K - 1 and are
+// zeroed as they are stored, since their A values are zeros and a product 0 * Inf would
+// otherwise be NaN.
+template <int BK, int NT>
+struct FusedStrip {
+  static constexpr int SR = 4;              // strip rows per tile
+  static constexpr int SS = NT / (SR * 16);  // k-slices per K-tile (one per thread role)
+  static constexpr int SK = BK / SS;         // k per slice
+  static constexpr int kStride = BK + 4;     // LDS row stride of one strip column (floats)
+  static constexpr int kStageFloats = 16 * kStride;
+
+  const float* bcol;  // load role: column n0 + min(t % 16, w - 1) of B at k = 0
+  long long ldb;
+  int kk, jl;         // load role: row kk = t / 16 of the K-tile, column jl = t % 16
+  int i, j, s;        // compute role: strip row i, column j, k-slice s
+  float reg[2];
+  float a[2][SK], b[2][SK];
+  float acc;
+  float cval;  // C at this thread's output (threads t < 16 SR, load_c)
+
+  __device__ __forceinline__ void init(const Problem& p, int n0, int w, int t) {
+    static_assert(NT == BK * 16, "one staged B value per thread and K-tile");
+    static_assert(SK % 4 == 0 && SK * SS == BK, "slices of whole 16-byte chunks");
+    kk = t / 16;
+    jl = t % 16;
+    ldb = p.ldb;
+    bcol = p.B + n0 + min(jl, w - 1);
+    i = t % SR;
+    j = (t / SR) % 16;
+    s = t / (SR * 16);
+    acc = 0.f;
+  }
+  // the strip's B values of a full K-tile at k0
+  template <int SET>
+  __device__ __forceinline__ void load_full(int k0) { reg[SET] = bcol[(long long)(k0 + kk) * ldb]; }
+  // the last K-tile, kl < BK valid rows: rows past K read row K - 1, and store zeroes them
+  // (a select right after the load would make the compiler wait for the load there)
+  template <int SET>
+  __device__ __forceinline__ void load_tail(int k0, int kl) { reg[SET] = bcol[(long long)(k0 + min(kk, kl - 1)) * ldb]; }
+  // a full K-tile's values to its LDS stage
+  template <int SET>
+  __device__ __forceinline__ void store(float* stage) const { stage[jl * kStride + kk] = reg[SET]; }
+  // a K-tile with kl valid rows (kl >= BK: full)
+  template <int SET>
+  __device__ __forceinline__ void store(float* stage, int kl) const {
+    stage[jl * kStride + kk] = kk < kl ? reg[SET] : 0.f;
+  }
+  // operands of this thread's slice: A row `row` of the tile's A stage (swizzled 16-byte
+  // chunks, operand stored along k) and strip column j
+  template <int S>
+  __device__ __forceinline__ void read(const float* a_stage, const float* stage, int row) {
+#pragma unroll
+    for (int c = 0; c < SK / 4; ++c) {
+      const float4 x = *reinterpret_cast<const float4*>(a_stage + swz_slot<BK>(row, s * SK / 4 + c));
+      const float4 y = *reinterpret_cast<const float4*>(stage + j * kStride + s * SK + 4 * c);
+      a[S][4 * c] = x.x; a[S][4 * c + 1] = x.y; a[S][4 * c + 2] = x.z; a[S][4 * c + 3] = x.w;
+      b[S][4 * c] = y.x; b[S][4 * c + 1] = y.y; b[S][4 * c + 2] = y.z; b[S][4 * c + 3] = y.w;
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void fma() {
+#pragma unroll
+    for (int e = 0; e < SK; ++e) acc = fmaf(a[S][e], b[S][e], acc);
+  }
+  // the C value of this thread's output (rows [r0, r0 + rows), columns [n0, n0 + w);
+  // threads t < 16 SR finish them), loaded before the tile's epilogue so that it arrives
+  // meanwhile; unconditional: the other threads read C's first element and do not use it
+  __device__ __forceinline__ void load_c(const Problem& p, int r0, int rows, int n0, int w, int t) {
+    if (p.beta == 0.0f) return;
+    const bool mine = t < SR * 16 && i < rows && j < w;
+    cval = p.C[mine ? (long long)(r0 + i) * p.ldc + n0 + j : 0];
+  }
+  // after the K loop: this thread's slice sum to LDS (red: NT floats that no wavefront
+  // reads any more), before a barrier that the caller provides
+  __device__ __forceinline__ void stash(float* red, int t) const { red[t] = acc; }
+  // after that barrier: the slices' sums in slice order, then C := alpha * sum + beta * C
+  // on rows [r0, r0 + rows) and columns [n0, n0 + w); cval holds C (load_c)
+  __device__ __forceinline__ void finish(const Problem& p, const float* red, int r0, int rows, int n0, int w,
+                                         int t) const {
+    if (t < SR * 16) {
+      float x = red[t];
+#pragma unroll
+      for (int q = 1; q < SS; ++q) x += red[q * SR * 16 + t];
+      if (i < rows && j < w) {
+        float* c = p.C + (long long)(r0 + i) * p.ldc + n0 + j;
+        *c = p.beta == 0.0f ? p.alpha * x : fmaf(p.alpha, x, p.beta * cval);
+      }
+    }
+  }
+};
+
 }  // namespace mfma_detail
 }  // namespace sgemm_impl

@@ -5,6 +5,7 @@
 
 #include <type_traits>
 #include "mfma_epilogue.h"
+#include "mfma_strips.h"
 
 namespace sgemm_impl {
 namespace mfma_detail {
@@ -171,9 +172,14 @@ __device__ __forceinline__ void sched_interleave() {
 //   set measured no better), two in the 256, 128 and 64 configurations (128, 32 and 8;
 //   in the 256 one the second set fits beside the 128 fragment registers once B's
 //   fragments are read as 128-bit vectors).
-template <int BM, int BN, int BK, int WM, int WN, int KS, int NSETS, bool TA, bool TB, bool VEC, int GUARD>
+//   FUSE: the tile also computes rows [srow0, srow0 + srows) of a right thin strip,
+//   columns [sn0, sn0 + sw) (FusedStrip): its loads, LDS stores and operand reads ride with
+//   the tile's, and its FMAs run during the MFMAs of the next K-tile.
+template <int BM, int BN, int BK, int WM, int WN, int KS, int NSETS, bool TA, bool TB, bool VEC, int GUARD,
+          bool FUSE = false>
 __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
-                                             float* part = nullptr) {
+                                             float* part = nullptr, int srow0 = 0, int srows = 0, int sn0 = 0,
+                                             int sw = 0) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
@@ -195,6 +201,17 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   OpB opb;
   opa.init(p.A, p.lda, m0, p.M - m0, t);
   opb.init(p.B, p.ldb, n0, p.N - n0, t);
+  using FS = FusedStrip<BK, Cfg::kThreads>;
+  static_assert(!FUSE || (!TA && !TB && KG == 1), "fused strips: A along k, B along n, one k-group per K-tile");
+  static_assert(!FUSE || KS > 1, "fused strips: finish_acc's K-split barrier orders the strip's sums");
+  static_assert(!FUSE || KS * WM * WN * FM * FN * 16 * 64 <= 2 * Cfg::kStageFloats,
+                "fused strips: finish_acc's K-split partials lie below the strip's stages");
+  FS fs;
+  if constexpr (FUSE) fs.init(p, sn0, sw, t);
+  // the strip's B stages follow the tile's two stages; its A row (clamped where the tile
+  // holds no strip rows)
+  auto s_stage = [&](int s) { return smem + 2 * Cfg::kStageFloats + s * FS::kStageFloats; };
+  const int srow = FUSE ? min(srow0 - m0 + fs.i, BM - 1) : 0;
 
   v16f acc[FM][FN];
 #pragma unroll
@@ -211,15 +228,24 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
     if (kt < nfull) {
       opa.template load_full<VEC, GA, R>(kt * BK);
       opb.template load_full<VEC, GB, R>(kt * BK);
+      if constexpr (FUSE) fs.template load_full<R>(kt * BK);
     } else {
       opa.template load_tail<VEC, GA, R>(kt * BK, p.K - kt * BK);
       opb.template load_tail<VEC, GB, R>(kt * BK, p.K - kt * BK);
+      if constexpr (FUSE) fs.template load_tail<R>(kt * BK, p.K - kt * BK);
     }
   };
-  auto store = [&](auto set, int s) {
+  // K-tile kt's global registers to LDS stage s (FULL: kt is a full K-tile)
+  auto store = [&](auto set, int s, int kt, auto full) {
     constexpr int R = decltype(set)::value % NSETS;
     opa.template store<R>(a_stage(s));
     opb.template store<R>(b_stage(s));
+    if constexpr (FUSE) {
+      if constexpr (decltype(full)::value)
+        fs.template store<R>(s_stage(s));
+      else
+        fs.template store<R>(s_stage(s), p.K - kt * BK);
+    }
   };
   auto frags = [&](auto set, int s) {
     constexpr int S = decltype(set)::value;
@@ -228,9 +254,11 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
       read_frags<OpA, FM, Cfg::VA>(a_stage(s), wm0, ks * KG + r, lr, lh, af[S][r]);
       read_frags<OpB, FN, Cfg::VB>(b_stage(s), wn0, ks * KG + r, lr, lh, bf[S][r]);
     }
+    if constexpr (FUSE) fs.template read<S>(a_stage(s), s_stage(s), srow);
   };
   auto mfmas = [&](auto set) {
     constexpr int S = decltype(set)::value;
+    if constexpr (FUSE) fs.template fma<S>();
 #pragma unroll
     for (int r = 0; r < KG; ++r)
 #pragma unroll
@@ -258,20 +286,21 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
         constexpr int R = decltype(set)::value % NSETS;
         opa.template load_full<VEC, GA, R>(kt * BK);
         opb.template load_full<VEC, GB, R>(kt * BK);
+        if constexpr (FUSE) fs.template load_full<R>(kt * BK);
       } else if (kt < ke) {
         load(set, kt);
       }
     };
     ld(Set0{}, kb);
     if constexpr (NSETS == 2) ld(Set1{}, kb + 1);
-    store(Set0{}, 0);
+    store(Set0{}, 0, kb, full);
     if constexpr (NSETS == 1)
       ld(Set1{}, kb + 1);
     else
       ld(Set0{}, kb + 2);
     __syncthreads();
     frags(Set0{}, 0);
-    if (FULL || kb + 1 < ke) store(Set1{}, 1);
+    if (FULL || kb + 1 < ke) store(Set1{}, 1, kb + 1, full);
     ld(std::integral_constant<int, D - 1>{}, kb + D - 1);
     __syncthreads();
   };
@@ -282,16 +311,18 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   // memory traffic in the shadow of the MFMAs; nothing moves across the barrier (the
   // compiler would otherwise hoist the barrier, and its wait on the fragment reads, above
   // the MFMAs).
-  constexpr int kStores = OpA::LOADS + OpB::LOADS;
-  constexpr int kLoads = OpA::kLoadInstrs(VEC) + OpB::kLoadInstrs(VEC);
-  constexpr int kMfmas = 8 * KG * FM * FN, kMemOps = kStores + kLoads + KG * Cfg::kFragReads;
+  constexpr int kStores = OpA::LOADS + OpB::LOADS + (FUSE ? 1 : 0);
+  constexpr int kLoads = OpA::kLoadInstrs(VEC) + OpB::kLoadInstrs(VEC) + (FUSE ? 1 : 0);
+  constexpr int kMfmas = 8 * KG * FM * FN;
+  constexpr int kMemOps = kStores + kLoads + KG * Cfg::kFragReads + (FUSE ? 2 * FS::SK / 4 : 0);
   constexpr int kPer = (kMemOps + kMfmas - 1) / kMfmas;
   auto steady = [&](auto set, int kt) {  // tiles kt+1 .. kt+D exist and kt+D is full
     constexpr int P = decltype(set)::value;
     __builtin_amdgcn_sched_barrier(0);
-    store(set, P);
+    store(set, P, kt + 2, std::true_type{});
     opa.template load_full<VEC, GA, P % NSETS>((kt + D) * BK);
     opb.template load_full<VEC, GB, P % NSETS>((kt + D) * BK);
+    if constexpr (FUSE) fs.template load_full<P % NSETS>((kt + D) * BK);
     frags(std::integral_constant<int, P ^ 1>{}, P ^ 1);
     mfmas(set);
     sched_interleave<0, kMfmas, kPer, kMemOps, kStores, kLoads>();
@@ -300,7 +331,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
   };
   auto step = [&](auto set, int kt) {
     constexpr int P = decltype(set)::value;
-    if (kt + 2 < ke) store(set, P);
+    if (kt + 2 < ke) store(set, P, kt + 2, std::false_type{});
     if (kt + D < ke) load(set, kt + D);
     if (kt + 1 < ke) frags(std::integral_constant<int, P ^ 1>{}, P ^ 1);
     mfmas(set);
@@ -329,8 +360,16 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
     step(Set0{}, kt);
     if (kt + 1 < ke) step(Set1{}, kt + 1);
   }
-
+  // The strip's slice sums go to its first LDS stage (free: the K loop's last fragment
+  // reads precede its last barrier, and finish_acc's K-split partials lie below it), and
+  // finish_acc's barrier orders them before they are added: a barrier of their own after
+  // the tile's C stores would make every wavefront wait for those stores to complete.
+  if constexpr (FUSE) {
+    fs.load_c(p, srow0, srows, sn0, sw, t);
+    fs.stash(s_stage(0), t);
+  }
   finish_acc<BM, BN, WM, WN, KS, FM, FN, Cfg::VA, Cfg::VB, GUARD>(p, acc, smem, m0, n0, part);
+  if constexpr (FUSE) fs.finish(p, s_stage(0), srow0, srows, sn0, sw, t);
 }
 
 }  // namespace mfma_detail

@@ -52,7 +52,7 @@ def _rows(path):
 
 
 def _short(name: str) -> str:
-    return name.split("(")[0].replace("void sgemm_impl::", "")
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void sgemm_impl::", "")
 
 
 def kernel_stats(tag_dir: str, last: int):

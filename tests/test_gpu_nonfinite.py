@@ -28,12 +28,15 @@ FAMILIES = {"naive": 1, "lds_tiled": 2, "regblock": 3, "mfma": 4, "auto": 0}
 TILES = {256: 5, 128: 6, 64: 7, 32: 8, 192: 9, 16: 10}
 # per forced configuration: shapes with a guarded remainder (>= its partial-tile width)
 # along M and a thin one along N, and the reverse; the 256 configuration's thin-strip form
-# (both remainders under 16) and its scalar edge tiles (wider remainders)
+# (both remainders under 16) and its scalar edge tiles (wider remainders); many tile
+# columns with a thin right strip (computed inside the tiles in the 64 configuration at
+# K >= 640)
 SHAPES = {
     256: [(2 * 256 + 4, 256 + 3, 70), (256 + 40, 256 + 33, 45)],
-    192: [(2 * 192 + 32, 192 + 5, 70), (192 + 7, 192 + 40, 45)],
-    128: [(2 * 128 + 32, 128 + 5, 70), (128 + 7, 128 + 40, 45)],
-    64: [(3 * 64 + 20, 64 + 6, 70), (64 + 9, 2 * 64 + 17, 99)],
+    192: [(2 * 192 + 32, 192 + 5, 70), (192 + 7, 192 + 40, 45), (192 + 20, 48 * 192 + 9, 45)],
+    128: [(2 * 128 + 32, 128 + 5, 70), (128 + 7, 128 + 40, 45), (128 + 20, 32 * 128 + 3, 45)],
+    64: [(3 * 64 + 20, 64 + 6, 70), (64 + 9, 2 * 64 + 17, 99), (2 * 64 + 20, 16 * 64 + 6, 70),
+         (64 + 20, 16 * 64 + 6, 700)],
     32: [(3 * 32 + 6, 2 * 32 + 2, 70), (2 * 32 + 1, 3 * 32 + 5, 45)],
     16: [(3 * 16 + 6, 2 * 16 + 2, 70), (2 * 16 + 1, 3 * 16 + 5, 1045)],
 }

@@ -326,6 +326,52 @@ def test_partial_tile_forms_integer_exact(oracle, tiles, M, N, K):
     check_padding(out, C, M, N, ldc)
 
 
+# Right thin strips computed inside the MFMA tiles (operands stored row-major, the 64
+# configuration, at least 16 tile columns, K >= 640): tile (bm, bn) takes 4 rows of the
+# strip.  Shapes: strips 1-15 wide past full tiles, the last 1-3 columns of a guarded
+# remainder, guarded tile rows (strip rows past the last tile's), M below one tile, K
+# tails, even and odd K-tile counts, and the smallest tile-column count that fuses; K
+# just under the threshold keeps the strip in workgroups of its own, as do the 192 and
+# 128 configurations' shapes with as many tile columns.
+FUSED_SHAPES = {
+    64: [(5 * 64 + 20, 16 * 64 + 11, 999), (5 * 64, 16 * 64 + 18, 640), (17, 16 * 64 + 1, 673),
+         (2 * 64 + 30, 40 * 64 + 15, 2100), (64, 16 * 64 + 9, 1024 + 32), (1000, 1030, 999),
+         (3 * 64 + 5, 16 * 64 + 3, 639), (2 * 64, 16 * 64 + 7, 70)],
+    192: [(2 * 192 + 40, 48 * 192 + 7, 70), (192 + 17, 48 * 192 + 16 + 3, 33)],
+    128: [(300, 32 * 128 + 5, 77), (20, 32 * 128 + 15, 45), (3 * 128, 33 * 128 + 1, 16 * 9 + 5)],
+}
+
+
+@pytest.mark.parametrize("tiles,M,N,K", [(t, *s) for t, shapes in FUSED_SHAPES.items() for s in shapes])
+def test_fused_right_strip_integer_exact(oracle, tiles, M, N, K):
+    """Right strips inside the tiles: bit-exact on integer inputs (padded leading
+    dimensions, NaN padding in A/B, sentinel in C), with beta != 0 and with beta = 0 over
+    a NaN C (which must not reach the output); the default path on the same inputs."""
+    from fp32_gemm_rm_amd import TILE_VARIANTS
+
+    lda, ldb, ldc = K + 4, N + 4, N + 1
+    a = integer_matrix(M, K, -4, 4, seed=M + 3 * K)
+    b = integer_matrix(K, N, -4, 4, seed=N + 3 * K)
+    c = integer_matrix(M, N, -4, 4, seed=M + 3 * N)
+    A, B, C = pad_rows(a, lda, np.nan), pad_rows(b, ldb, np.nan), pad_rows(c, ldc, C_PAD_SENTINEL)
+    print(f"[parity] fused strip tiles {tiles} {M}x{N}x{K}", flush=True)
+    ref, _ = oracle.full(M, N, K, -1.5, A, lda, B, ldb, 0.5, C, ldc)
+    for variant in (TILE_VARIANTS[tiles], VARIANTS["auto"]):
+        out = run_gemm(M, N, K, -1.5, A, lda, B, ldb, 0.5, C, ldc, variant)
+        got = c_window(out, M, N, ldc).astype(np.float64)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"variant {variant}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+        check_padding(out, C, M, N, ldc)
+    Cn = C.copy()
+    Cn.reshape(M, ldc)[:, :N] = np.nan
+    ref0, _ = oracle.full(M, N, K, 2.0, A, lda, B, ldb, 0.0, Cn, ldc)
+    out = run_gemm(M, N, K, 2.0, A, lda, B, ldb, 0.0, Cn, ldc, TILE_VARIANTS[tiles])
+    got = c_window(out, M, N, ldc).astype(np.float64)
+    bad = np.argwhere(got != ref0)
+    assert bad.size == 0, f"beta 0: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+    check_padding(out, Cn, M, N, ldc)
+
+
 @pytest.mark.parametrize("tiles", [256, 192, 128, 64, 32, 16])
 def test_tile_configs_random_bound(oracle, tiles):
     """Each forced tile configuration on the ragged 1000 x 1030 x 999 workload (alpha 1.5,
