@@ -44,6 +44,10 @@ LIBRARY_PREFIX = "void sgemm_impl::"
 N_CUS = 256
 N_SIMDS = 1024  # 256 CUs x 4 SIMDs
 N_XCDS = 8
+# nominal shader clock: the MFMA cycles of a SIMD over the traced kernel time at this clock
+# are the share of the kernel's duration in which its matrix core is busy (GRBM_GUI_ACTIVE
+# under counter collection spans more than the kernel: the passes serialize the dispatches)
+CLOCK_MHZ = 2400
 
 
 def _rows(path):
@@ -129,6 +133,7 @@ def summarize(prof_dir: str, tag: str, last: int = 20) -> dict:
         rec.update({
             "grbm_cycles": grbm,
             "mfma_busy": _mean(lib, "SQ_VALU_MFMA_BUSY_CYCLES") / (grbm * N_SIMDS),
+            "mfma_cycles_per_simd": _mean(lib, "SQ_VALU_MFMA_BUSY_CYCLES") / N_SIMDS,
             # SQ_ACTIVE_INST_VALU counts quad-cycles per SIMD: busy = 4 x count / (SIMDs x cycles)
             "valu_busy": 4 * _mean(lib, "SQ_ACTIVE_INST_VALU") / (grbm * N_SIMDS),
             "valu_fma_flop": _mean(lib, "SQ_INSTS_VALU_FMA_F32") * 64 * 2,
@@ -151,7 +156,8 @@ def _pct(x):
 
 def table(recs) -> str:
     """One row per tag: time, rate, pipe busy, FLOP counts, LDS conflicts, memory-side bytes."""
-    head = ("| workload | variant | kernel avg (timed calls) us | TFLOP/s | MFMA busy | VALU busy | "
+    head = ("| workload | variant | kernel avg (timed calls) us | TFLOP/s | MFMA busy | MFMA cycles / timed us "
+            "at 2.4 GHz | VALU busy | "
             "VALU FMA FLOP / 2MNK | MFMA FLOP / 2MNK | LDS conflicts | fabric reads / compulsory | "
             "DRAM-bound reads / compulsory | fabric writes / compulsory |")
     lines = [head, "|" + "---|" * (head.count("|") - 1)]
@@ -161,7 +167,9 @@ def table(recs) -> str:
         lines.append("| " + " | ".join([
             r["workload"], r["variant"], f"{t:.1f}" if t else "—",
             f"{r['flops'] / (t * 1e-6) / 1e12:.1f}" if t else "—",
-            _pct(r.get("mfma_busy")), _pct(r.get("valu_busy")),
+            _pct(r.get("mfma_busy")),
+            _pct(r["mfma_cycles_per_simd"] / (t * CLOCK_MHZ)) if t and "mfma_cycles_per_simd" in r else "—",
+            _pct(r.get("valu_busy")),
             f"{r['valu_fma_flop'] / r['flops']:.3f}" if "valu_fma_flop" in r else "—",
             f"{r['mfma_flop'] / r['flops']:.3f}" if "mfma_flop" in r else "—",
             f"{100 * r['lds_bank_conflict_rate']:.2f}%" if "lds_bank_conflict_rate" in r else "—",
