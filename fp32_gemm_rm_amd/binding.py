@@ -44,6 +44,7 @@ SGEMM_RM_OP_T = 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libsgemm_rm.so"
 _lib = None
+_poison_lib = None
 
 #: Names the header declares; the CPU tests check that the library exports each.
 EXPORTED_SYMBOLS = ("sgemm_rm", "sgemm_rm_ex", "sgemm_rm_strided_batched", "sgemm_rm_strided_batched_ex",
@@ -88,50 +89,62 @@ def load_library():
     """Load the built library (torch first, so that its HIP runtime is the one in use)."""
     global _lib
     if _lib is None:
-        import torch  # noqa: F401  (loads torch's HIP runtime before the library binds to one)
-
-        path = library_path()
-        if not os.path.exists(path):
-            raise ImportError(f"{path} is missing: build it with __graft_entry__.build()")
-        lib = ctypes.CDLL(path)
-        args = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
-                ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-        lib.sgemm_rm.argtypes = args
-        lib.sgemm_rm.restype = ctypes.c_int
-        lib.sgemm_rm_ex.argtypes = args + [ctypes.c_int]
-        lib.sgemm_rm_ex.restype = ctypes.c_int
-        bargs = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
-                 ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float,
-                 ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
-        lib.sgemm_rm_strided_batched.argtypes = bargs
-        lib.sgemm_rm_strided_batched.restype = ctypes.c_int
-        lib.sgemm_rm_strided_batched_ex.argtypes = bargs + [ctypes.c_int]
-        lib.sgemm_rm_strided_batched_ex.restype = ctypes.c_int
-        oargs = [ctypes.c_int, ctypes.c_int] + args
-        for name in ("sgemm_rm_op", "sgemm_cm"):
-            getattr(lib, name).argtypes = oargs
-            getattr(lib, name).restype = ctypes.c_int
-        obargs = [ctypes.c_int, ctypes.c_int] + bargs + [ctypes.c_int]
-        for name in ("sgemm_rm_op_strided_batched_ex", "sgemm_cm_strided_batched_ex"):
-            getattr(lib, name).argtypes = obargs
-            getattr(lib, name).restype = ctypes.c_int
-        wargs = [ctypes.c_int, ctypes.c_int] + bargs[:-1] + [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p,
-                                                           ctypes.c_int]
-        for name in ("sgemm_rm_op_strided_batched_ws", "sgemm_cm_strided_batched_ws"):
-            getattr(lib, name).argtypes = wargs
-            getattr(lib, name).restype = ctypes.c_int
-        lib.sgemm_rm_op_strided_batched_noalloc.argtypes = obargs
-        lib.sgemm_rm_op_strided_batched_noalloc.restype = ctypes.c_int
-        lib.sgemm_rm_workspace_size.argtypes = [ctypes.c_int] * 4
-        lib.sgemm_rm_workspace_size.restype = ctypes.c_longlong
-        lib.sgemm_rm_plan_tiles.argtypes = [ctypes.c_int] * 4
-        lib.sgemm_rm_plan_tiles.restype = ctypes.c_int
-        lib.sgemm_rm_strerror.argtypes = [ctypes.c_int]
-        lib.sgemm_rm_strerror.restype = ctypes.c_char_p
-        lib.sgemm_rm_version.argtypes = []
-        lib.sgemm_rm_version.restype = ctypes.c_int
-        _lib = lib
+        _lib = _load(library_path())
     return _lib
+
+
+def load_poison_library():
+    """The LDS-poisoning debug build of the library (every kernel fills its LDS with NaN
+    before use), loaded beside the production one with the same argument types; for tests."""
+    global _poison_lib
+    if _poison_lib is None:
+        _poison_lib = _load(os.path.join(os.path.dirname(library_path()), "libsgemm_rm_poison.so"))
+    return _poison_lib
+
+
+def _load(path):
+    import torch  # noqa: F401  (loads torch's HIP runtime before the library binds to one)
+
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    args = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.sgemm_rm.argtypes = args
+    lib.sgemm_rm.restype = ctypes.c_int
+    lib.sgemm_rm_ex.argtypes = args + [ctypes.c_int]
+    lib.sgemm_rm_ex.restype = ctypes.c_int
+    bargs = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+             ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float,
+             ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+    lib.sgemm_rm_strided_batched.argtypes = bargs
+    lib.sgemm_rm_strided_batched.restype = ctypes.c_int
+    lib.sgemm_rm_strided_batched_ex.argtypes = bargs + [ctypes.c_int]
+    lib.sgemm_rm_strided_batched_ex.restype = ctypes.c_int
+    oargs = [ctypes.c_int, ctypes.c_int] + args
+    for name in ("sgemm_rm_op", "sgemm_cm"):
+        getattr(lib, name).argtypes = oargs
+        getattr(lib, name).restype = ctypes.c_int
+    obargs = [ctypes.c_int, ctypes.c_int] + bargs + [ctypes.c_int]
+    for name in ("sgemm_rm_op_strided_batched_ex", "sgemm_cm_strided_batched_ex"):
+        getattr(lib, name).argtypes = obargs
+        getattr(lib, name).restype = ctypes.c_int
+    wargs = [ctypes.c_int, ctypes.c_int] + bargs[:-1] + [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p,
+                                                       ctypes.c_int]
+    for name in ("sgemm_rm_op_strided_batched_ws", "sgemm_cm_strided_batched_ws"):
+        getattr(lib, name).argtypes = wargs
+        getattr(lib, name).restype = ctypes.c_int
+    lib.sgemm_rm_op_strided_batched_noalloc.argtypes = obargs
+    lib.sgemm_rm_op_strided_batched_noalloc.restype = ctypes.c_int
+    lib.sgemm_rm_workspace_size.argtypes = [ctypes.c_int] * 4
+    lib.sgemm_rm_workspace_size.restype = ctypes.c_longlong
+    lib.sgemm_rm_plan_tiles.argtypes = [ctypes.c_int] * 4
+    lib.sgemm_rm_plan_tiles.restype = ctypes.c_int
+    lib.sgemm_rm_strerror.argtypes = [ctypes.c_int]
+    lib.sgemm_rm_strerror.restype = ctypes.c_char_p
+    lib.sgemm_rm_version.argtypes = []
+    lib.sgemm_rm_version.restype = ctypes.c_int
+    return lib
 
 
 def sgemm_rm_op_strided_batched_ws(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,

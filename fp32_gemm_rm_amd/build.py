@@ -3,6 +3,10 @@
 Every HIP source is compiled with ``-Xclang -target-feature -Xclang
 -packed-fp32-ops`` so that the compiler never emits packed FP32 VALU
 instructions, and without fast-math so that FP32 rounding is IEEE.
+
+A second library, ``libsgemm_rm_poison.so``, is the same sources with
+``-DSGEMM_RM_POISON_LDS=1``: every kernel fills its LDS with NaN before
+use, so that the GPU tests that load it catch a read of unwritten LDS.
 """
 from __future__ import annotations
 
@@ -16,6 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsgemm_rm.so")
+POISON_BUILD_DIR = os.path.join(HERE, "_build_poison")
+POISON_LIB = os.path.join(HERE, "libsgemm_rm_poison.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -28,9 +34,10 @@ HIP_FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, out_dir, extra = job
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{proc.stdout}\n{proc.stderr}")
@@ -73,19 +80,32 @@ def build_c_client(out_dir: str) -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every kernel source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
+    # -Bsymbolic: the library's calls between its own entry points stay inside it, also
+    # when the production and the poisoned library are loaded in one process
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-Bsymbolic", "-o", tmp, *objs]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"link failed:\n{proc.stdout}\n{proc.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, poison: bool = True) -> str:
+    """Compile every kernel source and link the shared library (and, with `poison`, the
+    LDS-poisoning debug library beside it); returns the production library's path."""
+    jobs = [(src, BUILD_DIR, []) for src in SOURCES]
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    if poison:
+        os.makedirs(POISON_BUILD_DIR, exist_ok=True)
+        jobs += [(src, POISON_BUILD_DIR, ["-DSGEMM_RM_POISON_LDS=1"]) for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    if poison:
+        _link(objs[len(SOURCES):], POISON_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB}" + (f" and {POISON_LIB}" if poison else ""))
     return LIB
 
 

@@ -130,4 +130,19 @@ constexpr long long kStrideBlocks = 1LL << 20;
 constexpr long long kBandElems = 1LL << 32;
 constexpr int kBandAlign = 768;
 
+// Debug build (-DSGEMM_RM_POISON_LDS=1, built as libsgemm_rm_poison.so): every kernel that
+// uses LDS fills it with NaN before anything else, so that a read of LDS that no thread of
+// the launch has written (a missing barrier, a part of a tile left unfilled) turns into
+// NaN in C instead of reading whatever an earlier launch left there.  The production
+// build compiles this to nothing.
+#ifndef SGEMM_RM_POISON_LDS
+#define SGEMM_RM_POISON_LDS 0
+#endif
+__device__ __forceinline__ void poison_lds(float* p, int n) {
+  if constexpr (SGEMM_RM_POISON_LDS != 0) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = __builtin_nanf("");
+    __syncthreads();
+  }
+}
+
 }  // namespace sgemm_impl

@@ -50,6 +50,8 @@ __global__ __launch_bounds__(256) void lds_tiled_kernel(Problem p, int col_block
   p = batch_entry(p);
   __shared__ __attribute__((aligned(16))) float As[T][T + 1];
   __shared__ __attribute__((aligned(16))) float Bs[T][T];
+  poison_lds(&As[0][0], T * (T + 1));
+  poison_lds(&Bs[0][0], T * T);
   const int t = threadIdx.x;
   const int tx = t % 8, ty = t / 8;
   const int bm = blockIdx.x / col_blocks;

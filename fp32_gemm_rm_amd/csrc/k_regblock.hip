@@ -13,6 +13,7 @@ __global__ __launch_bounds__(256) void regblock_kernel(Problem p, int col_blocks
   p = batch_entry(p);
   using RB = RegBlock<BM, BN, BK, TM, TN, 256, PAD_A>;
   __shared__ __attribute__((aligned(16))) float lds[RB::kLdsFloats];
+  poison_lds(lds, RB::kLdsFloats);
   const int bm = blockIdx.x / col_blocks;
   const int bn = blockIdx.x - bm * col_blocks;
   const int m0 = bm * BM, n0 = bn * BN;

@@ -164,6 +164,7 @@ void mfma_kernel(Problem p, TileMap map) {
   constexpr int kFloats = kFloats0 > kFuseFloats ? kFloats0 : kFuseFloats;
   static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
+  poison_lds(smem, kFloats);
   // the MFMA tiles see the matrix as [0, Mf) x [0, Nf): what lies past it is the strips'
   Problem pt = p;
   pt.M = map.Mf;
@@ -450,6 +451,7 @@ template <int NT, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(NT) void block16_kernel(Problem p, int blocks_n) {
   p = batch_entry(p);
   __shared__ __attribute__((aligned(16))) float smem[thin_red_floats<NT>()];
+  poison_lds(smem, thin_red_floats<NT>());
   const int bm = blockIdx.x / blocks_n, bn = blockIdx.x - (blockIdx.x / blocks_n) * blocks_n;
   const int first = bm * kThinMax, lo = bn * kThinMax;
   thin_strip<NT, TA, TB, VEC>(p, true, first, min(kThinMax, p.M - first), lo, min(kThinMax, p.N - lo), smem);

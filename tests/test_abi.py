@@ -43,6 +43,18 @@ def test_library_exports_every_declared_symbol(lib):
     assert lib.sgemm_rm_version() == 400
 
 
+def test_poison_library_exports_every_declared_symbol(lib):
+    """The LDS-poisoning debug build (the GPU tests' check for reads of unwritten LDS) is
+    built beside the library and exports the same C ABI."""
+    from fp32_gemm_rm_amd.binding import load_poison_library
+
+    poison = load_poison_library()
+    for name in _declared_functions():
+        assert hasattr(poison, name), name
+    assert poison.sgemm_rm_version() == 400
+    assert poison.sgemm_rm_plan_tiles(4096, 4096, 4096, 1) == lib.sgemm_rm_plan_tiles(4096, 4096, 4096, 1)
+
+
 F = 0x1000  # a non-null dummy pointer: never dereferenced, the calls return before any launch
 
 
