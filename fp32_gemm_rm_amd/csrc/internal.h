@@ -123,12 +123,27 @@ inline bool grid_fits(long long blocks, int threads) {
 // The one-thread-per-element kernels (naive, scale) cap their grid at this many blocks and
 // stride over the rest, so that any M x N fits one launch.
 constexpr long long kStrideBlocks = 1LL << 20;
-// Largest output window one tiled launch covers: a larger C runs as row (and column) bands
-// of at most this many elements, each band a launch of its own on the same stream, so that
-// every launcher's grid stays within 32-bit work-item counts.  Band sides are multiples of
-// kBandAlign (a multiple of every tile side: 256, 192, 128, 64, 32).
-constexpr long long kBandElems = 1LL << 32;
+// Largest output window one tiled launch covers.  No tiled launch runs more than 32
+// threads per row of C and 16 of its columns (the 16 configuration: a 512-thread workgroup
+// per 16 x 16 block; the other configurations, the thin strips and the edge tiles run
+// fewer, also on windows narrower than their tiles), so a launch over R rows and C columns
+// has at most 32 ceil16(R) ceil(C / 16) work-items.  A window where that product could
+// pass 2^32 - 1 runs as bands of rows (and of columns, for rows wider than
+// kBandUnits / kBandAlign units of 16), each band a launch of its own on the same stream.
+// Band edges fall on multiples of kBandAlign, a multiple of every tile side (256, 192,
+// 128, 64, 32, 16), so each band sees whole tiles where the window has them.
+constexpr long long kBandUnits = (1LL << 27) - 1;  // ceil16(R) x ceil(C / 16) per launch
 constexpr int kBandAlign = 768;
+inline bool needs_bands(long long M, long long N) { return (M + 15) / 16 * 16 * ((N + 15) / 16) > kBandUnits; }
+// Rows bm and columns bn of the bands of an M x N window (the last band of a row or column
+// may be smaller).
+inline void band_shape(long long M, long long N, int& bm, int& bn) {
+  const long long units = (N + 15) / 16, max_units = kBandUnits / kBandAlign;
+  const long long cols = units <= max_units ? N : max_units * 16 / kBandAlign * kBandAlign;
+  const long long rows = kBandUnits / ((cols + 15) / 16) / kBandAlign * kBandAlign;  // >= kBandAlign
+  bm = (int)(rows < M ? rows : M);
+  bn = (int)cols;
+}
 
 // Debug build (-DSGEMM_RM_POISON_LDS=1, built as libsgemm_rm_poison.so): every kernel that
 // uses LDS fills it with NaN before anything else, so that a read of LDS that no thread of

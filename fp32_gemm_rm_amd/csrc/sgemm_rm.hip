@@ -179,21 +179,16 @@ int launch_batches(Problem p, int batch, hipStream_t stream, int variant, float*
   return 0;
 }
 
-// As launch_batches, with a C window of more than kBandElems elements cut into bands of
-// rows (and of columns, for rows wider than kBandElems / kBandAlign) that each launch on
-// their own, in order on the same stream: a tiled launcher's work-item count then stays
-// within 32 bits.  The one-thread-per-element kernels (naive, and the scale pass of
-// alpha == 0 or K == 0) stride over any grid and take the window whole.
+// As launch_batches, with a C window too large for one tiled launch's 32-bit work-item
+// count (needs_bands) cut into bands of rows, and of columns for very long rows
+// (band_shape), that launch one after another on the same stream.  The
+// one-thread-per-element kernels (naive, and the scale pass of alpha == 0 or K == 0)
+// stride over a capped grid and take the window whole.
 int launch(const Problem& p, int batch, hipStream_t stream, int variant, float* ws) {
-  using sgemm_impl::kBandAlign;
-  using sgemm_impl::kBandElems;
   const bool strided = variant == SGEMM_RM_VARIANT_NAIVE || p.alpha == 0.0f || p.K == 0;
-  if (strided || (long long)p.M * p.N <= kBandElems) return launch_batches(p, batch, stream, variant, ws);
-  const int bn = (long long)p.N * kBandAlign <= kBandElems
-                     ? p.N
-                     : (int)(kBandElems / kBandAlign / kBandAlign * kBandAlign);
-  const long long rows = kBandElems / bn / kBandAlign * kBandAlign;
-  const int bm = rows > kBandAlign ? (int)(rows < p.M ? rows : p.M) : kBandAlign;
+  if (strided || !sgemm_impl::needs_bands(p.M, p.N)) return launch_batches(p, batch, stream, variant, ws);
+  int bm, bn;
+  sgemm_impl::band_shape(p.M, p.N, bm, bn);
   for (long long m0 = 0; m0 < p.M; m0 += bm)
     for (long long n0 = 0; n0 < p.N; n0 += bn) {
       const int rows_b = (int)(bm < p.M - m0 ? bm : p.M - m0), cols_b = (int)(bn < p.N - n0 ? bn : p.N - n0);
@@ -212,7 +207,7 @@ long long workspace_need(const Problem& p, int batch, int variant) {
   if (batch != 1 || p.alpha == 0.0f || p.K == 0) return 0;
   if (variant == SGEMM_RM_VARIANT_MFMA_T256) return sgemm_impl::kStreamKBytes;
   if (variant != SGEMM_RM_VARIANT_AUTO && variant != SGEMM_RM_VARIANT_MFMA) return 0;
-  if ((long long)p.M * p.N > sgemm_impl::kBandElems) return sgemm_impl::kStreamKBytes;
+  if (sgemm_impl::needs_bands(p.M, p.N)) return sgemm_impl::kStreamKBytes;
   return sgemm_impl::plan_tiles(p.M, p.N, p.K, 1, true).stream_k ? sgemm_impl::kStreamKBytes : 0;
 }
 

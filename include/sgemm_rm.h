@@ -100,11 +100,13 @@ int sgemm_rm(int M, int N, int K, float alpha, const float* A, int lda, const fl
  * pointer; 128-bit global loads are used only where the base pointers, the
  * leading dimensions and, in the batched calls, the batch strides keep them
  * 16-byte aligned.  Every call is one or a few launches on `stream`: a C window
- * of more than 2^32 elements runs, in the tiled families, as bands of rows (and
- * of columns for rows wider than 2^32 / 768 elements) launched one after another,
- * so that no grid exceeds the 32-bit work-item count of a dispatch; the naive
- * family and the C := beta*C pass of alpha == 0 or K == 0 take any window in
- * one launch.
+ * whose tiled launch could need 2^32 or more work-items (M rounded up to 16 times
+ * ceil(N / 16) above 2^27 - 1: about 2^31 elements, fewer for windows narrower
+ * than 16 columns) runs, in the tiled families, as bands of rows (and of columns
+ * for rows of more than about 2.8 million elements) launched one after another,
+ * band edges on multiples of 768 rows and columns, so that no grid exceeds the
+ * 32-bit work-item count of a dispatch; the naive family and the C := beta*C pass
+ * of alpha == 0 or K == 0 take any window in one launch.
  */
 int sgemm_rm_ex(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb,
                 float beta, float* C, int ldc, hipStream_t stream, int variant);

@@ -339,3 +339,30 @@ def test_scratch_limit_code(lib):
     text = open(HEADER).read()
     assert "#define SGEMM_RM_SCRATCH_BYTES (128LL << 20)" in text
     assert "#define SGEMM_RM_ERR_SCRATCH_LIMIT (-100)" in text
+
+
+# Windows whose tiled launches would need 2^32 or more work-items in one grid: large squares,
+# windows a few columns wide and very long ones, and ones just past the banding threshold.
+HUGE_WINDOWS = [(65537, 65537, 7), (46341, 46341, 3), (2**31 - 1, 1, 5), (2**31 - 1, 3, 2), (1, 2**31 - 1, 5),
+                (3, 2**31 - 1, 2), (100000, 40000, 9), (40000, 100000, 9), (8193, 2**18 + 7, 4)]
+
+
+@pytest.mark.parametrize("M,N,K", HUGE_WINDOWS)
+def test_huge_windows_fit_the_grid_in_every_variant(lib, M, N, K):
+    """Host-side check of the launch arithmetic (no GPU here): on a machine without a
+    device every call gets as far as its first launch and returns the runtime's
+    "no device" code; a grid past the 32-bit work-item count of a dispatch would be
+    refused before that with hipErrorInvalidConfiguration (9).  The first launch of a
+    banded window is its largest band, so every variant's largest grid is checked.  The
+    pointers are dummies that nothing dereferences: no launch can run here."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("needs a machine without a GPU (the calls would launch on dummy pointers)")
+    hip_error_invalid_configuration = 9
+    for variant in range(11):
+        for ta, tb in ((0, 0), (1, 1)):
+            lda, ldb = (M if ta else K), (K if tb else N)
+            rc = lib.sgemm_rm_op_strided_batched_ex(ta, tb, M, N, K, 1.0, F, lda, 0, F, ldb, 0, 0.0, F, N, 0, 1, None,
+                                                    variant)
+            assert rc > 0 and rc != hip_error_invalid_configuration, (variant, ta, tb, rc)

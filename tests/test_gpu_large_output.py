@@ -3,8 +3,9 @@
 A dispatch counts its work-items in 32 bits per grid dimension.  The
 one-thread-per-element kernels (naive, and the C := beta*C pass that alpha == 0
 or K == 0 runs in every variant) stride over a capped grid, and the tiled
-families run such a window as bands of rows launched one after another.  The
-inputs follow closed forms whose every output is exact in float32, so the
+families run such a window as bands of rows launched one after another (the
+host-side arithmetic of every variant's grids is checked on the CPU by
+tests/test_abi.py).  The inputs follow closed forms whose every output is exact in float32, so the
 whole output is checked on the device chunk by chunk: beta * C for alpha = 0
 (special case of the definition with the product term absent), and
 K * u_i * v_j for A(i, k) = u_i, B(k, j) = v_j (the rank-1 structure: every
@@ -69,7 +70,9 @@ def test_alpha_zero_scales_whole_window(variant):
     _release()
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3])  # auto, naive, LDS-tiled, register-blocked
+# auto, naive, LDS-tiled, register-blocked, and the 64 and 16 MFMA configurations forced (the
+# 16 one runs 512 threads per 16 x 16 block: the most work-items per output of any launcher)
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 7, 10])
 def test_rank_one_structure_whole_window(oracle, variant):
     """A(i, k) = u_i and B(k, j) = v_j with small integers, K = 3: C = 3 u_i v_j exactly
     at every one of the 4.3e9 outputs (beta = 0 with C NaN before the call)."""
@@ -92,9 +95,10 @@ def test_rank_one_structure_whole_window(oracle, variant):
         r1 = min(r0 + CHUNK, M)
         want = K * torch.outer(u[r0:r1], v)
         assert torch.equal(C[r0:r1], want), f"rows {r0}..{r1}"
-    # rows around the seam of the row bands (bands of 65280 rows) and the last row,
+    # rows around the seams of the row bands (bands of 32256 rows: 42 x 768, the most whose
+    # 16-row-rounded count times ceil(N / 16) = 4097 stays below 2^27) and the last row,
     # against the oracle, bit for bit
-    rows = np.array([0, 65279, 65280, 65281, M - 1])
+    rows = np.array([0, 32255, 32256, 32257, 64511, 64512, 64513, M - 1])
     a_rows = A[torch.from_numpy(rows).cuda()].cpu().numpy().reshape(-1)
     b = B.cpu().numpy().reshape(-1)
     ref, _ = oracle.full(len(rows), N, K, 1.0, a_rows, K, b, N, 0.0, None, N, with_absab=False)
