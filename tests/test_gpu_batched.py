@@ -88,6 +88,18 @@ def test_batched_aligned_rows_odd_strides(oracle, variant):
     _check_entries(oracle, out, M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, range(batch))
 
 
+@pytest.mark.parametrize("variant", [7, 0])  # the 64 x 64 configuration forced, and the default path
+def test_batched_fused_right_strip(oracle, variant):
+    """Entries whose right strip runs inside the 64 x 64 tiles (16 tile columns, 5 strip
+    columns, K >= 640, guarded tile rows): each entry's strip reads its own B columns."""
+    M, N, K, batch = 130, 16 * 64 + 5, 700, 3
+    lda, ldb, ldc = K + 3, N + 1, N + 2
+    sA, sB, sC = M * lda + 7, K * ldb + 5, M * ldc + 11
+    A, B, C = make_batched_inputs(batch, M, N, K, lda, ldb, ldc, sA, sB, sC, "uniform", seed=31, c_init="random")
+    out = _run_batched(M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, batch, variant)
+    _check_entries(oracle, out, M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, range(batch))
+
+
 def test_batched_more_entries_than_one_launch(oracle):
     """70000 entries: two launches (65535 + 4465); integer inputs, checked bit for bit at the seams."""
     import torch
