@@ -72,15 +72,19 @@ hipError_t launch_regblock(const Problem& p, int batch, hipStream_t stream);
 // MFMA tiles for the full BM x BN tiles plus bounds-checked register-blocked
 // tiles (the scalar edge-tile path) for the strips past them, in one launch; one
 // instantiation per operand orientation (p.ta, p.tb), dispatched by launch_mfma.
-// tiles: the tile configuration by its side (256, 192, 128, 64 or 32; see tile_plan.h).
-// ws: nullptr, or kStreamKBytes of device memory for stream-K (256 configuration, batch 1).
-hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
-hipError_t launch_mfma_nt(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
-hipError_t launch_mfma_tn(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
-hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws);
-inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr) {
-  if (p.ta) return p.tb ? launch_mfma_tt(p, batch, stream, tiles, ws) : launch_mfma_tn(p, batch, stream, tiles, ws);
-  return p.tb ? launch_mfma_nt(p, batch, stream, tiles, ws) : launch_mfma_nn(p, batch, stream, tiles, ws);
+// tiles: the tile configuration by its side (256, 192, 128, 64, 32 or 16; see tile_plan.h).
+// ws: nullptr, or kStreamKBytes of device memory for stream-K (256 configuration, batch 1)
+// or for the K slices of the 64 configuration (slices > 1, batch 1; k_slices).
+hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws, int slices);
+hipError_t launch_mfma_nt(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws, int slices);
+hipError_t launch_mfma_tn(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws, int slices);
+hipError_t launch_mfma_tt(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws, int slices);
+inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr,
+                              int slices = 1) {
+  if (p.ta)
+    return p.tb ? launch_mfma_tt(p, batch, stream, tiles, ws, slices)
+                : launch_mfma_tn(p, batch, stream, tiles, ws, slices);
+  return p.tb ? launch_mfma_nt(p, batch, stream, tiles, ws, slices) : launch_mfma_nn(p, batch, stream, tiles, ws, slices);
 }
 
 // Compute units of an MI355X (8 XCDs of 32).

@@ -3,8 +3,9 @@
 
 namespace sgemm_impl {
 
-hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws) {
-  return mfma_detail::launch_op<false, false>(p, batch, stream, tiles, ws);
+hipError_t launch_mfma_nn(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws,
+                           int slices) {
+  return mfma_detail::launch_op<false, false>(p, batch, stream, tiles, ws, slices);
 }
 
 }  // namespace sgemm_impl

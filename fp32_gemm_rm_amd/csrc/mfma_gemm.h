@@ -104,6 +104,9 @@ struct TileMap {
   // StreamK); partial tiles go to ws
   int dp_tiles, sk_wgs;
   float* ws;
+  // K slices (SLICED kernels, slices > 1): workgroup u + s * tiles computes the K-tiles
+  // [s iters / slices, (s + 1) iters / slices) of tile u into workspace slot s * tiles + u
+  int slices;
 };
 
 // The stream-K split: the K-tiles ("iterations") of the stream-K tiles, tile-major, are
@@ -144,7 +147,7 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // FUSE: the right thin strip is computed inside the tiles (FusedStrip): tile (bm, bn) takes
 // strip rows [bm BM + 4 bn, + 4), and the launch holds no right-strip workgroups.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          int EDGE_MIN, bool STREAM_K, bool VEC, bool PF, bool FUSE = false>
+          int EDGE_MIN, bool STREAM_K, bool VEC, bool PF, bool FUSE = false, bool SLICED = false>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
@@ -183,72 +186,87 @@ void mfma_kernel(Problem p, TileMap map) {
   const int nmfma = map.tiles_m * map.tiles_n;
   const int ndp = STREAM_K ? map.dp_tiles : nmfma;
   const int iters = (p.K + BK - 1) / BK;
-  int e = (int)blockIdx.x - ndp;
-  if (e < 0) {  // one whole tile
-    int bm, bn;
-    tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
-    const int m0 = bm * BM, n0 = bn * BN;
-    if constexpr (FUSE) {
-      constexpr int SR = FusedStrip<BK, Cfg::kThreads>::SR;
-      srow0 = m0 + SR * bn;
-      srows = max(0, min(SR, min(m0 + BM, map.Mf) - srow0));
-    }
+  // the guard form of tile (m0, n0): full, past M, past N or both
+  auto guarded_tile = [&](int m0, int n0, int kb, int ke, float* part) {
     if constexpr (kGuarded) {
       const bool past_m = m0 + BM > pt.M, past_n = n0 + BN > pt.N;
       if (!past_m && !past_n)
-        tile(std::integral_constant<int, 0>{}, m0, n0, 0, iters, nullptr);
+        tile(std::integral_constant<int, 0>{}, m0, n0, kb, ke, part);
       else if (!past_n)
-        tile(std::integral_constant<int, 1>{}, m0, n0, 0, iters, nullptr);
+        tile(std::integral_constant<int, 1>{}, m0, n0, kb, ke, part);
       else if (!past_m)
-        tile(std::integral_constant<int, 2>{}, m0, n0, 0, iters, nullptr);
+        tile(std::integral_constant<int, 2>{}, m0, n0, kb, ke, part);
       else
-        tile(std::integral_constant<int, 3>{}, m0, n0, 0, iters, nullptr);
+        tile(std::integral_constant<int, 3>{}, m0, n0, kb, ke, part);
     } else {
-      tile(std::integral_constant<int, 0>{}, m0, n0, 0, iters, nullptr);
+      tile(std::integral_constant<int, 0>{}, m0, n0, kb, ke, part);
     }
-    return;
-  }
-  if (STREAM_K && e < map.sk_wgs) {  // one stream-K range (full tiles only)
-    const StreamK sk{(long long)(nmfma - map.dp_tiles) * iters, iters, map.sk_wgs};
-    const long long j0 = sk.start(e), j1 = sk.start(e + 1);
-    for (long long j = j0; j < j1;) {
-      const int u = (int)(j / iters);  // stream-K tile
-      const long long tile_end = (long long)(u + 1) * iters;
-      const long long seg_end = j1 < tile_end ? j1 : tile_end;
-      const int kb = (int)(j - (long long)u * iters), ke = (int)(seg_end - (long long)u * iters);
-      float* part = nullptr;
-      if (kb > 0 || ke < iters)
-        part = map.ws + (2LL * e + (j == j0 ? 0 : 1)) * (long long)(BM * BN);
+  };
+  if constexpr (SLICED) {  // one K slice of one tile, raw to the workspace (no strips in the launch)
+    static_assert(!STREAM_K && !FUSE, "K slices run alone");
+    const int u = (int)blockIdx.x % nmfma, s = (int)blockIdx.x / nmfma;
+    int bm, bn;
+    tile_coords<GROUP_M>(u, map.tiles_m, map.tiles_n, bm, bn);
+    const int kb = (int)((long long)s * iters / map.slices), ke = (int)((long long)(s + 1) * iters / map.slices);
+    guarded_tile(bm * BM, bn * BN, kb, ke, map.ws + ((long long)s * nmfma + u) * (BM * BN));
+  } else {
+    int e = (int)blockIdx.x - ndp;
+    if (e < 0) {  // one whole tile
       int bm, bn;
-      tile_coords<GROUP_M>(map.dp_tiles + u, map.tiles_m, map.tiles_n, bm, bn);
-      if (j != j0) __syncthreads();  // the previous piece's epilogue may still read LDS
-      tile(std::integral_constant<int, 0>{}, bm * BM, bn * BN, kb, ke, part);
-      j = seg_end;
+      tile_coords<GROUP_M>(blockIdx.x, map.tiles_m, map.tiles_n, bm, bn);
+      const int m0 = bm * BM, n0 = bn * BN;
+      if constexpr (FUSE) {
+        constexpr int SR = FusedStrip<BK, Cfg::kThreads>::SR;
+        srow0 = m0 + SR * bn;
+        srows = max(0, min(SR, min(m0 + BM, map.Mf) - srow0));
+      }
+      guarded_tile(m0, n0, 0, iters, nullptr);
+      return;
     }
-    return;
-  }
-  if (STREAM_K) e -= map.sk_wgs;
-  if constexpr (kEdges) {
-    int m0, n0;
-    const int n_right = map.right_m * map.right_n;
-    if (e < n_right) {
-      m0 = (e / map.right_n) * kEdge;
-      n0 = map.Nf + (e % map.right_n) * kEdge;
-    } else {
-      e -= n_right;
-      m0 = map.Mf + (e / map.bottom_n) * kEdge;
-      n0 = (e % map.bottom_n) * kEdge;
+    if (STREAM_K && e < map.sk_wgs) {  // one stream-K range (full tiles only)
+      const StreamK sk{(long long)(nmfma - map.dp_tiles) * iters, iters, map.sk_wgs};
+      const long long j0 = sk.start(e), j1 = sk.start(e + 1);
+      for (long long j = j0; j < j1;) {
+        const int u = (int)(j / iters);  // stream-K tile
+        const long long tile_end = (long long)(u + 1) * iters;
+        const long long seg_end = j1 < tile_end ? j1 : tile_end;
+        const int kb = (int)(j - (long long)u * iters), ke = (int)(seg_end - (long long)u * iters);
+        float* part = nullptr;
+        if (kb > 0 || ke < iters)
+          part = map.ws + (2LL * e + (j == j0 ? 0 : 1)) * (long long)(BM * BN);
+        int bm, bn;
+        tile_coords<GROUP_M>(map.dp_tiles + u, map.tiles_m, map.tiles_n, bm, bn);
+        if (j != j0) __syncthreads();  // the previous piece's epilogue may still read LDS
+        tile(std::integral_constant<int, 0>{}, bm * BM, bn * BN, kb, ke, part);
+        j = seg_end;
+      }
+      return;
     }
-    edge_tile<kGroups, TA, TB, VEC>(p, m0, n0, smem);
-  }
-  if constexpr (kThin) {
-    const int n_right = map.right_m;  // right strip: columns [Nf, N) of rows [0, Mf)
-    if (e < n_right) {
-      const int first = e * kThinMax;
-      thin_strip<Cfg::kThreads, TA, TB, VEC>(p, true, first, min(kThinMax, map.Mf - first), map.Nf, p.N - map.Nf, smem);
-    } else {  // bottom strip: rows [Mf, M) of columns [0, N)
-      const int first = (e - n_right) * kThinMax;
-      thin_strip<Cfg::kThreads, TA, TB, VEC>(p, false, first, min(kThinMax, p.N - first), map.Mf, p.M - map.Mf, smem);
+    if (STREAM_K) e -= map.sk_wgs;
+    if constexpr (kEdges) {
+      int m0, n0;
+      const int n_right = map.right_m * map.right_n;
+      if (e < n_right) {
+        m0 = (e / map.right_n) * kEdge;
+        n0 = map.Nf + (e % map.right_n) * kEdge;
+      } else {
+        e -= n_right;
+        m0 = map.Mf + (e / map.bottom_n) * kEdge;
+        n0 = (e % map.bottom_n) * kEdge;
+      }
+      edge_tile<kGroups, TA, TB, VEC>(p, m0, n0, smem);
+    }
+    if constexpr (kThin) {
+      const int n_right = map.right_m;  // right strip: columns [Nf, N) of rows [0, Mf)
+      if (e < n_right) {
+        const int first = e * kThinMax;
+        thin_strip<Cfg::kThreads, TA, TB, VEC>(p, true, first, min(kThinMax, map.Mf - first), map.Nf,
+                                               p.N - map.Nf, smem);
+      } else {  // bottom strip: rows [Mf, M) of columns [0, N)
+        const int first = (e - n_right) * kThinMax;
+        thin_strip<Cfg::kThreads, TA, TB, VEC>(p, false, first, min(kThinMax, p.N - first), map.Mf,
+                                               p.M - map.Mf, smem);
+      }
     }
   }
 }
@@ -324,19 +342,68 @@ __global__ __launch_bounds__(256) void sk_fixup_kernel(Problem p, TileMap map) {
   }
 }
 
+// K-slice fix-up: C := alpha * (sum of the tile's slices) + beta * C over the matrix part
+// of the tiles, one workgroup per tile row (BN / 4 float4 columns, kSliceGroups groups of
+// threads).  Group g adds slices [g S / G, (g + 1) S / G) in order (G = min(S,
+// kSliceGroups)), and the groups' sums are added in group order through LDS: a fixed
+// order, so results are deterministic, and no thread waits on a long chain of loads
+// (a single thread per output over 256 slices would issue 256 dependent additions).
+constexpr int kSliceGroups = 16;
+template <int BM, int BN, int GROUP_M>
+__global__ __launch_bounds__(BN / 4 * kSliceGroups) void slice_fixup_kernel(Problem p, TileMap map) {
+  constexpr int kQuads = BN / 4;
+  __shared__ float4 red[kSliceGroups][kQuads];
+  poison_lds(&red[0][0].x, kSliceGroups * kQuads * 4);
+  const int q = threadIdx.x % kQuads, g = threadIdx.x / kQuads;
+  const int nmfma = map.tiles_m * map.tiles_n, u = blockIdx.x, r = blockIdx.y;
+  const int S = map.slices, G = S < kSliceGroups ? S : kSliceGroups;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (g < G) {
+    const int s0 = (int)((long long)g * S / G), s1 = (int)((long long)(g + 1) * S / G);
+    const float* col = map.ws + (long long)u * (BM * BN) + r * BN + 4 * q;
+    sum = *reinterpret_cast<const float4*>(col + (long long)s0 * nmfma * (BM * BN));
+    for (int s = s0 + 1; s < s1; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(col + (long long)s * nmfma * (BM * BN));
+      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+  }
+  red[g][q] = sum;
+  __syncthreads();
+  if (g != 0) return;
+  for (int h = 1; h < G; ++h) {
+    const float4 v = red[h][q];
+    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+  }
+  int bm, bn;
+  tile_coords<GROUP_M>(u, map.tiles_m, map.tiles_n, bm, bn);
+  const int row = bm * BM + r, col0 = bn * BN + 4 * q;
+  if (row >= p.M) return;
+  float* c = p.C + (long long)row * p.ldc + col0;
+  const float x[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (col0 + e < p.N) c[e] = p.beta == 0.0f ? p.alpha * x[e] : fmaf(p.alpha, x[e], p.beta * c[e]);
+}
+
 // ws != nullptr (batch 1, configurations with EDGE_MIN = 0): stream-K over 256
 // workgroups for the last partial wave of tiles, plus the full wave before it where the
 // partial one holds fewer than 32 tiles (the tiles before those run one per workgroup);
 // ws holds 2 * 256 * BM * BN floats.  Measured, us, partial wave alone against with the
 // wave before it: 5120^3 1911 / 1923, 4608^3 1423 / 1440, 6144^3 3227 / 3247,
 // 5120 x 5120 x 2048 823 / 833; 4352 x 4096 x 4096 (16 tiles in the partial wave) 1095 / 1079.
+//
+// slices > 1 (ws != nullptr, batch 1, the 64 configuration, a launch of MFMA tiles only):
+// every tile's K-tiles are cut into `slices` contiguous slices, each a workgroup that writes
+// its raw partial tile to ws (slices x tiles x BM x BN floats), and slice_fixup_kernel adds
+// them in slice order and applies alpha and beta.  For products of few tiles and long K.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
           int EDGE_MIN = 0, bool PF = false>
-hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws = nullptr) {
+hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws = nullptr, int slices = 1) {
   static_assert(BM == BN && BM % kEdge == 0, "square tiles whose sides are multiples of the edge tile");
   TileMap map;
   map.dp_tiles = map.sk_wgs = 0;
   map.ws = nullptr;
+  map.slices = 1;
   // extent of the MFMA tiles: rows [0, Mf), columns [0, Nf) (mfma_extent, tile_plan.h uses
   // the same rule); the strips past it (columns [Nf, N) of rows [0, Mf), then rows [Mf, M)
   // of every column) are scalar edge tiles or thin strips
@@ -372,6 +439,28 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   long long edge_tiles = (long long)map.right_m * map.right_n + (long long)map.bottom_m * map.bottom_n;
   const dim3 block(WM * WN * KS * 64);
   const bool vec = vec_loads_ok(p, batch);
+  if constexpr (BM == 64 && PF) {
+    if (slices > 1 && ws != nullptr && batch == 1 && edge_tiles == 0 && nmfma > 0 &&
+        nmfma * slices * (BM * BN) * 4 <= kStreamKBytes) {
+      map.slices = slices;
+      map.ws = ws;
+      const long long blocks = nmfma * slices;
+      if (!grid_fits(blocks, block.x)) return hipErrorInvalidConfiguration;
+      if (vec)
+        hipLaunchKernelGGL(
+            (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF, false, true>),
+            dim3((unsigned)blocks), block, 0, stream, p, map);
+      else
+        hipLaunchKernelGGL(
+            (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, false, PF, false, true>),
+            dim3((unsigned)blocks), block, 0, stream, p, map);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL((slice_fixup_kernel<BM, BN, GROUP_M>), dim3((unsigned)nmfma, BM), dim3(BN / 4 * kSliceGroups),
+                         0, stream, p, map);
+      return hipGetLastError();
+    }
+  }
   if constexpr (EDGE_MIN == 0 && BM == 256 && BN == 256) {  // the workspace holds 256 x 256 slots
     if (ws != nullptr && batch == 1 && nmfma % kStreamKWgs != 0) {
       // the partial wave, and the full wave before it where the partial one is under 1/8
@@ -489,9 +578,11 @@ hipError_t launch_block16(const Problem& p, int batch, hipStream_t stream) {
 // Partial tiles (mfma_edge_min): guarded MFMA tiles of the same grid in the 192, 128, 64
 // and 32 configurations, except strips thinner than 16 in the 192, 128 and 64
 // configurations (thin strips); the scalar edge-tile path in the 256 configuration.
-// ws: stream-K workspace (kStreamKBytes) for the 256 configuration, or nullptr.
+// ws: stream-K workspace (kStreamKBytes) for the 256 configuration, or for the 64 one's
+// K slices (slices > 1), or nullptr.
 template <bool TA, bool TB>
-hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr) {
+hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles, float* ws = nullptr,
+                     int slices = 1) {
   switch (tiles) {
     case 256:
       // remainders thinner than kThin256 past the full tiles: thin strips after the tiles
@@ -521,8 +612,9 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
                    : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true>(p, batch, stream);
     }
     case 64:
-      if (p.M % 64 == 0 && p.N % 64 == 0) return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true>(p, batch, stream);
-      return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, mfma_edge_min(64), true>(p, batch, stream);
+      if (p.M % 64 == 0 && p.N % 64 == 0)
+        return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true>(p, batch, stream, ws, slices);
+      return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, mfma_edge_min(64), true>(p, batch, stream, ws, slices);
     case 32:
       if (p.M % 32 == 0 && p.N % 32 == 0) return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4>(p, batch, stream);
       return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, mfma_edge_min(32)>(p, batch, stream);

@@ -152,8 +152,8 @@ int launch_batches(Problem p, int batch, hipStream_t stream, int variant, float*
         case SGEMM_RM_VARIANT_MFMA_T128:
           err = sgemm_impl::launch_mfma(p, chunk, stream, 128);
           break;
-        case SGEMM_RM_VARIANT_MFMA_T64:
-          err = sgemm_impl::launch_mfma(p, chunk, stream, 64);
+        case SGEMM_RM_VARIANT_MFMA_T64:  // with a workspace: K slices wherever k_slices applies
+          err = sgemm_impl::launch_mfma(p, chunk, stream, 64, ws, sgemm_impl::k_slices(p.M, p.N, p.K, chunk));
           break;
         case SGEMM_RM_VARIANT_MFMA_T32:
           err = sgemm_impl::launch_mfma(p, chunk, stream, 32);
@@ -165,7 +165,8 @@ int launch_batches(Problem p, int batch, hipStream_t stream, int variant, float*
         case SGEMM_RM_VARIANT_AUTO:
         default: {
           const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(p.M, p.N, p.K, chunk, ws != nullptr);
-          err = sgemm_impl::launch_mfma(p, chunk, stream, plan.side, plan.stream_k ? ws : nullptr);
+          err = sgemm_impl::launch_mfma(p, chunk, stream, plan.side, plan.stream_k || plan.slices > 1 ? ws : nullptr,
+                                        plan.slices);
           break;
         }
       }
@@ -200,15 +201,19 @@ int launch(const Problem& p, int batch, hipStream_t stream, int variant, float* 
 }
 
 // Workspace bytes that a call's kernels may use given a large enough workspace (0: none
-// of them can): stream-K, single products only, where the default path's cost model picks
-// it, the 256 configuration is forced, or a banded window (launch) leaves the choice to
-// each band.  An over-estimate only costs the scratch lookup; the launchers decide.
+// of them can): stream-K or K slices, single products only, where the default path's cost
+// model picks them, the 256 configuration is forced (stream-K), the 64 one is forced on a
+// shape that K slices apply to, or a banded window (launch) leaves the choice to each band.
+// An over-estimate only costs the scratch lookup; the launchers decide.
 long long workspace_need(const Problem& p, int batch, int variant) {
   if (batch != 1 || p.alpha == 0.0f || p.K == 0) return 0;
   if (variant == SGEMM_RM_VARIANT_MFMA_T256) return sgemm_impl::kStreamKBytes;
+  if (variant == SGEMM_RM_VARIANT_MFMA_T64)
+    return sgemm_impl::k_slices(p.M, p.N, p.K, 1) > 1 ? sgemm_impl::kStreamKBytes : 0;
   if (variant != SGEMM_RM_VARIANT_AUTO && variant != SGEMM_RM_VARIANT_MFMA) return 0;
   if (sgemm_impl::needs_bands(p.M, p.N)) return sgemm_impl::kStreamKBytes;
-  return sgemm_impl::plan_tiles(p.M, p.N, p.K, 1, true).stream_k ? sgemm_impl::kStreamKBytes : 0;
+  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(p.M, p.N, p.K, 1, true);
+  return plan.stream_k || plan.slices > 1 ? sgemm_impl::kStreamKBytes : 0;
 }
 
 // Validate, then run as a row-major problem.  A column-major product C = op(A) op(B)
@@ -339,7 +344,8 @@ long long sgemm_rm_workspace_size(int M, int N, int K, int batch) {
   if (K < 0) return -3;
   if (batch < 0) return -4;
   if (M == 0 || N == 0 || K == 0 || batch == 0) return 0;
-  return sgemm_impl::plan_tiles(M, N, K, batch, true).stream_k ? sgemm_impl::kStreamKBytes : 0;
+  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(M, N, K, batch, true);
+  return plan.stream_k || plan.slices > 1 ? sgemm_impl::kStreamKBytes : 0;
 }
 
 int sgemm_rm_plan_tiles(int M, int N, int K, int batch) {

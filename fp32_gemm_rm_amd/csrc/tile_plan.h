@@ -95,13 +95,50 @@ inline double modelled_stream_k_time(int M, int N, int K, int batch) {
   return (double)tiles / kStreamKWgs * kStreamKCost * (double)K / 1024.0 + kStreamKOverhead;
 }
 
+// K slices (64 configuration, batch 1, with a workspace): a product of few tiles and long K
+// leaves most CUs idle however its tiles are cut; its K range can be cut instead.  Each of
+// the tiles' K ranges is split into S contiguous slices, one workgroup each, so that the
+// launch holds about two workgroups per CU (the configuration's co-residency) with at
+// least kMinSliceIters K-tiles of 32 per slice; the raw partial tiles go to the workspace
+// and a second kernel adds them in slice order (deterministic) and applies alpha and beta.
+// Thin strips do not split, so the form applies where the 64 configuration's tiles cover
+// the matrix (remainders of 0 or at least 16 rows, and of 0 or at least 16 columns that
+// are a multiple of 4).  Returns S, or 1 where slicing does not apply.
+constexpr int kMinSliceIters = 16;
+inline int k_slices(int M, int N, int K, int batch) {
+  if (batch != 1 || M <= 0 || N <= 0 || K <= 0) return 1;
+  const bool covered = (M % 64 == 0 || M % 64 >= 16) && (N % 64 == 0 || (N % 64 >= 16 && N % 4 == 0));
+  if (!covered) return 1;
+  const long long tiles = (long long)((M + 63) / 64) * ((N + 63) / 64);
+  const long long iters = (K + 31) / 32;
+  long long s = 2 * kCUs / tiles;
+  if (s > iters / kMinSliceIters) s = iters / kMinSliceIters;
+  return s >= 2 ? (int)s : 1;
+}
+// Modelled time of the sliced form: the layers of tiles x S workgroups at the 64
+// configuration's cost over K / S, plus the fix-up (a launch and the partial tiles read
+// at about 2 TB/s); negative where it does not apply.
+constexpr double kSliceFixupUs = 3.0;
+inline double modelled_sliced_time(int M, int N, int K, int batch) {
+  const int S = k_slices(M, N, K, batch);
+  if (S < 2) return -1.0;
+  const long long tiles = (long long)((M + 63) / 64) * ((N + 63) / 64);
+  const long long layers = (tiles * S + kCUs - 1) / kCUs;
+  static_assert(kTileCosts[3].side == 64, "the 64 configuration's costs");
+  const TileCost& c64 = kTileCosts[3];
+  const double part_bytes = (double)tiles * S * 64 * 64 * 4;
+  return (double)layers * (layers > 1 ? c64.u2 : c64.u1) * ((double)K / S) / 1024.0 + kSliceFixupUs +
+         part_bytes / 2.0e6;
+}
+
 struct TilePlan {
   int side;        // tile configuration
   bool stream_k;   // stream-K over the last waves (side 256 only)
+  int slices = 1;  // K slices (side 64 only; k_slices)
 };
 
-// The configuration with the least modelled time (ties: the larger tile); stream-K is a
-// candidate when a workspace is available.
+// The configuration with the least modelled time (ties: the larger tile); stream-K and K
+// slices are candidates when a workspace is available.
 inline TilePlan plan_tiles(int M, int N, int K, int batch, bool workspace = false) {
   TilePlan best{kTileCosts[0].side, false};
   double t = modelled_time(kTileCosts[0], M, N, K, batch);
@@ -112,6 +149,8 @@ inline TilePlan plan_tiles(int M, int N, int K, int batch, bool workspace = fals
   if (workspace) {
     const double tsk = modelled_stream_k_time(M, N, K, batch);
     if (tsk >= 0.0 && tsk < t) best = TilePlan{256, true}, t = tsk;
+    const double tsl = modelled_sliced_time(M, N, K, batch);
+    if (tsl >= 0.0 && tsl < t) best = TilePlan{64, false, k_slices(M, N, K, batch)}, t = tsl;
   }
   return best;
 }

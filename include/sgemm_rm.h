@@ -197,18 +197,24 @@ int sgemm_cm_strided_batched_ex(int transA, int transB, int M, int N, int K, flo
 
 /*
  * The general row-major call with a caller-owned workspace: as
- * sgemm_rm_op_strided_batched_ex, and where a single product's 256 x 256 tiles leave the
- * last wave of 256 workgroups partly empty, the last waves run as "stream-K" (their
- * K-tiles shared evenly by 256 workgroups; after the Stream-K work decomposition, not a
- * technique of the pages) when the library's cost model expects it to be faster.
- * Partial tiles go to `workspace` (device memory, at least sgemm_rm_workspace_size
- * bytes; the library only writes and reads it during the call's kernels) and a second
- * kernel adds them in a fixed order, so results are deterministic; their summation
- * order, and so their rounding, differs from the call without a workspace.  With
- * workspace NULL, not 16-byte aligned (hipMalloc gives 256) or workspace_bytes below
- * the size needed, the call is exactly sgemm_rm_op_strided_batched_ex.  SGEMM_RM_VARIANT_MFMA_T256 with a large enough
- * workspace uses stream-K whenever the tiles leave a partial wave (for tests and
- * sweeps); the other forced variants ignore the workspace.  Calls that share a
+ * sgemm_rm_op_strided_batched_ex, and, for a single product, where the library's cost
+ * model expects it to be faster: (a) where its 256 x 256 tiles leave the last wave of 256
+ * workgroups partly empty, the last waves run as "stream-K" (their K-tiles shared evenly
+ * by 256 workgroups; after the Stream-K work decomposition, not a technique of the
+ * pages); (b) where a product of few 64 x 64 tiles has a long K (e.g. 256 x 256 x 65536),
+ * each tile's K range is cut into slices, one workgroup each, so that the CUs fill ("K
+ * slices", the deterministic split-K that small outputs call for).  Partial tiles go to
+ * `workspace` (device memory, at least sgemm_rm_workspace_size bytes; the library only
+ * writes and reads it during the call's kernels) and a second kernel adds them in a fixed
+ * order, so results are deterministic; their summation order, and so their rounding,
+ * differs from the call without a workspace.  With workspace NULL, not 16-byte aligned
+ * (hipMalloc gives 256) or workspace_bytes below the size needed, the call is exactly
+ * sgemm_rm_op_strided_batched_ex.  With a large enough workspace, SGEMM_RM_VARIANT_MFMA_T256
+ * uses stream-K whenever the tiles leave a partial wave and SGEMM_RM_VARIANT_MFMA_T64 uses
+ * K slices wherever they apply (a single product covered by 64 x 64 tiles, remainders of
+ * 0 or at least 16 rows and columns, whose tiles fill under two workgroups per CU and whose
+ * K gives each slice at least 512), for tests and sweeps; the other forced variants ignore
+ * the workspace.  Calls that share a
  * workspace must not overlap (same stream, or synchronised).  Return codes as
  * sgemm_rm_op_strided_batched_ex, plus -18 workspace NULL with workspace_bytes > 0,
  * -19 workspace_bytes < 0; the stream is argument 20 and -21 is an unknown variant.

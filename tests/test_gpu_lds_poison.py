@@ -13,7 +13,7 @@ case is compared bit for bit with the oracle, over every output, and C's padding
 untouched.  The cases reach each LDS layout and pipeline: the LDS-tiled and
 register-blocked VALU kernels, every forced MFMA tile configuration with full, guarded and
 thin-strip partial tiles, the fused right strip, the 256 configuration's thin-strip form
-and scalar edge tiles, stream-K pieces with their fix-up, 16 x 16 blocks, the one-layer 128
+and scalar edge tiles, stream-K pieces with their fix-up, K slices with theirs, 16 x 16 blocks, the one-layer 128
 form, a strided batch, transposed operands and K tails.
 """
 import numpy as np
@@ -42,6 +42,7 @@ CASES = [
     (0, 0, 0, 70, 50, 33, 7, False),  # strided batch, default path
     (5, 0, 0, 1024, 1280, 77, 1, True),  # stream-K (256 forced, with a workspace): every tile split
     (5, 0, 0, 17 * 256, 17 * 256, 40, 1, True),  # stream-K: whole tiles and pieces
+    (7, 0, 0, 210, 148, 30000, 1, True),  # K slices (64 forced, with a workspace) and their fix-up
 ]
 
 
@@ -85,7 +86,7 @@ def test_poisoned_lds_integer_exact(oracle, lib, variant, ta, tb, M, N, K, batch
     dA, dB, dC = device(np.concatenate(As)), device(np.concatenate(Bs)), device(np.concatenate(Cs))
     from fp32_gemm_rm_amd.binding import SGEMM_RM_SCRATCH_BYTES
 
-    need = SGEMM_RM_SCRATCH_BYTES if use_ws else 0  # the stream-K workspace (128 MiB)
+    need = SGEMM_RM_SCRATCH_BYTES if use_ws else 0  # the stream-K / K-slice workspace (128 MiB)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     s = torch.cuda.current_stream()
     rc = lib.sgemm_rm_op_strided_batched_ws(ta, tb, M, N, K, -1.5, dA.data_ptr(), lda, sA, dB.data_ptr(), ldb, sB,

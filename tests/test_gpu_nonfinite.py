@@ -120,3 +120,13 @@ def test_stream_k(oracle):
     ws = torch.empty(2 * 256 * 256 * 256 * 4, dtype=torch.uint8, device="cuda")
     run_case(oracle, 1024, 1280, 77, TILES[256], seed=11, ws=ws)
     run_case(oracle, 4352 + 37, 4352 + 19, 40, TILES[256], seed=12, ws=ws)
+
+
+def test_k_slices(oracle):
+    """K slices (the 64 configuration forced, with a workspace): the non-finite values fall in
+    different slices of a tile, and the fix-up adds the partial tiles."""
+    import torch
+
+    ws = torch.empty(128 << 20, dtype=torch.uint8, device="cuda")
+    run_case(oracle, 210, 148, 30000, TILES[64], seed=13, ws=ws)
+    run_case(oracle, 64, 64, 100000, TILES[64], seed=14, ws=ws)

@@ -6,8 +6,8 @@ workspace, so on the same inputs the two give the same bits.  Two calls in a row
 (the second on a smaller problem, which leaves the first call's partial tiles in
 the scratch) are each compared with the _ws call given a caller workspace, bit for
 bit, and with the oracle: integer inputs (every summation order exact) bit for
-bit, random ones within the bound.  The shapes run stream-K (the scratch in use)
-and the one-tile path (scratch unused).
+bit, random ones within the bound.  The shapes run stream-K and K slices (the
+scratch in use) and the one-tile path (scratch unused).
 """
 import numpy as np
 import pytest
@@ -99,3 +99,23 @@ def test_noalloc_default_path_random_twice(oracle):
         assert_within_bound(c_window(got, M, N, ldc), ref, S, f"noalloc {M}x{N}x{K}")
         check_padding(got, C, M, N, ldc)
     assert sgemm_rm_workspace_size(4608, 4608, 4608) == WS_BYTES
+
+
+@pytest.mark.parametrize("variant", [7, 0])  # the 64 configuration forced, the default path
+def test_noalloc_k_slices_twice(oracle, variant):
+    """K slices (12 tiles x 42 slices, then one tile x 195 slices, whose partial tiles
+    overwrite the first call's in the scratch): each call equals the _ws call bit for bit
+    and the oracle bit for bit (integer inputs)."""
+    import torch
+
+    ws = torch.empty(WS_BYTES, dtype=torch.uint8, device="cuda")
+    for M, N, K, seed in ((210, 148, 30000, 41), (64, 64, 100000, 42)):
+        print(f"[noalloc] K slices {M}x{N}x{K} variant {variant}", flush=True)
+        M, N, K, lda, ldb, ldc, A, B, C = _integer_case(M, N, K, seed)
+        got = _call(True, M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, variant)
+        want = _call(False, M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, variant, ws)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"{M}x{N}x{K}: differs from the _ws call"
+        ref, _ = oracle.full(M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, with_absab=False)
+        bad = np.argwhere(c_window(got, M, N, ldc).astype(np.float64) != ref)
+        assert bad.size == 0, f"{M}x{N}x{K}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+        check_padding(got, C, M, N, ldc)
