@@ -98,8 +98,10 @@ inline double modelled_stream_k_time(int M, int N, int K, int batch) {
 // K slices (64 configuration, batch 1, with a workspace): a product of few tiles and long K
 // leaves most CUs idle however its tiles are cut; its K range can be cut instead.  Each of
 // the tiles' K ranges is split into S contiguous slices, one workgroup each, so that the
-// launch holds about two workgroups per CU (the configuration's co-residency) with at
-// least kMinSliceIters K-tiles of 32 per slice; the raw partial tiles go to the workspace
+// launch holds about one workgroup per CU with at least kMinSliceIters K-tiles of 32 per
+// slice (about two per CU measured 2-24% slower on 6 of 8 shapes, e.g. 64 x 64 x 262144:
+// 38.3 against 30.7 us, 512 x 512 x 16384: 80.7 against 74.3 us; faster on 1024 x 64 x
+// 65536: 85.6 against 90.8 us); the raw partial tiles go to the workspace
 // and a second kernel adds them in slice order (deterministic) and applies alpha and beta.
 // Thin strips do not split, so the form applies where the 64 configuration's tiles cover
 // the matrix (remainders of 0 or at least 16 rows, and of 0 or at least 16 columns that
@@ -111,11 +113,11 @@ inline int k_slices(int M, int N, int K, int batch) {
   if (!covered) return 1;
   const long long tiles = (long long)((M + 63) / 64) * ((N + 63) / 64);
   const long long iters = (K + 31) / 32;
-  long long s = 2 * kCUs / tiles;
+  long long s = kCUs / tiles;
   if (s > iters / kMinSliceIters) s = iters / kMinSliceIters;
   return s >= 2 ? (int)s : 1;
 }
-// Modelled time of the sliced form: the layers of tiles x S workgroups at the 64
+// Modelled time of the sliced form: the layer of tiles x S workgroups at the 64
 // configuration's cost over K / S, plus the fix-up (a launch and the partial tiles read
 // at about 2 TB/s); negative where it does not apply.
 constexpr double kSliceFixupUs = 3.0;

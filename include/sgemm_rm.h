@@ -212,7 +212,7 @@ int sgemm_cm_strided_batched_ex(int transA, int transB, int M, int N, int K, flo
  * sgemm_rm_op_strided_batched_ex.  With a large enough workspace, SGEMM_RM_VARIANT_MFMA_T256
  * uses stream-K whenever the tiles leave a partial wave and SGEMM_RM_VARIANT_MFMA_T64 uses
  * K slices wherever they apply (a single product covered by 64 x 64 tiles, remainders of
- * 0 or at least 16 rows and columns, whose tiles fill under two workgroups per CU and whose
+ * 0 or at least 16 rows and columns, whose tiles fill under one workgroup per CU and whose
  * K gives each slice at least 512), for tests and sweeps; the other forced variants ignore
  * the workspace.  Calls that share a
  * workspace must not overlap (same stream, or synchronised).  Return codes as

@@ -6,7 +6,7 @@ to the workspace and a second kernel adds them in slice order and applies alpha 
 (the deterministic split-K for small outputs).  The result must match the oracle like any
 other path: bit for bit on integer inputs (every order of the sums is exact), within the
 bound on random ones, the same on every run, with beta = 0 not reading C, and C's padding
-untouched.  Shapes: one tile (S = 512), 16 tiles, guarded tiles on both sides, a K tail,
+untouched.  Shapes: one tile (S = 256), 16 tiles, guarded tiles on both sides, a K tail,
 transposed operands, and the default path's choice against the forced 64 configuration.
 """
 import numpy as np

@@ -103,7 +103,7 @@ def test_noalloc_default_path_random_twice(oracle):
 
 @pytest.mark.parametrize("variant", [7, 0])  # the 64 configuration forced, the default path
 def test_noalloc_k_slices_twice(oracle, variant):
-    """K slices (12 tiles x 42 slices, then one tile x 195 slices, whose partial tiles
+    """K slices (12 tiles x 21 slices, then one tile x 195 slices, whose partial tiles
     overwrite the first call's in the scratch): each call equals the _ws call bit for bit
     and the oracle bit for bit (integer inputs)."""
     import torch
