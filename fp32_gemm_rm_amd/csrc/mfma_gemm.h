@@ -361,11 +361,18 @@ __global__ __launch_bounds__(BN / 4 * kSliceGroups) void slice_fixup_kernel(Prob
   if (g < G) {
     const int s0 = (int)((long long)g * S / G), s1 = (int)((long long)(g + 1) * S / G);
     const float* col = map.ws + (long long)u * (BM * BN) + r * BN + 4 * q;
-    sum = *reinterpret_cast<const float4*>(col + (long long)s0 * nmfma * (BM * BN));
-    for (int s = s0 + 1; s < s1; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(col + (long long)s * nmfma * (BM * BN));
-      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    auto slice = [&](int s) { return *reinterpret_cast<const float4*>(col + (long long)s * nmfma * (BM * BN)); };
+    auto add = [&](const float4& v) { sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w; };
+    sum = slice(s0);
+    int s = s0 + 1;
+    for (; s + 4 <= s1; s += 4) {  // four loads in flight, added in slice order
+      const float4 v0 = slice(s), v1 = slice(s + 1), v2 = slice(s + 2), v3 = slice(s + 3);
+      add(v0);
+      add(v1);
+      add(v2);
+      add(v3);
     }
+    for (; s < s1; ++s) add(slice(s));
   }
   red[g][q] = sum;
   __syncthreads();
