@@ -107,6 +107,26 @@ def test_edge_shapes_integer_exact(oracle, variant, orient, cm):
         assert c_padding_unchanged(out, C, M, N, ldc, cm), f"C padding written, shape {(M, N, K)}"
 
 
+@pytest.mark.parametrize("variant", [7, 0])  # the 64 configuration forced, the default path
+def test_column_major_fused_right_strip(oracle, variant):
+    """A column-major NN call runs as the row-major product C^T = B^T A^T, whose right strip
+    (columns past 16 tile columns of 64) is computed inside the 64 x 64 tiles at K >= 640:
+    here the strip is the last 5 rows of the column-major C."""
+    M, N, K = 16 * 64 + 5, 200, 700
+    a = integer_matrix(M, K, -4, 4, seed=71)
+    b = integer_matrix(K, N, -4, 4, seed=72)
+    c = integer_matrix(M, N, -4, 4, seed=73)
+    lda, ldb, ldc = M + 3, K + 1, M + 2
+    A, B, C = store(a, False, True, lda, np.nan), store(b, False, True, ldb, np.nan), store(c, False, True, ldc,
+                                                                                             C_PAD_SENTINEL)
+    out = run_op(0, 0, M, N, K, 2.0, A, lda, B, ldb, -1.0, C, ldc, variant, cm=True)
+    ref, _ = oracle_logical(oracle, M, N, K, 2.0, a, b, -1.0, c)
+    got = read_c(out, M, N, ldc, True).astype(np.float64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+    assert c_padding_unchanged(out, C, M, N, ldc, True)
+
+
 @pytest.mark.parametrize("orient", ["nt", "tn", "tt"])
 @pytest.mark.parametrize("variant", list(VARIANTS))
 def test_ragged_random_bound(oracle, variant, orient):
