@@ -84,7 +84,8 @@ inline hipError_t launch_mfma(const Problem& p, int batch, hipStream_t stream, i
   if (p.ta)
     return p.tb ? launch_mfma_tt(p, batch, stream, tiles, ws, slices)
                 : launch_mfma_tn(p, batch, stream, tiles, ws, slices);
-  return p.tb ? launch_mfma_nt(p, batch, stream, tiles, ws, slices) : launch_mfma_nn(p, batch, stream, tiles, ws, slices);
+  return p.tb ? launch_mfma_nt(p, batch, stream, tiles, ws, slices)
+              : launch_mfma_nn(p, batch, stream, tiles, ws, slices);
 }
 
 // Compute units of an MI355X (8 XCDs of 32).

@@ -168,9 +168,10 @@ __device__ __forceinline__ void thin_strip(const Problem& p, bool cols, int firs
   }
 }
 
-// A right thin strip (columns [n0, n0 + w) of C, w < 16) fused into the MFMA tiles of the
-// 192, 128 and 64 configurations, for operands stored row-major (A along k, B along n): a
-// separate thin-strip workgroup on a CU beside a tile takes that tile's MFMA, LDS and load
+// A right thin strip (columns [n0, n0 + w) of C, w < 16) fused into the MFMA tiles (the
+// launch uses it in the 64 configuration, for operands stored row-major: A along k, B along
+// n; written for any configuration whose K-tile gives each thread one B value): a separate
+// thin-strip workgroup on a CU beside a tile takes that tile's MFMA, LDS and load
 // slots for the strip's whole latency-bound K loop (1000 x 1030 x 999 on 64 x 64 tiles:
 // 23.8 us, against 21.5 us for the 1024 columns of tiles alone).  Fused, tile (bm, bn)
 // computes rows [bm BM + 4 bn, + 4) of the strip from the A rows its K-tiles already hold
@@ -220,7 +221,9 @@ struct FusedStrip {
   // the last K-tile, kl < BK valid rows: rows past K read row K - 1, and store zeroes them
   // (a select right after the load would make the compiler wait for the load there)
   template <int SET>
-  __device__ __forceinline__ void load_tail(int k0, int kl) { reg[SET] = bcol[(long long)(k0 + min(kk, kl - 1)) * ldb]; }
+  __device__ __forceinline__ void load_tail(int k0, int kl) {
+    reg[SET] = bcol[(long long)(k0 + min(kk, kl - 1)) * ldb];
+  }
   // a full K-tile's values to its LDS stage
   template <int SET>
   __device__ __forceinline__ void store(float* stage) const { stage[jl * kStride + kk] = reg[SET]; }
