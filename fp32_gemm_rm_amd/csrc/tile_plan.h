@@ -30,10 +30,15 @@ struct TileCost {
 // tile costs against forced-configuration timings of 75 shapes (squares, skinny, long-K,
 // ragged, batched, and 40 seeded random ones): the choice costs 0.5% on average against
 // the fastest configuration of each shape.
-// The 16 configuration's blocks (one per workgroup of 8 wavefronts, several workgroups per
-// CU) are priced per layer of 256 blocks: 2.6 us per 1024 of K for one layer, 2.8 for more
-// (256 x 256 x 1024: 5.8 us against 8.7 on 32 x 32 tiles; 512^3, four layers: 8.8 against
-// 6.5 us), so it is chosen for outputs of at most a few hundred blocks.
+// The 16 configuration's blocks (one per workgroup of 8 wavefronts) read their operands
+// straight from global memory, without the tiles' reuse through LDS, so their cost grows
+// with the blocks in flight as well as with the layers: kBlock16Base + kBlock16PerBlock B
+// us per 1024 of K for one layer of B <= 256 blocks, kBlock16Layer per layer beyond (a fit
+// to eager timings of 120 seeded random shapes, every configuration forced: 2.6 us for any
+// layer before, which chose 16 x 16 blocks over 32 x 32 tiles where those were up to 1.5x
+// faster, e.g. 3057 x 61 x 573, 768 blocks: 11.1 against 7.5 us; mean loss against the
+// fastest configuration 2.0% -> 1.6%).  The kTileCosts entry of side 16 is not used.
+constexpr double kBlock16Base = 2.5, kBlock16PerBlock = 0.006, kBlock16Layer = 4.0;
 constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 4.0},
                                    {192, 134.0, 133.3, 0.0},
                                    {128, 60.5, 59.5, 0.0},
@@ -67,6 +72,9 @@ inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
   if (c.side == 256 && !thin256(M, N)) return 1e30;
   const long long tiles = modelled_tiles(M, c.side) * modelled_tiles(N, c.side) * batch;
   const long long layers = (tiles + 255) / 256;
+  if (c.side == 16)
+    return (layers == 1 ? kBlock16Base + kBlock16PerBlock * (double)tiles : kBlock16Layer * (double)layers) *
+           (double)K / 1024.0;
   // the 256 thin-strip form only over one layer of tiles: past it the strips' workgroups,
   // each on a whole CU, add up (8200^3: 7809 against 7773 us on 128 x 128 tiles)
   if (c.side == 256 && (M % 256 != 0 || N % 256 != 0) && layers > 1) return 1e30;
