@@ -1,0 +1,272 @@
+// MFMA SGEMM, the direct-to-LDS K loop of the 256 configuration: the operands of each
+// K-tile go from global memory straight into an LDS stage (buffer_load_dwordx4 ... lds,
+// gfx950's 128-bit LDS-DMA load), with no register staging and no LDS store instructions.
+#pragma once
+
+#include <type_traits>
+#include "mfma_tiles.h"
+
+namespace sgemm_impl {
+namespace mfma_detail {
+
+// LDS stages of the direct pipeline (4 x 32.25 KiB).  A K-tile is loaded NST K-tiles ahead
+// of its MFMAs, and the wait before each barrier leaves the last NST - 2 K-tiles' loads in
+// flight.  Measured at 4096^3: 2 stages 932, 3 stages 922, 4 stages 913 us.
+constexpr int kDirectStages = 4;
+// One load instruction after every kDirectSpacing-th MFMA of a K-tile (4096^3: after every
+// 1st, 2nd, 4th, 8th, 16th: 914.6, 913.4, 909.4, 914.5, 918.5 us; all eight loads before
+// the MFMAs: 950.3 us).
+constexpr int kDirectSpacing = 4;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// x, the same in every lane, as a value the compiler knows to be uniform (scalar
+// registers): address arithmetic on it then stays on the scalar unit.
+__device__ __forceinline__ long long uniform64(long long x) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)x);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)((unsigned long long)x >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// Buffer resource of a raw buffer at `base` (64-bit address, stride 0, no range limit
+// below 2^31 bytes; gfx9 data format word).  `base` is uniform; computed from uniform64
+// values it is already in scalar registers and the readfirstlanes fold away.
+__device__ __forceinline__ v4i buffer_rsrc(const float* base) {
+  const long long a = uniform64(reinterpret_cast<long long>(base));
+  return v4i{(int)(unsigned)a, (int)(unsigned)((unsigned long long)a >> 32), 0x7fffffff, 0x00020000};
+}
+
+// Byte address of p inside the workgroup's LDS.
+__device__ __forceinline__ unsigned lds_address(const float* p) {
+  return (unsigned)reinterpret_cast<unsigned long long>((__attribute__((address_space(3))) const float*)p);
+}
+
+// One 128-bit LDS-DMA load: lane l reads 16 bytes at base + voff and writes them to LDS
+// bytes [lds + 16 l, lds + 16 l + 16).  Written as inline assembly: the compiler treats
+// its own LDS-DMA loads as LDS writes of unknown address and waits for all of them before
+// every LDS read, which would serialise the pipeline; here the waits are explicit
+// (direct_barrier).  s_nop 4: five wait states between a VALU write of an SGPR operand
+// and the load's read of it; s_nop 0 after the M0 write, before the load reads M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(v4i rsrc, unsigned lds, unsigned voff) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(__builtin_amdgcn_readfirstlane((int)lds)),
+      "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory instructions of this wavefront are outstanding and
+// all its LDS operations are done, then the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void direct_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+// One operand of the 256 configuration loaded by LDS-DMA: its stage layout is Operand's
+// (R = 256, BK = 16), so the fragment reads are unchanged.  Each of the 4 wavefronts
+// issues 4 loads per K-tile, each writing 1 KiB of the stage:
+//   KROWS (A, or B^T): load i of wavefront w fills rows 64w + 16i .. + 15, four 16-byte
+//     chunks each; lane l takes row 64w + 16i + l/4 at chunk position l%4, which holds
+//     chunk (l%4) ^ (l/16) (swz_slot: rows 16 apart share the XOR, (row/4) % 4 = l/16);
+//   otherwise (A^T, or B): load i of wavefront w fills k-row 4w + i, 256 floats, lane l
+//     taking floats 4l .. 4l+3 (the row's 4 padding words stay unwritten and unread).
+template <bool KROWS>
+struct DirectOperand {
+  static constexpr int R = 256, BK = 16;
+  using Op = Operand<R, BK, 256, KROWS>;
+  const float* base;  // element (r0, k = 0) of the tile's slice
+  long long kstep;    // floats between consecutive K-tiles
+  unsigned voff[4];   // byte offsets of this lane's 16 bytes from the K-tile's origin
+  unsigned lds[4];    // stage-relative LDS byte offsets of the wavefront's 4 loads
+
+  __device__ __forceinline__ void init(const float* X, long long ld, int r0, int w, int l) {
+    // uniform: the K-tile origins base + kt * kstep are then computed by scalar instructions
+    // (as vector ones, followed by readfirstlane, the loop ran 2% slower)
+    base = reinterpret_cast<const float*>(uniform64(reinterpret_cast<long long>(KROWS ? X + (long long)r0 * ld : X + r0)));
+    kstep = uniform64(KROWS ? BK : BK * ld);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (KROWS) {
+        const int row = 64 * w + 16 * i + l / 4, chunk = (l % 4) ^ (l / 16);
+        voff[i] = (unsigned)((long long)row * ld + 4 * chunk) * 4u;
+        lds[i] = (unsigned)((64 * w + 16 * i) * BK) * 4u;
+      } else {
+        voff[i] = (unsigned)((long long)(4 * w + i) * ld + 4 * l) * 4u;
+        lds[i] = (unsigned)((4 * w + i) * Op::STRIDE) * 4u;
+      }
+    }
+  }
+  // load i of K-tile kt into the stage at LDS byte address `stage`
+  __device__ __forceinline__ void load(int i, int kt, unsigned stage) const {
+    lds_dma16(buffer_rsrc(base + (long long)__builtin_amdgcn_readfirstlane(kt) * kstep), stage + lds[i], voff[i]);
+  }
+};
+
+// Whether the direct pipeline can load this problem: 16-byte aligned rows (vec_loads_ok)
+// and every byte offset from a K-tile's origin below 2^31 (the buffer offsets are 32-bit).
+inline bool direct_ok(const Problem& p, int batch) {
+  if (!vec_loads_ok(p, batch)) return false;
+  constexpr long long kLimit = 1LL << 31;
+  const long long a = p.ta ? 15 * p.lda + 256 : 255 * p.lda + 16;  // floats past the origin
+  const long long b = p.tb ? 255 * p.ldb + 16 : 15 * p.ldb + 256;
+  return a * 4 < kLimit && b * 4 < kLimit;
+}
+
+// K-tiles [kb, ke) of the 256 x 256 tile at (m0, n0), as mfma_tile_pf with WM = WN = 2,
+// KS = 1, BK = 16, with kDirectStages LDS stages filled by LDS-DMA loads.  Tile j lives in
+// stage (j - kb) % NST and fragment set (j - kb) % 2.  During K-tile t:
+//   - tile t + NST is loaded into stage t's (its fragments were read during K-tile t - 1,
+//     before the last barrier), one load after every kDirectSpacing-th MFMA;
+//   - the fragments of tile t + 1 are read from its stage into the other set;
+//   - the MFMAs of tile t run on their set;
+// and before the barrier that ends it, each wavefront waits for its loads of tile t + 2
+// (the last NST - 2 K-tiles' loads stay in flight), so that after the barrier tile t + 2
+// is in LDS for every wavefront.  A last, partial K-tile (K % 16 != 0) is loaded through
+// registers and LDS stores instead (Operand::load_tail, zeros past K).
+template <bool TA, bool TB, int GUARD>
+__device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
+                                                 float* part) {
+  constexpr int BM = 256, BN = 256, BK = 16, WM = 2, WN = 2, NST = kDirectStages, SP = kDirectSpacing;
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, 1, TA, TB>;
+  using OpA = typename Cfg::OpA;
+  using OpB = typename Cfg::OpB;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN;
+  static_assert(Cfg::kThreads == 256 && Cfg::KG == 1 && FM == 4 && FN == 4, "4 wavefronts of 128 x 128, BK 16");
+  static_assert(NST * Cfg::kStageFloats * 4 <= 160 * 1024, "stages fit the LDS");
+  constexpr int kLoads = 8;  // LDS-DMA loads per wavefront and K-tile
+  static_assert(7 * SP < 8 * FM * FN, "the loads go out during the K-tile's MFMAs");
+  auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
+  auto b_stage = [&](int s) { return smem + s * Cfg::kStageFloats + OpA::kStageFloats; };
+
+  const int t = threadIdx.x, l = t % 64;
+  const int w = __builtin_amdgcn_readfirstlane(t / 64);
+  const int lr = l % 32, lh = l / 32;
+  const int wm0 = (w / WN) * (BM / WM), wn0 = (w % WN) * (BN / WN);
+
+  DirectOperand<!TA> da;
+  DirectOperand<TB> db;
+  da.init(p.A, p.lda, m0, w, l);
+  db.init(p.B, p.ldb, n0, w, l);
+  const unsigned lds0 = lds_address(smem);
+  const int nfull = p.K / BK;
+  auto load_one = [&](int q, int kt, int s) {  // load q (0-3 A, 4-7 B) of full K-tile kt
+    const unsigned stage = lds0 + (unsigned)(s * Cfg::kStageFloats) * 4u;
+    if (q < 4)
+      da.load(q, kt, stage);
+    else
+      db.load(q - 4, kt, stage + OpA::kStageFloats * 4u);
+  };
+  // K-tile kt into stage s: LDS-DMA loads, or for the partial last K-tile registers and
+  // LDS stores (its loads are the compiler's: it waits for them before the stores)
+  auto fill = [&](int kt, int s) {
+    if (kt < nfull) {
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) load_one(q, kt, s);
+    } else {
+      OpA opa;
+      OpB opb;
+      opa.init(p.A, p.lda, m0, BM, t);
+      opb.init(p.B, p.ldb, n0, BN, t);
+      opa.template load_tail<true, false, 0>(kt * BK, p.K - kt * BK);
+      opb.template load_tail<true, false, 0>(kt * BK, p.K - kt * BK);
+      opa.template store<0>(a_stage(s));
+      opb.template store<0>(b_stage(s));
+    }
+  };
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  float af[2][FM][8], bf[2][FN][8];
+  auto frags = [&](auto set, int s) {
+    constexpr int S = decltype(set)::value;
+    read_frags<OpA, FM, Cfg::VA>(a_stage(s), wm0, 0, lr, lh, af[S]);
+    read_frags<OpB, FN, Cfg::VB>(b_stage(s), wn0, 0, lr, lh, bf[S]);
+  };
+  auto mfma = [&](auto set, auto mc) {
+    constexpr int S = decltype(set)::value, m = decltype(mc)::value;
+    constexpr int e = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[S][i][e], bf[S][j][e], acc[i][j], 0, 0, 0);
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+
+  // prologue: tiles kb .. kb + NST - 1 into stages 0 .. NST - 1; tile kb's fragments
+  const int n = ke - kb;
+  for (int j = 0; j < NST; ++j)
+    if (j < n) fill(kb + j, j);
+  if (n >= NST)
+    direct_barrier<kLoads * (NST - 1)>();
+  else
+    direct_barrier<0>();
+  frags(Set0{}, 0);
+  if (n >= NST)
+    direct_barrier<kLoads * (NST - 2)>();
+  else
+    direct_barrier<0>();
+
+  // steady K-tile (tile kt + NST exists and is full): explicit order, since the compiler
+  // cannot place inline assembly among the MFMAs by itself
+  constexpr int kLast = (kLoads - 1) * SP;  // the MFMA after which the last load goes
+  constexpr int kMfmas = 8 * FM * FN;
+  auto steady = [&](auto set, int kt) {
+    constexpr int P = decltype(set)::value;
+    const int s = (kt - kb) % NST;
+    static_for<kLast + 1>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      mfma(set, mc);
+      if constexpr (m % SP == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_one(m / SP, kt + NST, s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+    frags(std::integral_constant<int, P ^ 1>{}, (s + 1) % NST);
+    static_for<kMfmas - kLast - 1>(
+        [&](auto mc) { mfma(set, std::integral_constant<int, decltype(mc)::value + kLast + 1>{}); });
+    sched_interleave<0, kMfmas - kLast - 1, 1, Cfg::kFragReads, 0, 0>();
+    direct_barrier<kLoads * (NST - 2)>();
+  };
+  auto step = [&](auto set, int kt) {
+    constexpr int P = decltype(set)::value;
+    const int s = (kt - kb) % NST;
+    if (kt + NST < ke) fill(kt + NST, s);
+    if (kt + 1 < ke) frags(std::integral_constant<int, P ^ 1>{}, (s + 1) % NST);
+    static_for<kMfmas>([&](auto mc) { mfma(set, mc); });
+    direct_barrier<0>();
+  };
+  int kt = kb;
+  const int steady_end = min(ke, nfull);
+  for (; kt + 1 + NST < steady_end; kt += 2) {  // tiles kt + NST and kt + NST + 1 are full and in range
+    steady(Set0{}, kt);
+    steady(Set1{}, kt + 1);
+  }
+  for (; kt < ke; kt += 2) {
+    step(Set0{}, kt);
+    if (kt + 1 < ke) step(Set1{}, kt + 1);
+  }
+  finish_acc<BM, BN, WM, WN, 1, FM, FN, Cfg::VA, Cfg::VB, GUARD>(p, acc, smem, m0, n0, part);
+}
+
+}  // namespace mfma_detail
+}  // namespace sgemm_impl

@@ -30,7 +30,7 @@
 // SIMD a single wavefront, run 4 wavefronts per SIMD and hide LDS, barrier and
 // MFMA latencies.
 //
-// Pipelines (one barrier per K-tile, two LDS stages):
+// Pipelines (one barrier per K-tile):
 //   mfma_tile (32 configuration): the global loads of tile t+2 are issued as tile t's
 //     MFMAs start, into the second of two register sets, and tile t+1's registers are
 //     stored half-way through those MFMAs; fragments are read from LDS at the start of
@@ -39,7 +39,10 @@
 //     and K-tile): fragments are read one K-tile ahead into a second register set, so
 //     no MFMA waits for LDS; the global loads (one K-tile ahead of their LDS stores in
 //     the 192 configuration, two in the others), LDS stores and fragment reads are
-//     interleaved with the MFMAs.
+//     interleaved with the MFMAs.  Two LDS stages.
+//   mfma_tile_direct (256 configuration with 16-byte aligned rows, mfma_direct.h): as
+//     mfma_tile_pf, but the operands go from global memory straight to LDS (LDS-DMA
+//     loads, four stages, issued four K-tiles ahead): no register staging, no LDS stores.
 // LDS layout:
 //   A tile, BM rows of BK floats (BK/4 16-byte chunks), no padding.  For
 //     BK = 16, chunk c of row r is stored at chunk position c ^ ((r/4) % 4).  On
@@ -86,6 +89,7 @@
 
 #include <type_traits>
 
+#include "mfma_direct.h"
 #include "mfma_strips.h"
 #include "mfma_tiles.h"
 
@@ -146,8 +150,10 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // PF: the tiles run mfma_tile_pf (one k-group per wavefront and K-tile) instead of mfma_tile.
 // FUSE: the right thin strip is computed inside the tiles (FusedStrip): tile (bm, bn) takes
 // strip rows [bm BM + 4 bn, + 4), and the launch holds no right-strip workgroups.
+// DIRECT (256 configuration, VEC, direct_ok): the tiles run mfma_tile_direct.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          int EDGE_MIN, bool STREAM_K, bool VEC, bool PF, bool FUSE = false, bool SLICED = false>
+          int EDGE_MIN, bool STREAM_K, bool VEC, bool PF, bool FUSE = false, bool SLICED = false,
+          bool DIRECT = false>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
@@ -163,8 +169,12 @@ void mfma_kernel(Problem p, TileMap map) {
   constexpr int kEdgeFloats = kEdges ? kGroups * EdgeTile::kLdsFloats  // >= its reduction floats
                                      : kThin ? thin_red_floats<Cfg::kThreads>() : 0;
   constexpr int kFuseFloats = FUSE ? 2 * Cfg::kStageFloats + 2 * FusedStrip<BK, Cfg::kThreads>::kStageFloats : 0;
+  static_assert(!DIRECT || (BM == 256 && BN == 256 && BK == 16 && KS == 1 && VEC && !FUSE && !SLICED),
+                "the direct pipeline serves the 256 configuration");
+  constexpr int kDirectFloats = DIRECT ? kDirectStages * Cfg::kStageFloats : 0;
   constexpr int kFloats0 = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
-  constexpr int kFloats = kFloats0 > kFuseFloats ? kFloats0 : kFuseFloats;
+  constexpr int kFloats1 = kFloats0 > kFuseFloats ? kFloats0 : kFuseFloats;
+  constexpr int kFloats = kFloats1 > kDirectFloats ? kFloats1 : kDirectFloats;
   static_assert(kFloats * 4 <= 160 * 1024, "LDS of one workgroup fits a CU");
   __shared__ __attribute__((aligned(16))) float smem[kFloats];
   poison_lds(smem, kFloats);
@@ -174,10 +184,14 @@ void mfma_kernel(Problem p, TileMap map) {
   pt.N = map.Nf;
   // fused strip rows of the tile being run (FUSE; set by the one-tile branch below)
   int srow0 = 0, srows = 0;
-  auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) {
+  // always inlined: called from the one-tile and the stream-K branches, the compiler would
+  // otherwise emit it as a function, whose call spills the accumulators
+  auto tile = [&](auto guard, int m0, int n0, int kb, int ke, float* part) __attribute__((always_inline)) {
     // guard bits 0-1 (the tile's partial sides), bit 2: the launch has full tiles only
     constexpr int G = decltype(guard)::value | (kGuarded ? 0 : 4);
-    if constexpr (PF)
+    if constexpr (DIRECT)
+      mfma_tile_direct<TA, TB, G>(pt, m0, n0, kb, ke, smem, part);
+    else if constexpr (PF)
       mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G, FUSE>(
           pt, m0, n0, kb, ke, smem, part, srow0, srows, map.Nf, p.N - map.Nf);
     else
@@ -187,7 +201,7 @@ void mfma_kernel(Problem p, TileMap map) {
   const int ndp = STREAM_K ? map.dp_tiles : nmfma;
   const int iters = (p.K + BK - 1) / BK;
   // the guard form of tile (m0, n0): full, past M, past N or both
-  auto guarded_tile = [&](int m0, int n0, int kb, int ke, float* part) {
+  auto guarded_tile = [&](int m0, int n0, int kb, int ke, float* part) __attribute__((always_inline)) {
     if constexpr (kGuarded) {
       const bool past_m = m0 + BM > pt.M, past_n = n0 + BN > pt.N;
       if (!past_m && !past_n)
@@ -479,7 +493,11 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
       map.ws = ws;
       const long long blocks = map.dp_tiles + map.sk_wgs + edge_tiles;
       if (!grid_fits(blocks, block.x)) return hipErrorInvalidConfiguration;
-      if (vec)
+      if (direct_ok(p, batch))
+        hipLaunchKernelGGL(
+            (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, 0, true, true, PF, false, false, true>),
+            dim3((unsigned)blocks), block, 0, stream, p, map);
+      else if (vec)
         hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, 0, true, true, PF>),
                            dim3((unsigned)blocks), block, 0, stream, p, map);
       else
@@ -524,6 +542,14 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
         hipLaunchKernelGGL(
             (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, false, PF, true>), grid,
             block, 0, stream, p, map);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (BM == 256) {
+    if (nmfma > 0 && direct_ok(p, batch)) {
+      hipLaunchKernelGGL(
+          (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF, false, false, true>),
+          grid, block, 0, stream, p, map);
       return hipGetLastError();
     }
   }
