@@ -1,0 +1,102 @@
+"""The 256 configuration's two K loops: LDS-DMA loads and register-staged loads.
+
+Where every row of A and B is 16-byte aligned and the byte offsets inside a K-tile fit in
+31 bits, the 256 x 256 tiles load their operands straight into LDS (buffer_load ... lds);
+a leading dimension past about 2.1 million floats (along k) takes the register-staged
+pipeline instead.  Both must give the oracle's result bit for bit on integer inputs (every
+partial sum is exact), and, since both read the same LDS layout in the same order, the same
+bits as each other on random inputs too.  Shapes cover a K tail (the last K-tile loaded
+through registers in the direct pipeline), fewer K-tiles than LDS stages, and B stored
+transposed.  The operand padding is NaN, so a read past a row reaches C.
+"""
+import numpy as np
+import pytest
+
+from fp32_gemm_rm_amd.workloads import integer_matrix
+
+from .parity import c_window
+
+pytestmark = pytest.mark.gpu
+
+T256 = 5  # SGEMM_RM_VARIANT_MFMA_T256
+# smallest multiple of 4 with 255 * ld * 4 bytes >= 2^31: rows along k this far apart leave
+# the direct pipeline
+HUGE_LD = ((2**31 + 4 * 255 - 1) // (4 * 255) + 3) // 4 * 4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp32_gemm_rm_amd import load_library
+
+    load_library()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _ld4(n):
+    return (n + 3) // 4 * 4
+
+
+def _stored_on_device(x, ld):
+    """Row-major rows x cols matrix x on the device with leading dimension ld, NaN padding."""
+    import torch
+
+    rows, cols = x.shape
+    buf = torch.full((rows * ld,), float("nan"), device="cuda")
+    buf.view(rows, ld)[:, :cols] = torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    return buf
+
+
+def _run(M, N, K, a, lda, b, ldb, tb, c, alpha, beta):
+    """C := alpha op(A) op(B) + beta C on the 256 configuration; b is op(B) (K x N), stored
+    transposed (N x K) when tb."""
+    import torch
+
+    from fp32_gemm_rm_amd.binding import sgemm_rm_op_strided_batched_ex
+
+    dA = _stored_on_device(a, lda)
+    dB = _stored_on_device(np.ascontiguousarray(b.T) if tb else b, ldb)
+    dC = torch.from_numpy(np.ascontiguousarray(c)).to("cuda")
+    s = torch.cuda.current_stream()
+    sgemm_rm_op_strided_batched_ex(0, tb, M, N, K, alpha, dA.data_ptr(), lda, 0, dB.data_ptr(), ldb, 0, beta,
+                                   dC.data_ptr(), N, 0, 1, s.cuda_stream, T256)
+    s.synchronize()
+    out = dC.cpu().numpy()
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    return out
+
+
+@pytest.mark.parametrize("tb", [0, 1])
+@pytest.mark.parametrize("M,N,K", [(256, 512, 16 * 9 + 5), (512, 256, 48), (256, 256, 16 * 40)])
+def test_direct_and_staged_integer_exact(oracle, M, N, K, tb):
+    print(f"[direct] {M}x{N}x{K} tb={tb} huge ld {HUGE_LD}", flush=True)
+    a = integer_matrix(M, K, -4, 4, seed=M + K)
+    b = integer_matrix(K, N, -4, 4, seed=N + K)
+    c = integer_matrix(M, N, -4, 4, seed=M + N)
+    ref, _ = oracle.full(M, N, K, -1.5, a.reshape(-1), K, b.reshape(-1), N, 0.5, c.reshape(-1), N, with_absab=False)
+    # leading dimensions that are multiples of 4 (16-byte rows): the direct pipeline
+    lda_small, ldb_small = _ld4(K) + 4, _ld4(K if tb else N) + 4
+    direct = _run(M, N, K, a, lda_small, b, ldb_small, tb, c, -1.5, 0.5)
+    # A's rows HUGE_LD apart: the register-staged pipeline (and B^T's too, when tb)
+    staged = _run(M, N, K, a, HUGE_LD, b, HUGE_LD if tb else ldb_small, tb, c, -1.5, 0.5)
+    for name, out in (("direct", direct), ("staged", staged)):
+        got = c_window(out, M, N, N).astype(np.float64)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"{name}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 16 * 33 + 7)])
+def test_direct_and_staged_same_bits(M, N, K):
+    """Random inputs: the two pipelines add the same products in the same order."""
+    rng = np.random.default_rng(11)
+    a = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    b = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    c = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    direct = _run(M, N, K, a, _ld4(K), b, N, 0, c, 1.25, -0.75)
+    staged = _run(M, N, K, a, HUGE_LD, b, N, 0, c, 1.25, -0.75)
+    assert np.array_equal(direct.view(np.uint32), staged.view(np.uint32))
