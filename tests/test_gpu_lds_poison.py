@@ -12,8 +12,8 @@ Integer inputs in [-4, 4] with NaN padding in A and B make every result exact, s
 case is compared bit for bit with the oracle, over every output, and C's padding must be
 untouched.  The cases reach each LDS layout and pipeline: the LDS-tiled and
 register-blocked VALU kernels, every forced MFMA tile configuration with full, guarded and
-thin-strip partial tiles, the fused right strip, the 256 configuration's thin-strip form
-and scalar edge tiles, stream-K pieces with their fix-up, K slices with theirs, 16 x 16 blocks, the one-layer 128
+thin-strip partial tiles, the fused right strip, the 256 configuration's thin-strip form,
+scalar edge tiles and LDS-DMA loads, stream-K pieces with their fix-up, K slices with theirs, 16 x 16 blocks, the one-layer 128
 form, a strided batch, transposed operands and K tails.
 """
 import numpy as np
@@ -40,6 +40,10 @@ CASES = [
     (8, 0, 0, 3 * 32 + 2, 2 * 32 + 3, 70, 1, False), (8, 1, 0, 2 * 32 + 6, 3 * 32 + 6, 300, 1, False),
     (10, 0, 0, 17, 33, 70, 1, False), (10, 0, 1, 5 * 16 + 3, 3 * 16 + 9, 1100, 1, False),
     (0, 0, 0, 70, 50, 33, 7, False),  # strided batch, default path
+    # 256 tiles through LDS-DMA loads (16-byte rows): K tail, fewer K-tiles than stages and transposed,
+    # thin strips beside them, a strided batch
+    (5, 0, 0, 512, 768, 148, 1, False), (5, 1, 1, 512, 512, 48, 1, False), (5, 0, 1, 256 + 8, 512, 164, 1, False),
+    (5, 0, 0, 256, 256, 64, 3, False),
     (5, 0, 0, 1024, 1280, 77, 1, True),  # stream-K (256 forced, with a workspace): every tile split
     (5, 0, 0, 17 * 256, 17 * 256, 40, 1, True),  # stream-K: whole tiles and pieces
     (7, 0, 0, 210, 148, 30000, 1, True),  # K slices (64 forced, with a workspace) and their fix-up
