@@ -11,11 +11,12 @@ namespace mfma_detail {
 
 // LDS stages of the direct pipeline (4 x 32.25 KiB).  A K-tile is loaded NST K-tiles ahead
 // of its MFMAs, and the wait before each barrier leaves the last NST - 2 K-tiles' loads in
-// flight.  Measured at 4096^3: 2 stages 932, 3 stages 922, 4 stages 913 us.
+// flight.  Measured at 4096^3 (a standalone copy, one load per 1 or 2 MFMAs): 3 stages 922,
+// 4 stages 913-915 us.
 constexpr int kDirectStages = 4;
-// One load instruction after every kDirectSpacing-th MFMA of a K-tile (4096^3: after every
-// 1st, 2nd, 4th, 8th, 16th: 914.6, 913.4, 909.4, 914.5, 918.5 us; all eight loads before
-// the MFMAs: 950.3 us).
+// One load instruction after every kDirectSpacing-th MFMA of a K-tile (two runs at 4096^3:
+// after every 1st, 2nd, 4th MFMA 914.6, 913.4, 913.2 us; every 4th, 8th, 16th 909.4, 914.5,
+// 918.5 us; all eight loads before the MFMAs 950.3 us).
 constexpr int kDirectSpacing = 4;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -98,7 +99,8 @@ struct DirectOperand {
   __device__ __forceinline__ void init(const float* X, long long ld, int r0, int w, int l) {
     // uniform: the K-tile origins base + kt * kstep are then computed by scalar instructions
     // (as vector ones, followed by readfirstlane, the loop ran 2% slower)
-    base = reinterpret_cast<const float*>(uniform64(reinterpret_cast<long long>(KROWS ? X + (long long)r0 * ld : X + r0)));
+    base = reinterpret_cast<const float*>(
+        uniform64(reinterpret_cast<long long>(KROWS ? X + (long long)r0 * ld : X + r0)));
     kstep = uniform64(KROWS ? BK : BK * ld);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

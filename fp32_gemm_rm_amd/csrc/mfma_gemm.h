@@ -547,9 +547,9 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   }
   if constexpr (BM == 256) {
     if (nmfma > 0 && direct_ok(p, batch)) {
-      hipLaunchKernelGGL(
-          (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF, false, false, true>),
-          grid, block, 0, stream, p, map);
+      hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF,
+                                      false, false, true>),
+                         grid, block, 0, stream, p, map);
       return hipGetLastError();
     }
   }

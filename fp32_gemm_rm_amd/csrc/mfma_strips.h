@@ -114,8 +114,10 @@ __device__ __forceinline__ void thin_strip(const Problem& p, bool cols, int firs
         else
           y = make_float4(yk(kl), yk(kl + 1), yk(kl + 2), yk(kl + 3));
         const bool xo = x_in && kin, yo = y_in && kin;
-        xv[S][u][0] = xo ? x.x : 0.f; xv[S][u][1] = xo ? x.y : 0.f; xv[S][u][2] = xo ? x.z : 0.f; xv[S][u][3] = xo ? x.w : 0.f;
-        yv[S][u][0] = yo ? y.x : 0.f; yv[S][u][1] = yo ? y.y : 0.f; yv[S][u][2] = yo ? y.z : 0.f; yv[S][u][3] = yo ? y.w : 0.f;
+        xv[S][u][0] = xo ? x.x : 0.f; xv[S][u][1] = xo ? x.y : 0.f;
+        xv[S][u][2] = xo ? x.z : 0.f; xv[S][u][3] = xo ? x.w : 0.f;
+        yv[S][u][0] = yo ? y.x : 0.f; yv[S][u][1] = yo ? y.y : 0.f;
+        yv[S][u][2] = yo ? y.z : 0.f; yv[S][u][3] = yo ? y.w : 0.f;
       }
     };
     auto steps = [&](auto set) {

@@ -13,8 +13,8 @@ case is compared bit for bit with the oracle, over every output, and C's padding
 untouched.  The cases reach each LDS layout and pipeline: the LDS-tiled and
 register-blocked VALU kernels, every forced MFMA tile configuration with full, guarded and
 thin-strip partial tiles, the fused right strip, the 256 configuration's thin-strip form,
-scalar edge tiles and LDS-DMA loads, stream-K pieces with their fix-up, K slices with theirs, 16 x 16 blocks, the one-layer 128
-form, a strided batch, transposed operands and K tails.
+scalar edge tiles and LDS-DMA loads, stream-K pieces with their fix-up, K slices with theirs,
+16 x 16 blocks, the one-layer 128 form, a strided batch, transposed operands and K tails.
 """
 import numpy as np
 import pytest
