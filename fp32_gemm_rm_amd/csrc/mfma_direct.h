@@ -11,12 +11,14 @@ namespace mfma_detail {
 
 // LDS stages of the direct pipeline (4 x 32.25 KiB).  A K-tile is loaded NST K-tiles ahead
 // of its MFMAs, and the wait before each barrier leaves the last NST - 2 K-tiles' loads in
-// flight.  Measured at 4096^3 (a standalone copy, one load per 1 or 2 MFMAs): 3 stages 922,
-// 4 stages 913-915 us.
+// flight.  Measured at 4096^3 (a standalone copy on 2 x 2 wavefronts, one load per 1 or 2
+// MFMAs): 3 stages 922, 4 stages 913-915 us.
 constexpr int kDirectStages = 4;
-// One load instruction after every kDirectSpacing-th MFMA of a K-tile (two runs at 4096^3:
-// after every 1st, 2nd, 4th MFMA 914.6, 913.4, 913.2 us; every 4th, 8th, 16th 909.4, 914.5,
-// 918.5 us; all eight loads before the MFMAs 950.3 us).
+// One load instruction after every kDirectSpacing-th MFMA of a K-tile.  4096^3 on 2 x 2
+// wavefronts (8 loads, 128 MFMAs per wavefront and K-tile), two runs: after every 1st, 2nd,
+// 4th MFMA 914.6, 913.4, 913.2 us; every 4th, 8th, 16th 909.4, 914.5, 918.5 us; all eight
+// loads before the MFMAs 950.3 us.  On 4 x 2 wavefronts (4 loads, 64 MFMAs): every 4th or
+// 8th 909.1 and 908.5 us.
 constexpr int kDirectSpacing = 4;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -79,22 +81,24 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// One operand of the 256 configuration loaded by LDS-DMA: its stage layout is Operand's
-// (R = 256, BK = 16), so the fragment reads are unchanged.  Each of the 4 wavefronts
-// issues 4 loads per K-tile, each writing 1 KiB of the stage:
-//   KROWS (A, or B^T): load i of wavefront w fills rows 64w + 16i .. + 15, four 16-byte
-//     chunks each; lane l takes row 64w + 16i + l/4 at chunk position l%4, which holds
-//     chunk (l%4) ^ (l/16) (swz_slot: rows 16 apart share the XOR, (row/4) % 4 = l/16);
-//   otherwise (A^T, or B): load i of wavefront w fills k-row 4w + i, 256 floats, lane l
-//     taking floats 4l .. 4l+3 (the row's 4 padding words stay unwritten and unread).
-template <bool KROWS>
+// One operand of the 256 configuration loaded by LDS-DMA by W wavefronts: its stage layout
+// is Operand's (R = 256, BK = 16), so the fragment reads are unchanged.  16 loads per
+// K-tile, each writing 1 KiB of the stage; wavefront w issues L = 16 / W of them, load i
+// being load j = L w + i:
+//   KROWS (A, or B^T): load j fills rows 16j .. 16j + 15, four 16-byte chunks each; lane l
+//     takes row 16j + l/4 at chunk position l%4, which holds chunk (l%4) ^ (l/16)
+//     (swz_slot: rows 16 apart share the XOR, (row/4) % 4 = l/16);
+//   otherwise (A^T, or B): load j fills k-row j, 256 floats, lane l taking floats 4l .. 4l+3
+//     (the row's 4 padding words stay unwritten and unread).
+template <bool KROWS, int W>
 struct DirectOperand {
-  static constexpr int R = 256, BK = 16;
-  using Op = Operand<R, BK, 256, KROWS>;
+  static constexpr int R = 256, BK = 16, L = 16 / W;
+  static_assert(L * W == 16, "the 16 loads split evenly over the wavefronts");
+  using Op = Operand<R, BK, 64 * W, KROWS>;
   const float* base;  // element (r0, k = 0) of the tile's slice
   long long kstep;    // floats between consecutive K-tiles
-  unsigned voff[4];   // byte offsets of this lane's 16 bytes from the K-tile's origin
-  unsigned lds[4];    // stage-relative LDS byte offsets of the wavefront's 4 loads
+  unsigned voff[L];   // byte offsets of this lane's 16 bytes from the K-tile's origin
+  unsigned lds[L];    // stage-relative LDS byte offsets of the wavefront's loads
 
   __device__ __forceinline__ void init(const float* X, long long ld, int r0, int w, int l) {
     // uniform: the K-tile origins base + kt * kstep are then computed by scalar instructions
@@ -103,14 +107,15 @@ struct DirectOperand {
         uniform64(reinterpret_cast<long long>(KROWS ? X + (long long)r0 * ld : X + r0)));
     kstep = uniform64(KROWS ? BK : BK * ld);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < L; ++i) {
+      const int j = L * w + i;
       if (KROWS) {
-        const int row = 64 * w + 16 * i + l / 4, chunk = (l % 4) ^ (l / 16);
+        const int row = 16 * j + l / 4, chunk = (l % 4) ^ (l / 16);
         voff[i] = (unsigned)((long long)row * ld + 4 * chunk) * 4u;
-        lds[i] = (unsigned)((64 * w + 16 * i) * BK) * 4u;
+        lds[i] = (unsigned)(16 * j * BK) * 4u;
       } else {
-        voff[i] = (unsigned)((long long)(4 * w + i) * ld + 4 * l) * 4u;
-        lds[i] = (unsigned)((4 * w + i) * Op::STRIDE) * 4u;
+        voff[i] = (unsigned)((long long)j * ld + 4 * l) * 4u;
+        lds[i] = (unsigned)(j * Op::STRIDE) * 4u;
       }
     }
   }
@@ -130,9 +135,10 @@ inline bool direct_ok(const Problem& p, int batch) {
   return a * 4 < kLimit && b * 4 < kLimit;
 }
 
-// K-tiles [kb, ke) of the 256 x 256 tile at (m0, n0), as mfma_tile_pf with WM = WN = 2,
-// KS = 1, BK = 16, with kDirectStages LDS stages filled by LDS-DMA loads.  Tile j lives in
-// stage (j - kb) % NST and fragment set (j - kb) % 2.  During K-tile t:
+// K-tiles [kb, ke) of the 256 x 256 tile at (m0, n0), as mfma_tile_pf with WM x WN
+// wavefronts (4 x 2 in the library: two per SIMD, each 64 x 128), KS = 1, BK = 16, with
+// kDirectStages LDS stages filled by LDS-DMA loads.  Tile j lives in stage (j - kb) % NST
+// and fragment set (j - kb) % 2.  During K-tile t:
 //   - tile t + NST is loaded into stage t's (its fragments were read during K-tile t - 1,
 //     before the last barrier), one load after every kDirectSpacing-th MFMA;
 //   - the fragments of tile t + 1 are read from its stage into the other set;
@@ -141,18 +147,20 @@ inline bool direct_ok(const Problem& p, int batch) {
 // (the last NST - 2 K-tiles' loads stay in flight), so that after the barrier tile t + 2
 // is in LDS for every wavefront.  A last, partial K-tile (K % 16 != 0) is loaded through
 // registers and LDS stores instead (Operand::load_tail, zeros past K).
-template <bool TA, bool TB, int GUARD>
+template <int WM, int WN, bool TA, bool TB, int GUARD>
 __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                                  float* part) {
-  constexpr int BM = 256, BN = 256, BK = 16, WM = 2, WN = 2, NST = kDirectStages, SP = kDirectSpacing;
+  constexpr int BM = 256, BN = 256, BK = 16, NST = kDirectStages, SP = kDirectSpacing;
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, 1, TA, TB>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
+  using DA = DirectOperand<!TA, WM * WN>;
+  using DB = DirectOperand<TB, WM * WN>;
   constexpr int FM = Cfg::FM, FN = Cfg::FN;
-  static_assert(Cfg::kThreads == 256 && Cfg::KG == 1 && FM == 4 && FN == 4, "4 wavefronts of 128 x 128, BK 16");
+  static_assert(Cfg::KG == 1, "BK 16, one k-group per wavefront");
   static_assert(NST * Cfg::kStageFloats * 4 <= 160 * 1024, "stages fit the LDS");
-  constexpr int kLoads = 8;  // LDS-DMA loads per wavefront and K-tile
-  static_assert(7 * SP < 8 * FM * FN, "the loads go out during the K-tile's MFMAs");
+  constexpr int kLoads = DA::L + DB::L;  // LDS-DMA loads per wavefront and K-tile
+  static_assert((kLoads - 1) * SP < 8 * FM * FN, "the loads go out during the K-tile's MFMAs");
   auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
   auto b_stage = [&](int s) { return smem + s * Cfg::kStageFloats + OpA::kStageFloats; };
 
@@ -161,18 +169,18 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
   const int lr = l % 32, lh = l / 32;
   const int wm0 = (w / WN) * (BM / WM), wn0 = (w % WN) * (BN / WN);
 
-  DirectOperand<!TA> da;
-  DirectOperand<TB> db;
+  DA da;
+  DB db;
   da.init(p.A, p.lda, m0, w, l);
   db.init(p.B, p.ldb, n0, w, l);
   const unsigned lds0 = lds_address(smem);
   const int nfull = p.K / BK;
-  auto load_one = [&](int q, int kt, int s) {  // load q (0-3 A, 4-7 B) of full K-tile kt
+  auto load_one = [&](int q, int kt, int s) {  // load q (A's, then B's) of full K-tile kt
     const unsigned stage = lds0 + (unsigned)(s * Cfg::kStageFloats) * 4u;
-    if (q < 4)
+    if (q < DA::L)
       da.load(q, kt, stage);
     else
-      db.load(q - 4, kt, stage + OpA::kStageFloats * 4u);
+      db.load(q - DA::L, kt, stage + OpA::kStageFloats * 4u);
   };
   // K-tile kt into stage s: LDS-DMA loads, or for the partial last K-tile registers and
   // LDS stores (its loads are the compiler's: it waits for them before the stores)

@@ -42,7 +42,8 @@
 //     interleaved with the MFMAs.  Two LDS stages.
 //   mfma_tile_direct (256 configuration with 16-byte aligned rows, mfma_direct.h): as
 //     mfma_tile_pf, but the operands go from global memory straight to LDS (LDS-DMA
-//     loads, four stages, issued four K-tiles ahead): no register staging, no LDS stores.
+//     loads, four stages, issued four K-tiles ahead): no register staging, no LDS stores,
+//     and with the registers this frees, two wavefronts per SIMD.
 // LDS layout:
 //   A tile, BM rows of BK floats (BK/4 16-byte chunks), no padding.  For
 //     BK = 16, chunk c of row r is stored at chunk position c ^ ((r/4) % 4).  On
@@ -190,7 +191,7 @@ void mfma_kernel(Problem p, TileMap map) {
     // guard bits 0-1 (the tile's partial sides), bit 2: the launch has full tiles only
     constexpr int G = decltype(guard)::value | (kGuarded ? 0 : 4);
     if constexpr (DIRECT)
-      mfma_tile_direct<TA, TB, G>(pt, m0, n0, kb, ke, smem, part);
+      mfma_tile_direct<WM, WN, TA, TB, G>(pt, m0, n0, kb, ke, smem, part);
     else if constexpr (PF)
       mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G, FUSE>(
           pt, m0, n0, kb, ke, smem, part, srow0, srows, map.Nf, p.N - map.Nf);
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(BN / 4 * kSliceGroups) void slice_fixup_kernel(Prob
 // its raw partial tile to ws (slices x tiles x BM x BN floats), and slice_fixup_kernel adds
 // them in slice order and applies alpha and beta.  For products of few tiles and long K.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          int EDGE_MIN = 0, bool PF = false>
+          int EDGE_MIN = 0, bool PF = false, bool DIRECT = false>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws = nullptr, int slices = 1) {
   static_assert(BM == BN && BM % kEdge == 0, "square tiles whose sides are multiples of the edge tile");
   TileMap map;
@@ -493,7 +494,7 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
       map.ws = ws;
       const long long blocks = map.dp_tiles + map.sk_wgs + edge_tiles;
       if (!grid_fits(blocks, block.x)) return hipErrorInvalidConfiguration;
-      if (direct_ok(p, batch))
+      if constexpr (DIRECT)
         hipLaunchKernelGGL(
             (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, 0, true, true, PF, false, false, true>),
             dim3((unsigned)blocks), block, 0, stream, p, map);
@@ -545,20 +546,18 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
       return hipGetLastError();
     }
   }
-  if constexpr (BM == 256) {
-    if (nmfma > 0 && direct_ok(p, batch)) {
-      hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF,
-                                      false, false, true>),
+  if constexpr (DIRECT) {
+    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF,
+                                    false, false, true>),
+                       grid, block, 0, stream, p, map);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF>),
                          grid, block, 0, stream, p, map);
-      return hipGetLastError();
-    }
+    else
+      hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, false, PF>),
+                         grid, block, 0, stream, p, map);
   }
-  if (vec)
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF>),
-                       grid, block, 0, stream, p, map);
-  else
-    hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, false, PF>),
-                       grid, block, 0, stream, p, map);
   return hipGetLastError();
 }
 
@@ -594,8 +593,10 @@ hipError_t launch_block16(const Problem& p, int batch, hipStream_t stream) {
 
 // The tile configurations (tile_plan.h), by tile side.  All but the 32 configuration run
 // mfma_tile_pf (fragments read one K-tile ahead).
-//   256: 256 x 256 tiles, 2 x 2 wavefronts of 128 x 128 (one per SIMD, 256 accumulator
-//        registers each), BK 16, one global register set: one workgroup per CU.
+//   256: 256 x 256 tiles, BK 16, one workgroup per CU.  With the direct K loop (16-byte
+//        aligned rows, direct_ok) 4 x 2 wavefronts of 64 x 128, two per SIMD (128
+//        accumulator registers each); otherwise 2 x 2 wavefronts of 128 x 128, one per SIMD
+//        (256 accumulator registers each), loads two K-tiles ahead through registers.
 //   192: 192 x 192 tiles, 2 x 2 wavefronts of 96 x 96 (144 accumulator registers), BK 16,
 //        one global register set: one workgroup per CU.  Its tile counts fill whole waves
 //        where the others do not (3072^3: 256 tiles).
@@ -619,7 +620,15 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
   switch (tiles) {
     case 256:
       // remainders thinner than kThin256 past the full tiles: thin strips after the tiles
-      // (4100^3: see tile_plan.h); wider ones: scalar edge tiles
+      // (4100^3: see tile_plan.h); wider ones: scalar edge tiles.  Rows that LDS-DMA loads
+      // can read (direct_ok): the direct K loop on 4 x 2 wavefronts of 64 x 128, two per
+      // SIMD (4096^3: 909 against 918 us on 2 x 2 wavefronts of 128 x 128, one per SIMD);
+      // otherwise the register-staged loop on 2 x 2 wavefronts.
+      if (direct_ok(p, batch)) {
+        if ((p.M % 256 != 0 || p.N % 256 != 0) && thin256(p.M, p.N))
+          return launch_cfg<256, 256, 16, 4, 2, 1, TA, TB, 8, 1, kThin256, true, true>(p, batch, stream);
+        return launch_cfg<256, 256, 16, 4, 2, 1, TA, TB, 8, 1, mfma_edge_min(256), true, true>(p, batch, stream, ws);
+      }
       if ((p.M % 256 != 0 || p.N % 256 != 0) && thin256(p.M, p.N))
         return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, kThin256, true>(p, batch, stream);
       return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(256), true>(p, batch, stream, ws);
