@@ -125,10 +125,13 @@ struct DirectOperand {
   }
 };
 
-// Whether the direct pipeline can load this problem: 16-byte aligned rows (vec_loads_ok)
-// and every byte offset from a K-tile's origin below 2^31 (the buffer offsets are 32-bit).
+// Whether the direct pipeline can load this problem: 16-byte aligned rows (vec_loads_ok),
+// whole K-tiles (K a multiple of 16: a partial one would need zeros past K, which the
+// LDS-DMA loads cannot write; loaded through registers beside them, it made the kernel
+// spill) and every byte offset from a K-tile's origin below 2^31 (the buffer offsets are
+// 32-bit).
 inline bool direct_ok(const Problem& p, int batch) {
-  if (!vec_loads_ok(p, batch)) return false;
+  if (!vec_loads_ok(p, batch) || p.K % 16 != 0) return false;
   constexpr long long kLimit = 1LL << 31;
   const long long a = p.ta ? 15 * p.lda + 256 : 255 * p.lda + 16;  // floats past the origin
   const long long b = p.tb ? 255 * p.ldb + 16 : 15 * p.ldb + 256;
@@ -145,8 +148,7 @@ inline bool direct_ok(const Problem& p, int batch) {
 //   - the MFMAs of tile t run on their set;
 // and before the barrier that ends it, each wavefront waits for its loads of tile t + 2
 // (the last NST - 2 K-tiles' loads stay in flight), so that after the barrier tile t + 2
-// is in LDS for every wavefront.  A last, partial K-tile (K % 16 != 0) is loaded through
-// registers and LDS stores instead (Operand::load_tail, zeros past K).
+// is in LDS for every wavefront.  Every K-tile is whole (direct_ok).
 template <int WM, int WN, bool TA, bool TB, int GUARD>
 __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                                  float* part) {
@@ -174,7 +176,6 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
   da.init(p.A, p.lda, m0, w, l);
   db.init(p.B, p.ldb, n0, w, l);
   const unsigned lds0 = lds_address(smem);
-  const int nfull = p.K / BK;
   auto load_one = [&](int q, int kt, int s) {  // load q (A's, then B's) of full K-tile kt
     const unsigned stage = lds0 + (unsigned)(s * Cfg::kStageFloats) * 4u;
     if (q < DA::L)
@@ -182,22 +183,10 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
     else
       db.load(q - DA::L, kt, stage + OpA::kStageFloats * 4u);
   };
-  // K-tile kt into stage s: LDS-DMA loads, or for the partial last K-tile registers and
-  // LDS stores (its loads are the compiler's: it waits for them before the stores)
+  // K-tile kt into stage s
   auto fill = [&](int kt, int s) {
-    if (kt < nfull) {
 #pragma unroll
-      for (int q = 0; q < kLoads; ++q) load_one(q, kt, s);
-    } else {
-      OpA opa;
-      OpB opb;
-      opa.init(p.A, p.lda, m0, BM, t);
-      opb.init(p.B, p.ldb, n0, BN, t);
-      opa.template load_tail<true, false, 0>(kt * BK, p.K - kt * BK);
-      opb.template load_tail<true, false, 0>(kt * BK, p.K - kt * BK);
-      opa.template store<0>(a_stage(s));
-      opb.template store<0>(b_stage(s));
-    }
+    for (int q = 0; q < kLoads; ++q) load_one(q, kt, s);
   };
 
   v16f acc[FM][FN];
@@ -235,7 +224,7 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
   else
     direct_barrier<0>();
 
-  // steady K-tile (tile kt + NST exists and is full): explicit order, since the compiler
+  // steady K-tile (tile kt + NST exists): explicit order, since the compiler
   // cannot place inline assembly among the MFMAs by itself
   constexpr int kLast = (kLoads - 1) * SP;  // the MFMA after which the last load goes
   constexpr int kMfmas = 8 * FM * FN;
@@ -266,8 +255,7 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
     direct_barrier<0>();
   };
   int kt = kb;
-  const int steady_end = min(ke, nfull);
-  for (; kt + 1 + NST < steady_end; kt += 2) {  // tiles kt + NST and kt + NST + 1 are full and in range
+  for (; kt + 1 + NST < ke; kt += 2) {  // tiles kt + NST and kt + NST + 1 are in range
     steady(Set0{}, kt);
     steady(Set1{}, kt + 1);
   }

@@ -1,13 +1,14 @@
 """The 256 configuration's two K loops: LDS-DMA loads and register-staged loads.
 
-Where every row of A and B is 16-byte aligned and the byte offsets inside a K-tile fit in
-31 bits, the 256 x 256 tiles load their operands straight into LDS (buffer_load ... lds);
-a leading dimension past about 2.1 million floats (along k) takes the register-staged
-pipeline instead.  Both must give the oracle's result bit for bit on integer inputs (every
-partial sum is exact), and, since both read the same LDS layout in the same order, the same
-bits as each other on random inputs too.  Shapes cover a K tail (the last K-tile loaded
-through registers in the direct pipeline), fewer K-tiles than LDS stages, and B stored
-transposed.  The operand padding is NaN, so a read past a row reaches C.
+Where every row of A and B is 16-byte aligned, K is a multiple of 16 and the byte offsets
+inside a K-tile fit in 31 bits, the 256 x 256 tiles load their operands straight into LDS
+(buffer_load ... lds, on 4 x 2 wavefronts); a leading dimension past about 2.1 million
+floats (along k), or a K tail, takes the register-staged pipeline (2 x 2 wavefronts)
+instead.  Both must give the oracle's result bit for bit on integer inputs (every partial
+sum is exact), and, since both read the same LDS layout and add each output's products in
+the same order, the same bits as each other on random inputs too.  Shapes cover fewer
+K-tiles than LDS stages, B stored transposed, and a K tail (both runs then staged).  The
+operand padding is NaN, so a read past a row reaches C.
 """
 import numpy as np
 import pytest
@@ -72,7 +73,7 @@ def _run(M, N, K, a, lda, b, ldb, tb, c, alpha, beta):
 
 
 @pytest.mark.parametrize("tb", [0, 1])
-@pytest.mark.parametrize("M,N,K", [(256, 512, 16 * 9 + 5), (512, 256, 48), (256, 256, 16 * 40)])
+@pytest.mark.parametrize("M,N,K", [(256, 512, 16 * 9), (512, 256, 48), (256, 256, 16 * 40), (256, 512, 16 * 9 + 5)])
 def test_direct_and_staged_integer_exact(oracle, M, N, K, tb):
     print(f"[direct] {M}x{N}x{K} tb={tb} huge ld {HUGE_LD}", flush=True)
     a = integer_matrix(M, K, -4, 4, seed=M + K)
@@ -90,7 +91,7 @@ def test_direct_and_staged_integer_exact(oracle, M, N, K, tb):
         assert bad.size == 0, f"{name}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 16 * 33 + 7)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 16 * 33), (512, 256, 16 * 20)])
 def test_direct_and_staged_same_bits(M, N, K):
     """Random inputs: the two pipelines add the same products in the same order."""
     rng = np.random.default_rng(11)

@@ -40,9 +40,9 @@ CASES = [
     (8, 0, 0, 3 * 32 + 2, 2 * 32 + 3, 70, 1, False), (8, 1, 0, 2 * 32 + 6, 3 * 32 + 6, 300, 1, False),
     (10, 0, 0, 17, 33, 70, 1, False), (10, 0, 1, 5 * 16 + 3, 3 * 16 + 9, 1100, 1, False),
     (0, 0, 0, 70, 50, 33, 7, False),  # strided batch, default path
-    # 256 tiles through LDS-DMA loads (16-byte rows): K tail, fewer K-tiles than stages and transposed,
-    # thin strips beside them, a strided batch
-    (5, 0, 0, 512, 768, 148, 1, False), (5, 1, 1, 512, 512, 48, 1, False), (5, 0, 1, 256 + 8, 512, 164, 1, False),
+    # 256 tiles through LDS-DMA loads (16-byte rows, K a multiple of 16): fewer K-tiles than
+    # stages and transposed, thin strips beside them, a strided batch
+    (5, 0, 0, 512, 768, 144, 1, False), (5, 1, 1, 512, 512, 48, 1, False), (5, 0, 1, 256 + 8, 512, 160, 1, False),
     (5, 0, 0, 256, 256, 64, 3, False),
     (5, 0, 0, 1024, 1280, 77, 1, True),  # stream-K (256 forced, with a workspace): every tile split
     (5, 0, 0, 17 * 256, 17 * 256, 40, 1, True),  # stream-K: whole tiles and pieces
