@@ -63,6 +63,19 @@ inline bool vec_loads_ok(const Problem& p, int batch) {
   return vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb) && (batch <= 1 || (p.sA % 4 == 0 && p.sB % 4 == 0));
 }
 
+// Whether the 256 configuration's direct K loop (mfma_direct.h, LDS-DMA loads) can load
+// this problem: 16-byte aligned rows (vec_loads_ok), whole K-tiles (K a multiple of 16: a
+// partial one would need zeros past K, which the LDS-DMA loads cannot write; loaded
+// through registers beside them, it made the kernel spill) and every byte offset from a
+// K-tile's origin below 2^31 (the buffer offsets are 32-bit).
+inline bool direct_ok(const Problem& p, int batch) {
+  if (!vec_loads_ok(p, batch) || p.K % 16 != 0) return false;
+  constexpr long long kLimit = 1LL << 31;
+  const long long a = p.ta ? 15 * p.lda + 256 : 255 * p.lda + 16;  // floats past the origin
+  const long long b = p.tb ? 255 * p.ldb + 16 : 15 * p.ldb + 256;
+  return a * 4 < kLimit && b * 4 < kLimit;
+}
+
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the launch status.
 // Every launcher accepts any M, N >= 1 and K >= 1 and any leading dimensions, and runs
 // `batch` (1 .. kMaxBatch) problems spaced by p.sA, p.sB, p.sC as grid dimension y.
@@ -99,13 +112,15 @@ constexpr long long kStreamKBytes = 2LL * kStreamKWgs * 256 * 256 * 4;
 // mfma_edge_min(side) wide runs as guarded MFMA tiles of the same grid; a thinner one runs
 // as thin strips (192, 128 and 64 configurations: 16, below which a strip would pay for a
 // whole tile row or column of MFMA work; 32 configuration: 4) or, in the 256 configuration
-// (0: never MFMA), as scalar edge tiles (its workgroups fill a CU's register file and a
-// guarded tile there costs a whole 256 x 256 tile; the cost model steers ragged shapes to
-// the smaller configurations); in the 16 configuration every block is guarded (1).
+// on the register-staged loop (0: never MFMA), as scalar edge tiles (its workgroups fill a
+// CU's register file; the cost model steers ragged shapes to the smaller configurations);
+// in the 16 configuration every block is guarded (1).  The 256 configuration's direct K
+// loop (direct_ok) runs guarded tiles down to kThin256 and thin strips below it.
 constexpr int mfma_edge_min(int side) { return side == 256 ? 0 : side == 32 ? 4 : side == 16 ? 1 : 16; }
-// The 256 configuration's thin-strip form: where both remainders past its full tiles are
-// thinner than kThin256, they run as thin strips (same launch, after the tiles) instead of
-// scalar edge tiles; a 256 x 256 tile is never guarded.
+// The 256 configuration's thin-strip form on the register-staged loop: where both
+// remainders past its full tiles are thinner than kThin256, they run as thin strips (same
+// launch, after the tiles) instead of scalar edge tiles.  On the direct loop it is also
+// the narrowest guarded tile.
 constexpr int kThin256 = 16;
 constexpr bool thin256(int M, int N) { return M % 256 < kThin256 && N % 256 < kThin256; }
 // The extent [0, result) of rows (columns) that MFMA tiles of this side cover, out of n.

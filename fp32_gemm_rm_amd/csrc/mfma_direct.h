@@ -90,6 +90,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 //     (swz_slot: rows 16 apart share the XOR, (row/4) % 4 = l/16);
 //   otherwise (A^T, or B): load j fills k-row j, 256 floats, lane l taking floats 4l .. 4l+3
 //     (the row's 4 padding words stay unwritten and unread).
+// GUARD (a tile reaching past M or N): lines at or past lim, the slice's lines inside the
+// matrix, load the last row (KROWS) or the last float4 inside (otherwise; lim is then a
+// multiple of 4), as Operand::load_full does: their values reach only outputs that are not
+// stored.
 template <bool KROWS, int W>
 struct DirectOperand {
   static constexpr int R = 256, BK = 16, L = 16 / W;
@@ -100,21 +104,25 @@ struct DirectOperand {
   unsigned voff[L];   // byte offsets of this lane's 16 bytes from the K-tile's origin
   unsigned lds[L];    // stage-relative LDS byte offsets of the wavefront's loads
 
-  __device__ __forceinline__ void init(const float* X, long long ld, int r0, int w, int l) {
+  template <bool GUARD>
+  __device__ __forceinline__ void init(const float* X, long long ld, int r0, int rows_left, int w, int l) {
     // uniform: the K-tile origins base + kt * kstep are then computed by scalar instructions
     // (as vector ones, followed by readfirstlane, the loop ran 2% slower)
     base = reinterpret_cast<const float*>(
         uniform64(reinterpret_cast<long long>(KROWS ? X + (long long)r0 * ld : X + r0)));
     kstep = uniform64(KROWS ? BK : BK * ld);
+    const int lim = rows_left < R ? rows_left : R;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int j = L * w + i;
       if (KROWS) {
         const int row = 16 * j + l / 4, chunk = (l % 4) ^ (l / 16);
-        voff[i] = (unsigned)((long long)row * ld + 4 * chunk) * 4u;
+        const int r = (!GUARD || row < lim) ? row : lim - 1;
+        voff[i] = (unsigned)((long long)r * ld + 4 * chunk) * 4u;
         lds[i] = (unsigned)(16 * j * BK) * 4u;
       } else {
-        voff[i] = (unsigned)((long long)j * ld + 4 * l) * 4u;
+        const int c = GUARD ? min(4 * l, lim - 4) : 4 * l;
+        voff[i] = (unsigned)((long long)j * ld + c) * 4u;
         lds[i] = (unsigned)(j * Op::STRIDE) * 4u;
       }
     }
@@ -124,19 +132,6 @@ struct DirectOperand {
     lds_dma16(buffer_rsrc(base + (long long)__builtin_amdgcn_readfirstlane(kt) * kstep), stage + lds[i], voff[i]);
   }
 };
-
-// Whether the direct pipeline can load this problem: 16-byte aligned rows (vec_loads_ok),
-// whole K-tiles (K a multiple of 16: a partial one would need zeros past K, which the
-// LDS-DMA loads cannot write; loaded through registers beside them, it made the kernel
-// spill) and every byte offset from a K-tile's origin below 2^31 (the buffer offsets are
-// 32-bit).
-inline bool direct_ok(const Problem& p, int batch) {
-  if (!vec_loads_ok(p, batch) || p.K % 16 != 0) return false;
-  constexpr long long kLimit = 1LL << 31;
-  const long long a = p.ta ? 15 * p.lda + 256 : 255 * p.lda + 16;  // floats past the origin
-  const long long b = p.tb ? 255 * p.ldb + 16 : 15 * p.ldb + 256;
-  return a * 4 < kLimit && b * 4 < kLimit;
-}
 
 // K-tiles [kb, ke) of the 256 x 256 tile at (m0, n0), as mfma_tile_pf with WM x WN
 // wavefronts (4 x 2 in the library: two per SIMD, each 64 x 128), KS = 1, BK = 16, with
@@ -148,7 +143,8 @@ inline bool direct_ok(const Problem& p, int batch) {
 //   - the MFMAs of tile t run on their set;
 // and before the barrier that ends it, each wavefront waits for its loads of tile t + 2
 // (the last NST - 2 K-tiles' loads stay in flight), so that after the barrier tile t + 2
-// is in LDS for every wavefront.  Every K-tile is whole (direct_ok).
+// is in LDS for every wavefront.  Every K-tile is whole (direct_ok).  GUARD: as mfma_tile_pf's
+// (bit 0 A rows past M, bit 1 B columns past N, bit 2 a launch of full tiles only).
 template <int WM, int WN, bool TA, bool TB, int GUARD>
 __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                                  float* part) {
@@ -173,8 +169,8 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
 
   DA da;
   DB db;
-  da.init(p.A, p.lda, m0, w, l);
-  db.init(p.B, p.ldb, n0, w, l);
+  da.template init<(GUARD & 1) != 0>(p.A, p.lda, m0, p.M - m0, w, l);
+  db.template init<(GUARD & 2) != 0>(p.B, p.ldb, n0, p.N - n0, w, l);
   const unsigned lds0 = lds_address(smem);
   auto load_one = [&](int q, int kt, int s) {  // load q (A's, then B's) of full K-tile kt
     const unsigned stage = lds0 + (unsigned)(s * Cfg::kStageFloats) * 4u;

@@ -161,9 +161,10 @@ void mfma_kernel(Problem p, TileMap map) {
   p = batch_entry(p);
   constexpr int kGroups = Cfg::kThreads / 256;
   constexpr bool kEdges = EDGE_MIN == 0, kThin = EDGE_MIN > 1;  // scalar edge tiles / thin strips may exist
-  // guarded MFMA tiles may exist (the 256 configuration's thin-strip form has none: its
-  // launches have remainders thinner than kThin256 only)
-  constexpr bool kGuarded = EDGE_MIN != 0 && BM != 256;
+  // guarded MFMA tiles may exist (the register-staged 256 configuration's thin-strip form has
+  // none: its launches have remainders thinner than kThin256 only; the direct one's guarded
+  // form has both)
+  constexpr bool kGuarded = EDGE_MIN != 0 && (BM != 256 || DIRECT);
   static_assert(BM != 256 || EDGE_MIN == 0 || EDGE_MIN == kThin256, "256 tiles: scalar edges or thin strips");
   static_assert(kThin256 == kThinMax, "the 256 thin-strip form's remainders fit one thin strip");
   static_assert(EDGE_MIN <= kThinMax, "thin strips are at most kThinMax wide");
@@ -611,7 +612,8 @@ hipError_t launch_block16(const Problem& p, int batch, hipStream_t stream) {
 //        (block16_kernel).
 // Partial tiles (mfma_edge_min): guarded MFMA tiles of the same grid in the 192, 128, 64
 // and 32 configurations, except strips thinner than 16 in the 192, 128 and 64
-// configurations (thin strips); the scalar edge-tile path in the 256 configuration.
+// configurations (thin strips); in the 256 configuration the same on the direct K loop,
+// else thin strips (both remainders under 16) or the scalar edge-tile path.
 // ws: stream-K workspace (kStreamKBytes) for the 256 configuration, or for the 64 one's
 // K slices (slices > 1), or nullptr.
 template <bool TA, bool TB>
@@ -619,15 +621,19 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
                      int slices = 1) {
   switch (tiles) {
     case 256:
-      // remainders thinner than kThin256 past the full tiles: thin strips after the tiles
-      // (4100^3: see tile_plan.h); wider ones: scalar edge tiles.  Rows that LDS-DMA loads
-      // can read (direct_ok): the direct K loop on 4 x 2 wavefronts of 64 x 128, two per
+      // Rows that LDS-DMA loads can read (direct_ok): the direct K loop on 4 x 2 wavefronts of 64 x 128, two per
       // SIMD (4096^3: 909 against 918 us on 2 x 2 wavefronts of 128 x 128, one per SIMD);
       // otherwise the register-staged loop on 2 x 2 wavefronts.
+      // The direct loop also runs the partial tiles: remainders of at least kThin256 as guarded
+      // tiles of the same grid, thinner ones as thin strips (4000^3: 892 against 947 us on
+      // 128 x 128 tiles; 8000^3: 7089 against 7352 us on 192 x 192 tiles); full tiles only:
+      // stream-K where a workspace is given.  The register-staged loop: remainders both
+      // thinner than kThin256 as thin strips after the tiles (4100^3: see tile_plan.h),
+      // wider ones as scalar edge tiles.
       if (direct_ok(p, batch)) {
-        if ((p.M % 256 != 0 || p.N % 256 != 0) && thin256(p.M, p.N))
+        if (p.M % 256 != 0 || p.N % 256 != 0)
           return launch_cfg<256, 256, 16, 4, 2, 1, TA, TB, 8, 1, kThin256, true, true>(p, batch, stream);
-        return launch_cfg<256, 256, 16, 4, 2, 1, TA, TB, 8, 1, mfma_edge_min(256), true, true>(p, batch, stream, ws);
+        return launch_cfg<256, 256, 16, 4, 2, 1, TA, TB, 8, 1, 0, true, true>(p, batch, stream, ws);
       }
       if ((p.M % 256 != 0 || p.N % 256 != 0) && thin256(p.M, p.N))
         return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, kThin256, true>(p, batch, stream);

@@ -164,7 +164,8 @@ int launch_batches(Problem p, int batch, hipStream_t stream, int variant, float*
         case SGEMM_RM_VARIANT_MFMA:
         case SGEMM_RM_VARIANT_AUTO:
         default: {
-          const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(p.M, p.N, p.K, chunk, ws != nullptr);
+          const sgemm_impl::TilePlan plan =
+              sgemm_impl::plan_tiles(p.M, p.N, p.K, chunk, ws != nullptr, sgemm_impl::direct_ok(p, chunk));
           err = sgemm_impl::launch_mfma(p, chunk, stream, plan.side, plan.stream_k || plan.slices > 1 ? ws : nullptr,
                                         plan.slices);
           break;
@@ -212,7 +213,7 @@ long long workspace_need(const Problem& p, int batch, int variant) {
     return sgemm_impl::k_slices(p.M, p.N, p.K, 1) > 1 ? sgemm_impl::kStreamKBytes : 0;
   if (variant != SGEMM_RM_VARIANT_AUTO && variant != SGEMM_RM_VARIANT_MFMA) return 0;
   if (sgemm_impl::needs_bands(p.M, p.N)) return sgemm_impl::kStreamKBytes;
-  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(p.M, p.N, p.K, 1, true);
+  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(p.M, p.N, p.K, 1, true, sgemm_impl::direct_ok(p, 1));
   return plan.stream_k || plan.slices > 1 ? sgemm_impl::kStreamKBytes : 0;
 }
 
@@ -344,7 +345,8 @@ long long sgemm_rm_workspace_size(int M, int N, int K, int batch) {
   if (K < 0) return -3;
   if (batch < 0) return -4;
   if (M == 0 || N == 0 || K == 0 || batch == 0) return 0;
-  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(M, N, K, batch, true);
+  // operands as torch allocates them: 16-byte aligned rows
+  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(M, N, K, batch, true, K % 16 == 0);
   return plan.stream_k || plan.slices > 1 ? sgemm_impl::kStreamKBytes : 0;
 }
 
@@ -354,7 +356,10 @@ int sgemm_rm_plan_tiles(int M, int N, int K, int batch) {
   if (K < 0) return -3;
   if (batch < 0) return -4;
   if (M == 0 || N == 0 || K == 0 || batch == 0) return 0;
-  return sgemm_impl::plan_tiles(M, N, K, batch < sgemm_impl::kMaxBatch ? batch : sgemm_impl::kMaxBatch).side;
+  // operands as torch allocates them: 16-byte aligned rows
+  return sgemm_impl::plan_tiles(M, N, K, batch < sgemm_impl::kMaxBatch ? batch : sgemm_impl::kMaxBatch, false,
+                                K % 16 == 0)
+      .side;
 }
 
 const char* sgemm_rm_strerror(int code) {

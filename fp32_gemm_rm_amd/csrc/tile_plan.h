@@ -48,8 +48,8 @@ constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 4.0},
 
 // MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
 // counts as a tile row (column); a thin strip, which runs beside the MFMA tiles, does not.
-inline long long modelled_tiles(int n, int side) {
-  return (mfma_extent(n, side, mfma_edge_min(side)) + side - 1) / side;
+inline long long modelled_tiles(int n, int side, int edge_min) {
+  return (mfma_extent(n, side, edge_min) + side - 1) / side;
 }
 
 // Thin-strip workgroups (16 lines each) of one product, for B stored along n (the last
@@ -61,24 +61,31 @@ inline long long modelled_thin_wgs(int M, int N, int side) {
   return (Nf < N ? (Mf + 15) / 16 : 0) + (Mf < M ? (N + 15) / 16 : 0);
 }
 
-// Modelled microseconds; M, N, K, batch > 0.  The 256 configuration is a candidate only
-// where its tiles cover the matrix, or leave remainders thinner than kThin256 over one
-// layer of tiles (thin strips after the tiles: 4096 x 4100 x 4096 940 us against 969 on
-// 128 x 128 tiles; 4100^3 980 against 993, which the model still gives to 128).  Wider
-// strips would run as scalar edge tiles, which cannot share a CU with its workgroups and
-// are latency-bound chains of K-steps (4000^3: 1434 us, against 949 us on 128 x 128 tiles;
-// 4090^3: 1887 against 1021 us).
-inline double modelled_time(const TileCost& c, int M, int N, int K, int batch) {
-  if (c.side == 256 && !thin256(M, N)) return 1e30;
-  const long long tiles = modelled_tiles(M, c.side) * modelled_tiles(N, c.side) * batch;
+// Modelled microseconds; M, N, K, batch > 0.  direct: the operands suit the 256
+// configuration's direct K loop (direct_ok), which runs guarded tiles too (4000^3: 892 us
+// against 947 on 128 x 128 tiles; 3900 x 3900 x 3904: 871 against 933; 8000^3: 7089
+// against 7352 on 192 x 192 tiles, while the model keeps 192 for 3000 x 3000 x 3008, 394
+// us against 670 on guarded 256 tiles, whose one layer of 144 tiles leaves CUs idle).
+// Without it the 256 configuration is a candidate only where its tiles cover the matrix,
+// or leave remainders thinner than kThin256 over one layer of tiles (thin strips after
+// the tiles: 4096 x 4100 x 4096 940 us against 969 on 128 x 128 tiles; 4100^3 980 against
+// 993, which the model still gives to 128).  Wider strips would run as scalar edge tiles, which
+// cannot share a CU with its workgroups and are latency-bound chains of K-steps (4000^3:
+// 1434 us, against 949 us on 128 x 128 tiles; 4090^3: 1887 against 1021 us).  A guarded
+// 256 x 256 tile costs a whole tile, as in the other configurations.
+inline double modelled_time(const TileCost& c, int M, int N, int K, int batch, bool direct = false) {
+  if (c.side == 256 && !direct && !thin256(M, N)) return 1e30;
+  const int em = c.side == 256 ? (direct ? kThin256 : 0) : mfma_edge_min(c.side);
+  const long long tiles = modelled_tiles(M, c.side, em) * modelled_tiles(N, c.side, em) * batch;
   const long long layers = (tiles + 255) / 256;
   if (c.side == 16)
     return (layers == 1 ? kBlock16Base + kBlock16PerBlock * (double)tiles : kBlock16Layer * (double)layers) *
            (double)K / 1024.0;
-  // the 256 thin-strip form only over one layer of tiles: past it the strips' workgroups,
-  // each on a whole CU, add up (8200^3: 7809 against 7773 us on 128 x 128 tiles)
-  if (c.side == 256 && (M % 256 != 0 || N % 256 != 0) && layers > 1) return 1e30;
-  const long long thin_rounds = (modelled_thin_wgs(M, N, c.side) * batch + 255) / 256;
+  // thin strips in the 256 configuration only over one layer of tiles: past it the strips'
+  // workgroups, each on a whole CU, add up (8200^3: 7809 against 7773 us on 128 x 128 tiles)
+  const long long thin_wgs = modelled_thin_wgs(M, N, c.side);
+  if (c.side == 256 && thin_wgs > 0 && layers > 1) return 1e30;
+  const long long thin_rounds = (thin_wgs * batch + 255) / 256;
   return ((double)layers * (layers > 1 ? c.u2 : c.u1) + (double)thin_rounds * c.thin) * (double)K / 1024.0;
 }
 
@@ -148,12 +155,12 @@ struct TilePlan {
 };
 
 // The configuration with the least modelled time (ties: the larger tile); stream-K and K
-// slices are candidates when a workspace is available.
-inline TilePlan plan_tiles(int M, int N, int K, int batch, bool workspace = false) {
+// slices are candidates when a workspace is available; direct as modelled_time's.
+inline TilePlan plan_tiles(int M, int N, int K, int batch, bool workspace = false, bool direct = false) {
   TilePlan best{kTileCosts[0].side, false};
-  double t = modelled_time(kTileCosts[0], M, N, K, batch);
+  double t = modelled_time(kTileCosts[0], M, N, K, batch, direct);
   for (const TileCost& c : kTileCosts) {
-    const double tc = modelled_time(c, M, N, K, batch);
+    const double tc = modelled_time(c, M, N, K, batch, direct);
     if (tc < t) best = TilePlan{c.side, false}, t = tc;
   }
   if (workspace) {

@@ -263,17 +263,20 @@ int sgemm_rm_op_strided_batched_noalloc(int transA, int transB, int M, int N, in
 
 /*
  * Workspace bytes with which the _ws calls run an M x N x K problem (repeated `batch`
- * times) as stream-K, or 0 where the cost model keeps the one-tile-per-workgroup path.
- * Currently 0 or 128 MiB (two 256 x 256 float partial tiles for each of 256
- * workgroups).  -1 M < 0, -2 N < 0, -3 K < 0, -4 batch < 0.  Host only: no HIP call.
- * The transpose flags and storage order do not change the answer.
+ * times) as stream-K or with K slices, or 0 where the cost model keeps the
+ * one-tile-per-workgroup path, for operands whose rows are 16-byte aligned (as
+ * sgemm_rm_plan_tiles).  Currently 0 or 128 MiB (two 256 x 256 float partial tiles for
+ * each of 256 workgroups).  -1 M < 0, -2 N < 0, -3 K < 0, -4 batch < 0.  Host only: no
+ * HIP call.  The transpose flags and storage order do not change the answer.
  */
 long long sgemm_rm_workspace_size(int M, int N, int K, int batch);
 
 /*
  * Tile side (256, 192, 128, 64, 32 or 16) of the MFMA configuration that SGEMM_RM_VARIANT_AUTO
  * and SGEMM_RM_VARIANT_MFMA use for an M x N x K problem repeated `batch` times (any
- * orientation or storage order; batches above 65535 are planned per launch of 65535).
+ * orientation or storage order; batches above 65535 are planned per launch of 65535), for
+ * operands whose rows are 16-byte aligned (pointers and leading dimensions; the 256
+ * configuration's partial tiles need such rows, and without them the choice may differ).
  * 0 when nothing would be launched for the product (M, N, K or batch 0).  -1 M < 0,
  * -2 N < 0, -3 K < 0, -4 batch < 0.  Host only: no HIP call.
  */

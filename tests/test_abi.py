@@ -264,13 +264,20 @@ def test_plan_tiles(lib):
     assert sgemm_rm_plan_tiles(256, 256, 256) == 16  # 256 blocks of 16^2
     assert sgemm_rm_plan_tiles(512, 512, 512) == 32  # 1024 blocks of 16^2 would take four layers
     assert sgemm_rm_plan_tiles(3072, 3072, 3072) == 192  # 256 tiles of 192^2: one whole wave
-    # 256 x 256 tiles only where they cover the matrix, or leave strips thinner than 16 over one
-    # layer of tiles (thin strips after the tiles); wider strips would run as scalar edge tiles
-    for n in (4000, 4090, 3900, 8000):
+    # K not a multiple of 16 (no LDS-DMA K loop): 256 x 256 tiles only where they cover the
+    # matrix, or leave strips thinner than 16 over one layer of tiles (thin strips after the
+    # tiles); wider strips would run as scalar edge tiles
+    for n in (4090, 3900):
         assert sgemm_rm_plan_tiles(n, n, n) != 256, n
-    assert sgemm_rm_plan_tiles(4096, 4000, 4096) != 256
-    assert sgemm_rm_plan_tiles(4096, 4100, 4096) == 256  # 256 tiles and a 4-column thin strip
+    assert sgemm_rm_plan_tiles(4096, 4100, 4100) == 256  # 256 tiles and a 4-column thin strip
     assert sgemm_rm_plan_tiles(8200, 8200, 8200) != 256  # thin strips past four layers of tiles
+    # K a multiple of 16 (the query assumes 16-byte aligned rows): the direct K loop runs
+    # guarded 256 x 256 tiles (4000^3: 892 against 947 us on 128 x 128 tiles), where their
+    # layers cost less than the other configurations'
+    for M, N, K in ((4000, 4000, 4000), (8000, 8000, 8000), (4096, 4000, 4096), (4096, 4100, 4096)):
+        assert sgemm_rm_plan_tiles(M, N, K) == 256, (M, N, K)
+    assert sgemm_rm_plan_tiles(3000, 3000, 3008) == 192  # 144 tiles of 256^2 against 256 of 192^2
+    assert sgemm_rm_plan_tiles(5000, 5000, 5008) != 256  # 400 tiles: two layers
     assert sgemm_rm_plan_tiles(1000, 1030, 999) == 64  # 6-column thin strip beside 64 x 64 tiles
     assert sgemm_rm_plan_tiles(64, 64, 64, 1024) == 64
     for M, N, K, b in [(1, 1, 1, 1), (5000, 3, 7, 1), (3, 5000, 70000, 1), (65535, 65535, 1, 1000000)]:

@@ -8,7 +8,8 @@ instead.  Both must give the oracle's result bit for bit on integer inputs (ever
 sum is exact), and, since both read the same LDS layout and add each output's products in
 the same order, the same bits as each other on random inputs too.  Shapes cover fewer
 K-tiles than LDS stages, B stored transposed, and a K tail (both runs then staged).  The
-operand padding is NaN, so a read past a row reaches C.
+operand padding is NaN, so a read past a row reaches C.  The direct loop also runs the tiles
+that reach past M or N (guarded tiles, with thin strips for remainders under 16).
 """
 import numpy as np
 import pytest
@@ -52,18 +53,18 @@ def _stored_on_device(x, ld):
     return buf
 
 
-def _run(M, N, K, a, lda, b, ldb, tb, c, alpha, beta):
-    """C := alpha op(A) op(B) + beta C on the 256 configuration; b is op(B) (K x N), stored
-    transposed (N x K) when tb."""
+def _run(M, N, K, a, lda, b, ldb, tb, c, alpha, beta, ta=0):
+    """C := alpha op(A) op(B) + beta C on the 256 configuration; a is op(A) (M x K), stored
+    transposed (K x M) when ta; b is op(B) (K x N), stored transposed (N x K) when tb."""
     import torch
 
     from fp32_gemm_rm_amd.binding import sgemm_rm_op_strided_batched_ex
 
-    dA = _stored_on_device(a, lda)
+    dA = _stored_on_device(np.ascontiguousarray(a.T) if ta else a, lda)
     dB = _stored_on_device(np.ascontiguousarray(b.T) if tb else b, ldb)
     dC = torch.from_numpy(np.ascontiguousarray(c)).to("cuda")
     s = torch.cuda.current_stream()
-    sgemm_rm_op_strided_batched_ex(0, tb, M, N, K, alpha, dA.data_ptr(), lda, 0, dB.data_ptr(), ldb, 0, beta,
+    sgemm_rm_op_strided_batched_ex(ta, tb, M, N, K, alpha, dA.data_ptr(), lda, 0, dB.data_ptr(), ldb, 0, beta,
                                    dC.data_ptr(), N, 0, 1, s.cuda_stream, T256)
     s.synchronize()
     out = dC.cpu().numpy()
@@ -101,3 +102,33 @@ def test_direct_and_staged_same_bits(M, N, K):
     direct = _run(M, N, K, a, _ld4(K), b, N, 0, c, 1.25, -0.75)
     staged = _run(M, N, K, a, HUGE_LD, b, N, 0, c, 1.25, -0.75)
     assert np.array_equal(direct.view(np.uint32), staged.view(np.uint32))
+
+
+# (M, N, K, ta, tb): remainders past the full 256 x 256 tiles of at least 16 run as guarded
+# direct tiles, thinner ones as thin strips (rows 7 past 512; the last 2 columns of N = 274,
+# which the guarded tiles along n leave to a strip since their limit is a multiple of 4)
+GUARDED = [(256 + 40, 512 + 24, 144, 0, 0), (512 + 7, 256 + 100, 160, 0, 0), (256 + 16, 256 + 18, 48, 0, 0),
+           (300, 520, 64, 1, 0), (300, 520, 64, 0, 1), (260 + 24, 256 + 36, 96, 1, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,ta,tb", GUARDED)
+def test_direct_guarded_tiles_integer_exact(oracle, M, N, K, ta, tb):
+    """Guarded direct tiles against the oracle, and against the register-staged path (rows of
+    A HUGE_LD apart: scalar edge tiles or thin strips there), bit for bit; C's padding columns
+    untouched is implied by comparing whole rows of width N."""
+    print(f"[direct] guarded {M}x{N}x{K} ta={ta} tb={tb}", flush=True)
+    a = integer_matrix(M, K, -4, 4, seed=M + 7 * K)
+    b = integer_matrix(K, N, -4, 4, seed=N + 7 * K)
+    c = integer_matrix(M, N, -4, 4, seed=M + 7 * N)
+    ref, _ = oracle.full(M, N, K, 1.5, a.reshape(-1), K, b.reshape(-1), N, -0.5, c.reshape(-1), N, with_absab=False)
+    lda = _ld4(M if ta else K) + 4
+    ldb = _ld4(K if tb else N) + 4
+    direct = _run(M, N, K, a, lda, b, ldb, tb, c, 1.5, -0.5, ta)
+    got = c_window(direct, M, N, N).astype(np.float64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"direct: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+    if not ta:  # the register-staged 256 path, with A's rows too far apart for LDS-DMA
+        staged = _run(M, N, K, a, HUGE_LD, b, ldb, tb, c, 1.5, -0.5, ta)
+        got = c_window(staged, M, N, N).astype(np.float64)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"staged: {len(bad)} mismatches, first at {bad[:3].tolist()}"
