@@ -153,3 +153,17 @@ def test_batched_tensor_binding():
     torch.cuda.synchronize()
     want = torch.bmm(A.double().cpu(), B.double().cpu()).float()
     assert torch.equal(C.cpu(), want)
+
+
+@pytest.mark.parametrize("M,N,K", [(256 + 40, 512 + 24, 144), (300, 256 + 7, 64)])
+def test_batched_direct_guarded_tiles(oracle, M, N, K):
+    """The 256 x 256 configuration forced on entries with 16-byte aligned rows and strides:
+    the LDS-DMA K loop with guarded tiles (remainders of 40 rows and 24 columns; 44 rows)
+    and a thin strip (7 columns), each entry reading its own operands between NaN gaps."""
+    lda, ldb, ldc = K + 4, (N + 7) // 4 * 4, N + 2
+    sA, sB, sC = M * lda + 8, K * ldb + 4, M * ldc + 11
+    batch = 3
+    A, B, C = make_batched_inputs(batch, M, N, K, lda, ldb, ldc, sA, sB, sC, "uniform", seed=M + K,
+                                  c_init="random")
+    out = _run_batched(M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, batch, 5)
+    _check_entries(oracle, out, M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, range(batch))
