@@ -63,16 +63,17 @@ inline bool vec_loads_ok(const Problem& p, int batch) {
   return vec4_ok(p.A, p.lda) && vec4_ok(p.B, p.ldb) && (batch <= 1 || (p.sA % 4 == 0 && p.sB % 4 == 0));
 }
 
-// Whether the 256 configuration's direct K loop (mfma_direct.h, LDS-DMA loads) can load
-// this problem: 16-byte aligned rows (vec_loads_ok), whole K-tiles (K a multiple of 16: a
-// partial one would need zeros past K, which the LDS-DMA loads cannot write; loaded
-// through registers beside them, it made the kernel spill) and every byte offset from a
-// K-tile's origin below 2^31 (the buffer offsets are 32-bit).
-inline bool direct_ok(const Problem& p, int batch) {
+// Whether the direct K loop (mfma_direct.h, LDS-DMA loads) of the configuration with
+// tiles of side R (256, 192 or 128; BK 16) can load this problem: 16-byte aligned rows
+// (vec_loads_ok), whole K-tiles (K a multiple of 16: a partial one would need zeros past
+// K, which the LDS-DMA loads cannot write; loaded through registers beside them, it made
+// the kernel spill) and every byte offset from a K-tile's origin below 2^31 (the buffer
+// offsets are 32-bit).
+inline bool direct_ok(const Problem& p, int batch, int R = 256) {
   if (!vec_loads_ok(p, batch) || p.K % 16 != 0) return false;
   constexpr long long kLimit = 1LL << 31;
-  const long long a = p.ta ? 15 * p.lda + 256 : 255 * p.lda + 16;  // floats past the origin
-  const long long b = p.tb ? 255 * p.ldb + 16 : 15 * p.ldb + 256;
+  const long long a = p.ta ? 15LL * p.lda + R : (R - 1LL) * p.lda + 16;  // floats past the origin
+  const long long b = p.tb ? (R - 1LL) * p.ldb + 16 : 15LL * p.ldb + R;
   return a * 4 < kLimit && b * 4 < kLimit;
 }
 

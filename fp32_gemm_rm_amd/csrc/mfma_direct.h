@@ -1,6 +1,7 @@
-// MFMA SGEMM, the direct-to-LDS K loop of the 256 configuration: the operands of each
-// K-tile go from global memory straight into an LDS stage (buffer_load_dwordx4 ... lds,
-// gfx950's 128-bit LDS-DMA load), with no register staging and no LDS store instructions.
+// MFMA SGEMM, the direct-to-LDS K loop (the 256 configuration, and the 128 one's
+// two-workgroup form): the operands of each K-tile go from global memory straight into an
+// LDS stage (buffer_load_dwordx4 ... lds, gfx950's 128-bit LDS-DMA load), with no register
+// staging and no LDS store instructions.
 #pragma once
 
 #include <type_traits>
@@ -81,28 +82,30 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// One operand of the 256 configuration loaded by LDS-DMA by W wavefronts: its stage layout
-// is Operand's (R = 256, BK = 16), so the fragment reads are unchanged.  16 loads per
-// K-tile, each writing 1 KiB of the stage; wavefront w issues L = 16 / W of them, load i
-// being load j = L w + i:
-//   KROWS (A, or B^T): load j fills rows 16j .. 16j + 15, four 16-byte chunks each; lane l
-//     takes row 16j + l/4 at chunk position l%4, which holds chunk (l%4) ^ (l/16)
-//     (swz_slot: rows 16 apart share the XOR, (row/4) % 4 = l/16);
-//   otherwise (A^T, or B): load j fills k-row j, 256 floats, lane l taking floats 4l .. 4l+3
-//     (the row's 4 padding words stay unwritten and unread).
+// One R x 16 operand slice (R a multiple of 64 up to 256) loaded by LDS-DMA by W
+// wavefronts: its stage layout is Operand's (BK = 16), so the fragment reads are unchanged.
+// NI loads per K-tile; wavefront w issues L = NI / W of them, load i being load j = L w + i:
+//   KROWS (A, or B^T): NI = R / 16; load j fills rows 16j .. 16j + 15 (1 KiB), four
+//     16-byte chunks each; lane l takes row 16j + l/4 at chunk position l%4, which holds
+//     chunk (l%4) ^ (l/16) (swz_slot: rows 16 apart share the XOR, (row/4) % 4 = l/16);
+//   otherwise (A^T, or B): NI = 16; load j fills k-row j, R floats, lane l < R/4 taking
+//     floats 4l .. 4l+3 (the other lanes are masked off; the row's 4 padding words stay
+//     unwritten and unread).
 // GUARD (a tile reaching past M or N): lines at or past lim, the slice's lines inside the
 // matrix, load the last row (KROWS) or the last float4 inside (otherwise; lim is then a
 // multiple of 4), as Operand::load_full does: their values reach only outputs that are not
 // stored.
-template <bool KROWS, int W>
+template <int R, bool KROWS, int W>
 struct DirectOperand {
-  static constexpr int R = 256, BK = 16, L = 16 / W;
-  static_assert(L * W == 16, "the 16 loads split evenly over the wavefronts");
+  static constexpr int BK = 16, NI = KROWS ? R / 16 : BK, L = NI / W;
+  static constexpr int kLanes = KROWS ? 64 : R / 4;  // lanes that load
+  static_assert(R % 64 == 0 && R <= 256 && L * W == NI, "the loads split evenly over the wavefronts");
   using Op = Operand<R, BK, 64 * W, KROWS>;
   const float* base;  // element (r0, k = 0) of the tile's slice
   long long kstep;    // floats between consecutive K-tiles
   unsigned voff[L];   // byte offsets of this lane's 16 bytes from the K-tile's origin
   unsigned lds[L];    // stage-relative LDS byte offsets of the wavefront's loads
+  bool active;        // this lane loads (l < kLanes)
 
   template <bool GUARD>
   __device__ __forceinline__ void init(const float* X, long long ld, int r0, int rows_left, int w, int l) {
@@ -112,6 +115,7 @@ struct DirectOperand {
         uniform64(reinterpret_cast<long long>(KROWS ? X + (long long)r0 * ld : X + r0)));
     kstep = uniform64(KROWS ? BK : BK * ld);
     const int lim = rows_left < R ? rows_left : R;
+    active = l < kLanes;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int j = L * w + i;
@@ -121,7 +125,7 @@ struct DirectOperand {
         voff[i] = (unsigned)((long long)r * ld + 4 * chunk) * 4u;
         lds[i] = (unsigned)(16 * j * BK) * 4u;
       } else {
-        const int c = GUARD ? min(4 * l, lim - 4) : 4 * l;
+        const int c = min(4 * l, (GUARD ? lim : R) - 4);
         voff[i] = (unsigned)((long long)j * ld + c) * 4u;
         lds[i] = (unsigned)(j * Op::STRIDE) * 4u;
       }
@@ -129,13 +133,15 @@ struct DirectOperand {
   }
   // load i of K-tile kt into the stage at LDS byte address `stage`
   __device__ __forceinline__ void load(int i, int kt, unsigned stage) const {
-    lds_dma16(buffer_rsrc(base + (long long)__builtin_amdgcn_readfirstlane(kt) * kstep), stage + lds[i], voff[i]);
+    const v4i rsrc = buffer_rsrc(base + (long long)__builtin_amdgcn_readfirstlane(kt) * kstep);
+    if (kLanes == 64 || active) lds_dma16(rsrc, stage + lds[i], voff[i]);
   }
 };
 
-// K-tiles [kb, ke) of the 256 x 256 tile at (m0, n0), as mfma_tile_pf with WM x WN
-// wavefronts (4 x 2 in the library: two per SIMD, each 64 x 128), KS = 1, BK = 16, with
-// kDirectStages LDS stages filled by LDS-DMA loads.  Tile j lives in stage (j - kb) % NST
+// K-tiles [kb, ke) of the BM x BM tile at (m0, n0), as mfma_tile_pf with WM x WN
+// wavefronts (256: 4 x 2, two per SIMD, each 64 x 128; 128: 2 x 2 of 64 x 64, two
+// workgroups per CU), KS = 1, BK = 16, with kDirectStages LDS stages filled by LDS-DMA
+// loads.  Tile j lives in stage (j - kb) % NST
 // and fragment set (j - kb) % 2.  During K-tile t:
 //   - tile t + NST is loaded into stage t's (its fragments were read during K-tile t - 1,
 //     before the last barrier), one load after every kDirectSpacing-th MFMA;
@@ -145,15 +151,15 @@ struct DirectOperand {
 // (the last NST - 2 K-tiles' loads stay in flight), so that after the barrier tile t + 2
 // is in LDS for every wavefront.  Every K-tile is whole (direct_ok).  GUARD: as mfma_tile_pf's
 // (bit 0 A rows past M, bit 1 B columns past N, bit 2 a launch of full tiles only).
-template <int WM, int WN, bool TA, bool TB, int GUARD>
+template <int BM, int WM, int WN, bool TA, bool TB, int GUARD>
 __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                                  float* part) {
-  constexpr int BM = 256, BN = 256, BK = 16, NST = kDirectStages, SP = kDirectSpacing;
+  constexpr int BN = BM, BK = 16, NST = kDirectStages, SP = kDirectSpacing;
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, 1, TA, TB>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
-  using DA = DirectOperand<!TA, WM * WN>;
-  using DB = DirectOperand<TB, WM * WN>;
+  using DA = DirectOperand<BM, !TA, WM * WN>;
+  using DB = DirectOperand<BN, TB, WM * WN>;
   constexpr int FM = Cfg::FM, FN = Cfg::FN;
   static_assert(Cfg::KG == 1, "BK 16, one k-group per wavefront");
   static_assert(NST * Cfg::kStageFloats * 4 <= 160 * 1024, "stages fit the LDS");

@@ -171,8 +171,8 @@ void mfma_kernel(Problem p, TileMap map) {
   constexpr int kEdgeFloats = kEdges ? kGroups * EdgeTile::kLdsFloats  // >= its reduction floats
                                      : kThin ? thin_red_floats<Cfg::kThreads>() : 0;
   constexpr int kFuseFloats = FUSE ? 2 * Cfg::kStageFloats + 2 * FusedStrip<BK, Cfg::kThreads>::kStageFloats : 0;
-  static_assert(!DIRECT || (BM == 256 && BN == 256 && BK == 16 && KS == 1 && VEC && !FUSE && !SLICED),
-                "the direct pipeline serves the 256 configuration");
+  static_assert(!DIRECT || (BM == BN && BK == 16 && KS == 1 && VEC && !FUSE && !SLICED),
+                "the direct pipeline: square tiles, BK 16, no K split");
   constexpr int kDirectFloats = DIRECT ? kDirectStages * Cfg::kStageFloats : 0;
   constexpr int kFloats0 = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
   constexpr int kFloats1 = kFloats0 > kFuseFloats ? kFloats0 : kFuseFloats;
@@ -192,7 +192,7 @@ void mfma_kernel(Problem p, TileMap map) {
     // guard bits 0-1 (the tile's partial sides), bit 2: the launch has full tiles only
     constexpr int G = decltype(guard)::value | (kGuarded ? 0 : 4);
     if constexpr (DIRECT)
-      mfma_tile_direct<WM, WN, TA, TB, G>(pt, m0, n0, kb, ke, smem, part);
+      mfma_tile_direct<BM, WM, WN, TA, TB, G>(pt, m0, n0, kb, ke, smem, part);
     else if constexpr (PF)
       mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G, FUSE>(
           pt, m0, n0, kb, ke, smem, part, srow0, srows, map.Nf, p.N - map.Nf);
@@ -601,9 +601,9 @@ hipError_t launch_block16(const Problem& p, int batch, hipStream_t stream) {
 //   192: 192 x 192 tiles, 2 x 2 wavefronts of 96 x 96 (144 accumulator registers), BK 16,
 //        one global register set: one workgroup per CU.  Its tile counts fill whole waves
 //        where the others do not (3072^3: 256 tiles).
-//   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64, BK 16, two global register sets;
-//        two workgroups per CU.  At most one tile per CU: 4 x 2 wavefronts of 32 x 64,
-//        one workgroup per CU.
+//   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64, BK 16, two workgroups per CU: the
+//        direct K loop where direct_ok, else two global register sets.  At most one tile
+//        per CU: 4 x 2 wavefronts of 32 x 64, one workgroup per CU, through registers.
 //   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32, two
 //        global register sets; two workgroups per CU.
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
@@ -648,7 +648,11 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
       // other's barrier waits (2048^3: 123.0 us, against 125.2 with 2 x 2 wavefronts and
       // BK 32, and 127.7 with the two-workgroup form; guarded tiles, 1900^3: 116.1 against
       // 121.0 us).  With more tiles the two-workgroup form is as fast or faster (4000^3:
-      // 941 against 956 us for BK 32 at one workgroup per CU).
+      // 941 against 956 us for BK 32 at one workgroup per CU).  The two-workgroup form runs
+      // the direct K loop where the rows allow it (4096^3: 931 against 966 us; 2048 x 4096
+      // x 4096: 474 against 488), the one-layer form does not (2048^3: 124.2 against 123.9
+      // us), nor does the 192 configuration (3072^3: 405 against 399 us; 6144^3: 3193
+      // against 3143): there each SIMD holds one wavefront or one workgroup's two.
       constexpr int em = mfma_edge_min(128);
       const bool exact = p.M % 128 == 0 && p.N % 128 == 0;
       const long long tiles = (long long)((mfma_extent(p.M, 128, exact ? 0 : em) + 127) / 128) *
@@ -656,6 +660,9 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
       if (tiles <= kCUs)
         return exact ? launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, 0, true>(p, batch, stream)
                      : launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, em, true>(p, batch, stream);
+      if (direct_ok(p, batch, 128))
+        return exact ? launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true, true>(p, batch, stream)
+                     : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true, true>(p, batch, stream);
       return exact ? launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true>(p, batch, stream)
                    : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true>(p, batch, stream);
     }

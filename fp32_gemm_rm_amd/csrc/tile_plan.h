@@ -45,6 +45,14 @@ constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 4.0},
                                    {64, 15.3, 16.0, 0.0},
                                    {32, 5.4, 4.95, 4.0},
                                    {16, 2.6, 2.8, 0.0}};
+// The direct K loops (direct_ok), priced relative to the register-staged ones they
+// replace.  128 configuration, two-workgroup form: u2 3.3% below the staged loop's (net of
+// launch cost, the mean of six shapes timed both ways on one box: 4096^3 931 against 966
+// us, 2048 x 4096 x 4096 474 / 488, 4096 x 2048 x 2048 237 / 247, 2816^3 326 / 337,
+// 1024 x 8192 x 1024 122.9 / 126.7, 7168^3 5386 / 5521).  256 configuration (4 x 2
+// wavefronts): 4096^3 906-908 us against 963-966 on staged 128 x 128 tiles on the same
+// boxes, i.e. 0.941 of the 128 configuration's modelled time there.
+constexpr double kDirect128U2 = 57.5, kDirect256U = 224.0;
 
 // MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
 // counts as a tile row (column); a thin strip, which runs beside the MFMA tiles, does not.
@@ -61,11 +69,12 @@ inline long long modelled_thin_wgs(int M, int N, int side) {
   return (Nf < N ? (Mf + 15) / 16 : 0) + (Mf < M ? (N + 15) / 16 : 0);
 }
 
-// Modelled microseconds; M, N, K, batch > 0.  direct: the operands suit the 256
-// configuration's direct K loop (direct_ok), which runs guarded tiles too (4000^3: 892 us
-// against 947 on 128 x 128 tiles; 3900 x 3900 x 3904: 871 against 933; 8000^3: 7089
-// against 7352 on 192 x 192 tiles, while the model keeps 192 for 3000 x 3000 x 3008, 394
-// us against 670 on guarded 256 tiles, whose one layer of 144 tiles leaves CUs idle).
+// Modelled microseconds; M, N, K, batch > 0.  direct: the operands suit the direct K loops
+// (direct_ok): the 256 configuration and the 128 one's two-workgroup form then cost
+// kDirect256U and kDirect128U2, and the 256 configuration runs guarded tiles too (4000^3:
+// 892 us against 947 on 128 x 128 tiles; 3900 x 3900 x 3904: 871 against 933; 8000^3:
+// 7089 against 7352 on 192 x 192 tiles, while the model keeps 192 for 3000 x 3000 x 3008,
+// 394 us against 670 on guarded 256 tiles, whose one layer of 144 tiles leaves CUs idle).
 // Without it the 256 configuration is a candidate only where its tiles cover the matrix,
 // or leave remainders thinner than kThin256 over one layer of tiles (thin strips after
 // the tiles: 4096 x 4100 x 4096 940 us against 969 on 128 x 128 tiles; 4100^3 980 against
@@ -86,7 +95,9 @@ inline double modelled_time(const TileCost& c, int M, int N, int K, int batch, b
   const long long thin_wgs = modelled_thin_wgs(M, N, c.side);
   if (c.side == 256 && thin_wgs > 0 && layers > 1) return 1e30;
   const long long thin_rounds = (thin_wgs * batch + 255) / 256;
-  return ((double)layers * (layers > 1 ? c.u2 : c.u1) + (double)thin_rounds * c.thin) * (double)K / 1024.0;
+  const double u1 = c.side == 256 && direct ? kDirect256U : c.u1;
+  const double u2 = !direct ? c.u2 : c.side == 256 ? kDirect256U : c.side == 128 ? kDirect128U2 : c.u2;
+  return ((double)layers * (layers > 1 ? u2 : u1) + (double)thin_rounds * c.thin) * (double)K / 1024.0;
 }
 
 // Stream-K (256 configuration, batch 1, with a workspace, full tiles only): the K-tiles of

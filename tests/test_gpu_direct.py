@@ -1,4 +1,5 @@
-"""The 256 configuration's two K loops: LDS-DMA loads and register-staged loads.
+"""The two K loops of the 256 configuration, and of the 128 one's two-workgroup form: LDS-DMA
+loads and register-staged loads.
 
 Where every row of A and B is 16-byte aligned, K is a multiple of 16 and the byte offsets
 inside a K-tile fit in 31 bits, the 256 x 256 tiles load their operands straight into LDS
@@ -9,7 +10,10 @@ sum is exact), and, since both read the same LDS layout and add each output's pr
 the same order, the same bits as each other on random inputs too.  Shapes cover fewer
 K-tiles than LDS stages, B stored transposed, and a K tail (both runs then staged).  The
 operand padding is NaN, so a read past a row reaches C.  The direct loop also runs the tiles
-that reach past M or N (guarded tiles, with thin strips for remainders under 16).
+that reach past M or N (guarded tiles, with thin strips for remainders under 16).  The 128
+configuration takes the direct loop in its two-workgroup form (more than 256 tiles) under
+the same conditions; there the register-staged loop runs for rows that are not 16-byte
+aligned.
 """
 import numpy as np
 import pytest
@@ -21,6 +25,7 @@ from .parity import c_window
 pytestmark = pytest.mark.gpu
 
 T256 = 5  # SGEMM_RM_VARIANT_MFMA_T256
+T128 = 6  # SGEMM_RM_VARIANT_MFMA_T128
 # smallest multiple of 4 with 255 * ld * 4 bytes >= 2^31: rows along k this far apart leave
 # the direct pipeline
 HUGE_LD = ((2**31 + 4 * 255 - 1) // (4 * 255) + 3) // 4 * 4
@@ -53,9 +58,10 @@ def _stored_on_device(x, ld):
     return buf
 
 
-def _run(M, N, K, a, lda, b, ldb, tb, c, alpha, beta, ta=0):
-    """C := alpha op(A) op(B) + beta C on the 256 configuration; a is op(A) (M x K), stored
-    transposed (K x M) when ta; b is op(B) (K x N), stored transposed (N x K) when tb."""
+def _run(M, N, K, a, lda, b, ldb, tb, c, alpha, beta, ta=0, variant=T256):
+    """C := alpha op(A) op(B) + beta C on a forced configuration (256 by default); a is op(A)
+    (M x K), stored transposed (K x M) when ta; b is op(B) (K x N), stored transposed (N x K)
+    when tb."""
     import torch
 
     from fp32_gemm_rm_amd.binding import sgemm_rm_op_strided_batched_ex
@@ -65,7 +71,7 @@ def _run(M, N, K, a, lda, b, ldb, tb, c, alpha, beta, ta=0):
     dC = torch.from_numpy(np.ascontiguousarray(c)).to("cuda")
     s = torch.cuda.current_stream()
     sgemm_rm_op_strided_batched_ex(ta, tb, M, N, K, alpha, dA.data_ptr(), lda, 0, dB.data_ptr(), ldb, 0, beta,
-                                   dC.data_ptr(), N, 0, 1, s.cuda_stream, T256)
+                                   dC.data_ptr(), N, 0, 1, s.cuda_stream, variant)
     s.synchronize()
     out = dC.cpu().numpy()
     del dA, dB, dC
@@ -132,3 +138,40 @@ def test_direct_guarded_tiles_integer_exact(oracle, M, N, K, ta, tb):
         got = c_window(staged, M, N, N).astype(np.float64)
         bad = np.argwhere(got != ref)
         assert bad.size == 0, f"staged: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+# (M, N, K, ta, tb) on the 128 configuration, more than 256 tiles (its two-workgroup form):
+# full tiles (272), guarded rows and columns with the last 2 columns of N = 2090 in a thin
+# strip, A or B stored transposed, and a 12-row thin strip below the tiles
+DIRECT128 = [(17 * 128, 16 * 128, 144, 0, 0), (2100, 2090, 160, 0, 0), (2100, 2088, 96, 1, 0),
+             (2100, 2088, 96, 0, 1), (2060, 2100, 48, 1, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,ta,tb", DIRECT128)
+def test_direct_128_integer_exact(oracle, M, N, K, ta, tb):
+    """The 128 configuration's direct loop against the oracle, bit for bit."""
+    print(f"[direct] 128 {M}x{N}x{K} ta={ta} tb={tb}", flush=True)
+    a = integer_matrix(M, K, -4, 4, seed=M + 3 * K)
+    b = integer_matrix(K, N, -4, 4, seed=N + 3 * K)
+    c = integer_matrix(M, N, -4, 4, seed=M + 3 * N)
+    ref, _ = oracle.full(M, N, K, -1.5, a.reshape(-1), K, b.reshape(-1), N, 0.5, c.reshape(-1), N, with_absab=False)
+    lda = _ld4(M if ta else K) + 4
+    ldb = _ld4(K if tb else N) + 4
+    out = _run(M, N, K, a, lda, b, ldb, tb, c, -1.5, 0.5, ta, T128)
+    got = c_window(out, M, N, N).astype(np.float64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+def test_direct_128_and_staged_same_bits():
+    """Random inputs on the 128 configuration's two-workgroup form: the direct loop (rows
+    16-byte aligned) and the register-staged one (lda = K + 1) add the same products in the
+    same order."""
+    M, N, K = 17 * 128, 16 * 128, 16 * 20
+    rng = np.random.default_rng(12)
+    a = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    b = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    c = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    direct = _run(M, N, K, a, K, b, N, 0, c, 1.25, -0.75, 0, T128)
+    staged = _run(M, N, K, a, K + 1, b, N, 0, c, 1.25, -0.75, 0, T128)
+    assert np.array_equal(direct.view(np.uint32), staged.view(np.uint32))
