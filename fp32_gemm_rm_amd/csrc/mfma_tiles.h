@@ -256,18 +256,23 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
     }
     if constexpr (FUSE) fs.template read<S>(a_stage(s), s_stage(s), srow);
   };
-  auto mfmas = [&](auto set) {
+  const int ks_u = __builtin_amdgcn_readfirstlane(ks);  // K-group, as a uniform value
+  // kl: the K-tile's valid k (BK: a full one).  MFMA step e of k-group g takes k = 16g + e
+  // and 16g + 8 + e; where both lie past K their operands are zeros, and the step is
+  // skipped (adding +0 products to an accumulator that starts at +0 changes no bit).
+  auto mfmas = [&](auto set, int kl = BK) {
     constexpr int S = decltype(set)::value;
     if constexpr (FUSE) fs.template fma<S>();
 #pragma unroll
     for (int r = 0; r < KG; ++r)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
+        if (kl >= BK || 16 * (ks_u * KG + r) + e < kl)
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[S][r][i][e], bf[S][r][j][e], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[S][r][i][e], bf[S][r][j][e], acc[i][j], 0, 0, 0);
   };
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
@@ -334,7 +339,7 @@ __device__ __forceinline__ void mfma_tile_pf(const Problem& p, int m0, int n0, i
     if (kt + 2 < ke) store(set, P, kt + 2, std::false_type{});
     if (kt + D < ke) load(set, kt + D);
     if (kt + 1 < ke) frags(std::integral_constant<int, P ^ 1>{}, P ^ 1);
-    mfmas(set);
+    mfmas(set, kt < nfull ? BK : p.K - kt * BK);
     __syncthreads();
   };
   int kt = kb;
