@@ -155,15 +155,19 @@ def test_batched_tensor_binding():
     assert torch.equal(C.cpu(), want)
 
 
-@pytest.mark.parametrize("M,N,K", [(256 + 40, 512 + 24, 144), (300, 256 + 7, 64)])
-def test_batched_direct_guarded_tiles(oracle, M, N, K):
-    """The 256 x 256 configuration forced on entries with 16-byte aligned rows and strides:
-    the LDS-DMA K loop with guarded tiles (remainders of 40 rows and 24 columns; 44 rows)
-    and a thin strip (7 columns), each entry reading its own operands between NaN gaps."""
+@pytest.mark.parametrize("tiles,M,N,K,batch", [(256, 256 + 40, 512 + 24, 144, 3), (256, 300, 256 + 7, 64, 3),
+                                                 (128, 300, 296, 64, 40), (128, 2 * 128 + 9, 3 * 128, 48, 50)])
+def test_batched_direct_guarded_tiles(oracle, tiles, M, N, K, batch):
+    """The 256 x 256 configuration, and the 128 one with more than 256 tiles over the batch
+    (its two-workgroup form), forced on entries with 16-byte aligned rows and strides: the
+    LDS-DMA K loop with guarded tiles (256: remainders of 40 rows and 24 columns; 44 rows;
+    128: 44 rows and 40 columns) and thin strips (7 columns; 9 rows), each entry reading
+    its own operands between NaN gaps."""
+    from fp32_gemm_rm_amd import TILE_VARIANTS
+
     lda, ldb, ldc = K + 4, (N + 7) // 4 * 4, N + 2
     sA, sB, sC = M * lda + 8, K * ldb + 4, M * ldc + 11
-    batch = 3
     A, B, C = make_batched_inputs(batch, M, N, K, lda, ldb, ldc, sA, sB, sC, "uniform", seed=M + K,
                                   c_init="random")
-    out = _run_batched(M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, batch, 5)
+    out = _run_batched(M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, batch, TILE_VARIANTS[tiles])
     _check_entries(oracle, out, M, N, K, 1.5, A, lda, sA, B, ldb, sB, -0.5, C, ldc, sC, range(batch))
