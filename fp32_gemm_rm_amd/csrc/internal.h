@@ -64,17 +64,28 @@ inline bool vec_loads_ok(const Problem& p, int batch) {
 }
 
 // Whether the direct K loop (mfma_direct.h, LDS-DMA loads) of the configuration with
-// tiles of side R (256, 192 or 128; BK 16) can load this problem: 16-byte aligned rows
-// (vec_loads_ok), whole K-tiles (K a multiple of 16: a partial one would need zeros past
+// R x R tiles and K-tiles of BK can load this problem: 16-byte aligned rows
+// (vec_loads_ok), whole K-tiles (K a multiple of BK: a partial one would need zeros past
 // K, which the LDS-DMA loads cannot write; loaded through registers beside them, it made
 // the kernel spill) and every byte offset from a K-tile's origin below 2^31 (the buffer
 // offsets are 32-bit).
-inline bool direct_ok(const Problem& p, int batch, int R = 256) {
-  if (!vec_loads_ok(p, batch) || p.K % 16 != 0) return false;
+inline bool direct_ok(const Problem& p, int batch, int R = 256, int BK = 16) {
+  if (!vec_loads_ok(p, batch) || p.K % BK != 0) return false;
   constexpr long long kLimit = 1LL << 31;
-  const long long a = p.ta ? 15LL * p.lda + R : (R - 1LL) * p.lda + 16;  // floats past the origin
-  const long long b = p.tb ? (R - 1LL) * p.ldb + 16 : 15LL * p.ldb + R;
+  const long long a = p.ta ? (BK - 1LL) * p.lda + R : (R - 1LL) * p.lda + BK;  // floats past the origin
+  const long long b = p.tb ? (R - 1LL) * p.ldb + BK : (BK - 1LL) * p.ldb + R;
   return a * 4 < kLimit && b * 4 < kLimit;
+}
+
+// The configurations whose direct K loop runs a problem, one bit per tile side: the 256
+// configuration wherever direct_ok allows it; the 128 (BK 16) and 64 (BK 32) ones in their
+// two-workgroup forms (more than one tile per CU) and with A stored along k only (with
+// A^T, whose k-rows load through half or a quarter of the lanes, the loop measured 3-5%
+// slower than the register-staged one).
+enum : int { kDirect256 = 1, kDirect128 = 2, kDirect64 = 4 };
+inline int direct_mask(const Problem& p, int batch) {
+  return (direct_ok(p, batch) ? kDirect256 : 0) | (!p.ta && direct_ok(p, batch, 128) ? kDirect128 : 0) |
+         (!p.ta && direct_ok(p, batch, 64, 32) ? kDirect64 : 0);
 }
 
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the launch status.

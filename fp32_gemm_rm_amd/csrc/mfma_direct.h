@@ -1,5 +1,5 @@
-// MFMA SGEMM, the direct-to-LDS K loop (the 256 configuration, and the 128 one's
-// two-workgroup form): the operands of each K-tile go from global memory straight into an
+// MFMA SGEMM, the direct-to-LDS K loop (the 256 configuration, and the 128 and 64 ones'
+// two-workgroup forms): the operands of each K-tile go from global memory straight into an
 // LDS stage (buffer_load_dwordx4 ... lds, gfx950's 128-bit LDS-DMA load), with no register
 // staging and no LDS store instructions.
 #pragma once
@@ -82,24 +82,26 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// One R x 16 operand slice (R a multiple of 64 up to 256) loaded by LDS-DMA by W
-// wavefronts: its stage layout is Operand's (BK = 16), so the fragment reads are unchanged.
-// NI loads per K-tile; wavefront w issues L = NI / W of them, load i being load j = L w + i:
-//   KROWS (A, or B^T): NI = R / 16; load j fills rows 16j .. 16j + 15 (1 KiB), four
-//     16-byte chunks each; lane l takes row 16j + l/4 at chunk position l%4, which holds
-//     chunk (l%4) ^ (l/16) (swz_slot: rows 16 apart share the XOR, (row/4) % 4 = l/16);
-//   otherwise (A^T, or B): NI = 16; load j fills k-row j, R floats, lane l < R/4 taking
+// One R x BK operand slice (R a multiple of 64 up to 256, BK 16 or 32) loaded by LDS-DMA
+// by W wavefronts: its stage layout is Operand's, so the fragment reads are unchanged.  NI
+// loads per K-tile; wavefront w issues L = NI / W of them, load i being load j = L w + i:
+//   KROWS (A, or B^T): NI = R BK / 256; load j fills the RPI = 256 / BK rows from RPI j
+//     (1 KiB), KC = BK / 4 16-byte chunks each; lane l takes row RPI j + l / KC at chunk
+//     position l % KC, which holds the chunk that swz_slot puts there (position XOR the
+//     row's swizzle: for BK 16, (l % 4) ^ (l / 16));
+//   otherwise (A^T, or B): NI = BK; load j fills k-row j, R floats, lane l < R/4 taking
 //     floats 4l .. 4l+3 (the other lanes are masked off; the row's 4 padding words stay
 //     unwritten and unread).
 // GUARD (a tile reaching past M or N): lines at or past lim, the slice's lines inside the
 // matrix, load the last row (KROWS) or the last float4 inside (otherwise; lim is then a
 // multiple of 4), as Operand::load_full does: their values reach only outputs that are not
 // stored.
-template <int R, bool KROWS, int W>
+template <int R, int BK, bool KROWS, int W>
 struct DirectOperand {
-  static constexpr int BK = 16, NI = KROWS ? R / 16 : BK, L = NI / W;
+  static constexpr int KC = BK / 4, RPI = 256 / BK, NI = KROWS ? R * BK / 256 : BK, L = NI / W;
   static constexpr int kLanes = KROWS ? 64 : R / 4;  // lanes that load
-  static_assert(R % 64 == 0 && R <= 256 && L * W == NI, "the loads split evenly over the wavefronts");
+  static_assert(R % 64 == 0 && R <= 256 && (BK == 16 || BK == 32) && L * W == NI,
+                "the loads split evenly over the wavefronts");
   using Op = Operand<R, BK, 64 * W, KROWS>;
   const float* base;  // element (r0, k = 0) of the tile's slice
   long long kstep;    // floats between consecutive K-tiles
@@ -120,10 +122,11 @@ struct DirectOperand {
     for (int i = 0; i < L; ++i) {
       const int j = L * w + i;
       if (KROWS) {
-        const int row = 16 * j + l / 4, chunk = (l % 4) ^ (l / 16);
+        const int row = RPI * j + l / KC, pos = l % KC;
+        const int chunk = pos ^ ((swz_slot<BK>(row, 0) - row * BK) / 4);  // the row's XOR
         const int r = (!GUARD || row < lim) ? row : lim - 1;
         voff[i] = (unsigned)((long long)r * ld + 4 * chunk) * 4u;
-        lds[i] = (unsigned)(16 * j * BK) * 4u;
+        lds[i] = (unsigned)(RPI * j * BK) * 4u;
       } else {
         const int c = min(4 * l, (GUARD ? lim : R) - 4);
         voff[i] = (unsigned)((long long)j * ld + c) * 4u;
@@ -138,40 +141,47 @@ struct DirectOperand {
   }
 };
 
-// K-tiles [kb, ke) of the BM x BM tile at (m0, n0), as mfma_tile_pf with WM x WN
-// wavefronts (256: 4 x 2, two per SIMD, each 64 x 128; 128: 2 x 2 of 64 x 64, two
-// workgroups per CU), KS = 1, BK = 16, with kDirectStages LDS stages filled by LDS-DMA
-// loads.  Tile j lives in stage (j - kb) % NST
-// and fragment set (j - kb) % 2.  During K-tile t:
+// K-tiles [kb, ke) of the BM x BM tile at (m0, n0), as mfma_tile_pf with WM x WN x KS
+// wavefronts (256: 4 x 2, two per SIMD, each 64 x 128; 128: 2 x 2 of 64 x 64 and 64: 2 x 2
+// of 32 x 32 with a 2-way K split, two workgroups per CU), with kDirectStages LDS stages
+// filled by LDS-DMA loads.  Tile j lives in stage (j - kb) % NST and fragment set
+// (j - kb) % 2.  During K-tile t:
 //   - tile t + NST is loaded into stage t's (its fragments were read during K-tile t - 1,
-//     before the last barrier), one load after every kDirectSpacing-th MFMA;
+//     before the last barrier), one load after every SP-th MFMA;
 //   - the fragments of tile t + 1 are read from its stage into the other set;
 //   - the MFMAs of tile t run on their set;
 // and before the barrier that ends it, each wavefront waits for its loads of tile t + 2
 // (the last NST - 2 K-tiles' loads stay in flight), so that after the barrier tile t + 2
-// is in LDS for every wavefront.  Every K-tile is whole (direct_ok).  GUARD: as mfma_tile_pf's
-// (bit 0 A rows past M, bit 1 B columns past N, bit 2 a launch of full tiles only).
-template <int BM, int WM, int WN, bool TA, bool TB, int GUARD>
+// is in LDS for every wavefront.  Every K-tile is whole (direct_ok).  GUARD: as
+// mfma_tile_pf's (bit 0 A rows past M, bit 1 B columns past N, bit 2 a launch of full
+// tiles only).
+template <int BM, int BK, int WM, int WN, int KS, bool TA, bool TB, int GUARD>
 __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                                  float* part) {
-  constexpr int BN = BM, BK = 16, NST = kDirectStages, SP = kDirectSpacing;
-  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, 1, TA, TB>;
+  constexpr int BN = BM, NST = kDirectStages, W = WM * WN * KS;
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
-  using DA = DirectOperand<BM, !TA, WM * WN>;
-  using DB = DirectOperand<BN, TB, WM * WN>;
-  constexpr int FM = Cfg::FM, FN = Cfg::FN;
-  static_assert(Cfg::KG == 1, "BK 16, one k-group per wavefront");
+  using DA = DirectOperand<BM, BK, !TA, W>;
+  using DB = DirectOperand<BN, BK, TB, W>;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, KG = Cfg::KG;
   static_assert(NST * Cfg::kStageFloats * 4 <= 160 * 1024, "stages fit the LDS");
   constexpr int kLoads = DA::L + DB::L;  // LDS-DMA loads per wavefront and K-tile
-  static_assert((kLoads - 1) * SP < 8 * FM * FN, "the loads go out during the K-tile's MFMAs");
+  constexpr int kMfmas = 8 * KG * FM * FN;
+  // one load after every SP-th MFMA, all of them during the K-tile's MFMAs
+  constexpr int SP = kLoads <= 1                                       ? kDirectSpacing
+                     : (kMfmas - 1) / (kLoads - 1) < kDirectSpacing ? (kMfmas - 1) / (kLoads - 1)
+                                                                      : kDirectSpacing;
+  static_assert(SP >= 1 && (kLoads - 1) * SP < kMfmas, "the loads go out during the K-tile's MFMAs");
   auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
   auto b_stage = [&](int s) { return smem + s * Cfg::kStageFloats + OpA::kStageFloats; };
 
   const int t = threadIdx.x, l = t % 64;
   const int w = __builtin_amdgcn_readfirstlane(t / 64);
   const int lr = l % 32, lh = l / 32;
-  const int wm0 = (w / WN) * (BM / WM), wn0 = (w % WN) * (BN / WN);
+  // K-group and spatial position of this wavefront
+  const int ks = KS == 1 ? 0 : w / (WM * WN), sp = KS == 1 ? w : w % (WM * WN);
+  const int wm0 = (sp / WN) * (BM / WM), wn0 = (sp % WN) * (BN / WN);
 
   DA da;
   DB db;
@@ -198,16 +208,19 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  float af[2][FM][8], bf[2][FN][8];
+  float af[2][KG][FM][8], bf[2][KG][FN][8];
   auto frags = [&](auto set, int s) {
     constexpr int S = decltype(set)::value;
-    read_frags<OpA, FM, Cfg::VA>(a_stage(s), wm0, 0, lr, lh, af[S]);
-    read_frags<OpB, FN, Cfg::VB>(b_stage(s), wn0, 0, lr, lh, bf[S]);
+#pragma unroll
+    for (int r = 0; r < KG; ++r) {
+      read_frags<OpA, FM, Cfg::VA>(a_stage(s), wm0, ks * KG + r, lr, lh, af[S][r]);
+      read_frags<OpB, FN, Cfg::VB>(b_stage(s), wn0, ks * KG + r, lr, lh, bf[S][r]);
+    }
   };
   auto mfma = [&](auto set, auto mc) {
     constexpr int S = decltype(set)::value, m = decltype(mc)::value;
-    constexpr int e = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[S][i][e], bf[S][j][e], acc[i][j], 0, 0, 0);
+    constexpr int r = m / (8 * FM * FN), e = (m / (FM * FN)) % 8, i = (m / FN) % FM, j = m % FN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[S][r][i][e], bf[S][r][j][e], acc[i][j], 0, 0, 0);
   };
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
@@ -229,7 +242,11 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
   // steady K-tile (tile kt + NST exists): explicit order, since the compiler
   // cannot place inline assembly among the MFMAs by itself
   constexpr int kLast = (kLoads - 1) * SP;  // the MFMA after which the last load goes
-  constexpr int kMfmas = 8 * FM * FN;
+  constexpr int kRest = kMfmas - kLast - 1;  // MFMAs after it, among which the fragment reads go
+  constexpr int kReads = KG * Cfg::kFragReads;
+  // fragment reads per MFMA: one (the 256 and 128 forms, whose last read or none is left
+  // to the scheduler), or as many as it takes to place them all
+  constexpr int kPer = kReads <= kRest + 1 ? 1 : (kReads + kRest - 1) / (kRest > 0 ? kRest : 1);
   auto steady = [&](auto set, int kt) {
     constexpr int P = decltype(set)::value;
     const int s = (kt - kb) % NST;
@@ -243,9 +260,8 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
       }
     });
     frags(std::integral_constant<int, P ^ 1>{}, (s + 1) % NST);
-    static_for<kMfmas - kLast - 1>(
-        [&](auto mc) { mfma(set, std::integral_constant<int, decltype(mc)::value + kLast + 1>{}); });
-    sched_interleave<0, kMfmas - kLast - 1, 1, Cfg::kFragReads, 0, 0>();
+    static_for<kRest>([&](auto mc) { mfma(set, std::integral_constant<int, decltype(mc)::value + kLast + 1>{}); });
+    if constexpr (kRest > 0) sched_interleave<0, kRest, kPer, kReads, 0, 0>();
     direct_barrier<kLoads * (NST - 2)>();
   };
   auto step = [&](auto set, int kt) {
@@ -265,7 +281,9 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
     step(Set0{}, kt);
     if (kt + 1 < ke) step(Set1{}, kt + 1);
   }
-  finish_acc<BM, BN, WM, WN, 1, FM, FN, Cfg::VA, Cfg::VB, GUARD>(p, acc, smem, m0, n0, part);
+  // the last direct_barrier<0> leaves no load in flight and no fragment read pending, so
+  // finish_acc may pass the K-split partials through the stages
+  finish_acc<BM, BN, WM, WN, KS, FM, FN, Cfg::VA, Cfg::VB, GUARD>(p, acc, smem, m0, n0, part);
 }
 
 }  // namespace mfma_detail

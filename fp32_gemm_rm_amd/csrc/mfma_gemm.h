@@ -171,8 +171,7 @@ void mfma_kernel(Problem p, TileMap map) {
   constexpr int kEdgeFloats = kEdges ? kGroups * EdgeTile::kLdsFloats  // >= its reduction floats
                                      : kThin ? thin_red_floats<Cfg::kThreads>() : 0;
   constexpr int kFuseFloats = FUSE ? 2 * Cfg::kStageFloats + 2 * FusedStrip<BK, Cfg::kThreads>::kStageFloats : 0;
-  static_assert(!DIRECT || (BM == BN && BK == 16 && KS == 1 && VEC && !FUSE && !SLICED),
-                "the direct pipeline: square tiles, BK 16, no K split");
+  static_assert(!DIRECT || (BM == BN && VEC && !FUSE && !SLICED), "the direct pipeline: square tiles");
   constexpr int kDirectFloats = DIRECT ? kDirectStages * Cfg::kStageFloats : 0;
   constexpr int kFloats0 = Cfg::kLdsFloats > kEdgeFloats ? Cfg::kLdsFloats : kEdgeFloats;
   constexpr int kFloats1 = kFloats0 > kFuseFloats ? kFloats0 : kFuseFloats;
@@ -192,7 +191,7 @@ void mfma_kernel(Problem p, TileMap map) {
     // guard bits 0-1 (the tile's partial sides), bit 2: the launch has full tiles only
     constexpr int G = decltype(guard)::value | (kGuarded ? 0 : 4);
     if constexpr (DIRECT)
-      mfma_tile_direct<BM, WM, WN, TA, TB, G>(pt, m0, n0, kb, ke, smem, part);
+      mfma_tile_direct<BM, BK, WM, WN, KS, TA, TB, G>(pt, m0, n0, kb, ke, smem, part);
     else if constexpr (PF)
       mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G, FUSE>(
           pt, m0, n0, kb, ke, smem, part, srow0, srows, map.Nf, p.N - map.Nf);
@@ -605,7 +604,8 @@ hipError_t launch_block16(const Problem& p, int batch, hipStream_t stream) {
 //        direct K loop where direct_ok, else two global register sets.  At most one tile
 //        per CU: 4 x 2 wavefronts of 32 x 64, one workgroup per CU, through registers.
 //   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32, two
-//        global register sets; two workgroups per CU.
+//        workgroups per CU: with more than one tile per CU the direct K loop where
+//        direct_mask allows it, else two global register sets.
 //   32:  32 x 32 tiles, one 32 x 32 block per wavefront and a 4-way K split, BK 64,
 //        256 threads, mfma_tile; four workgroups per CU.
 //   16:  16 x 16 blocks on 16 x 16 x 4 MFMA, K split over 8 wavefronts, no LDS staging
@@ -652,7 +652,9 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
       // the direct K loop where the rows allow it (4096^3: 931 against 966 us; 2048 x 4096
       // x 4096: 474 against 488), the one-layer form does not (2048^3: 124.2 against 123.9
       // us), nor does the 192 configuration (3072^3: 405 against 399 us; 6144^3: 3193
-      // against 3143): there each SIMD holds one wavefront or one workgroup's two.
+      // against 3143): there each SIMD holds one wavefront or one workgroup's two.  With
+      // A^T (k-rows loaded through half the lanes) it is slower too (2048 x 4096 x 4096
+      // TN: 500 against 487 us), so that form keeps the register-staged loop.
       constexpr int em = mfma_edge_min(128);
       const bool exact = p.M % 128 == 0 && p.N % 128 == 0;
       const long long tiles = (long long)((mfma_extent(p.M, 128, exact ? 0 : em) + 127) / 128) *
@@ -660,16 +662,31 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
       if (tiles <= kCUs)
         return exact ? launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, 0, true>(p, batch, stream)
                      : launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, em, true>(p, batch, stream);
-      if (direct_ok(p, batch, 128))
-        return exact ? launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true, true>(p, batch, stream)
-                     : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true, true>(p, batch, stream);
+      if constexpr (!TA) {
+        if (direct_mask(p, batch) & kDirect128)
+          return exact ? launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true, true>(p, batch, stream)
+                       : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true, true>(p, batch, stream);
+      }
       return exact ? launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true>(p, batch, stream)
                    : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true>(p, batch, stream);
     }
-    case 64:
-      if (p.M % 64 == 0 && p.N % 64 == 0)
-        return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true>(p, batch, stream, ws, slices);
-      return launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, mfma_edge_min(64), true>(p, batch, stream, ws, slices);
+    case 64: {
+      // The two-workgroup form (more than one tile per CU) runs the direct K loop where
+      // the rows allow it (2560^3: 273.5 against 284.6 us; 4608^3 1455 against 1518); one
+      // tile per CU does not (1024^3: 20.3 against 19.9 us), nor does A^T (2560^3 322 against
+      // 313 us), whose k-rows load through a quarter of the lanes.
+      constexpr int em = mfma_edge_min(64);
+      const bool exact = p.M % 64 == 0 && p.N % 64 == 0;
+      const long long tiles = (long long)((mfma_extent(p.M, 64, exact ? 0 : em) + 63) / 64) *
+                              ((mfma_extent(p.N, 64, exact ? 0 : em) + 63) / 64) * batch;
+      if constexpr (!TA) {
+        if (tiles > kCUs && (direct_mask(p, batch) & kDirect64))
+          return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true, true>(p, batch, stream, ws, slices)
+                       : launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, em, true, true>(p, batch, stream, ws, slices);
+      }
+      return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true>(p, batch, stream, ws, slices)
+                   : launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, em, true>(p, batch, stream, ws, slices);
+    }
     case 32:
       if (p.M % 32 == 0 && p.N % 32 == 0) return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4>(p, batch, stream);
       return launch_cfg<32, 32, 64, 1, 1, 4, TA, TB, 8, 4, mfma_edge_min(32)>(p, batch, stream);

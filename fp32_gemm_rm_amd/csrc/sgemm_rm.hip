@@ -165,7 +165,7 @@ int launch_batches(Problem p, int batch, hipStream_t stream, int variant, float*
         case SGEMM_RM_VARIANT_AUTO:
         default: {
           const sgemm_impl::TilePlan plan =
-              sgemm_impl::plan_tiles(p.M, p.N, p.K, chunk, ws != nullptr, sgemm_impl::direct_ok(p, chunk));
+              sgemm_impl::plan_tiles(p.M, p.N, p.K, chunk, ws != nullptr, sgemm_impl::direct_mask(p, chunk));
           err = sgemm_impl::launch_mfma(p, chunk, stream, plan.side, plan.stream_k || plan.slices > 1 ? ws : nullptr,
                                         plan.slices);
           break;
@@ -213,7 +213,7 @@ long long workspace_need(const Problem& p, int batch, int variant) {
     return sgemm_impl::k_slices(p.M, p.N, p.K, 1) > 1 ? sgemm_impl::kStreamKBytes : 0;
   if (variant != SGEMM_RM_VARIANT_AUTO && variant != SGEMM_RM_VARIANT_MFMA) return 0;
   if (sgemm_impl::needs_bands(p.M, p.N)) return sgemm_impl::kStreamKBytes;
-  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(p.M, p.N, p.K, 1, true, sgemm_impl::direct_ok(p, 1));
+  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(p.M, p.N, p.K, 1, true, sgemm_impl::direct_mask(p, 1));
   return plan.stream_k || plan.slices > 1 ? sgemm_impl::kStreamKBytes : 0;
 }
 
@@ -249,6 +249,12 @@ int run(const Call& c, const Positions& pos, hipStream_t stream, bool use_scratc
 }
 
 }  // namespace
+
+// The direct loops (direct_mask) of a query's problem, with its operands as torch allocates
+// them: row-major, 16-byte aligned rows.
+static int query_direct(int K) {
+  return (K % 16 == 0 ? sgemm_impl::kDirect256 | sgemm_impl::kDirect128 : 0) | (K % 32 == 0 ? sgemm_impl::kDirect64 : 0);
+}
 
 extern "C" {
 
@@ -345,8 +351,7 @@ long long sgemm_rm_workspace_size(int M, int N, int K, int batch) {
   if (K < 0) return -3;
   if (batch < 0) return -4;
   if (M == 0 || N == 0 || K == 0 || batch == 0) return 0;
-  // operands as torch allocates them: 16-byte aligned rows
-  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(M, N, K, batch, true, K % 16 == 0);
+  const sgemm_impl::TilePlan plan = sgemm_impl::plan_tiles(M, N, K, batch, true, query_direct(K));
   return plan.stream_k || plan.slices > 1 ? sgemm_impl::kStreamKBytes : 0;
 }
 
@@ -356,9 +361,8 @@ int sgemm_rm_plan_tiles(int M, int N, int K, int batch) {
   if (K < 0) return -3;
   if (batch < 0) return -4;
   if (M == 0 || N == 0 || K == 0 || batch == 0) return 0;
-  // operands as torch allocates them: 16-byte aligned rows
   return sgemm_impl::plan_tiles(M, N, K, batch < sgemm_impl::kMaxBatch ? batch : sgemm_impl::kMaxBatch, false,
-                                K % 16 == 0)
+                                query_direct(K))
       .side;
 }
 

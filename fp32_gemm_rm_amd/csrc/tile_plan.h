@@ -52,7 +52,11 @@ constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 4.0},
 // 1024 x 8192 x 1024 122.9 / 126.7, 7168^3 5386 / 5521).  256 configuration (4 x 2
 // wavefronts): 4096^3 906-908 us against 963-966 on staged 128 x 128 tiles on the same
 // boxes, i.e. 0.941 of the 128 configuration's modelled time there.
-constexpr double kDirect128U2 = 57.5, kDirect256U = 224.0;
+// 64 configuration, two-workgroup form: u2 4.4% below the staged loop's on one box (2560^3
+// 273.5 against 284.6 us, 3584^3 701 / 732, 4608^3 1455 / 1518, 2304^3 211.8 / 221.7,
+// 1536 x 4096 x 4096 374 / 388: 15.3), 15.7-16.4 on another (eight squares and
+// rectangles from 2560 to 7168, next to 57.4-60.3 for the 128 form there).
+constexpr double kDirect128U2 = 57.5, kDirect256U = 224.0, kDirect64U2 = 15.6;
 
 // MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
 // counts as a tile row (column); a thin strip, which runs beside the MFMA tiles, does not.
@@ -69,9 +73,10 @@ inline long long modelled_thin_wgs(int M, int N, int side) {
   return (Nf < N ? (Mf + 15) / 16 : 0) + (Mf < M ? (N + 15) / 16 : 0);
 }
 
-// Modelled microseconds; M, N, K, batch > 0.  direct: the operands suit the direct K loops
-// (direct_ok): the 256 configuration and the 128 one's two-workgroup form then cost
-// kDirect256U and kDirect128U2, and the 256 configuration runs guarded tiles too (4000^3:
+// Modelled microseconds; M, N, K, batch > 0.  direct: the configurations whose direct K
+// loops run the problem (direct_mask): the 256 configuration and the 128 and 64 ones'
+// two-workgroup forms then cost kDirect256U, kDirect128U2 and kDirect64U2, and the 256
+// configuration runs guarded tiles too (4000^3:
 // 892 us against 947 on 128 x 128 tiles; 3900 x 3900 x 3904: 871 against 933; 8000^3:
 // 7089 against 7352 on 192 x 192 tiles, while the model keeps 192 for 3000 x 3000 x 3008,
 // 394 us against 670 on guarded 256 tiles, whose one layer of 144 tiles leaves CUs idle).
@@ -82,9 +87,10 @@ inline long long modelled_thin_wgs(int M, int N, int side) {
 // cannot share a CU with its workgroups and are latency-bound chains of K-steps (4000^3:
 // 1434 us, against 949 us on 128 x 128 tiles; 4090^3: 1887 against 1021 us).  A guarded
 // 256 x 256 tile costs a whole tile, as in the other configurations.
-inline double modelled_time(const TileCost& c, int M, int N, int K, int batch, bool direct = false) {
-  if (c.side == 256 && !direct && !thin256(M, N)) return 1e30;
-  const int em = c.side == 256 ? (direct ? kThin256 : 0) : mfma_edge_min(c.side);
+inline double modelled_time(const TileCost& c, int M, int N, int K, int batch, int direct = 0) {
+  const bool d256 = (direct & kDirect256) != 0;
+  if (c.side == 256 && !d256 && !thin256(M, N)) return 1e30;
+  const int em = c.side == 256 ? (d256 ? kThin256 : 0) : mfma_edge_min(c.side);
   const long long tiles = modelled_tiles(M, c.side, em) * modelled_tiles(N, c.side, em) * batch;
   const long long layers = (tiles + 255) / 256;
   if (c.side == 16)
@@ -95,8 +101,11 @@ inline double modelled_time(const TileCost& c, int M, int N, int K, int batch, b
   const long long thin_wgs = modelled_thin_wgs(M, N, c.side);
   if (c.side == 256 && thin_wgs > 0 && layers > 1) return 1e30;
   const long long thin_rounds = (thin_wgs * batch + 255) / 256;
-  const double u1 = c.side == 256 && direct ? kDirect256U : c.u1;
-  const double u2 = !direct ? c.u2 : c.side == 256 ? kDirect256U : c.side == 128 ? kDirect128U2 : c.u2;
+  const double u1 = c.side == 256 && d256 ? kDirect256U : c.u1;
+  const double u2 = c.side == 256 && d256                       ? kDirect256U
+                    : c.side == 128 && (direct & kDirect128) != 0 ? kDirect128U2
+                    : c.side == 64 && (direct & kDirect64) != 0   ? kDirect64U2
+                                                                  : c.u2;
   return ((double)layers * (layers > 1 ? u2 : u1) + (double)thin_rounds * c.thin) * (double)K / 1024.0;
 }
 
@@ -109,16 +118,20 @@ inline double modelled_time(const TileCost& c, int M, int N, int K, int batch, b
 // each workgroup's two partial pieces (pipeline fill and 256 KB partial-tile stores) and
 // the fix-up pass (about 45 us for 300 split tiles).  Measured (us, stream-K against the
 // model): 4352 x 4096 x 4096 1079 / 1113, x 8192 2067 / 2116, 4608^3 1423 / 1454, 5120^3
-// 1911 / 1954, 6144^3 3227 / 3296.  With fewer than 256 tiles every tile is split and the
-// pieces' overheads dominate, so stream-K is a candidate only past one full wave.
-// Returns a negative value where it does not apply.
-constexpr double kStreamKCost = 236.0;     // us per 1024 of K per layer of 256 tiles
-constexpr double kStreamKOverhead = 110.0;  // us
-inline double modelled_stream_k_time(int M, int N, int K, int batch) {
+// 1911 / 1954, 6144^3 3227 / 3296.  On the direct K loop (direct: direct_ok; its tile
+// code inlined into the stream-K kernel) the pieces cost less: 4352 x 4096 x 4096 1020 us,
+// 4608^3 1333, 5120^3 1822 (a least-squares fit gives 226 us per layer-1024 and 56 us).
+// With fewer than 256 tiles every tile is split and the pieces' overheads dominate, so
+// stream-K is a candidate only past one full wave.  Returns a negative value where it does
+// not apply.
+constexpr double kStreamKCost = 236.0, kStreamKOverhead = 110.0;               // us per layer-1024, us
+constexpr double kDirectStreamKCost = 228.0, kDirectStreamKOverhead = 50.0;  // on the direct K loop
+inline double modelled_stream_k_time(int M, int N, int K, int batch, bool direct = false) {
   const long long tiles = (long long)(M / 256) * (N / 256);
   if (batch != 1 || M % 256 != 0 || N % 256 != 0) return -1.0;
   if (tiles <= kStreamKWgs || tiles % kStreamKWgs == 0) return -1.0;
-  return (double)tiles / kStreamKWgs * kStreamKCost * (double)K / 1024.0 + kStreamKOverhead;
+  return (double)tiles / kStreamKWgs * (direct ? kDirectStreamKCost : kStreamKCost) * (double)K / 1024.0 +
+         (direct ? kDirectStreamKOverhead : kStreamKOverhead);
 }
 
 // K slices (64 configuration, batch 1, with a workspace): a product of few tiles and long K
@@ -167,7 +180,7 @@ struct TilePlan {
 
 // The configuration with the least modelled time (ties: the larger tile); stream-K and K
 // slices are candidates when a workspace is available; direct as modelled_time's.
-inline TilePlan plan_tiles(int M, int N, int K, int batch, bool workspace = false, bool direct = false) {
+inline TilePlan plan_tiles(int M, int N, int K, int batch, bool workspace = false, int direct = 0) {
   TilePlan best{kTileCosts[0].side, false};
   double t = modelled_time(kTileCosts[0], M, N, K, batch, direct);
   for (const TileCost& c : kTileCosts) {
@@ -175,7 +188,7 @@ inline TilePlan plan_tiles(int M, int N, int K, int batch, bool workspace = fals
     if (tc < t) best = TilePlan{c.side, false}, t = tc;
   }
   if (workspace) {
-    const double tsk = modelled_stream_k_time(M, N, K, batch);
+    const double tsk = modelled_stream_k_time(M, N, K, batch, (direct & kDirect256) != 0);
     if (tsk >= 0.0 && tsk < t) best = TilePlan{256, true}, t = tsk;
     const double tsl = modelled_sliced_time(M, N, K, batch);
     if (tsl >= 0.0 && tsl < t) best = TilePlan{64, false, k_slices(M, N, K, batch)}, t = tsl;

@@ -156,13 +156,14 @@ def test_batched_tensor_binding():
 
 
 @pytest.mark.parametrize("tiles,M,N,K,batch", [(256, 256 + 40, 512 + 24, 144, 3), (256, 300, 256 + 7, 64, 3),
-                                                 (128, 300, 296, 64, 40), (128, 2 * 128 + 9, 3 * 128, 48, 50)])
+                                                 (128, 300, 296, 64, 40), (128, 2 * 128 + 9, 3 * 128, 48, 50),
+                                                 (64, 150, 140, 64, 50)])
 def test_batched_direct_guarded_tiles(oracle, tiles, M, N, K, batch):
-    """The 256 x 256 configuration, and the 128 one with more than 256 tiles over the batch
-    (its two-workgroup form), forced on entries with 16-byte aligned rows and strides: the
+    """The 256 x 256 configuration, and the 128 and 64 ones with more than 256 tiles over the
+    batch (their two-workgroup forms), forced on entries with 16-byte aligned rows and strides: the
     LDS-DMA K loop with guarded tiles (256: remainders of 40 rows and 24 columns; 44 rows;
-    128: 44 rows and 40 columns) and thin strips (7 columns; 9 rows), each entry reading
-    its own operands between NaN gaps."""
+    128: 44 rows and 40 columns; 64: 22 rows) and thin strips (7 columns; 9 rows; 12
+    columns), each entry reading its own operands between NaN gaps."""
     from fp32_gemm_rm_amd import TILE_VARIANTS
 
     lda, ldb, ldc = K + 4, (N + 7) // 4 * 4, N + 2

@@ -1,5 +1,5 @@
-"""The two K loops of the 256 configuration, and of the 128 one's two-workgroup form: LDS-DMA
-loads and register-staged loads.
+"""The two K loops of the 256 configuration, and of the 128 and 64 ones' two-workgroup forms:
+LDS-DMA loads and register-staged loads.
 
 Where every row of A and B is 16-byte aligned, K is a multiple of 16 and the byte offsets
 inside a K-tile fit in 31 bits, the 256 x 256 tiles load their operands straight into LDS
@@ -11,9 +11,9 @@ the same order, the same bits as each other on random inputs too.  Shapes cover 
 K-tiles than LDS stages, B stored transposed, and a K tail (both runs then staged).  The
 operand padding is NaN, so a read past a row reaches C.  The direct loop also runs the tiles
 that reach past M or N (guarded tiles, with thin strips for remainders under 16).  The 128
-configuration takes the direct loop in its two-workgroup form (more than 256 tiles) under
-the same conditions; there the register-staged loop runs for rows that are not 16-byte
-aligned.
+and 64 configurations take the direct loop in their two-workgroup forms (more than 256
+tiles) under the same conditions (the 64 one with K a multiple of 32), with A stored along
+k; there the register-staged loop runs for rows that are not 16-byte aligned and for A^T.
 """
 import numpy as np
 import pytest
@@ -26,6 +26,7 @@ pytestmark = pytest.mark.gpu
 
 T256 = 5  # SGEMM_RM_VARIANT_MFMA_T256
 T128 = 6  # SGEMM_RM_VARIANT_MFMA_T128
+T64 = 7  # SGEMM_RM_VARIANT_MFMA_T64
 # smallest multiple of 4 with 255 * ld * 4 bytes >= 2^31: rows along k this far apart leave
 # the direct pipeline
 HUGE_LD = ((2**31 + 4 * 255 - 1) // (4 * 255) + 3) // 4 * 4
@@ -174,4 +175,42 @@ def test_direct_128_and_staged_same_bits():
     c = rng.uniform(-1, 1, (M, N)).astype(np.float32)
     direct = _run(M, N, K, a, K, b, N, 0, c, 1.25, -0.75, 0, T128)
     staged = _run(M, N, K, a, K + 1, b, N, 0, c, 1.25, -0.75, 0, T128)
+    assert np.array_equal(direct.view(np.uint32), staged.view(np.uint32))
+
+
+# (M, N, K, ta, tb) on the 64 configuration, more than 256 tiles: full tiles (272), thin
+# strips on both sides (remainders 12 and 2), guarded rows and columns with B^T, a single
+# K-tile (fewer than the stages), and two cases on the register-staged loop (A^T; K a
+# multiple of 16 but not of 32)
+DIRECT64 = [(17 * 64, 16 * 64, 96, 0, 0), (1100, 1090, 160, 0, 0), (1130, 1110, 64, 0, 1), (1060, 1060, 32, 0, 0),
+            (1130, 1110, 64, 1, 0), (1100, 1100, 48, 0, 0)]
+
+
+@pytest.mark.parametrize("M,N,K,ta,tb", DIRECT64)
+def test_direct_64_integer_exact(oracle, M, N, K, ta, tb):
+    """The 64 configuration's two-workgroup form against the oracle, bit for bit."""
+    print(f"[direct] 64 {M}x{N}x{K} ta={ta} tb={tb}", flush=True)
+    a = integer_matrix(M, K, -4, 4, seed=M + 5 * K)
+    b = integer_matrix(K, N, -4, 4, seed=N + 5 * K)
+    c = integer_matrix(M, N, -4, 4, seed=M + 5 * N)
+    ref, _ = oracle.full(M, N, K, 1.5, a.reshape(-1), K, b.reshape(-1), N, -0.5, c.reshape(-1), N, with_absab=False)
+    lda = _ld4(M if ta else K) + 4
+    ldb = _ld4(K if tb else N) + 4
+    out = _run(M, N, K, a, lda, b, ldb, tb, c, 1.5, -0.5, ta, T64)
+    got = c_window(out, M, N, N).astype(np.float64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+def test_direct_64_and_staged_same_bits():
+    """Random inputs on the 64 configuration's two-workgroup form: the direct loop and the
+    register-staged one (lda = K + 1) add the same products in the same order, K-split
+    partials included."""
+    M, N, K = 17 * 64, 16 * 64, 32 * 9
+    rng = np.random.default_rng(13)
+    a = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    b = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    c = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    direct = _run(M, N, K, a, K, b, N, 0, c, 1.25, -0.75, 0, T64)
+    staged = _run(M, N, K, a, K + 1, b, N, 0, c, 1.25, -0.75, 0, T64)
     assert np.array_equal(direct.view(np.uint32), staged.view(np.uint32))
