@@ -79,13 +79,11 @@ inline bool direct_ok(const Problem& p, int batch, int R = 256, int BK = 16) {
 
 // The configurations whose direct K loop runs a problem, one bit per tile side: the 256
 // configuration wherever direct_ok allows it; the 128 (BK 16) and 64 (BK 32) ones in their
-// two-workgroup forms (more than one tile per CU) and with A stored along k only (with
-// A^T, whose k-rows load through half or a quarter of the lanes, the loop measured 3-5%
-// slower than the register-staged one).
+// two-workgroup forms (more than one tile per CU; the launchers check that).
 enum : int { kDirect256 = 1, kDirect128 = 2, kDirect64 = 4 };
 inline int direct_mask(const Problem& p, int batch) {
-  return (direct_ok(p, batch) ? kDirect256 : 0) | (!p.ta && direct_ok(p, batch, 128) ? kDirect128 : 0) |
-         (!p.ta && direct_ok(p, batch, 64, 32) ? kDirect64 : 0);
+  return (direct_ok(p, batch) ? kDirect256 : 0) | (direct_ok(p, batch, 128) ? kDirect128 : 0) |
+         (direct_ok(p, batch, 64, 32) ? kDirect64 : 0);
 }
 
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the launch status.

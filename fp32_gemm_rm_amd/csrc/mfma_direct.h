@@ -91,18 +91,20 @@ __device__ __forceinline__ void static_for(F&& f) {
 //     row's swizzle: for BK 16, (l % 4) ^ (l / 16));
 //   otherwise (A^T, or B): NI = BK; load j fills k-row j, R floats, lane l < R/4 taking
 //     floats 4l .. 4l+3 (the other lanes are masked off; the row's 4 padding words stay
-//     unwritten and unread).
+//     unwritten and unread); PACKED (Operand's packed layout, R < 256): NI = R BK / 256,
+//     load j filling the 256 / R k-rows from 256 j / R, every lane loading the 4 floats
+//     that kslot puts at its 16 bytes.
 // GUARD (a tile reaching past M or N): lines at or past lim, the slice's lines inside the
 // matrix, load the last row (KROWS) or the last float4 inside (otherwise; lim is then a
 // multiple of 4), as Operand::load_full does: their values reach only outputs that are not
 // stored.
-template <int R, int BK, bool KROWS, int W>
+template <int R, int BK, bool KROWS, int W, bool PACKED = false>
 struct DirectOperand {
-  static constexpr int KC = BK / 4, RPI = 256 / BK, NI = KROWS ? R * BK / 256 : BK, L = NI / W;
-  static constexpr int kLanes = KROWS ? 64 : R / 4;  // lanes that load
+  static constexpr int KC = BK / 4, RPI = 256 / BK, NI = KROWS || PACKED ? R * BK / 256 : BK, L = NI / W;
+  static constexpr int kLanes = KROWS || PACKED ? 64 : R / 4;  // lanes that load
   static_assert(R % 64 == 0 && R <= 256 && (BK == 16 || BK == 32) && L * W == NI,
                 "the loads split evenly over the wavefronts");
-  using Op = Operand<R, BK, 64 * W, KROWS>;
+  using Op = Operand<R, BK, 64 * W, KROWS, PACKED>;
   const float* base;  // element (r0, k = 0) of the tile's slice
   long long kstep;    // floats between consecutive K-tiles
   unsigned voff[L];   // byte offsets of this lane's 16 bytes from the K-tile's origin
@@ -127,6 +129,13 @@ struct DirectOperand {
         const int r = (!GUARD || row < lim) ? row : lim - 1;
         voff[i] = (unsigned)((long long)r * ld + 4 * chunk) * 4u;
         lds[i] = (unsigned)(RPI * j * BK) * 4u;
+      } else if (PACKED) {
+        // k-row k = (256 / R) j + l / (R / 4); the 16 bytes at column position p hold the
+        // line that kslot stores there
+        const int k = (256 / R) * j + l / (R / 4), p = 4 * (l % (R / 4));
+        const int c = min(p ^ (((k >> 3) & 1) << 5), (GUARD ? lim : R) - 4);
+        voff[i] = (unsigned)((long long)k * ld + c) * 4u;
+        lds[i] = (unsigned)(256 * j) * 4u;
       } else {
         const int c = min(4 * l, (GUARD ? lim : R) - 4);
         voff[i] = (unsigned)((long long)j * ld + c) * 4u;
@@ -159,11 +168,14 @@ template <int BM, int BK, int WM, int WN, int KS, bool TA, bool TB, int GUARD>
 __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                                  float* part) {
   constexpr int BN = BM, NST = kDirectStages, W = WM * WN * KS;
-  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
+  // operands stored along m or n in Operand's packed layout below 256 (one load per 256 / BM
+  // k-rows, every lane loading, instead of one per k-row on BM / 4 lanes)
+  constexpr bool kPacked = BM < 256;
+  using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB, kPacked>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
-  using DA = DirectOperand<BM, BK, !TA, W>;
-  using DB = DirectOperand<BN, BK, TB, W>;
+  using DA = DirectOperand<BM, BK, !TA, W, kPacked && TA>;
+  using DB = DirectOperand<BN, BK, TB, W, kPacked && !TB>;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, KG = Cfg::KG;
   static_assert(NST * Cfg::kStageFloats * 4 <= 160 * 1024, "stages fit the LDS");
   constexpr int kLoads = DA::L + DB::L;  // LDS-DMA loads per wavefront and K-tile

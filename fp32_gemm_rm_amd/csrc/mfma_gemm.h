@@ -652,9 +652,10 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
       // the direct K loop where the rows allow it (4096^3: 931 against 966 us; 2048 x 4096
       // x 4096: 474 against 488), the one-layer form does not (2048^3: 124.2 against 123.9
       // us), nor does the 192 configuration (3072^3: 405 against 399 us; 6144^3: 3193
-      // against 3143): there each SIMD holds one wavefront or one workgroup's two.  With
-      // A^T (k-rows loaded through half the lanes) it is slower too (2048 x 4096 x 4096
-      // TN: 500 against 487 us), so that form keeps the register-staged loop.
+      // against 3143): there each SIMD holds one wavefront or one workgroup's two.  The
+      // operands stored along m or n take the packed layout (one load per two k-rows): with
+      // one k-row per load on half the lanes, A^T ran slower than through registers
+      // (2048 x 4096 x 4096 TN: 500 against 487 us; packed: 469 against 488).
       constexpr int em = mfma_edge_min(128);
       const bool exact = p.M % 128 == 0 && p.N % 128 == 0;
       const long long tiles = (long long)((mfma_extent(p.M, 128, exact ? 0 : em) + 127) / 128) *
@@ -662,28 +663,24 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
       if (tiles <= kCUs)
         return exact ? launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, 0, true>(p, batch, stream)
                      : launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, em, true>(p, batch, stream);
-      if constexpr (!TA) {
-        if (direct_mask(p, batch) & kDirect128)
-          return exact ? launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true, true>(p, batch, stream)
-                       : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true, true>(p, batch, stream);
-      }
+      if (direct_mask(p, batch) & kDirect128)
+        return exact ? launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true, true>(p, batch, stream)
+                     : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true, true>(p, batch, stream);
       return exact ? launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, 0, true>(p, batch, stream)
                    : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true>(p, batch, stream);
     }
     case 64: {
       // The two-workgroup form (more than one tile per CU) runs the direct K loop where
-      // the rows allow it (2560^3: 273.5 against 284.6 us; 4608^3 1455 against 1518); one
-      // tile per CU does not (1024^3: 20.3 against 19.9 us), nor does A^T (2560^3 322 against
-      // 313 us), whose k-rows load through a quarter of the lanes.
+      // the rows allow it (2560^3: 267 against 285 us; 4608^3 1455 against 1518 before the
+      // packed layout; 2560^3 TN 272 against 313); one tile per CU does not (1024^3: 20.3
+      // against 19.9 us).
       constexpr int em = mfma_edge_min(64);
       const bool exact = p.M % 64 == 0 && p.N % 64 == 0;
       const long long tiles = (long long)((mfma_extent(p.M, 64, exact ? 0 : em) + 63) / 64) *
                               ((mfma_extent(p.N, 64, exact ? 0 : em) + 63) / 64) * batch;
-      if constexpr (!TA) {
-        if (tiles > kCUs && (direct_mask(p, batch) & kDirect64))
-          return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true, true>(p, batch, stream, ws, slices)
-                       : launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, em, true, true>(p, batch, stream, ws, slices);
-      }
+      if (tiles > kCUs && (direct_mask(p, batch) & kDirect64))
+        return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true, true>(p, batch, stream, ws, slices)
+                     : launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, em, true, true>(p, batch, stream, ws, slices);
       return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true>(p, batch, stream, ws, slices)
                    : launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, em, true>(p, batch, stream, ws, slices);
     }

@@ -41,13 +41,22 @@ __device__ __forceinline__ float4 load4(const float* p, int left) {
 // the stage holds R rows of BK floats with swizzled 16-byte chunks and a fragment
 // is two 128-bit reads.  Otherwise (A^T, or B) the stage holds BK rows of R floats
 // with stride R + 4, and the fragments of V blocks (frag_line) are eight V-float reads.
-template <int R, int BK, int NT, bool KROWS>
+// PACKED (rows along m or n, R >= 64; the LDS-DMA loads, which write 1 KiB runs): stride R
+// instead, column c of k-row k at c ^ 32 in the k-rows 8-15 of every 16 (kslot): the
+// fragment reads of k and k + 8 (the two lane halves) then fall on different banks, as the
+// 4 padding words make them do otherwise.
+template <int R, int BK, int NT, bool KROWS, bool PACKED = false>
 struct Operand {
   static constexpr int KC = BK / 4;
   static constexpr int LOADS = R * BK / 4 / NT;  // float4 per thread per K-tile
-  static constexpr int STRIDE = KROWS ? BK : R + 4;
-  static constexpr int kStageFloats = KROWS ? R * BK : BK * (R + 4);
+  static constexpr int STRIDE = KROWS ? BK : PACKED ? R : R + 4;
+  static constexpr int kStageFloats = KROWS ? R * BK : BK * STRIDE;
   static_assert(LOADS >= 1 && LOADS * NT * 4 == R * BK, "even load split");
+  static_assert(!PACKED || (!KROWS && R >= 64), "packed rows along m or n, at least 64 floats");
+  // word offset of X(line c, k) in a stage stored along m or n
+  __device__ __forceinline__ static constexpr int kslot(int k, int c) {
+    return k * STRIDE + (PACKED ? c ^ (((k >> 3) & 1) << 5) : c);
+  }
 
   const float* base;  // element (r0, k = 0) of this tile's slice
   long long ld;
@@ -112,7 +121,7 @@ struct Operand {
   __device__ __forceinline__ void store(float* stage) const {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : row[i] * STRIDE + col[i])) =
+      *reinterpret_cast<float4*>(stage + (KROWS ? swz_slot<BK>(row[i], col[i]) : kslot(row[i], col[i]))) =
           reg[SET][i];
   }
   // out[f0 + v][e] = X(c + v, 16g + 8lh + e), v < V, e = 0..7 (stage along m or n only):
@@ -124,7 +133,7 @@ struct Operand {
     static_assert(!KROWS && (V == 2 || V == 4), "vector fragment reads along m or n");
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float* q = stage + (16 * g + 8 * lh + e) * STRIDE + c;
+      const float* q = stage + kslot(16 * g + 8 * lh + e, c);
       if constexpr (V == 4) {
         const float4 x = *reinterpret_cast<const float4*>(q);
         out[f0][e] = x.x; out[f0 + 1][e] = x.y; out[f0 + 2][e] = x.z; out[f0 + 3][e] = x.w;
@@ -143,7 +152,7 @@ struct Operand {
       out[4] = x1.x; out[5] = x1.y; out[6] = x1.z; out[7] = x1.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = stage[(16 * g + 8 * lh + e) * STRIDE + rr];
+      for (int e = 0; e < 8; ++e) out[e] = stage[kslot(16 * g + 8 * lh + e, rr)];
     }
   }
 };
@@ -171,13 +180,14 @@ __device__ __forceinline__ void read_frags(const float* stage, int w0, int g, in
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB>
+// PACKED: the operands stored along m or n take Operand's packed layout (LDS-DMA loads).
+template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, bool PACKED = false>
 struct MfmaCfg {
   static constexpr int KG = BK / (16 * KS);  // 16-deep k-groups per wavefront per K-tile
   static constexpr int kThreads = WM * WN * KS * 64;
   static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;  // 32x32 blocks per wavefront
-  using OpA = Operand<BM, BK, kThreads, !TA>;
-  using OpB = Operand<BN, BK, kThreads, TB>;
+  using OpA = Operand<BM, BK, kThreads, !TA, PACKED && TA>;
+  using OpB = Operand<BN, BK, kThreads, TB, PACKED && !TB>;
   // fragment vector widths (frag_line) of A along m and B along n
   static constexpr int VA = frag_vec(!TA, FM), VB = frag_vec(TB, FN);
   // LDS fragment-read instructions of one wavefront per 16-deep k-group

@@ -55,8 +55,10 @@ constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 4.0},
 // 64 configuration, two-workgroup form: u2 4.4% below the staged loop's on one box (2560^3
 // 273.5 against 284.6 us, 3584^3 701 / 732, 4608^3 1455 / 1518, 2304^3 211.8 / 221.7,
 // 1536 x 4096 x 4096 374 / 388: 15.3), 15.7-16.4 on another (eight squares and
-// rectangles from 2560 to 7168, next to 57.4-60.3 for the 128 form there).
-constexpr double kDirect128U2 = 57.5, kDirect256U = 224.0, kDirect64U2 = 15.6;
+// rectangles from 2560 to 7168, next to 57.4-60.3 for the 128 form there), with B loaded
+// one k-row per instruction; with B in the packed layout 3% less again (2560^3 267 against
+// 276 us).
+constexpr double kDirect128U2 = 57.5, kDirect256U = 224.0, kDirect64U2 = 15.2;
 
 // MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
 // counts as a tile row (column); a thin strip, which runs beside the MFMA tiles, does not.

@@ -12,8 +12,9 @@ K-tiles than LDS stages, B stored transposed, and a K tail (both runs then stage
 operand padding is NaN, so a read past a row reaches C.  The direct loop also runs the tiles
 that reach past M or N (guarded tiles, with thin strips for remainders under 16).  The 128
 and 64 configurations take the direct loop in their two-workgroup forms (more than 256
-tiles) under the same conditions (the 64 one with K a multiple of 32), with A stored along
-k; there the register-staged loop runs for rows that are not 16-byte aligned and for A^T.
+tiles) under the same conditions (the 64 one with K a multiple of 32), their operands stored
+along m or n in a packed, XOR-swizzled LDS layout; there the register-staged loop runs for
+rows that are not 16-byte aligned.
 """
 import numpy as np
 import pytest
@@ -164,24 +165,26 @@ def test_direct_128_integer_exact(oracle, M, N, K, ta, tb):
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
 
 
-def test_direct_128_and_staged_same_bits():
+@pytest.mark.parametrize("ta", [0, 1])
+def test_direct_128_and_staged_same_bits(ta):
     """Random inputs on the 128 configuration's two-workgroup form: the direct loop (rows
-    16-byte aligned) and the register-staged one (lda = K + 1) add the same products in the
-    same order."""
+    16-byte aligned) and the register-staged one (a leading dimension of A one float
+    longer) add the same products in the same order, with A stored along k or along m."""
     M, N, K = 17 * 128, 16 * 128, 16 * 20
-    rng = np.random.default_rng(12)
+    rng = np.random.default_rng(12 + ta)
     a = rng.uniform(-1, 1, (M, K)).astype(np.float32)
     b = rng.uniform(-1, 1, (K, N)).astype(np.float32)
     c = rng.uniform(-1, 1, (M, N)).astype(np.float32)
-    direct = _run(M, N, K, a, K, b, N, 0, c, 1.25, -0.75, 0, T128)
-    staged = _run(M, N, K, a, K + 1, b, N, 0, c, 1.25, -0.75, 0, T128)
+    ld = M if ta else K
+    direct = _run(M, N, K, a, ld, b, N, 0, c, 1.25, -0.75, ta, T128)
+    staged = _run(M, N, K, a, ld + 1, b, N, 0, c, 1.25, -0.75, ta, T128)
     assert np.array_equal(direct.view(np.uint32), staged.view(np.uint32))
 
 
 # (M, N, K, ta, tb) on the 64 configuration, more than 256 tiles: full tiles (272), thin
-# strips on both sides (remainders 12 and 2), guarded rows and columns with B^T, a single
-# K-tile (fewer than the stages), and two cases on the register-staged loop (A^T; K a
-# multiple of 16 but not of 32)
+# strips on both sides (remainders 12 and 2), guarded rows and columns with B^T and with
+# A^T, a single K-tile (fewer than the stages), and K a multiple of 16 but not of 32 (the
+# register-staged loop)
 DIRECT64 = [(17 * 64, 16 * 64, 96, 0, 0), (1100, 1090, 160, 0, 0), (1130, 1110, 64, 0, 1), (1060, 1060, 32, 0, 0),
             (1130, 1110, 64, 1, 0), (1100, 1100, 48, 0, 0)]
 

@@ -48,7 +48,7 @@ CASES = [
     (5, 0, 1, 256 + 16, 256 + 18, 48, 1, False),  # guarded direct tiles and a 2-column thin strip
     # the 128 configuration's two-workgroup form (more than 256 tiles) through LDS-DMA loads
     (6, 0, 0, 2100, 2090, 160, 1, False), (6, 0, 1, 2060, 2100, 48, 1, False),
-    (6, 1, 1, 2060, 2100, 48, 1, False),  # A^T: the register-staged loop
+    (6, 1, 1, 2060, 2100, 48, 1, False), (7, 1, 0, 1130, 1110, 64, 1, False),  # A^T
     # and the 64 one's (K a multiple of 32)
     (7, 0, 0, 1130, 1110, 64, 1, False), (7, 0, 1, 1100, 1090, 96, 1, False),
     (5, 0, 0, 1024, 1280, 77, 1, True),  # stream-K (256 forced, with a workspace): every tile split
