@@ -1,7 +1,7 @@
-// MFMA SGEMM, the direct-to-LDS K loop (the 256 configuration, and the 128 and 64 ones'
-// two-workgroup forms): the operands of each K-tile go from global memory straight into an
-// LDS stage (buffer_load_dwordx4 ... lds, gfx950's 128-bit LDS-DMA load), with no register
-// staging and no LDS store instructions.
+// MFMA SGEMM, the direct-to-LDS K loop (the 256, 192 and 128 configurations, and the 64
+// one's two-workgroup form): the operands of each K-tile go from global memory straight
+// into an LDS stage (buffer_load_dwordx4 ... lds, gfx950's 128-bit LDS-DMA load), with no
+// register staging and no LDS store instructions.
 #pragma once
 
 #include <type_traits>
@@ -92,8 +92,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 //   otherwise (A^T, or B): NI = BK; load j fills k-row j, R floats, lane l < R/4 taking
 //     floats 4l .. 4l+3 (the other lanes are masked off; the row's 4 padding words stay
 //     unwritten and unread); PACKED (Operand's packed layout, R < 256): NI = R BK / 256,
-//     load j filling the 256 / R k-rows from 256 j / R, every lane loading the 4 floats
-//     that kslot puts at its 16 bytes.
+//     load j filling floats 256 j .. 256 j + 255 of the stage (256 / R k-rows, or parts of
+//     two), every lane loading the 4 floats that kslot puts at its 16 bytes.
 // GUARD (a tile reaching past M or N): lines at or past lim, the slice's lines inside the
 // matrix, load the last row (KROWS) or the last float4 inside (otherwise; lim is then a
 // multiple of 4), as Operand::load_full does: their values reach only outputs that are not
@@ -130,9 +130,9 @@ struct DirectOperand {
         voff[i] = (unsigned)((long long)r * ld + 4 * chunk) * 4u;
         lds[i] = (unsigned)(RPI * j * BK) * 4u;
       } else if (PACKED) {
-        // k-row k = (256 / R) j + l / (R / 4); the 16 bytes at column position p hold the
-        // line that kslot stores there
-        const int k = (256 / R) * j + l / (R / 4), p = 4 * (l % (R / 4));
+        // float 256 j + 4 l of the stage: k-row k, column position p, whose 16 bytes hold the
+        // lines that kslot stores there
+        const int k = (256 * j + 4 * l) / R, p = (256 * j + 4 * l) % R;
         const int c = min(p ^ (((k >> 3) & 1) << 5), (GUARD ? lim : R) - 4);
         voff[i] = (unsigned)((long long)k * ld + c) * 4u;
         lds[i] = (unsigned)(256 * j) * 4u;
@@ -151,9 +151,10 @@ struct DirectOperand {
 };
 
 // K-tiles [kb, ke) of the BM x BM tile at (m0, n0), as mfma_tile_pf with WM x WN x KS
-// wavefronts (256: 4 x 2, two per SIMD, each 64 x 128; 128: 2 x 2 of 64 x 64 and 64: 2 x 2
-// of 32 x 32 with a 2-way K split, two workgroups per CU), with kDirectStages LDS stages
-// filled by LDS-DMA loads.  Tile j lives in stage (j - kb) % NST and fragment set
+// wavefronts (256: 4 x 2, two per SIMD, each 64 x 128; 192: 2 x 2 of 96 x 96; 128: 4 x 2
+// of 32 x 64, or 2 x 2 of 64 x 64 at two workgroups per CU; 64: 2 x 2 of 32 x 32 with a
+// 2-way K split, two workgroups per CU), with kDirectStages LDS stages filled by LDS-DMA
+// loads.  Tile j lives in stage (j - kb) % NST and fragment set
 // (j - kb) % 2.  During K-tile t:
 //   - tile t + NST is loaded into stage t's (its fragments were read during K-tile t - 1,
 //     before the last barrier), one load after every SP-th MFMA;

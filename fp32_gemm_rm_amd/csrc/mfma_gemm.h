@@ -598,11 +598,12 @@ hipError_t launch_block16(const Problem& p, int batch, hipStream_t stream) {
 //        accumulator registers each); otherwise 2 x 2 wavefronts of 128 x 128, one per SIMD
 //        (256 accumulator registers each), loads two K-tiles ahead through registers.
 //   192: 192 x 192 tiles, 2 x 2 wavefronts of 96 x 96 (144 accumulator registers), BK 16,
-//        one global register set: one workgroup per CU.  Its tile counts fill whole waves
-//        where the others do not (3072^3: 256 tiles).
+//        one workgroup per CU: the direct K loop where direct_ok, else one global
+//        register set.  Its tile counts fill whole waves where the others do not (3072^3:
+//        256 tiles).
 //   128: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64, BK 16, two workgroups per CU: the
 //        direct K loop where direct_ok, else two global register sets.  At most one tile
-//        per CU: 4 x 2 wavefronts of 32 x 64, one workgroup per CU, through registers.
+//        per CU: 4 x 2 wavefronts of 32 x 64, one workgroup per CU, the same two loops.
 //   64:  64 x 64 tiles, 2 x 2 wavefronts of 32 x 32 and a 2-way K split, BK 32, two
 //        workgroups per CU: with more than one tile per CU the direct K loop where
 //        direct_mask allows it, else two global register sets.
@@ -639,6 +640,14 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
         return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, kThin256, true>(p, batch, stream);
       return launch_cfg<256, 256, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(256), true>(p, batch, stream, ws);
     case 192:
+      // the direct K loop where the rows allow it: as fast as the register-staged loop with
+      // operands along k (3072^3: 398.9 against 399.2 us), faster with A^T (398.1 against
+      // 407.4 us)
+      if (direct_ok(p, batch, 192)) {
+        if (p.M % 192 == 0 && p.N % 192 == 0)
+          return launch_cfg<192, 192, 16, 2, 2, 1, TA, TB, 8, 1, 0, true, true>(p, batch, stream);
+        return launch_cfg<192, 192, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(192), true, true>(p, batch, stream);
+      }
       if (p.M % 192 == 0 && p.N % 192 == 0)
         return launch_cfg<192, 192, 16, 2, 2, 1, TA, TB, 8, 1, 0, true>(p, batch, stream);
       return launch_cfg<192, 192, 16, 2, 2, 1, TA, TB, 8, 1, mfma_edge_min(192), true>(p, batch, stream);
@@ -648,18 +657,20 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
       // other's barrier waits (2048^3: 123.0 us, against 125.2 with 2 x 2 wavefronts and
       // BK 32, and 127.7 with the two-workgroup form; guarded tiles, 1900^3: 116.1 against
       // 121.0 us).  With more tiles the two-workgroup form is as fast or faster (4000^3:
-      // 941 against 956 us for BK 32 at one workgroup per CU).  The two-workgroup form runs
-      // the direct K loop where the rows allow it (4096^3: 931 against 966 us; 2048 x 4096
-      // x 4096: 474 against 488), the one-layer form does not (2048^3: 124.2 against 123.9
-      // us), nor does the 192 configuration (3072^3: 405 against 399 us; 6144^3: 3193
-      // against 3143): there each SIMD holds one wavefront or one workgroup's two.  The
-      // operands stored along m or n take the packed layout (one load per two k-rows): with
-      // one k-row per load on half the lanes, A^T ran slower than through registers
-      // (2048 x 4096 x 4096 TN: 500 against 487 us; packed: 469 against 488).
+      // 941 against 956 us for BK 32 at one workgroup per CU).  Both forms run the direct K
+      // loop where the rows allow it (two-workgroup form, 4096^3: 931 against 966 us;
+      // 2048 x 4096 x 4096: 474 against 488; one-layer form, 2048^3: 122.4 against 123.7
+      // us), with the operands stored along m or n in the packed layout (one load per two
+      // k-rows): with one k-row per load on half the lanes, the one-layer form ran slower
+      // than through registers (124.2 against 123.9 us), and so did A^T (2048 x 4096 x
+      // 4096 TN: 500 against 487 us; packed: 469 against 488).
       constexpr int em = mfma_edge_min(128);
       const bool exact = p.M % 128 == 0 && p.N % 128 == 0;
       const long long tiles = (long long)((mfma_extent(p.M, 128, exact ? 0 : em) + 127) / 128) *
                               ((mfma_extent(p.N, 128, exact ? 0 : em) + 127) / 128) * batch;
+      if (tiles <= kCUs && (direct_mask(p, batch) & kDirect128))
+        return exact ? launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, 0, true, true>(p, batch, stream)
+                     : launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, em, true, true>(p, batch, stream);
       if (tiles <= kCUs)
         return exact ? launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, 0, true>(p, batch, stream)
                      : launch_cfg<128, 128, 16, 4, 2, 1, TA, TB, 8, 1, em, true>(p, batch, stream);

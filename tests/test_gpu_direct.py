@@ -1,5 +1,5 @@
-"""The two K loops of the 256 configuration, and of the 128 and 64 ones' two-workgroup forms:
-LDS-DMA loads and register-staged loads.
+"""The two K loops of the 256, 192 and 128 configurations and of the 64 one's two-workgroup
+form: LDS-DMA loads and register-staged loads.
 
 Where every row of A and B is 16-byte aligned, K is a multiple of 16 and the byte offsets
 inside a K-tile fit in 31 bits, the 256 x 256 tiles load their operands straight into LDS
@@ -10,9 +10,9 @@ sum is exact), and, since both read the same LDS layout and add each output's pr
 the same order, the same bits as each other on random inputs too.  Shapes cover fewer
 K-tiles than LDS stages, B stored transposed, and a K tail (both runs then staged).  The
 operand padding is NaN, so a read past a row reaches C.  The direct loop also runs the tiles
-that reach past M or N (guarded tiles, with thin strips for remainders under 16).  The 128
-and 64 configurations take the direct loop in their two-workgroup forms (more than 256
-tiles) under the same conditions (the 64 one with K a multiple of 32), their operands stored
+that reach past M or N (guarded tiles, with thin strips for remainders under 16).  The 192
+and 128 configurations, and the 64 one in its two-workgroup form (more than 256 tiles, K a
+multiple of 32), take the direct loop under the same conditions, their operands stored
 along m or n in a packed, XOR-swizzled LDS layout; there the register-staged loop runs for
 rows that are not 16-byte aligned.
 """
@@ -27,6 +27,7 @@ pytestmark = pytest.mark.gpu
 
 T256 = 5  # SGEMM_RM_VARIANT_MFMA_T256
 T128 = 6  # SGEMM_RM_VARIANT_MFMA_T128
+T192 = 9  # SGEMM_RM_VARIANT_MFMA_T192
 T64 = 7  # SGEMM_RM_VARIANT_MFMA_T64
 # smallest multiple of 4 with 255 * ld * 4 bytes >= 2^31: rows along k this far apart leave
 # the direct pipeline
@@ -216,4 +217,43 @@ def test_direct_64_and_staged_same_bits():
     c = rng.uniform(-1, 1, (M, N)).astype(np.float32)
     direct = _run(M, N, K, a, K, b, N, 0, c, 1.25, -0.75, 0, T64)
     staged = _run(M, N, K, a, K + 1, b, N, 0, c, 1.25, -0.75, 0, T64)
+    assert np.array_equal(direct.view(np.uint32), staged.view(np.uint32))
+
+
+# (variant, M, N, K, ta, tb): the 192 configuration (full tiles; guarded rows and columns;
+# A^T or B^T; thin strips of 7 and 3) and the 128 one's one-layer form (one workgroup of
+# 4 x 2 wavefronts per CU: full tiles, guarded A^T B^T, thin strips of 9 and 2)
+DIRECT_MORE = [(T192, 3 * 192, 2 * 192, 144, 0, 0), (T192, 3 * 192 + 40, 2 * 192 + 20, 96, 0, 0),
+               (T192, 420, 400, 64, 1, 0), (T192, 400, 420, 48, 0, 1), (T192, 2 * 192 + 7, 192 + 3, 64, 0, 0),
+               (T128, 3 * 128, 2 * 128, 144, 0, 0), (T128, 300, 296, 64, 1, 1), (T128, 2 * 128 + 9, 3 * 128 + 2, 48, 0, 0)]
+
+
+@pytest.mark.parametrize("variant,M,N,K,ta,tb", DIRECT_MORE)
+def test_direct_192_and_128_one_layer_integer_exact(oracle, variant, M, N, K, ta, tb):
+    """The 192 configuration's and the 128 one-layer form's direct loops against the oracle,
+    bit for bit."""
+    print(f"[direct] variant {variant} {M}x{N}x{K} ta={ta} tb={tb}", flush=True)
+    a = integer_matrix(M, K, -4, 4, seed=M + 9 * K)
+    b = integer_matrix(K, N, -4, 4, seed=N + 9 * K)
+    c = integer_matrix(M, N, -4, 4, seed=M + 9 * N)
+    ref, _ = oracle.full(M, N, K, -1.5, a.reshape(-1), K, b.reshape(-1), N, 0.5, c.reshape(-1), N, with_absab=False)
+    lda = _ld4(M if ta else K) + 4
+    ldb = _ld4(K if tb else N) + 4
+    out = _run(M, N, K, a, lda, b, ldb, tb, c, -1.5, 0.5, ta, variant)
+    got = c_window(out, M, N, N).astype(np.float64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("variant,M,N", [(T192, 2 * 192, 3 * 192), (T128, 2 * 128, 2 * 128)])
+def test_direct_192_and_128_one_layer_same_bits(variant, M, N):
+    """Random inputs: the direct loop and the register-staged one (lda = K + 1) give the same
+    bits on the 192 configuration and the 128 one-layer form."""
+    K = 16 * 21
+    rng = np.random.default_rng(14)
+    a = rng.uniform(-1, 1, (M, K)).astype(np.float32)
+    b = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    c = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    direct = _run(M, N, K, a, K, b, N, 0, c, 1.25, -0.75, 0, variant)
+    staged = _run(M, N, K, a, K + 1, b, N, 0, c, 1.25, -0.75, 0, variant)
     assert np.array_equal(direct.view(np.uint32), staged.view(np.uint32))
