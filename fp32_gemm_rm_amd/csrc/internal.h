@@ -77,9 +77,10 @@ inline bool direct_ok(const Problem& p, int batch, int R = 256, int BK = 16) {
   return a * 4 < kLimit && b * 4 < kLimit;
 }
 
-// The configurations whose direct K loop runs a problem, one bit per tile side: the 256
-// configuration wherever direct_ok allows it; the 128 (BK 16) and 64 (BK 32) ones in their
-// two-workgroup forms (more than one tile per CU; the launchers check that).
+// The configurations whose direct K loop runs a problem and is priced apart (tile_plan.h),
+// one bit per tile side: the 256 and 128 configurations (BK 16) and the 64 one (BK 32),
+// wherever direct_ok allows it.  The 192 configuration's launcher checks direct_ok itself:
+// there the direct loop costs what the register-staged one does.
 enum : int { kDirect256 = 1, kDirect128 = 2, kDirect64 = 4 };
 inline int direct_mask(const Problem& p, int batch) {
   return (direct_ok(p, batch) ? kDirect256 : 0) | (direct_ok(p, batch, 128) ? kDirect128 : 0) |

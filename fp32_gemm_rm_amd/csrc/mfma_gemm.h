@@ -681,15 +681,13 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
                    : launch_cfg<128, 128, 16, 2, 2, 1, TA, TB, 8, 2, em, true>(p, batch, stream);
     }
     case 64: {
-      // The two-workgroup form (more than one tile per CU) runs the direct K loop where
-      // the rows allow it (2560^3: 267 against 285 us; 4608^3 1455 against 1518 before the
-      // packed layout; 2560^3 TN 272 against 313); one tile per CU does not (1024^3: 20.3
-      // against 19.9 us).
+      // The direct K loop where the rows allow it (K a multiple of 32): 2560^3 267 against
+      // 285 us, 4608^3 1455 against 1518 (before the packed layout), 2560^3 TN 272 against
+      // 313; at one tile per CU 1024^3 19.3-19.7 against 20.0-20.1 us (with one k-row of B
+      // per load it had been slower there: 20.3 against 19.9).
       constexpr int em = mfma_edge_min(64);
       const bool exact = p.M % 64 == 0 && p.N % 64 == 0;
-      const long long tiles = (long long)((mfma_extent(p.M, 64, exact ? 0 : em) + 63) / 64) *
-                              ((mfma_extent(p.N, 64, exact ? 0 : em) + 63) / 64) * batch;
-      if (tiles > kCUs && (direct_mask(p, batch) & kDirect64))
+      if (direct_mask(p, batch) & kDirect64)
         return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true, true>(p, batch, stream, ws, slices)
                      : launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, em, true, true>(p, batch, stream, ws, slices);
       return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true>(p, batch, stream, ws, slices)

@@ -58,7 +58,9 @@ constexpr TileCost kTileCosts[] = {{256, 231.0, 231.0, 4.0},
 // rectangles from 2560 to 7168, next to 57.4-60.3 for the 128 form there), with B loaded
 // one k-row per instruction; with B in the packed layout 3% less again (2560^3 267 against
 // 276 us).
-constexpr double kDirect128U2 = 57.5, kDirect256U = 224.0, kDirect64U2 = 15.2;
+// At one tile per CU the 64 configuration's direct loop (packed layout) runs 1024^3 in
+// 19.3-19.7 against 20.0-20.1 us: u1 3% below.
+constexpr double kDirect128U2 = 57.5, kDirect256U = 224.0, kDirect64U2 = 15.2, kDirect64U1 = 14.85;
 
 // MFMA tiles along one dimension of n.  A partial strip that runs as guarded MFMA tiles
 // counts as a tile row (column); a thin strip, which runs beside the MFMA tiles, does not.
@@ -103,7 +105,9 @@ inline double modelled_time(const TileCost& c, int M, int N, int K, int batch, i
   const long long thin_wgs = modelled_thin_wgs(M, N, c.side);
   if (c.side == 256 && thin_wgs > 0 && layers > 1) return 1e30;
   const long long thin_rounds = (thin_wgs * batch + 255) / 256;
-  const double u1 = c.side == 256 && d256 ? kDirect256U : c.u1;
+  const double u1 = c.side == 256 && d256                      ? kDirect256U
+                    : c.side == 64 && (direct & kDirect64) != 0 ? kDirect64U1
+                                                                 : c.u1;
   const double u2 = c.side == 256 && d256                       ? kDirect256U
                     : c.side == 128 && (direct & kDirect128) != 0 ? kDirect128U2
                     : c.side == 64 && (direct & kDirect64) != 0   ? kDirect64U2

@@ -1,5 +1,5 @@
-"""The two K loops of the 256, 192 and 128 configurations and of the 64 one's two-workgroup
-form: LDS-DMA loads and register-staged loads.
+"""The two K loops of the 256, 192, 128 and 64 configurations: LDS-DMA loads and
+register-staged loads.
 
 Where every row of A and B is 16-byte aligned, K is a multiple of 16 and the byte offsets
 inside a K-tile fit in 31 bits, the 256 x 256 tiles load their operands straight into LDS
@@ -10,11 +10,10 @@ sum is exact), and, since both read the same LDS layout and add each output's pr
 the same order, the same bits as each other on random inputs too.  Shapes cover fewer
 K-tiles than LDS stages, B stored transposed, and a K tail (both runs then staged).  The
 operand padding is NaN, so a read past a row reaches C.  The direct loop also runs the tiles
-that reach past M or N (guarded tiles, with thin strips for remainders under 16).  The 192
-and 128 configurations, and the 64 one in its two-workgroup form (more than 256 tiles, K a
-multiple of 32), take the direct loop under the same conditions, their operands stored
-along m or n in a packed, XOR-swizzled LDS layout; there the register-staged loop runs for
-rows that are not 16-byte aligned.
+that reach past M or N (guarded tiles, with thin strips for remainders under 16).  The 192,
+128 and 64 configurations (the last with K a multiple of 32) take the direct loop under the
+same conditions, their operands stored along m or n in a packed, XOR-swizzled LDS layout;
+there the register-staged loop runs for rows that are not 16-byte aligned.
 """
 import numpy as np
 import pytest
@@ -182,12 +181,14 @@ def test_direct_128_and_staged_same_bits(ta):
     assert np.array_equal(direct.view(np.uint32), staged.view(np.uint32))
 
 
-# (M, N, K, ta, tb) on the 64 configuration, more than 256 tiles: full tiles (272), thin
+# (M, N, K, ta, tb) on the 64 configuration, mostly more than 256 tiles: full tiles (272), thin
 # strips on both sides (remainders 12 and 2), guarded rows and columns with B^T and with
 # A^T, a single K-tile (fewer than the stages), and K a multiple of 16 but not of 32 (the
 # register-staged loop)
 DIRECT64 = [(17 * 64, 16 * 64, 96, 0, 0), (1100, 1090, 160, 0, 0), (1130, 1110, 64, 0, 1), (1060, 1060, 32, 0, 0),
-            (1130, 1110, 64, 1, 0), (1100, 1100, 48, 0, 0)]
+            (1130, 1110, 64, 1, 0), (1100, 1100, 48, 0, 0),
+            # one tile per CU: 256 full tiles, and 256 with guarded rows and columns
+            (1024, 1024, 96, 0, 0), (1000, 1000, 64, 0, 0)]
 
 
 @pytest.mark.parametrize("M,N,K,ta,tb", DIRECT64)
