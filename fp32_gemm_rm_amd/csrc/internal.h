@@ -67,10 +67,11 @@ inline bool vec_loads_ok(const Problem& p, int batch) {
 // R x R tiles and K-tiles of BK can load this problem: 16-byte aligned rows
 // (vec_loads_ok), whole K-tiles (K a multiple of BK: a partial one would need zeros past
 // K, which the LDS-DMA loads cannot write; loaded through registers beside them, it made
-// the kernel spill) and every byte offset from a K-tile's origin below 2^31 (the buffer
-// offsets are 32-bit).
-inline bool direct_ok(const Problem& p, int batch, int R = 256, int BK = 16) {
-  if (!vec_loads_ok(p, batch) || p.K % BK != 0) return false;
+// the 256 configuration's kernel spill) unless `tail` (the 64 configuration loads its
+// partial last K-tile through registers), and every byte offset from a K-tile's origin
+// below 2^31 (the buffer offsets are 32-bit).
+inline bool direct_ok(const Problem& p, int batch, int R = 256, int BK = 16, bool tail = false) {
+  if (!vec_loads_ok(p, batch) || (!tail && p.K % BK != 0)) return false;
   constexpr long long kLimit = 1LL << 31;
   const long long a = p.ta ? (BK - 1LL) * p.lda + R : (R - 1LL) * p.lda + BK;  // floats past the origin
   const long long b = p.tb ? (R - 1LL) * p.ldb + BK : (BK - 1LL) * p.ldb + R;
@@ -84,7 +85,7 @@ inline bool direct_ok(const Problem& p, int batch, int R = 256, int BK = 16) {
 enum : int { kDirect256 = 1, kDirect128 = 2, kDirect64 = 4 };
 inline int direct_mask(const Problem& p, int batch) {
   return (direct_ok(p, batch) ? kDirect256 : 0) | (direct_ok(p, batch, 128) ? kDirect128 : 0) |
-         (direct_ok(p, batch, 64, 32) ? kDirect64 : 0);
+         (direct_ok(p, batch, 64, 32, true) ? kDirect64 : 0);
 }
 
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the launch status.

@@ -162,10 +162,10 @@ struct DirectOperand {
 //   - the MFMAs of tile t run on their set;
 // and before the barrier that ends it, each wavefront waits for its loads of tile t + 2
 // (the last NST - 2 K-tiles' loads stay in flight), so that after the barrier tile t + 2
-// is in LDS for every wavefront.  Every K-tile is whole (direct_ok).  GUARD: as
-// mfma_tile_pf's (bit 0 A rows past M, bit 1 B columns past N, bit 2 a launch of full
-// tiles only).
-template <int BM, int BK, int WM, int WN, int KS, bool TA, bool TB, int GUARD>
+// is in LDS for every wavefront.  Every K-tile is whole (direct_ok) but, with TAIL, the
+// last (below).  GUARD: as mfma_tile_pf's (bit 0 A rows past M, bit 1 B columns past N,
+// bit 2 a launch of full tiles only).
+template <int BM, int BK, int WM, int WN, int KS, bool TA, bool TB, int GUARD, bool TAIL = false>
 __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n0, int kb, int ke, float* smem,
                                                  float* part) {
   constexpr int BN = BM, NST = kDirectStages, W = WM * WN * KS;
@@ -238,19 +238,40 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
 
+  // TAIL (a launch whose K is not a multiple of BK, one whole tile per workgroup): the
+  // partial last K-tile goes through registers, loaded at the start with zeros past K
+  // (Operand::load_tail; the loads are unconditional, since loads under a branch would be
+  // waited for where it joins: a range that ended before it would load the last full
+  // K-tile, unused) and stored to stage 0 after the direct loop.
+  constexpr bool kTail = TAIL;
+  const int nfull = p.K / BK;
+  const bool tail = kTail && ke > nfull;
+  const int kend = tail ? nfull : ke;  // the direct loop's K-tiles: [kb, kend)
+  OpA tail_a;
+  OpB tail_b;
+  if constexpr (kTail) {
+    const int k0 = (tail ? nfull : nfull - 1) * BK, kl = tail ? p.K - nfull * BK : BK;
+    tail_a.init(p.A, p.lda, m0, p.M - m0, t);
+    tail_b.init(p.B, p.ldb, n0, p.N - n0, t);
+    tail_a.template load_tail<true, (GUARD & 1) != 0>(k0, kl);
+    tail_b.template load_tail<true, (GUARD & 2) != 0>(k0, kl);
+  }
+
   // prologue: tiles kb .. kb + NST - 1 into stages 0 .. NST - 1; tile kb's fragments
-  const int n = ke - kb;
-  for (int j = 0; j < NST; ++j)
-    if (j < n) fill(kb + j, j);
-  if (n >= NST)
-    direct_barrier<kLoads * (NST - 1)>();
-  else
-    direct_barrier<0>();
-  frags(Set0{}, 0);
-  if (n >= NST)
-    direct_barrier<kLoads * (NST - 2)>();
-  else
-    direct_barrier<0>();
+  const int n = kend - kb;
+  if (!kTail || n > 0) {  // n == 0: a partial K-tile alone
+    for (int j = 0; j < NST; ++j)
+      if (j < n) fill(kb + j, j);
+    if (n >= NST)
+      direct_barrier<kLoads * (NST - 1)>();
+    else
+      direct_barrier<0>();
+    frags(Set0{}, 0);
+    if (n >= NST)
+      direct_barrier<kLoads * (NST - 2)>();
+    else
+      direct_barrier<0>();
+  }
 
   // steady K-tile (tile kt + NST exists): explicit order, since the compiler
   // cannot place inline assembly among the MFMAs by itself
@@ -280,22 +301,37 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
   auto step = [&](auto set, int kt) {
     constexpr int P = decltype(set)::value;
     const int s = (kt - kb) % NST;
-    if (kt + NST < ke) fill(kt + NST, s);
-    if (kt + 1 < ke) frags(std::integral_constant<int, P ^ 1>{}, (s + 1) % NST);
+    if (kt + NST < kend) fill(kt + NST, s);
+    if (kt + 1 < kend) frags(std::integral_constant<int, P ^ 1>{}, (s + 1) % NST);
     static_for<kMfmas>([&](auto mc) { mfma(set, mc); });
     direct_barrier<0>();
   };
   int kt = kb;
-  for (; kt + 1 + NST < ke; kt += 2) {  // tiles kt + NST and kt + NST + 1 are in range
+  for (; kt + 1 + NST < kend; kt += 2) {  // tiles kt + NST and kt + NST + 1 are in range
     steady(Set0{}, kt);
     steady(Set1{}, kt + 1);
   }
-  for (; kt < ke; kt += 2) {
+  for (; kt < kend; kt += 2) {
     step(Set0{}, kt);
-    if (kt + 1 < ke) step(Set1{}, kt + 1);
+    if (kt + 1 < kend) step(Set1{}, kt + 1);
   }
-  // the last direct_barrier<0> leaves no load in flight and no fragment read pending, so
-  // finish_acc may pass the K-split partials through the stages
+  if constexpr (kTail) {
+    if (tail) {  // the stages are free: the last direct_barrier<0> left no read pending
+      tail_a.store(a_stage(0));
+      tail_b.store(b_stage(0));
+      __syncthreads();
+      frags(Set0{}, 0);
+      // MFMA steps whose k all lie past K are skipped, as in mfma_tile_pf
+      const int kl = p.K - nfull * BK, ks_u = __builtin_amdgcn_readfirstlane(ks);
+      static_for<kMfmas>([&](auto mc) {
+        constexpr int m = decltype(mc)::value, r = m / (8 * FM * FN), e = (m / (FM * FN)) % 8;
+        if (16 * (ks_u * KG + r) + e < kl) mfma(Set0{}, mc);
+      });
+      __syncthreads();  // every wavefront's fragment reads done before finish_acc's writes
+    }
+  }
+  // the last direct_barrier<0> (or the tail's barrier) leaves no load in flight and no
+  // fragment read pending, so finish_acc may pass the K-split partials through the stages
   finish_acc<BM, BN, WM, WN, KS, FM, FN, Cfg::VA, Cfg::VB, GUARD>(p, acc, smem, m0, n0, part);
 }
 

@@ -151,10 +151,11 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // PF: the tiles run mfma_tile_pf (one k-group per wavefront and K-tile) instead of mfma_tile.
 // FUSE: the right thin strip is computed inside the tiles (FusedStrip): tile (bm, bn) takes
 // strip rows [bm BM + 4 bn, + 4), and the launch holds no right-strip workgroups.
-// DIRECT (256 configuration, VEC, direct_ok): the tiles run mfma_tile_direct.
+// DIRECT (VEC, direct_ok): the tiles run mfma_tile_direct; 2: with its partial-last-K-tile
+// path (the 64 configuration, K not a multiple of BK).
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
           int EDGE_MIN, bool STREAM_K, bool VEC, bool PF, bool FUSE = false, bool SLICED = false,
-          bool DIRECT = false>
+          int DIRECT = 0>
 __global__ __launch_bounds__(WM* WN* KS * 64) __attribute__((amdgpu_waves_per_eu(MIN_BLOCKS* WM* WN* KS / 4)))
 void mfma_kernel(Problem p, TileMap map) {
   using Cfg = MfmaCfg<BM, BN, BK, WM, WN, KS, TA, TB>;
@@ -191,7 +192,7 @@ void mfma_kernel(Problem p, TileMap map) {
     // guard bits 0-1 (the tile's partial sides), bit 2: the launch has full tiles only
     constexpr int G = decltype(guard)::value | (kGuarded ? 0 : 4);
     if constexpr (DIRECT)
-      mfma_tile_direct<BM, BK, WM, WN, KS, TA, TB, G>(pt, m0, n0, kb, ke, smem, part);
+      mfma_tile_direct<BM, BK, WM, WN, KS, TA, TB, G, DIRECT == 2>(pt, m0, n0, kb, ke, smem, part);
     else if constexpr (PF)
       mfma_tile_pf<BM, BN, BK, WM, WN, KS, (BM == 192 ? 1 : 2), TA, TB, VEC, G, FUSE>(
           pt, m0, n0, kb, ke, smem, part, srow0, srows, map.Nf, p.N - map.Nf);
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(BN / 4 * kSliceGroups) void slice_fixup_kernel(Prob
 // its raw partial tile to ws (slices x tiles x BM x BN floats), and slice_fixup_kernel adds
 // them in slice order and applies alpha and beta.  For products of few tiles and long K.
 template <int BM, int BN, int BK, int WM, int WN, int KS, bool TA, bool TB, int GROUP_M, int MIN_BLOCKS,
-          int EDGE_MIN = 0, bool PF = false, bool DIRECT = false>
+          int EDGE_MIN = 0, bool PF = false, int DIRECT = 0>
 hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws = nullptr, int slices = 1) {
   static_assert(BM == BN && BM % kEdge == 0, "square tiles whose sides are multiples of the edge tile");
   TileMap map;
@@ -496,7 +497,7 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
       if (!grid_fits(blocks, block.x)) return hipErrorInvalidConfiguration;
       if constexpr (DIRECT)
         hipLaunchKernelGGL(
-            (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, 0, true, true, PF, false, false, true>),
+            (mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, 0, true, true, PF, false, false, DIRECT>),
             dim3((unsigned)blocks), block, 0, stream, p, map);
       else if (vec)
         hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, 0, true, true, PF>),
@@ -548,7 +549,7 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   }
   if constexpr (DIRECT) {
     hipLaunchKernelGGL((mfma_kernel<BM, BN, BK, WM, WN, KS, TA, TB, GROUP_M, MIN_BLOCKS, EDGE_MIN, false, true, PF,
-                                    false, false, true>),
+                                    false, false, DIRECT>),
                        grid, block, 0, stream, p, map);
   } else {
     if (vec)
@@ -687,9 +688,13 @@ hipError_t launch_op(const Problem& p, int batch, hipStream_t stream, int tiles,
       // per load it had been slower there: 20.3 against 19.9).
       constexpr int em = mfma_edge_min(64);
       const bool exact = p.M % 64 == 0 && p.N % 64 == 0;
-      if (direct_mask(p, batch) & kDirect64)
+      if (direct_mask(p, batch) & kDirect64) {
+        if (p.K % 32 != 0)  // the partial last K-tile through registers
+          return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true, 2>(p, batch, stream, ws, slices)
+                       : launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, em, true, 2>(p, batch, stream, ws, slices);
         return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true, true>(p, batch, stream, ws, slices)
                      : launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, em, true, true>(p, batch, stream, ws, slices);
+      }
       return exact ? launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, 0, true>(p, batch, stream, ws, slices)
                    : launch_cfg<64, 64, 32, 2, 2, 2, TA, TB, 8, 2, em, true>(p, batch, stream, ws, slices);
     }

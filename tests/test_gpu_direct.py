@@ -11,9 +11,10 @@ the same order, the same bits as each other on random inputs too.  Shapes cover 
 K-tiles than LDS stages, B stored transposed, and a K tail (both runs then staged).  The
 operand padding is NaN, so a read past a row reaches C.  The direct loop also runs the tiles
 that reach past M or N (guarded tiles, with thin strips for remainders under 16).  The 192,
-128 and 64 configurations (the last with K a multiple of 32) take the direct loop under the
-same conditions, their operands stored along m or n in a packed, XOR-swizzled LDS layout;
-there the register-staged loop runs for rows that are not 16-byte aligned.
+128 and 64 configurations take the direct loop under the same conditions (the 64 one loads a
+partial last K-tile through registers), their operands stored along m or n in a packed,
+XOR-swizzled LDS layout; there the register-staged loop runs for rows that are not 16-byte
+aligned.
 """
 import numpy as np
 import pytest
@@ -183,12 +184,14 @@ def test_direct_128_and_staged_same_bits(ta):
 
 # (M, N, K, ta, tb) on the 64 configuration, mostly more than 256 tiles: full tiles (272), thin
 # strips on both sides (remainders 12 and 2), guarded rows and columns with B^T and with
-# A^T, a single K-tile (fewer than the stages), and K a multiple of 16 but not of 32 (the
-# register-staged loop)
+# A^T, a single K-tile (fewer than the stages), and K a multiple of 16 but not of 32
 DIRECT64 = [(17 * 64, 16 * 64, 96, 0, 0), (1100, 1090, 160, 0, 0), (1130, 1110, 64, 0, 1), (1060, 1060, 32, 0, 0),
             (1130, 1110, 64, 1, 0), (1100, 1100, 48, 0, 0),
             # one tile per CU: 256 full tiles, and 256 with guarded rows and columns
-            (1024, 1024, 96, 0, 0), (1000, 1000, 64, 0, 0)]
+            (1024, 1024, 96, 0, 0), (1000, 1000, 64, 0, 0),
+            # a partial last K-tile (through registers): one tile per CU, B^T, A^T B^T, and K
+            # below one K-tile (no direct K-tile at all)
+            (1024, 1024, 999, 0, 0), (1060, 1000, 40, 0, 1), (17 * 64, 16 * 64, 70, 1, 1), (1000, 1100, 21, 1, 0)]
 
 
 @pytest.mark.parametrize("M,N,K,ta,tb", DIRECT64)

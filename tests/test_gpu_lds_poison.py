@@ -53,7 +53,7 @@ CASES = [
     (9, 0, 0, 3 * 192 + 40, 2 * 192 + 20, 96, 1, False), (9, 1, 0, 420, 400, 64, 1, False),
     (6, 1, 1, 300, 296, 64, 1, False),
     # and the 64 one's (K a multiple of 32), with two workgroups per CU or one
-    (7, 0, 0, 1000, 1000, 96, 1, False),
+    (7, 0, 0, 1000, 1000, 96, 1, False), (7, 0, 1, 1060, 1000, 40, 1, False),  # the last with a partial K-tile
     (7, 0, 0, 1130, 1110, 64, 1, False), (7, 0, 1, 1100, 1090, 96, 1, False),
     (5, 0, 0, 1024, 1280, 77, 1, True),  # stream-K (256 forced, with a workspace): every tile split
     (5, 0, 0, 17 * 256, 17 * 256, 40, 1, True),  # stream-K: whole tiles and pieces
