@@ -19,8 +19,10 @@ constexpr int kDirectStages = 4;
 // wavefronts (8 loads, 128 MFMAs per wavefront and K-tile), two runs: after every 1st, 2nd,
 // 4th MFMA 914.6, 913.4, 913.2 us; every 4th, 8th, 16th 909.4, 914.5, 918.5 us; all eight
 // loads before the MFMAs 950.3 us.  On 4 x 2 wavefronts (4 loads, 64 MFMAs): every 4th or
-// 8th 909.1 and 908.5 us.
-constexpr int kDirectSpacing = 4;
+// 8th 909.1 and 908.5 us.  The smaller tiles take one after every 2nd (1024^3 on 64 x 64
+// tiles: 19.0-19.1 against 19.3 us; 2048^3 on 128 x 128: 121.1 against 121.6; 2560^3 on
+// 64 x 64: 265.6 against 264.8).
+constexpr int kDirectSpacing = 4, kDirectSpacingSmall = 2;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -182,9 +184,10 @@ __device__ __forceinline__ void mfma_tile_direct(const Problem& p, int m0, int n
   constexpr int kLoads = DA::L + DB::L;  // LDS-DMA loads per wavefront and K-tile
   constexpr int kMfmas = 8 * KG * FM * FN;
   // one load after every SP-th MFMA, all of them during the K-tile's MFMAs
-  constexpr int SP = kLoads <= 1                                       ? kDirectSpacing
-                     : (kMfmas - 1) / (kLoads - 1) < kDirectSpacing ? (kMfmas - 1) / (kLoads - 1)
-                                                                      : kDirectSpacing;
+  constexpr int kSpacing = BM == 256 ? kDirectSpacing : kDirectSpacingSmall;
+  constexpr int SP = kLoads <= 1                                 ? kSpacing
+                     : (kMfmas - 1) / (kLoads - 1) < kSpacing ? (kMfmas - 1) / (kLoads - 1)
+                                                                : kSpacing;
   static_assert(SP >= 1 && (kLoads - 1) * SP < kMfmas, "the loads go out during the K-tile's MFMAs");
   auto a_stage = [&](int s) { return smem + s * Cfg::kStageFloats; };
   auto b_stage = [&](int s) { return smem + s * Cfg::kStageFloats + OpA::kStageFloats; };
