@@ -519,10 +519,12 @@ hipError_t launch_cfg(const Problem& p, int batch, hipStream_t stream, float* ws
   // tile's end, against strip workgroups that take their own time per K (1000 x 1030 x 999:
   // 23.0 against 24.0 us; x 4000: 70.5 against 74.9 us; x 300: 11.6 against 10.9 us;
   // 1000 x 990 x 129: 8.6 against 7.8 us).  In the 128 configuration it measured slower
-  // (2048 x 4100 x 2048: 253 against 249 us), in the 192 one no faster.
+  // (2048 x 4100 x 2048: 253 against 249 us), in the 192 one no faster.  The direct K loop
+  // with strip workgroups beats it (1000 x 1030 x 999: 22.0-22.1 against 22.8 us), so it
+  // serves the register-staged loop only.
   constexpr int kFuseMinK = 640;
   constexpr int kThreadsPerWg = WM * WN * KS * 64;
-  constexpr bool kCanFuse = BM == 64 && EDGE_MIN > 1 && PF && !TA && !TB && kThreadsPerWg == BK * 16;
+  constexpr bool kCanFuse = BM == 64 && EDGE_MIN > 1 && PF && !TA && !TB && kThreadsPerWg == BK * 16 && !DIRECT;
   bool fuse = false;
   if constexpr (kCanFuse) {
     fuse = map.right_m > 0 && (long long)map.tiles_n * FusedStrip<BK, kThreadsPerWg>::SR >= BM && p.K >= kFuseMinK;
