@@ -80,7 +80,7 @@ enum sgemm_rm_variant {
   /* The MFMA kernel with its tile configuration forced, for tile sweeps (the pages name
      tuning the tile parameters as the next step: the sgemmNN page's closing section): */
   SGEMM_RM_VARIANT_MFMA_T256 = 5, /* 256 x 256 tiles, one workgroup per CU (8 or 4 wavefronts) */
-  SGEMM_RM_VARIANT_MFMA_T128 = 6, /* 128 x 128 tiles, 4 wavefronts of 64 x 64, two workgroups per CU */
+  SGEMM_RM_VARIANT_MFMA_T128 = 6, /* 128 x 128 tiles, two workgroups of 4 wavefronts per CU (8 at one tile per CU) */
   SGEMM_RM_VARIANT_MFMA_T64 = 7,  /* 64 x 64 tiles, 4 x 32 x 32 wavefronts, 2-way in-tile K split */
   SGEMM_RM_VARIANT_MFMA_T32 = 8,  /* 32 x 32 tiles, 4-way in-tile K split */
   SGEMM_RM_VARIANT_MFMA_T192 = 9, /* 192 x 192 tiles, 4 wavefronts of 96 x 96, one workgroup per CU */
