@@ -1,7 +1,7 @@
-// MFMA SGEMM, the direct-to-LDS K loop (the 256, 192 and 128 configurations, and the 64
-// one's two-workgroup form): the operands of each K-tile go from global memory straight
-// into an LDS stage (buffer_load_dwordx4 ... lds, gfx950's 128-bit LDS-DMA load), with no
-// register staging and no LDS store instructions.
+// MFMA SGEMM, the direct-to-LDS K loop (the 256, 192, 128 and 64 configurations): the
+// operands of each K-tile go from global memory straight into an LDS stage
+// (buffer_load_dwordx4 ... lds, gfx950's 128-bit LDS-DMA load), with no register staging
+// and no LDS store instructions.
 #pragma once
 
 #include <type_traits>
@@ -10,7 +10,9 @@
 namespace sgemm_impl {
 namespace mfma_detail {
 
-// LDS stages of the direct pipeline (4 x 32.25 KiB).  A K-tile is loaded NST K-tiles ahead
+// LDS stages of the direct pipeline (4 x 32.25 KiB in the 256 configuration, 4 x 16.5 KiB
+// in the 64 one, whose 5 or 6 stages measured slower: 1024^3 19.4 and 19.6 against 19.1
+// us).  A K-tile is loaded NST K-tiles ahead
 // of its MFMAs, and the wait before each barrier leaves the last NST - 2 K-tiles' loads in
 // flight.  Measured at 4096^3 (a standalone copy on 2 x 2 wavefronts, one load per 1 or 2
 // MFMAs): 3 stages 922, 4 stages 913-915 us.
@@ -93,9 +95,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 //     row's swizzle: for BK 16, (l % 4) ^ (l / 16));
 //   otherwise (A^T, or B): NI = BK; load j fills k-row j, R floats, lane l < R/4 taking
 //     floats 4l .. 4l+3 (the other lanes are masked off; the row's 4 padding words stay
-//     unwritten and unread); PACKED (Operand's packed layout, R < 256): NI = R BK / 256,
-//     load j filling floats 256 j .. 256 j + 255 of the stage (256 / R k-rows, or parts of
-//     two), every lane loading the 4 floats that kslot puts at its 16 bytes.
+//     unwritten and unread: the form of R = 256, where every lane loads; with fewer lanes
+//     it ran slower than register staging); PACKED (Operand's packed layout, R < 256):
+//     NI = R BK / 256, load j filling floats 256 j .. 256 j + 255 of the stage (256 / R
+//     k-rows, or parts of two), every lane loading the 4 floats that kslot puts at its 16
+//     bytes.
 // GUARD (a tile reaching past M or N): lines at or past lim, the slice's lines inside the
 // matrix, load the last row (KROWS) or the last float4 inside (otherwise; lim is then a
 // multiple of 4), as Operand::load_full does: their values reach only outputs that are not
