@@ -40,10 +40,13 @@
 //     no MFMA waits for LDS; the global loads (one K-tile ahead of their LDS stores in
 //     the 192 configuration, two in the others), LDS stores and fragment reads are
 //     interleaved with the MFMAs.  Two LDS stages.
-//   mfma_tile_direct (256 configuration with 16-byte aligned rows, mfma_direct.h): as
-//     mfma_tile_pf, but the operands go from global memory straight to LDS (LDS-DMA
-//     loads, four stages, issued four K-tiles ahead): no register staging, no LDS stores,
-//     and with the registers this frees, two wavefronts per SIMD.
+//   mfma_tile_direct (256, 192, 128 and 64 configurations with 16-byte aligned rows,
+//     mfma_direct.h): as mfma_tile_pf, but the operands go from global memory straight
+//     to LDS (LDS-DMA loads, four stages, issued four K-tiles ahead): no register
+//     staging, no LDS stores, and with the registers this frees, two wavefronts per SIMD
+//     in the 256 configuration.  Below 256 the operands stored along m or n take a packed
+//     B layout (stride BN, columns XOR 32 in k-rows 8-15 of every 16), so that one 1 KiB
+//     load fills whole k-rows.
 // LDS layout:
 //   A tile, BM rows of BK floats (BK/4 16-byte chunks), no padding.  For
 //     BK = 16, chunk c of row r is stored at chunk position c ^ ((r/4) % 4).  On
