@@ -157,10 +157,11 @@ def test_batched_tensor_binding():
 
 @pytest.mark.parametrize("tiles,M,N,K,batch", [(256, 256 + 40, 512 + 24, 144, 3), (256, 300, 256 + 7, 64, 3),
                                                  (128, 300, 296, 64, 40), (128, 2 * 128 + 9, 3 * 128, 48, 50),
-                                                 (64, 150, 140, 64, 50), (64, 150, 140, 68, 50), (64, 300, 200, 96, 2)])
+                                                 (64, 150, 140, 64, 50), (64, 150, 140, 68, 50), (64, 300, 200, 96, 2),
+                                                 (192, 2 * 192 + 40, 192 + 20, 48, 4), (128, 300, 296, 64, 3)])
 def test_batched_direct_guarded_tiles(oracle, tiles, M, N, K, batch):
-    """The 256 x 256 configuration, and the 128 and 64 ones with more than 256 tiles over the
-    batch (their two-workgroup forms), forced on entries with 16-byte aligned rows and strides: the
+    """The 256 x 256 configuration, the 192 one, and the 128 and 64 ones with more than 256
+    tiles over the batch (their two-workgroup forms) or fewer, forced on entries with 16-byte aligned rows and strides: the
     LDS-DMA K loop with guarded tiles (256: remainders of 40 rows and 24 columns; 44 rows;
     128: 44 rows and 40 columns; 64: 22 rows, also with a partial last K-tile, and 44 rows
     at one tile per CU) and thin strips (7 columns; 9 rows; 12 columns; 8 columns), each
