@@ -111,6 +111,19 @@ def test_tile_configurations(oracle, tiles, shape):
     run_case(oracle, *shape, TILES[tiles], seed=tiles + sum(shape))
 
 
+# 16-byte aligned rows (K and N multiples of 4, so K + 4 and N + 4 too): the LDS-DMA K loops,
+# their guarded tiles and thin strips, the packed layout below 256, the 128 configuration's
+# two forms, and the 64 one's partial last K-tile and right strip in workgroups of its own
+DIRECT_SHAPES = [(256, (256 + 40, 512 + 24, 144)), (256, (512, 256, 64)), (192, (2 * 192 + 32, 192 + 20, 96)),
+                 (128, (2 * 128 + 32, 128 + 20, 64)), (128, (2100, 2092, 48)), (64, (3 * 64 + 20, 64 + 8, 96)),
+                 (64, (1000, 1032, 68)), (64, (64 + 20, 16 * 64 + 8, 704))]
+
+
+@pytest.mark.parametrize("tiles,shape", DIRECT_SHAPES)
+def test_direct_loops(oracle, tiles, shape):
+    run_case(oracle, *shape, TILES[tiles], seed=3 * tiles + sum(shape))
+
+
 def test_stream_k(oracle):
     """The stream-K path: 20 full 256 x 256 tiles shared by 256 ranges (partial tiles in
     the workspace, added by the fix-up pass), and a shape with one-tile workgroups, stream-K
